@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba selective-scan forward path on one MI355X.
+
+One step = the whole hot path over one synthetic batch: depthwise causal conv1d
+(width 4) + SiLU, then the selective scan (softplus step sizes, exp(dt A)
+discretisation, the recurrence, C.h + D.u readout, SiLU(z) gate, per-document
+resets, final state).  Inputs are generated on the host with the seeded recipe
+of `workloads`, uploaded once, and are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is tokens/s of the step (conv + scan).  Extra
+objects: `roofline` for the dominant kernel (live HIP-event timing), the HBM
+roofline of the conv + scan pair, per-kernel timings and `cpu_baseline` (the fp64
+oracle timed on this host on a bounded sample).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan fwd tokens/s + % HBM roofline, B=2 L=32K D=1536 N=16 bf16"
+HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def scan_bytes(B, L, D, N, nheads, esz):
+    """Algorithmic HBM bytes of one selective-scan call: every input read once,
+    every output written once (u, delta, z, out, B, C, doc flags, params, state)."""
+    nd = nheads if nheads else D
+    per_token = esz * (D + nd + D + D) + 2 * esz * N + 1
+    params = 4 * ((nheads if nheads else D * N) + D + nd)
+    return B * L * per_token + params + B * D * N * 4
+
+
+def conv_bytes(B, L, D, esz):
+    """Algorithmic HBM bytes of one conv call: x read, u written, doc flags, weights."""
+    return B * L * (2 * esz * D + 1) + D * 5 * 4
+
+
+def scan_alu_flop_eq(B, L, D, N, nheads):
+    """Algorithmic fp32 VALU work of one scan call in flop-equivalents.
+
+    Counted in full-rate VALU issue slots (an FMA is one slot = 2 flops; a
+    transcendental v_exp/v_log/v_rcp runs at quarter rate = 4 slots = 8 flops),
+    so that the chip's 157.3 TFLOP/s fp32 vector peak is the matching ceiling.
+    Per (t, d, n) element, per-channel A: dt*A (1) + exp (4) + dt*u*B (1) + state
+    FMA (1) + C*h FMA (1) = 8 slots.  Scalar-A heads: dt*u*B + two FMAs = 3 slots,
+    plus one exp per (t, head).  Per (t, d): softplus (exp + log + 5) = 13, SiLU
+    (exp + rcp + 2) = 10, dt*u, D*u, gate = 3 slots (softplus per head for heads)."""
+    el = B * L * D * N
+    if nheads == 0:
+        slots = el * 8 + B * L * D * 26
+    else:
+        slots = el * 3 + B * L * D * 13 + B * L * nheads * (13 + 4 + 1)
+    return 2.0 * slots
+
+
+def conv_alu_flop_eq(B, L, D):
+    """4 FMAs + SiLU (exp, rcp, 2 ops) per (t, d) = 14 slots."""
+    return 2.0 * 14 * B * L * D
+
+
+def cpu_baseline(inp, tokens_per_row):
+    """Time the fp64 oracle (conv + scan, as it stands) on the first tokens of every row."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    T = min(tokens_per_row, inp.x.shape[1])
+    sl = slice(0, T)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        u = oracle.causal_conv1d(inp.x[:, sl], inp.conv_w, inp.conv_b, inp.doc_start[:, sl])
+        oracle.selective_scan(u, inp.delta[:, sl], inp.A, inp.B[:, sl], inp.C[:, sl], inp.D, inp.z[:, sl],
+                              inp.delta_bias, True, inp.doc_start[:, sl])
+        dt = time.perf_counter() - t0
+    ntok = inp.x.shape[0] * T
+    return dict(value=ntok / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {T} tokens of each of the {inp.x.shape[0]} rows, all {inp.x.shape[2]} channels "
+                       f"({ntok} tokens, {dt:.1f} s, fp64 numpy, one thread)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="packed_32k",
+                    help="workload name from workloads.CONFIGS (default: the 32K packed bf16 shape)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle sample: tokens per row")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the scan shards trivially over batch rows and channels; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import selective_state_space_23_amd as ssm
+    from workloads import CONFIGS, make_inputs
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import upload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ssm._lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    spec = CONFIGS[args.config]
+    inp = make_inputs(args.config)
+    B, L, D = inp.x.shape
+    N = inp.B.shape[-1]
+    H = inp.nheads
+    esz = 2 if inp.dtype == "bf16" else 4
+    t = upload(inp, dev)
+    u = torch.empty_like(t["x"])
+    out = torch.empty_like(t["x"])
+    fin = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ssm.scan_workspace_bytes(B, L, D, N, H, inp.dtype), 1), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ssm.causal_conv1d_fwd(t["x"], t["conv_w"], t["conv_b"], t["doc_start"], out=u)
+        if ev is not None:
+            ev[1].record()
+        ssm.selective_scan_fwd(u, t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                               t["doc_start"], out=out, final_state=fin, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    conv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+
+    tokens = B * L
+    sb = scan_bytes(B, L, D, N, H, esz)
+    cb = conv_bytes(B, L, D, esz)
+    scan_flops = scan_alu_flop_eq(B, L, D, N, H)
+    scan_tflops = scan_flops / (scan_ms * 1e-3) / 1e12
+    scan_gbs = sb / (scan_ms * 1e-3) / 1e9
+    pair_gbs = (sb + cb) / ((conv_ms + scan_ms) * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inp.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.config, "batch": B, "seqlen": L, "dim": D, "dstate": N, "nheads": H,
+                   "d_conv": 4, "doc_mean_len": spec["docs"], "io_dtype": inp.dtype, "state_dtype": "f32"},
+        "roofline": {
+            "kernel": "selective_scan_fwd (all launches of one call)",
+            "bound": "alu",
+            "achieved": scan_tflops,
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS,
+            "traffic": None,
+            "hbm_achieved_GBs": scan_gbs,
+            "hbm_frac": scan_gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": sb,
+            "algorithmic_flop_eq": scan_flops,
+            "avg_ms": scan_ms,
+        },
+        "hbm_roofline_pair": {
+            "achieved": pair_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pair_gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": sb + cb, "conv_ms": conv_ms, "scan_ms": scan_ms,
+            "conv_GBs": cb / (conv_ms * 1e-3) / 1e9,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

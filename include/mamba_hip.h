@@ -1,0 +1,141 @@
+/*
+ * mamba_hip.h -- C ABI of the MI355X (gfx950) Mamba selective-scan forward path.
+ *
+ * Two operations, each one or more HIP kernel launches on the caller's stream:
+ *
+ *   mamba_causal_conv1d_fwd   depthwise causal conv1d (width 4) + optional SiLU.
+ *       Defined by the "Mamba: Selective State Spaces (S6)" section of the Mamba
+ *       skill page (Conv1d(d_inner, d_inner, d_conv, padding=d_conv-1,
+ *       groups=d_inner), the first L outputs kept, then SiLU) and by the packing
+ *       paragraph of the axolotl "FLA Mamba and Mamba2" page (the convolution
+ *       state starts fresh at every document start).
+ *
+ *   mamba_selective_scan_fwd  the selective scan with input-dependent
+ *       discretisation, D skip and SiLU(z) gate.  Defined by the same skill page:
+ *       S6 block diagram (A_bar_t = exp(dt_t A), B_bar_t = dt_t B_t,
+ *       h_t = A_bar_t * h_{t-1} + B_bar_t x_t, y_t = C_t h_t), "Core Concept"
+ *       (y = C h + D x), the S6 code (dt = softplus(dt), y * silu(z)), the
+ *       "Mamba-2 (SSD)" section (scalar A per head, multi-head, headdim), and the
+ *       packing paragraph (recurrent state restarts at every document start).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never frees or retains them past the call's completion on the stream.
+ *     The library allocates no device memory and keeps no state between calls.
+ *   - Layouts are dense row-major: activations (B, L, D) with D contiguous,
+ *     B and C (B, L, N), A (D, N) or (H,), final state (B, D, N).
+ *   - `dtype` is the storage type of the activations (x, u, delta, B, C, z, out):
+ *     MAMBA_DTYPE_F32 or MAMBA_DTYPE_BF16.  Parameters (conv weight/bias, A, D,
+ *     delta_bias) and the final state are always float32.  All arithmetic and
+ *     the recurrent state are float32; bf16 outputs are rounded to nearest even.
+ *   - doc_start is (B, L) uint8; nonzero marks the first token of a document.
+ *     Token 0 of every row always starts a document.  NULL = one document per row.
+ *     A document start zeroes the conv history and the recurrent state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).
+ *   - Every call validates its arguments before any launch and returns a status
+ *     code; no exception crosses the ABI.  Errors raised by a kernel while it
+ *     runs surface at the caller's next synchronisation, as for any HIP call.
+ *   - Calls are reentrant.  Concurrent calls must not share output or workspace
+ *     buffers.  Inputs and outputs must not overlap.
+ */
+#ifndef MAMBA_HIP_H
+#define MAMBA_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MAMBA_DTYPE_F32 = 0,
+    MAMBA_DTYPE_BF16 = 1
+} mamba_dtype_t;
+
+enum {
+    MAMBA_OK = 0,
+    MAMBA_ERR_INVALID_ARGUMENT = -1, /* null required pointer, bad size, overlap  */
+    MAMBA_ERR_UNSUPPORTED = -2,      /* valid but not implemented (width, N, ...) */
+    MAMBA_ERR_MISALIGNED = -3,       /* pointer alignment below what is required  */
+    MAMBA_ERR_WORKSPACE = -4,        /* workspace missing or too small            */
+    MAMBA_ERR_HIP = -5               /* a HIP launch failed                        */
+};
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int mamba_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* mamba_status_string(int status);
+
+/* Causal depthwise conv1d.
+ *   x         (B, L, D) activations, `dtype`.
+ *   weight    (D, width) float32; weight[d, width-1] multiplies the current token,
+ *             weight[d, width-1-j] the token j steps back (PyTorch Conv1d layout
+ *             with the singleton group dimension dropped).
+ *   bias      (D,) float32 or NULL (zero).
+ *   doc_start (B, L) uint8 or NULL.
+ *   out       (B, L, D), `dtype`: act(bias + sum_j weight[., width-1-j] x[t-j]),
+ *             taps before the start of the token's document read zero;
+ *             act = SiLU if apply_silu else identity.
+ *   width     must be 4.
+ * Alignment: x and out aligned to their element size (16 bytes and D a
+ * multiple of 16 bytes' worth of elements select the vectorised kernel).
+ * Returns MAMBA_OK, or an error before any launch.  B, L or D of 0 is a no-op. */
+int mamba_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                            const uint8_t* doc_start, void* out,
+                            int64_t batch, int64_t seqlen, int64_t dim, int32_t width,
+                            int32_t dtype, int32_t apply_silu, void* stream);
+
+/* Shape of one selective-scan call. */
+typedef struct {
+    int64_t batch;          /* B                                                   */
+    int64_t seqlen;         /* L                                                   */
+    int64_t dim;            /* D: channels (d_inner)                               */
+    int64_t dstate;         /* N: state size per channel                           */
+    int32_t nheads;         /* 0: A is (D, N), delta (B, L, D), delta_bias (D,)    */
+                            /* H > 0: A is (H,), delta (B, L, H), delta_bias (H,), */
+                            /*        channel d belongs to head d / (D / H)        */
+    int32_t ngroups;        /* must be 1: B and C are shared by all channels       */
+    int32_t dtype;          /* mamba_dtype_t of u, delta, B, C, z, out             */
+    int32_t delta_softplus; /* nonzero: dt = softplus(delta + delta_bias)          */
+                            /* zero:    dt = delta + delta_bias                    */
+} mamba_scan_dims_t;
+
+/* Bytes of device workspace mamba_selective_scan_fwd needs for `dims`
+ * (written to *bytes; may be 0).  Returns a status like the launch itself. */
+int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes);
+
+/* Selective scan forward.
+ *   u          (B, L, D)         input x_t of the recurrence (the conv output).
+ *   delta      (B, L, D|H)       raw step size before bias and softplus.
+ *   A          (D, N) | (H,)     float32, the continuous-time decay (pass A < 0,
+ *                                e.g. -exp(A_log)); any finite value is accepted.
+ *   B, C       (B, L, N)         input and output projections, shared by channels.
+ *   D          (D,) float32 or NULL (no skip term).
+ *   z          (B, L, D) or NULL (no gate).
+ *   delta_bias (D|H,) float32 or NULL (zero).
+ *   doc_start  (B, L) uint8 or NULL.
+ *   out        (B, L, D)         y_t * silu(z_t), y_t = C_t . h_t + D u_t.
+ *   final_state (B, D, N) float32 or NULL: h after token L-1 (the state of the
+ *                                last document of each row).
+ *   workspace  device buffer of at least mamba_selective_scan_workspace_bytes
+ *              bytes, 256-byte aligned; contents on entry are ignored, and it is
+ *              scratch for chunk carries during the call.  May be NULL when the
+ *              required size is 0.
+ * Supported: ngroups == 1; N in {4, 8, 16} with nheads == 0; N in {16, 32, 64,
+ * 128} with nheads > 0.  Others return MAMBA_ERR_UNSUPPORTED.
+ * Alignment: activations aligned to their element size; B and C rows must be
+ * 4-byte aligned (N even for bf16).  B, L or D of 0 is a no-op. */
+int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims,
+                             const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D,
+                             const void* z, const float* delta_bias,
+                             const uint8_t* doc_start, void* out, float* final_state,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_HIP_H */

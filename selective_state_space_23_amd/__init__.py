@@ -1,0 +1,172 @@
+"""MI355X (gfx950) Mamba selective-scan forward path.
+
+Python binding over libmamba_hip.so: argument marshalling only.  Every step of
+the computation runs in the library's HIP kernels; PyTorch supplies device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing or the tensors are not on a GPU the calls raise.
+
+    u = causal_conv1d_fwd(x, weight, bias, doc_start)                  # (B, L, D)
+    out, h = selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, doc_start)
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from . import _lib
+from ._lib import MambaArgumentError, MambaError, ScanDims  # noqa: F401
+
+__all__ = [
+    "causal_conv1d_fwd",
+    "selective_scan_fwd",
+    "scan_workspace_bytes",
+    "MambaError",
+    "MambaArgumentError",
+    "library_path",
+    "version",
+]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def version() -> str:
+    v = _lib.load().mamba_version()
+    return f"{v >> 16}.{(v >> 8) & 255}.{v & 255}"
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return _lib.MAMBA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.MAMBA_DTYPE_BF16
+    raise MambaArgumentError(_lib.MAMBA_ERR_INVALID_ARGUMENT, f"unsupported activation dtype {t.dtype}")
+
+
+def _ptr(t, name, device, dtype=None, shape=None) -> Optional[int]:
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _check_device(x):
+    if x.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device (the library has no CPU path)")
+    return x.device
+
+
+def causal_conv1d_fwd(x, weight, bias=None, doc_start=None, apply_silu: bool = True, out=None):
+    """Depthwise causal conv1d (width 4) + SiLU; see mamba_causal_conv1d_fwd.
+
+    x (B, L, D) float32/bfloat16; weight (D, 4) or (D, 1, 4) float32; bias (D,)
+    float32; doc_start (B, L) uint8/bool.  Returns out (B, L, D), x's dtype."""
+    torch = _torch()
+    dev = _check_device(x)
+    if x.dim() != 3:
+        raise ValueError("x must be (B, L, D)")
+    Bt, L, Dm = x.shape
+    if weight.dim() == 3:
+        weight = weight.reshape(weight.shape[0], weight.shape[-1])
+    W = weight.shape[-1]
+    if doc_start is not None and doc_start.dtype == torch.bool:
+        doc_start = doc_start.to(torch.uint8)
+    if out is None:
+        out = torch.empty_like(x)
+    st = _lib.load().mamba_causal_conv1d_fwd(
+        _ptr(x, "x", dev), _ptr(weight, "weight", dev, torch.float32, (Dm, W)),
+        _ptr(bias, "bias", dev, torch.float32, (Dm,)),
+        _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(out, "out", dev, x.dtype, (Bt, L, Dm)), Bt, L, Dm, W, _dtype_code(x), int(bool(apply_silu)),
+        _stream(dev))
+    _lib.check(st, "mamba_causal_conv1d_fwd")
+    return out
+
+
+def _scan_dims(Bt, L, Dm, N, nheads, dtype_code, softplus) -> ScanDims:
+    return ScanDims(batch=Bt, seqlen=L, dim=Dm, dstate=N, nheads=nheads, ngroups=1, dtype=dtype_code,
+                    delta_softplus=int(bool(softplus)))
+
+
+def scan_workspace_bytes(batch, seqlen, dim, dstate, nheads=0, dtype="bf16") -> int:
+    code = _lib.MAMBA_DTYPE_BF16 if dtype == "bf16" else _lib.MAMBA_DTYPE_F32
+    dims = _scan_dims(batch, seqlen, dim, dstate, nheads, code, True)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().mamba_selective_scan_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)),
+               "mamba_selective_scan_workspace_bytes")
+    return int(n.value)
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, doc_start=None,
+                       delta_softplus: bool = True, out=None, final_state=True, workspace=None):
+    """Selective scan forward; see mamba_selective_scan_fwd.
+
+    u, z (B, L, D); delta (B, L, D) with A (D, N), or delta (B, L, H) with A (H,);
+    B, C (B, L, N); D (D,), delta_bias (D,) or (H,), float32.  ``final_state``:
+    True to allocate and return it, False/None to skip, or a (B, D, N) float32
+    tensor to fill.  ``workspace``: optional uint8 device tensor of at least
+    scan_workspace_bytes(...) bytes.  Returns (out, final_state or None)."""
+    torch = _torch()
+    dev = _check_device(u)
+    if u.dim() != 3:
+        raise ValueError("u must be (B, L, D)")
+    Bt, L, Dm = u.shape
+    N = B.shape[-1]
+    nheads = A.shape[0] if A.dim() == 1 else 0
+    nd = nheads if nheads else Dm
+    code = _dtype_code(u)
+    if doc_start is not None and doc_start.dtype == torch.bool:
+        doc_start = doc_start.to(torch.uint8)
+    if out is None:
+        out = torch.empty_like(u)
+    if final_state is True:
+        final_state = torch.empty((Bt, Dm, N), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    dims = _scan_dims(Bt, L, Dm, N, nheads, code, delta_softplus)
+    lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.mamba_selective_scan_workspace_bytes(ctypes.byref(dims), ctypes.byref(need)),
+               "mamba_selective_scan_workspace_bytes")
+    if need.value and workspace is None:
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace, "workspace", dev, torch.uint8) if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    st = lib.mamba_selective_scan_fwd(
+        ctypes.byref(dims),
+        _ptr(u, "u", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(delta, "delta", dev, u.dtype, (Bt, L, nd)),
+        _ptr(A, "A", dev, torch.float32, (nheads,) if nheads else (Dm, N)),
+        _ptr(B, "B", dev, u.dtype, (Bt, L, N)),
+        _ptr(C, "C", dev, u.dtype, (Bt, L, N)),
+        _ptr(D, "D", dev, torch.float32, (Dm,)),
+        _ptr(z, "z", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)),
+        _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(out, "out", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(final_state, "final_state", dev, torch.float32, (Bt, Dm, N)),
+        ws_ptr, ws_bytes, _stream(dev))
+    _lib.check(st, "mamba_selective_scan_fwd")
+    return out, final_state

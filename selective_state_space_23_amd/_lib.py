@@ -1,0 +1,97 @@
+"""ctypes loader for libmamba_hip.so (the C ABI declared in include/mamba_hip.h)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmamba_hip.so")
+
+MAMBA_DTYPE_F32 = 0
+MAMBA_DTYPE_BF16 = 1
+
+MAMBA_OK = 0
+MAMBA_ERR_INVALID_ARGUMENT = -1
+MAMBA_ERR_UNSUPPORTED = -2
+MAMBA_ERR_MISALIGNED = -3
+MAMBA_ERR_WORKSPACE = -4
+MAMBA_ERR_HIP = -5
+
+EXPORTED = (
+    "mamba_version",
+    "mamba_status_string",
+    "mamba_causal_conv1d_fwd",
+    "mamba_selective_scan_workspace_bytes",
+    "mamba_selective_scan_fwd",
+)
+
+
+class ScanDims(ctypes.Structure):
+    """mamba_scan_dims_t"""
+
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("nheads", ctypes.c_int32),
+        ("ngroups", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("delta_softplus", ctypes.c_int32),
+    ]
+
+
+class MambaError(RuntimeError):
+    """A non-zero status returned by the library; ``status`` keeps the code."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class MambaArgumentError(MambaError, ValueError):
+    pass
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library once.  Raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m selective_state_space_23_amd.build` "
+            "(the selective-scan path has no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.mamba_version.argtypes = []
+    lib.mamba_version.restype = ctypes.c_int
+    lib.mamba_status_string.argtypes = [ctypes.c_int]
+    lib.mamba_status_string.restype = ctypes.c_char_p
+    lib.mamba_causal_conv1d_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.mamba_causal_conv1d_fwd.restype = ctypes.c_int
+    lib.mamba_selective_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(sz)]
+    lib.mamba_selective_scan_workspace_bytes.restype = ctypes.c_int
+    lib.mamba_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, sz, vp]
+    lib.mamba_selective_scan_fwd.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().mamba_status_string(int(status)).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def check(status: int, what: str) -> None:
+    if status == MAMBA_OK:
+        return
+    if status in (MAMBA_ERR_INVALID_ARGUMENT, MAMBA_ERR_UNSUPPORTED, MAMBA_ERR_MISALIGNED, MAMBA_ERR_WORKSPACE):
+        raise MambaArgumentError(status, what)
+    raise MambaError(status, what)

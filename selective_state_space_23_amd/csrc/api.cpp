@@ -1,0 +1,162 @@
+// C ABI of the Mamba selective-scan forward path: argument validation and
+// dispatch to the HIP kernels.  Every check runs on the host before any launch,
+// so an invalid call never reaches the GPU.
+#include "../../include/mamba_hip.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;        // channels per row
+constexpr int64_t kMaxElems = int64_t(1) << 40;      // elements per tensor
+constexpr int64_t kMaxSeqlen = 3000000;              // grid.y limits of the kernels
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [p, p + bytes) and [q, q + qbytes) overlap (null or empty ranges never do).
+bool overlap(const void* p, size_t bytes, const void* q, size_t qbytes) {
+    if (!p || !q || bytes == 0 || qbytes == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + qbytes && b < a + bytes;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t c, int64_t* out) {
+    if (a < 0 || b < 0 || c < 0) return false;
+    __int128 r = static_cast<__int128>(a) * b * c;
+    if (r > kMaxElems) return false;
+    *out = static_cast<int64_t>(r);
+    return true;
+}
+
+int check_dims(const mamba_scan_dims_t* d) {
+    if (!d) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (d->batch < 0 || d->seqlen < 0 || d->dim < 0 || d->dstate < 1) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (d->dim > kMaxDim || d->batch > 65535 || d->nheads < 0) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (d->seqlen > kMaxSeqlen) return MAMBA_ERR_UNSUPPORTED;
+    if (d->dtype != MAMBA_DTYPE_F32 && d->dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (d->nheads > 0 && (d->dim % d->nheads) != 0) return MAMBA_ERR_INVALID_ARGUMENT;
+    int64_t n;
+    if (!mul_ok(d->batch, d->seqlen, d->dim, &n)) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (!mul_ok(d->batch, d->seqlen, d->dstate, &n)) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (d->ngroups != 1) return MAMBA_ERR_UNSUPPORTED;
+    if (!mamba::scan_supported(d->dstate, d->nheads)) return MAMBA_ERR_UNSUPPORTED;
+    return MAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char* mamba_status_string(int status) {
+    switch (status) {
+        case MAMBA_OK: return "ok";
+        case MAMBA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MAMBA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MAMBA_ERR_MISALIGNED: return "misaligned pointer";
+        case MAMBA_ERR_WORKSPACE: return "workspace missing or too small";
+        case MAMBA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int mamba_causal_conv1d_fwd(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
+                            void* out, int64_t batch, int64_t seqlen, int64_t dim, int32_t width, int32_t dtype,
+                            int32_t apply_silu, void* stream) {
+    if (batch < 0 || seqlen < 0 || dim < 0) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (width != 4) return MAMBA_ERR_UNSUPPORTED;
+    int64_t n;
+    if (!mul_ok(batch, seqlen, dim, &n) || dim > kMaxDim || batch > 65535) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (seqlen > kMaxSeqlen) return MAMBA_ERR_UNSUPPORTED;
+    if (n == 0) return MAMBA_OK;
+    if (!x || !weight || !out) return MAMBA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(out, esz) || !aligned(weight, 4) || (bias && !aligned(bias, 4)))
+        return MAMBA_ERR_MISALIGNED;
+    const size_t bytes = static_cast<size_t>(n) * esz;
+    if (overlap(x, bytes, out, bytes) || overlap(weight, dim * 16, out, bytes) ||
+        overlap(bias, dim * 4, out, bytes) || overlap(doc_start, batch * seqlen, out, bytes))
+        return MAMBA_ERR_INVALID_ARGUMENT;
+
+    mamba::ConvArgs a;
+    a.x = x; a.weight = weight; a.bias = bias; a.doc_start = doc_start; a.out = out;
+    a.batch = batch; a.seqlen = seqlen; a.dim = dim;
+    a.bf16 = dtype == MAMBA_DTYPE_BF16;
+    const int64_t vec = a.bf16 ? 8 : 4;
+    a.vectorized = (dim % vec) == 0 && aligned(x, 16) && aligned(out, 16);
+    a.apply_silu = apply_silu != 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    return mamba::launch_causal_conv1d(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes) {
+    if (!bytes) return MAMBA_ERR_INVALID_ARGUMENT;
+    *bytes = 0;
+    const int st = check_dims(dims);
+    if (st != MAMBA_OK) return st;
+    *bytes = mamba::scan_workspace_bytes(dims->batch, dims->seqlen, dims->dim, dims->dstate);
+    return MAMBA_OK;
+}
+
+int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, const uint8_t* doc_start, void* out, float* final_state,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = check_dims(dims);
+    if (st != MAMBA_OK) return st;
+    const int64_t Bt = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
+    if (Bt * L * Dm == 0) return MAMBA_OK;
+    if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+    const int64_t nd = dims->nheads ? dims->nheads : Dm;
+    if (!aligned(u, esz) || !aligned(delta, esz) || !aligned(out, esz) || (z && !aligned(z, esz)))
+        return MAMBA_ERR_MISALIGNED;
+    // B and C rows are read as 32-bit words.
+    if (!aligned(B, 4) || !aligned(C, 4) || (N * esz) % 4 != 0) return MAMBA_ERR_MISALIGNED;
+    if (!aligned(A, 4) || (D && !aligned(D, 4)) || (delta_bias && !aligned(delta_bias, 4)) ||
+        (final_state && !aligned(final_state, 4)))
+        return MAMBA_ERR_MISALIGNED;
+
+    const size_t act = static_cast<size_t>(Bt * L * Dm) * esz;
+    const size_t dlt = static_cast<size_t>(Bt * L * nd) * esz;
+    const size_t bc = static_cast<size_t>(Bt * L * N) * esz;
+    const size_t fsb = static_cast<size_t>(Bt * Dm * N) * 4;
+    const size_t abytes = static_cast<size_t>(dims->nheads ? dims->nheads : Dm * N) * 4;
+    const void* ins[] = {u, delta, B, C, z, A, D, delta_bias, doc_start};
+    const size_t insz[] = {act, dlt, bc, bc, act, abytes, static_cast<size_t>(Dm) * 4,
+                           static_cast<size_t>(nd) * 4, static_cast<size_t>(Bt * L)};
+    for (int i = 0; i < 9; ++i) {
+        if (overlap(ins[i], insz[i], out, act)) return MAMBA_ERR_INVALID_ARGUMENT;
+        if (overlap(ins[i], insz[i], final_state, fsb)) return MAMBA_ERR_INVALID_ARGUMENT;
+    }
+    if (overlap(out, act, final_state, fsb)) return MAMBA_ERR_INVALID_ARGUMENT;
+
+    const size_t need = mamba::scan_workspace_bytes(Bt, L, Dm, N);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;
+        for (int i = 0; i < 9; ++i)
+            if (overlap(ins[i], insz[i], workspace, need)) return MAMBA_ERR_INVALID_ARGUMENT;
+        if (overlap(out, act, workspace, need) || overlap(final_state, fsb, workspace, need))
+            return MAMBA_ERR_INVALID_ARGUMENT;
+    }
+
+    mamba::ScanArgs a;
+    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
+    a.delta_bias = delta_bias; a.doc_start = doc_start; a.out = out; a.final_state = final_state;
+    a.ws = static_cast<float*>(workspace);
+    a.batch = Bt; a.seqlen = L; a.dim = Dm; a.dstate = N;
+    a.nheads = dims->nheads;
+    a.bf16 = dims->dtype == MAMBA_DTYPE_BF16;
+    a.softplus = dims->delta_softplus != 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+}  // extern "C"

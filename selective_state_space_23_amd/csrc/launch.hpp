@@ -1,0 +1,56 @@
+// Host-side launch descriptors shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mamba {
+
+struct ConvArgs {
+    const void* x;
+    const float* weight;
+    const float* bias;
+    const uint8_t* doc_start;
+    void* out;
+    int64_t batch, seqlen, dim;
+    bool bf16;
+    bool vectorized;   // 16-byte loads: dim and pointers aligned
+    bool apply_silu;
+    hipStream_t stream;
+};
+
+hipError_t launch_causal_conv1d(const ConvArgs& a);
+
+struct ScanArgs {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* delta_bias;
+    const uint8_t* doc_start;
+    void* out;
+    float* final_state;
+    float* ws;          // chunk carries, see scan_workspace_floats
+    int64_t batch, seqlen, dim, dstate;
+    int nheads;         // 0: per-channel A (D, N); > 0: scalar A per head
+    bool bf16;
+    bool softplus;
+    hipStream_t stream;
+};
+
+// Chunking of the sequence used by the scan for a given shape.
+struct ScanPlan {
+    int64_t chunk_len;   // tokens per chunk (multiple of 64)
+    int64_t nchunks;     // ceil(L / chunk_len)
+};
+
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim);
+size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+bool scan_supported(int64_t dstate, int nheads);
+hipError_t launch_selective_scan(const ScanArgs& a);
+
+}  // namespace mamba

@@ -1,0 +1,454 @@
+// Selective-scan forward over packed documents, gfx950.
+//
+// What it computes (Mamba skill page: S6 block diagram, "Core Concept", the S6
+// code and the "Mamba-2 (SSD)" section; axolotl page: per-document restart):
+//   dt_t  = softplus(delta_t + delta_bias)          (or without softplus)
+//   h_t   = exp(dt_t * A) * h_{t-1} + dt_t * u_t * B_t   per channel d, state n
+//   y_t   = C_t . h_t + D * u_t,   out_t = y_t * silu(z_t)
+//   h := 0 at every document start; final_state = h after the last token.
+// A is (D, N) (diagonal per channel) or (H,) (one scalar per head).
+//
+// Mapping ("lanes are channels").  One lane owns one channel d of one row b and
+// keeps its N states in fp32 VGPRs; the 64 lanes of a wave are 64 consecutive
+// channels, so every activation load and store of a wave is one contiguous 128 B
+// (bf16) span of a (B, L, D) row, and B_t, C_t, doc_start and the token index
+// are wave-uniform: B_t and C_t are read with scalar loads into SGPRs and used as
+// VALU operands directly, and a document start is a uniform branch.  Per element
+// the recurrence costs one v_exp_f32 and four fp32 ops (dt*A, dt*u*B, the state
+// FMA, the C*h FMA).
+//
+// Parallelism along L.  B * D / 64 waves are far too few to fill 256 CUs at the
+// target shapes, so L is cut into chunks and the chunks are joined with the
+// associative operator of the "Hardware-Aware Parallel Scan" section:
+//   pass 1 (aggregate): every chunk but the last runs its recurrence from a zero
+//          state and stores (P, H): P = prod of exp(dt A) over the chunk (0 if a
+//          document starts inside it), H = its end state.
+//   pass 2 (carry):     per (b, d, n), carry_{c+1} = P_c * carry_c + H_c.
+//   pass 3 (output):    every chunk reruns its recurrence from its carry and
+//          writes out and, for the last chunk, final_state.
+// The carries are the only intermediate data; the (B, L, D, N) state trajectory
+// is never stored.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mamba {
+
+namespace {
+
+constexpr int kScanBlock = 256;    // 4 independent waves, 256 consecutive channels
+constexpr int kGroup = 4;          // tokens whose activations are fetched together
+
+struct ScanKParams {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* delta_bias;
+    const uint8_t* doc_start;
+    void* out;
+    float* final_state;
+    float* ws_P;        // [nchunks-1][B][D][N]: pass 1 P, then pass 2 carries
+    float* ws_H;        // [nchunks-1][B][D][N]: pass 1 H
+    int64_t seqlen;
+    int64_t chunk_len;
+    int dim;
+    int nheads;
+    int headdim;
+    int nbatch;
+    int softplus;
+};
+
+// Raw buffer access: a 128-bit resource (base, size) held in SGPRs plus a 32-bit
+// per-lane byte offset, so addresses need no 64-bit VALU arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    constexpr int kRsrcWord3 = 0x00020000;        // gfx9 data format: 32-bit, raw access
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+template <typename T>
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+    if constexpr (sizeof(T) == 2) {
+        const uint16_t v = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, byte_off, 0, 0));
+        return bf16_to_f32(v);
+    } else {
+        return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, 0)));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, int byte_off, float v) {
+    if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rs, byte_off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, byte_off, 0, 0);
+}
+
+// OUTPUT = false: pass 1 (aggregate of one chunk from a zero state).
+// OUTPUT = true:  pass 3 (outputs of one chunk from its carried state).
+//
+// Data movement inside a chunk:
+//   - B_t (and C_t) are shared by all channels: the block stages them for a
+//     64-token window in LDS as fp32 (one coalesced 16-byte load per thread,
+//     converted once for the 256 channels of the block), and every wave reads
+//     them back with broadcast ds_read_b128, so each lane gets B_t[n..n+3] as
+//     VGPR operands with no per-lane conversion;
+//   - per-lane activations (u, delta, z) of the next group of G tokens are
+//     fetched while the current group computes: two register sets in ping-pong,
+//     so no loaded register is ever copied (a copy would wait on the load);
+//   - addresses are a wave-uniform 64-bit row base plus a 32-bit element offset.
+template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(4))) void scan_chunk_kernel(
+    const ScanKParams p) {
+    constexpr int G = kGroup;
+    constexpr int kWin = 64;                                   // tokens per staged window
+    constexpr int kRows = OUTPUT ? 2 : 1;                      // B and C, or B only
+    constexpr int kWinFloats = kWin * N;                       // one tensor's window
+    __shared__ float4 smem4[kRows * kWinFloats / 4];
+    float* smem = reinterpret_cast<float*>(smem4);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int d = blockIdx.x * kScanBlock + tid;
+    const bool active = d < p.dim;
+    const int dc = active ? d : p.dim - 1;          // clamped channel for loads
+    const int64_t c = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int64_t L = p.seqlen;
+    const int64_t t_begin = c * p.chunk_len;
+    const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
+    const int head = HEADS ? dc / p.headdim : 0;
+    const int nd = HEADS ? p.nheads : p.dim;        // width of delta rows
+    const int dsel = HEADS ? head : dc;
+
+    // Per-row buffer resources (wave-uniform base + size) and 32-bit byte offsets
+    // for the per-lane activations: t * width + channel fits in 31 bits.
+    constexpr int kEsz = static_cast<int>(sizeof(T));
+    const int64_t act_row = L * p.dim;
+    const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(static_cast<const T*>(p.u) + b * act_row, act_row * kEsz);
+    const __amdgpu_buffer_rsrc_t dl_rs =
+        make_rsrc(static_cast<const T*>(p.delta) + b * L * nd, L * nd * kEsz);
+    const __amdgpu_buffer_rsrc_t z_rs =
+        make_rsrc(HAS_Z ? static_cast<const T*>(p.z) + b * act_row : static_cast<const T*>(p.u), act_row * kEsz);
+    const __amdgpu_buffer_rsrc_t out_rs = make_rsrc(static_cast<T*>(p.out) + b * act_row, act_row * kEsz);
+    const T* B_row = static_cast<const T*>(p.B) + b * L * N;
+    const T* C_row = static_cast<const T*>(p.C) + b * L * N;
+    const uint8_t* ds_row = p.doc_start ? p.doc_start + b * L : nullptr;
+
+    // Per-channel constants: A scaled by log2(e) so exp(dt A) = exp2(dt * Al2).
+    float Al2[HEADS ? 1 : N];
+    if constexpr (HEADS) {
+        Al2[0] = p.A[head] * kLog2e;
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) Al2[n] = p.A[static_cast<int64_t>(dc) * N + n] * kLog2e;
+    }
+    const float dbias = p.delta_bias ? p.delta_bias[dsel] : 0.0f;
+    const float Dd = (OUTPUT && p.D) ? p.D[dc] : 0.0f;
+
+    // Chunk carry (pass 3) or zero.
+    const int64_t slot_stride = static_cast<int64_t>(p.nbatch) * p.dim * N;
+    const int64_t my_slot = (b * p.dim + dc) * N;
+    float h[N];
+    if (OUTPUT && c > 0) {
+        const float* carry = p.ws_P + (c - 1) * slot_stride + my_slot;
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = carry[n];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = 0.0f;
+    }
+    float sum_dt = 0.0f;          // pass 1: sum of dt since the chunk start
+    bool any_reset = false;       // pass 1: a document starts inside the chunk
+
+    auto load_group = [&](int64_t g0, float (&uu)[G], float (&dl)[G], float (&zz)[G]) {
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int t = static_cast<int>((g0 + k < t_end) ? g0 + k : t_end - 1);  // clamp the tail
+            uu[k] = buf_load<T>(u_rs, (t * p.dim + dc) * kEsz);
+            dl[k] = buf_load<T>(dl_rs, (t * nd + dsel) * kEsz);
+            if constexpr (OUTPUT && HAS_Z) zz[k] = buf_load<T>(z_rs, (t * p.dim + dc) * kEsz);
+            else zz[k] = 0.0f;
+        }
+    };
+
+    // Stage B (and C) of tokens w0 .. w0+63 into LDS as fp32.  Each step moves
+    // VW consecutive elements of one token row (16 bytes when the row allows);
+    // tokens past the chunk end are clamped to its last token and never read back.
+    auto stage_window = [&](int64_t w0) {
+        constexpr int kVecElems = 16 / static_cast<int>(sizeof(T));
+        constexpr int VW = N < kVecElems ? N : kVecElems;
+        constexpr int kStepsPerTensor = kWinFloats / VW;
+        for (int i = tid; i < kRows * kStepsPerTensor; i += kScanBlock) {
+            const int tensor = i / kStepsPerTensor;
+            const int e0 = (i % kStepsPerTensor) * VW;        // element index inside the window
+            const int tok = e0 / N;
+            const int n0 = e0 % N;
+            const int64_t t = (w0 + tok < t_end) ? w0 + tok : t_end - 1;
+            const T* src = (tensor == 0 ? B_row : C_row) + t * N + n0;
+            float* dst = smem + tensor * kWinFloats + e0;
+            float v[VW];
+            if constexpr (sizeof(T) == 2) {
+                uint32_t wv[VW / 2];
+                if constexpr (VW == 8) {
+                    const uint4 r = *reinterpret_cast<const uint4*>(src);
+                    wv[0] = r.x; wv[1] = r.y; wv[2] = r.z; wv[3] = r.w;
+                } else if constexpr (VW == 4) {
+                    const uint2 r = *reinterpret_cast<const uint2*>(src);
+                    wv[0] = r.x; wv[1] = r.y;
+                } else {
+                    wv[0] = *reinterpret_cast<const uint32_t*>(src);
+                }
+#pragma unroll
+                for (int k = 0; k < VW / 2; ++k) {
+                    v[2 * k] = __uint_as_float(wv[k] << 16);
+                    v[2 * k + 1] = __uint_as_float(wv[k] & 0xffff0000u);
+                }
+            } else {
+                const float4 r = *reinterpret_cast<const float4*>(src);
+                v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+            }
+#pragma unroll
+            for (int k = 0; k < VW; k += 4)
+                *reinterpret_cast<float4*>(dst + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+        }
+    };
+
+    uint64_t starts = 0;
+    auto compute_group = [&](int64_t g0, const float (&cu)[G], const float (&cd)[G], const float (&cz)[G]) {
+        const int off = static_cast<int>((g0 - t_begin) & (kWin - 1));
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            // Tokens past the chunk end run as identity steps (dt = 0: decay 1, no
+            // input) so the group stays straight-line code.
+            const bool valid = g0 + k < t_end;
+            const int64_t t = g0 + k;
+            // A document start multiplies the carried state by exp2(-inf) = 0: the
+            // reset rides in the exponent's addend, with no branch and no extra op.
+            const bool reset = (starts >> (off + k)) & 1ull;
+            const float r = reset ? -__builtin_inff() : 0.0f;
+            if (!OUTPUT) {
+                any_reset = any_reset || reset;
+                sum_dt = reset ? 0.0f : sum_dt;
+            }
+            float dt = cd[k] + dbias;
+            if constexpr (SOFTPLUS) dt = softplus_f(dt);
+            dt = valid ? dt : 0.0f;
+            const float w = dt * cu[k];
+            float y0 = 0.0f, y1 = 0.0f, y2 = 0.0f, y3 = 0.0f;
+            float a_head = 0.0f;
+            if constexpr (HEADS) a_head = exp2_fast(__builtin_fmaf(dt, Al2[0], r));
+            const float4* Bq = reinterpret_cast<const float4*>(smem + (off + k) * N);
+            const float4* Cq = reinterpret_cast<const float4*>(smem + kWinFloats + (off + k) * N);
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q) {
+                const float4 bv = Bq[q];
+                float4 cv;
+                if constexpr (OUTPUT) cv = Cq[q];
+                const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+                const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = 4 * q + j;
+                    float a;
+                    if constexpr (HEADS) a = a_head;
+                    else a = exp2_fast(__builtin_fmaf(dt, Al2[n], r));
+                    h[n] = __builtin_fmaf(a, h[n], w * bb[j]);
+                    if constexpr (OUTPUT) {
+                        if (j == 0) y0 = __builtin_fmaf(cc[j], h[n], y0);
+                        else if (j == 1) y1 = __builtin_fmaf(cc[j], h[n], y1);
+                        else if (j == 2) y2 = __builtin_fmaf(cc[j], h[n], y2);
+                        else y3 = __builtin_fmaf(cc[j], h[n], y3);
+                    }
+                }
+            }
+            if constexpr (OUTPUT) {
+                float y = ((y0 + y1) + (y2 + y3)) + Dd * cu[k];
+                if constexpr (HAS_Z) y *= silu_f(cz[k]);
+                if (active && valid) buf_store<T>(out_rs, (static_cast<int>(t) * p.dim + d) * kEsz, y);
+            } else {
+                sum_dt += dt;
+            }
+            // Keep the scheduler from hoisting later tokens' exponentials: one
+            // token already offers N independent chains, and hoisting only
+            // raises register pressure.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    float au[G], ad[G], az[G], bu[G], bd[G], bz[G];
+    load_group(t_begin, au, ad, az);
+    for (int64_t w0 = t_begin; w0 < t_end; w0 += kWin) {
+        // Document starts of the window as a wave-uniform bit mask.
+        {
+            const int64_t tl = w0 + lane;
+            bool st = false;
+            if (tl < t_end) st = (tl == 0) || (ds_row != nullptr && ds_row[tl] != 0);
+            starts = __ballot(st);
+        }
+        __syncthreads();                 // every wave is done with the previous window
+        stage_window(w0);
+        __syncthreads();
+        const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
+        for (int64_t g0 = w0; g0 < wend; g0 += 2 * G) {
+            load_group(g0 + G, bu, bd, bz);
+            compute_group(g0, au, ad, az);
+            load_group(g0 + 2 * G, au, ad, az);
+            compute_group(g0 + G, bu, bd, bz);
+        }
+    }
+
+    if (!active) return;
+    if (OUTPUT) {
+        if (p.final_state != nullptr && t_end == L) {
+            float* fs = p.final_state + my_slot;
+#pragma unroll
+            for (int n = 0; n < N; ++n) fs[n] = h[n];
+        }
+    } else {
+        float* P = p.ws_P + c * slot_stride + my_slot;
+        float* H = p.ws_H + c * slot_stride + my_slot;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            float al;
+            if constexpr (HEADS) al = Al2[0];
+            else al = Al2[n];
+            P[n] = any_reset ? 0.0f : exp2_fast(sum_dt * al);
+            H[n] = h[n];
+        }
+    }
+}
+
+// Pass 2: carry_{c+1} = P_c * carry_c + H_c for every (b, d, n), written over
+// ws_P[c] (ws_P[c] then holds the state entering chunk c + 1).
+__global__ __launch_bounds__(256) void scan_carry_kernel(float* __restrict__ ws_P, const float* __restrict__ ws_H,
+                                                         int64_t count, int64_t nslots) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= count) return;
+    float carry = 0.0f;
+    int64_t c = 0;
+    for (; c + 4 <= nslots; c += 4) {
+        float P[4], H[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            P[k] = ws_P[(c + k) * count + i];
+            H[k] = ws_H[(c + k) * count + i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            carry = __builtin_fmaf(P[k], carry, H[k]);
+            ws_P[(c + k) * count + i] = carry;
+        }
+    }
+    for (; c < nslots; ++c) {
+        carry = __builtin_fmaf(ws_P[c * count + i], carry, ws_H[c * count + i]);
+        ws_P[c * count + i] = carry;
+    }
+}
+
+template <typename T, int N, bool HEADS>
+hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
+    ScanKParams p;
+    p.u = a.u; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
+    p.delta_bias = a.delta_bias; p.doc_start = a.doc_start; p.out = a.out; p.final_state = a.final_state;
+    const int64_t count = a.batch * a.dim * N;
+    const int64_t nslots = plan.nchunks - 1;
+    p.ws_P = a.ws;
+    p.ws_H = a.ws ? a.ws + nslots * count : nullptr;
+    p.seqlen = a.seqlen;
+    p.chunk_len = plan.chunk_len;
+    p.dim = static_cast<int>(a.dim);
+    p.nheads = a.nheads;
+    p.headdim = a.nheads ? static_cast<int>(a.dim / a.nheads) : 0;
+    p.nbatch = static_cast<int>(a.batch);
+    p.softplus = a.softplus ? 1 : 0;
+
+    const unsigned gx = static_cast<unsigned>((a.dim + kScanBlock - 1) / kScanBlock);
+    if (nslots > 0) {
+        dim3 g1(gx, static_cast<unsigned>(nslots), static_cast<unsigned>(a.batch));
+        if (a.softplus)
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, true>), g1, dim3(kScanBlock), 0,
+                               a.stream, p);
+        else
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, false>), g1, dim3(kScanBlock), 0,
+                               a.stream, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dim3 g2(static_cast<unsigned>((count + 255) / 256));
+        hipLaunchKernelGGL(scan_carry_kernel, g2, dim3(256), 0, a.stream, p.ws_P, p.ws_H, count, nslots);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    dim3 g3(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
+    if (a.z) {
+        if (a.softplus)
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, true, true>), g3, dim3(kScanBlock), 0,
+                               a.stream, p);
+        else
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, true, false>), g3, dim3(kScanBlock), 0,
+                               a.stream, p);
+    } else {
+        if (a.softplus)
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, false, true>), g3, dim3(kScanBlock), 0,
+                               a.stream, p);
+        else
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, false, false>), g3, dim3(kScanBlock), 0,
+                               a.stream, p);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_scan_dtype(const ScanArgs& a, const ScanPlan& plan) {
+    if (a.nheads == 0) {
+        switch (a.dstate) {
+            case 4: return launch_scan_typed<T, 4, false>(a, plan);
+            case 8: return launch_scan_typed<T, 8, false>(a, plan);
+            case 16: return launch_scan_typed<T, 16, false>(a, plan);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (a.dstate) {
+        case 16: return launch_scan_typed<T, 16, true>(a, plan);
+        case 32: return launch_scan_typed<T, 32, true>(a, plan);
+        case 64: return launch_scan_typed<T, 64, true>(a, plan);
+        case 128: return launch_scan_typed<T, 128, true>(a, plan);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool scan_supported(int64_t dstate, int nheads) {
+    if (nheads == 0) return dstate == 4 || dstate == 8 || dstate == 16;
+    return dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128;
+}
+
+// Chunks are sized so that pass 3 launches roughly 4096+ waves (four or more per
+// SIMD on 256 CUs) while keeping the carry workspace small.
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim) {
+    const int64_t chains = batch * ((dim + 63) / 64);
+    int64_t want_chunks = chains > 0 ? (4096 + chains - 1) / chains : 1;
+    if (want_chunks < 1) want_chunks = 1;
+    int64_t len = (seqlen + want_chunks - 1) / want_chunks;
+    int64_t chunk = 64;
+    while (chunk < len) chunk *= 2;
+    if (chunk > 4096) chunk = 4096;
+    ScanPlan p;
+    p.chunk_len = chunk;
+    p.nchunks = seqlen > 0 ? (seqlen + chunk - 1) / chunk : 0;
+    return p;
+}
+
+size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+    const ScanPlan plan = plan_scan(batch, seqlen, dim);
+    if (plan.nchunks <= 1) return 0;
+    return static_cast<size_t>(2 * (plan.nchunks - 1)) * static_cast<size_t>(batch * dim * dstate) * sizeof(float);
+}
+
+hipError_t launch_selective_scan(const ScanArgs& a) {
+    const ScanPlan plan = plan_scan(a.batch, a.seqlen, a.dim);
+    return a.bf16 ? launch_scan_dtype<bf16_t>(a, plan) : launch_scan_dtype<float>(a, plan);
+}
+
+}  // namespace mamba

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry
+point, and rejects invalid calls with a status code before touching the GPU.
+
+Every call here fails validation (or is an empty no-op), so no HIP API is
+reached and no GPU is needed."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_23_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mamba_hip.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmamba_hip.so is not built: run `python -m selective_state_space_23_amd.build`")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert "mamba_causal_conv1d_fwd" in names and "mamba_selective_scan_fwd" in names
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        s = lib.mamba_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.mamba_status_string(99).decode() == "unknown status"
+    assert lib.mamba_version() >= (0 << 16) | (1 << 8)
+
+
+FAKE = 0x10000  # a non-null address never dereferenced: every call below fails validation first
+
+
+def conv(lib, x=FAKE, w=FAKE, b=None, ds=None, out=FAKE * 4, B=1, L=8, D=16, W=4, dtype=1, silu=1):
+    return lib.mamba_causal_conv1d_fwd(x, w, b, ds, out, B, L, D, W, dtype, silu, None)
+
+
+def test_conv_validation(lib):
+    assert conv(lib, W=3) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert conv(lib, dtype=7) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv(lib, x=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv(lib, w=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv(lib, out=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv(lib, B=-1) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv(lib, x=FAKE + 1) == _lib.MAMBA_ERR_MISALIGNED
+    assert conv(lib, out=FAKE * 4 + 2, dtype=0) == _lib.MAMBA_ERR_MISALIGNED
+    assert conv(lib, out=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # aliases x
+    assert conv(lib, L=10 ** 7) == _lib.MAMBA_ERR_UNSUPPORTED
+    # empty shapes are a no-op, even with null pointers
+    assert conv(lib, x=None, w=None, out=None, B=0) == _lib.MAMBA_OK
+    assert conv(lib, x=None, w=None, out=None, L=0) == _lib.MAMBA_OK
+
+
+def dims(**kw):
+    base = dict(batch=2, seqlen=300000, dim=1536, dstate=16, nheads=0, ngroups=1, dtype=1, delta_softplus=1)
+    base.update(kw)
+    return _lib.ScanDims(**base)
+
+
+def ws_bytes(lib, d):
+    n = ctypes.c_size_t(123)
+    st = lib.mamba_selective_scan_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_query(lib):
+    st, n = ws_bytes(lib, dims())
+    assert st == _lib.MAMBA_OK and n > 0
+    st, n = ws_bytes(lib, dims(seqlen=64))
+    assert st == _lib.MAMBA_OK and n == 0                 # one chunk: no carries
+    assert ws_bytes(lib, dims(ngroups=2))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    assert ws_bytes(lib, dims(dstate=5))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    assert ws_bytes(lib, dims(nheads=7))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT     # 1536 % 7
+    assert ws_bytes(lib, dims(nheads=24, dstate=128))[0] == _lib.MAMBA_OK
+    assert ws_bytes(lib, dims(dtype=3))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert ws_bytes(lib, dims(dstate=0))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert lib.mamba_selective_scan_workspace_bytes(None, None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+
+
+def scan(lib, d=None, u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None, bias=None,
+         ds=None, out=FAKE * 6, fs=None, ws=None, wsb=0):
+    d = d or dims(batch=1, seqlen=64, dim=64)
+    return lib.mamba_selective_scan_fwd(ctypes.byref(d), u, delta, A, B, C, D, z, bias, ds, out, fs, ws, wsb, None)
+
+
+def test_scan_validation(lib):
+    assert scan(lib, u=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert scan(lib, A=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert scan(lib, out=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert scan(lib, u=FAKE + 1) == _lib.MAMBA_ERR_MISALIGNED
+    assert scan(lib, B=FAKE * 4 + 2) == _lib.MAMBA_ERR_MISALIGNED
+    assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=3)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert scan(lib, out=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT           # out overlaps u
+    assert scan(lib, fs=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT        # final_state overlaps out
+    # a multi-chunk shape without workspace, then with a too small one
+    big = dims(batch=1, seqlen=100000, dim=64)
+    st, need = ws_bytes(lib, big)
+    assert need > 0
+    base = 1 << 40
+    kw = dict(u=base, delta=base * 2, A=base * 3, B=base * 4, C=base * 5, out=base * 6)
+    assert scan(lib, d=big, **kw) == _lib.MAMBA_ERR_WORKSPACE
+    assert scan(lib, d=big, ws=base * 7, wsb=need - 1, **kw) == _lib.MAMBA_ERR_WORKSPACE
+    assert scan(lib, d=big, ws=base * 7 + 4, wsb=need, **kw) == _lib.MAMBA_ERR_MISALIGNED
+    assert scan(lib, d=big, ws=base, wsb=need, **kw) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # overlaps u
+    # empty shapes are a no-op
+    assert scan(lib, d=dims(batch=0), u=None, out=None) == _lib.MAMBA_OK
+    assert scan(lib, d=dims(seqlen=0), u=None, out=None) == _lib.MAMBA_OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import selective_state_space_23_amd as ssm
+    x = torch.zeros(1, 8, 16)
+    with pytest.raises(ValueError):
+        ssm.causal_conv1d_fwd(x, torch.zeros(16, 4))
+    with pytest.raises(ValueError):
+        ssm.selective_scan_fwd(x, x, torch.zeros(16, 4), torch.zeros(1, 8, 4), torch.zeros(1, 8, 4))
