@@ -94,7 +94,7 @@ def main():
     ap.add_argument("--config", default="packed_32k",
                     help="workload name from workloads.CONFIGS (default: the 32K packed bf16 shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle sample: tokens per row")
+    ap.add_argument("--cpu-tokens", type=int, default=32768, help="oracle sample: tokens per row")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

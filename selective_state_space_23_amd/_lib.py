@@ -5,7 +5,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmamba_hip.so")
+LIB_PATH = os.environ.get("MAMBA_HIP_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libmamba_hip.so")
 
 MAMBA_DTYPE_F32 = 0
 MAMBA_DTYPE_BF16 = 1

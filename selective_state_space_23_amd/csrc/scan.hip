@@ -36,7 +36,19 @@ namespace mamba {
 namespace {
 
 constexpr int kScanBlock = 256;    // 4 independent waves, 256 consecutive channels
-constexpr int kGroup = 4;          // tokens whose activations are fetched together
+#ifndef MAMBA_SCAN_SCHED_BARRIER
+#define MAMBA_SCAN_SCHED_BARRIER 1
+#endif
+#ifndef MAMBA_SCAN_GROUP
+#define MAMBA_SCAN_GROUP 4
+#endif
+#ifndef MAMBA_SCAN_TARGET_WAVES
+#define MAMBA_SCAN_TARGET_WAVES 4096
+#endif
+#ifndef MAMBA_SCAN_WAVES_PER_EU
+#define MAMBA_SCAN_WAVES_PER_EU 4
+#endif
+constexpr int kGroup = MAMBA_SCAN_GROUP;   // tokens whose activations are fetched together
 
 struct ScanKParams {
     const void* u;
@@ -98,7 +110,7 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, int byte_of
 //     so no loaded register is ever copied (a copy would wait on the load);
 //   - addresses are a wave-uniform 64-bit row base plus a 32-bit element offset.
 template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(4))) void scan_chunk_kernel(
+__global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMBA_SCAN_WAVES_PER_EU))) void scan_chunk_kernel(
     const ScanKParams p) {
     constexpr int G = kGroup;
     constexpr int kWin = 64;                                   // tokens per staged window
@@ -272,7 +284,9 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(4)))
             // Keep the scheduler from hoisting later tokens' exponentials: one
             // token already offers N independent chains, and hoisting only
             // raises register pressure.
+#if MAMBA_SCAN_SCHED_BARRIER
             __builtin_amdgcn_sched_barrier(0);
+#endif
         }
     };
 
@@ -428,7 +442,7 @@ bool scan_supported(int64_t dstate, int nheads) {
 // SIMD on 256 CUs) while keeping the carry workspace small.
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim) {
     const int64_t chains = batch * ((dim + 63) / 64);
-    int64_t want_chunks = chains > 0 ? (4096 + chains - 1) / chains : 1;
+    int64_t want_chunks = chains > 0 ? (MAMBA_SCAN_TARGET_WAVES + chains - 1) / chains : 1;
     if (want_chunks < 1) want_chunks = 1;
     int64_t len = (seqlen + want_chunks - 1) / want_chunks;
     int64_t chunk = 64;
