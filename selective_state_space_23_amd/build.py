@@ -13,6 +13,7 @@ import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 LIB_NAME = "libmamba_hip.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["api.cpp", "conv1d.hip", "scan.hip"]
@@ -33,7 +34,7 @@ def hipcc_path() -> str:
 def compile_cmd(out_path: str) -> list:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     return [hipcc_path(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
-            "-Wall", "-Wno-unused-result", *DEVICE_FLAGS, "-o", out_path, *srcs]
+            "-Wall", "-Wno-unused-result", "-I", INCLUDE, *DEVICE_FLAGS, "-o", out_path, *srcs]
 
 
 def build(verbose: bool = False) -> str:

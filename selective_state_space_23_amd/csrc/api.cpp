@@ -1,7 +1,7 @@
 // C ABI of the Mamba selective-scan forward path: argument validation and
 // dispatch to the HIP kernels.  Every check runs on the host before any launch,
 // so an invalid call never reaches the GPU.
-#include "../../include/mamba_hip.h"
+#include "mamba_hip.h"
 
 #include <hip/hip_runtime.h>
 
