@@ -66,6 +66,49 @@ def conv_alu_flop_eq(B, L, D):
     return 2.0 * 14 * B * L * D
 
 
+def copy_probe(torch, dev, mib=1024, reps=5):
+    """Device-to-device copy of `mib` MiB (read + write), timed with HIP events on the
+    current stream: the measured streaming ceiling the algorithmic GB/s is set against.
+    Its kernel also calibrates the FETCH_SIZE / WRITE_SIZE counters in profiling runs."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del src, dst
+    return {"bytes_per_copy": 2 * n, "ms": ms, "GBs": 2 * n / (ms * 1e-3) / 1e9}
+
+
+def recorded_traffic(path, source_files):
+    """HBM bytes per scan call from the committed FETCH_SIZE / WRITE_SIZE profile, or None
+    when the kernel sources have changed since those counters were taken."""
+    import hashlib
+
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in source_files:
+        h.update(open(f, "rb").read())
+    if fields.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(fields["scan_call_hbm_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp, tokens_per_row):
     """Time the fp64 oracle (conv + scan, as it stands) on the first tokens of every row."""
     from threadpoolctl import threadpool_limits
@@ -95,6 +138,7 @@ def main():
                     help="workload name from workloads.CONFIGS (default: the 32K packed bf16 shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768, help="oracle sample: tokens per row")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the device copy probe (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -157,6 +201,11 @@ def main():
     conv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
 
+    probe = copy_probe(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
+    csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
+    traffic = recorded_traffic(os.path.join(ROOT, "profiles", f"scan_{args.config}_hbm_traffic.txt"),
+                               [os.path.join(csrc, f) for f in ("scan.hip", "launch.hpp", "device_common.hpp")])
+
     tokens = B * L
     sb = scan_bytes(B, L, D, N, H, esz)
     cb = conv_bytes(B, L, D, esz)
@@ -186,7 +235,7 @@ def main():
             "peak": FP32_VECTOR_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": traffic,
             "hbm_achieved_GBs": scan_gbs,
             "hbm_frac": scan_gbs / HBM_PEAK_GBS,
             "algorithmic_bytes": sb,
@@ -198,6 +247,8 @@ def main():
             "algorithmic_bytes": sb + cb, "conv_ms": conv_ms, "scan_ms": scan_ms,
             "conv_GBs": cb / (conv_ms * 1e-3) / 1e9,
         },
+        "copy_probe": None if probe is None else dict(
+            probe, pair_frac_of_copy=pair_gbs / probe["GBs"], kernel="hipMemcpyAsync device-to-device"),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
