@@ -43,7 +43,7 @@ int check_dims(const mamba_scan_dims_t* d) {
     if (!mul_ok(d->batch, d->seqlen, d->dim, &n)) return MAMBA_ERR_INVALID_ARGUMENT;
     if (!mul_ok(d->batch, d->seqlen, d->dstate, &n)) return MAMBA_ERR_INVALID_ARGUMENT;
     if (d->ngroups != 1) return MAMBA_ERR_UNSUPPORTED;
-    if (!mamba::scan_supported(d->dstate, d->nheads)) return MAMBA_ERR_UNSUPPORTED;
+    if (!mamba::scan_supported(d->dim, d->dstate, d->nheads, d->dtype == MAMBA_DTYPE_BF16)) return MAMBA_ERR_UNSUPPORTED;
     return MAMBA_OK;
 }
 
@@ -100,7 +100,8 @@ int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* 
     *bytes = 0;
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
-    *bytes = mamba::scan_workspace_bytes(dims->batch, dims->seqlen, dims->dim, dims->dstate);
+    *bytes = mamba::scan_workspace_bytes(dims->batch, dims->seqlen, dims->dim, dims->dstate, dims->nheads,
+                                         dims->dtype == MAMBA_DTYPE_BF16);
     return MAMBA_OK;
 }
 
@@ -119,6 +120,10 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
         return MAMBA_ERR_MISALIGNED;
     // B and C rows are read as 32-bit words.
     if (!aligned(B, 4) || !aligned(C, 4) || (N * esz) % 4 != 0) return MAMBA_ERR_MISALIGNED;
+    // Scalar-A heads with bf16 I/O move u, z, out, B and C in 16-byte vectors.
+    if (dims->nheads > 0 && dims->dtype == MAMBA_DTYPE_BF16 &&
+        (!aligned(u, 16) || !aligned(out, 16) || (z && !aligned(z, 16)) || !aligned(B, 16) || !aligned(C, 16)))
+        return MAMBA_ERR_MISALIGNED;
     if (!aligned(A, 4) || (D && !aligned(D, 4)) || (delta_bias && !aligned(delta_bias, 4)) ||
         (final_state && !aligned(final_state, 4)))
         return MAMBA_ERR_MISALIGNED;
@@ -137,7 +142,7 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
     }
     if (overlap(out, act, final_state, fsb)) return MAMBA_ERR_INVALID_ARGUMENT;
 
-    const size_t need = mamba::scan_workspace_bytes(Bt, L, Dm, N);
+    const size_t need = mamba::scan_workspace_bytes(Bt, L, Dm, N, dims->nheads, dims->dtype == MAMBA_DTYPE_BF16);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;

@@ -49,8 +49,13 @@ struct ScanPlan {
 };
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim);
-size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
-bool scan_supported(int64_t dstate, int nheads);
+size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16);
+bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16);
 hipError_t launch_selective_scan(const ScanArgs& a);
+
+// Scalar-A heads with bf16 I/O: the chunked matrix-core form (ssd.hip).
+bool ssd_supported(int64_t dim, int64_t dstate, int nheads);
+size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads);
+hipError_t launch_ssd(const ScanArgs& a);
 
 }  // namespace mamba

@@ -414,27 +414,31 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
 
 template <typename T>
 hipError_t launch_scan_dtype(const ScanArgs& a, const ScanPlan& plan) {
-    if (a.nheads == 0) {
-        switch (a.dstate) {
-            case 4: return launch_scan_typed<T, 4, false>(a, plan);
-            case 8: return launch_scan_typed<T, 8, false>(a, plan);
-            case 16: return launch_scan_typed<T, 16, false>(a, plan);
-            default: return hipErrorInvalidValue;
-        }
-    }
     switch (a.dstate) {
-        case 16: return launch_scan_typed<T, 16, true>(a, plan);
-        case 32: return launch_scan_typed<T, 32, true>(a, plan);
-        case 64: return launch_scan_typed<T, 64, true>(a, plan);
-        case 128: return launch_scan_typed<T, 128, true>(a, plan);
+        case 4: return launch_scan_typed<T, 4, false>(a, plan);
+        case 8: return launch_scan_typed<T, 8, false>(a, plan);
+        case 16: return launch_scan_typed<T, 16, false>(a, plan);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Scalar-A heads with fp32 I/O keep the recurrent form (fp32 throughout): the
+// matrix-core form rounds its operands to bf16, below what fp32 I/O promises.
+hipError_t launch_heads_f32(const ScanArgs& a, const ScanPlan& plan) {
+    switch (a.dstate) {
+        case 16: return launch_scan_typed<float, 16, true>(a, plan);
+        case 32: return launch_scan_typed<float, 32, true>(a, plan);
+        case 64: return launch_scan_typed<float, 64, true>(a, plan);
+        case 128: return launch_scan_typed<float, 128, true>(a, plan);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-bool scan_supported(int64_t dstate, int nheads) {
+bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16) {
     if (nheads == 0) return dstate == 4 || dstate == 8 || dstate == 16;
+    if (bf16) return ssd_supported(dim, dstate, nheads);
     return dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128;
 }
 
@@ -454,13 +458,15 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim) {
     return p;
 }
 
-size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16) {
+    if (nheads > 0 && bf16) return ssd_workspace_bytes(batch, seqlen, dim, dstate, nheads);
     const ScanPlan plan = plan_scan(batch, seqlen, dim);
     if (plan.nchunks <= 1) return 0;
     return static_cast<size_t>(2 * (plan.nchunks - 1)) * static_cast<size_t>(batch * dim * dstate) * sizeof(float);
 }
 
 hipError_t launch_selective_scan(const ScanArgs& a) {
+    if (a.nheads > 0) return a.bf16 ? launch_ssd(a) : launch_heads_f32(a, plan_scan(a.batch, a.seqlen, a.dim));
     const ScanPlan plan = plan_scan(a.batch, a.seqlen, a.dim);
     return a.bf16 ? launch_scan_dtype<bf16_t>(a, plan) : launch_scan_dtype<float>(a, plan);
 }

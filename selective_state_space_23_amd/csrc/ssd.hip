@@ -1,0 +1,505 @@
+// Scalar-A heads (the Mamba-2 shape) as chunked matrix products on the matrix
+// cores, gfx950.
+//
+// Mamba skill page, "Mamba-2: Structured State Space Duality (SSD)": when A is
+// one scalar per head the recurrence inside a chunk equals a causal, decay-
+// weighted product of C against B (an attention-like Q x Q matrix), and chunks
+// talk to each other only through the N x P state of each head.  For one row b,
+// one head h (channels h*P .. h*P + P - 1) and a chunk of Q = 64 tokens:
+//
+//   dt_t    = softplus(delta[t, h] + delta_bias[h])
+//   cs_t    = log2(e) A[h] (dt_0 + ... + dt_t)          (inclusive, inside the chunk)
+//   seg_t   = number of document starts at or before t  (inside the chunk)
+//   M[t, s] = (C_t . B_s) 2^(cs_t - cs_s) dt_s   if s <= t and seg_t == seg_s, else 0
+//   Y[t, :] = sum_s M[t, s] x_s  +  [seg_t == 0] 2^cs_t  C_t . H_in
+//   H_out   = [seg_63 == 0] 2^cs_63 H_in  +  sum_s [seg_s == seg_63] 2^(cs_63 - cs_s) dt_s B_s x_s^T
+//   out_t   = (Y[t, :] + D x_t) * silu(z_t)
+//
+// This is the same recurrence as h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t with
+// the state zeroed at every document start, regrouped (exactly, up to rounding).
+// Every product runs as v_mfma_f32_16x16x32_bf16: bf16 operands (inputs are
+// bf16 already; M, dt-weighted B and the chunk-entry state are rounded to bf16)
+// and fp32 accumulation.  The state H of a head lives in fp32 MFMA accumulators
+// across all chunks of a segment.
+//
+// Parallelism: one workgroup (8 waves) per (row, head, segment of L).  Segments
+// are joined like the chunks of the per-channel scan: pass 1 computes every
+// segment's end state from zero and its total decay, pass 2 carries the states
+// across segments, pass 3 recomputes each segment from its carry and writes the
+// outputs.  Workgroups of the same (row, segment) read the same B and C rows, so
+// the block index is remapped to keep all heads of one (row, segment) on one XCD
+// (the dispatcher deals consecutive workgroups round-robin to the 8 XCDs, each
+// with its own L2).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mamba {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kQ = 64;                  // tokens per chunk
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int64_t kTargetBlocks = 768;  // workgroups per pass (three per CU)
+constexpr int kXcds = 8;
+
+struct SsdParams {
+    const uint16_t* u;
+    const uint16_t* delta;
+    const float* A;
+    const uint16_t* B;
+    const uint16_t* C;
+    const float* D;
+    const uint16_t* z;
+    const float* delta_bias;
+    const uint8_t* doc_start;
+    uint16_t* out;
+    float* final_state;
+    float* ws_H;        // [B*H][nseg-1][P][N]: segment end states, then carries
+    float* ws_G;        // [B*H][nseg-1]: segment decays
+    int64_t seqlen;
+    int64_t seg_len;    // multiple of kQ
+    int dim;
+    int nheads;
+    int dstate;
+    int nseg;
+    int nbatch;
+};
+
+__device__ __forceinline__ bf16x8_t frag(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+
+// D = A x B + C for a 16x16 tile, K = 32.  Lane l holds A[l % 16][8 (l / 16) + j]
+// and B[8 (l / 16) + j][l % 16] (j = 0..7); D[4 (l / 16) + i][l % 16] (i = 0..3).
+__device__ __forceinline__ f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// LDS layout of one workgroup.  Row strides carry 8 bf16 (16 bytes) of padding so
+// that the 16 rows read by one fragment load start on different banks.
+template <int NP, int P, bool OUTPUT>
+struct SsdLds {
+    static constexpr int SN = NP + 8;              // [*][NP] bf16 tiles
+    static constexpr int SQ = kQ + 8;              // [*][Q] bf16 tiles
+    static constexpr int SY = P + 4;               // fp32 Y tile
+    static constexpr int kBBytes = kQ * SN * 2;
+    static constexpr int kYBytes = OUTPUT ? kQ * SY * 4 : 0;
+    static constexpr int oC = 0;                                   // C rows [t][n]
+    static constexpr int oB = oC + (OUTPUT ? kQ * SN * 2 : 0);     // B rows [s][n], later Y [t][p] fp32
+    static constexpr int oBw = oB + (kBBytes > kYBytes ? kBBytes : kYBytes);  // weighted B^T [n][s]
+    static constexpr int oXT = oBw + NP * SQ * 2;                  // x^T [p][s]
+    static constexpr int oM = oXT + P * SQ * 2;                    // M [t][s]
+    static constexpr int oHT = oM + (OUTPUT ? kQ * SQ * 2 : 0);    // chunk-entry state^T [p][n]
+    static constexpr int oTok = oHT + (OUTPUT ? P * SN * 2 : 0);   // per-token scalars
+    static constexpr int kBytes = oTok + 5 * kQ * 4;
+};
+
+template <int NP, int P, bool OUTPUT, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) {
+    using Lay = SsdLds<NP, P, OUTPUT>;
+    constexpr int SN = Lay::SN, SQ = Lay::SQ, SY = Lay::SY;
+    constexpr int kTN = NP / 16, kTP = P / 16;
+    constexpr int kT = kTN * kTP;                          // state tiles
+    constexpr int kSt = (kT + kWaves - 1) / kWaves;        // state tiles per wave
+    constexpr int kTY = (kQ / 16) * kTP;                   // output tiles
+    constexpr int kYw = (kTY + kWaves - 1) / kWaves;
+    constexpr int kVN = NP / 8;                            // 16-byte vectors per B/C row
+    constexpr int kVP = P / 8;                             // 16-byte vectors per x row
+
+    __shared__ __attribute__((aligned(16))) unsigned char lds[Lay::kBytes];
+    uint16_t* sC = reinterpret_cast<uint16_t*>(lds + Lay::oC);
+    uint16_t* sB = reinterpret_cast<uint16_t*>(lds + Lay::oB);
+    float* sY = reinterpret_cast<float*>(lds + Lay::oB);
+    uint16_t* sBw = reinterpret_cast<uint16_t*>(lds + Lay::oBw);
+    uint16_t* sXT = reinterpret_cast<uint16_t*>(lds + Lay::oXT);
+    uint16_t* sM = reinterpret_cast<uint16_t*>(lds + Lay::oM);
+    uint16_t* sHT = reinterpret_cast<uint16_t*>(lds + Lay::oHT);
+    float* sDt = reinterpret_cast<float*>(lds + Lay::oTok);
+    float* sCs = sDt + kQ;
+    float* sW = sCs + kQ;
+    float* sScale = sW + kQ;
+    int* sSeg = reinterpret_cast<int*>(sScale + kQ);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+
+    // Workgroup -> (row, segment, head); all heads of a (row, segment) share an XCD.
+    const int total = p.nbatch * p.nheads * p.nseg;
+    int li = static_cast<int>(blockIdx.x);
+    if (total % kXcds == 0) li = (li % kXcds) * (total / kXcds) + li / kXcds;
+    const int h = li % p.nheads;
+    const int bs = li / p.nheads;
+    const int seg = bs % p.nseg;
+    const int b = bs / p.nseg;
+    if (!OUTPUT && seg == p.nseg - 1) return;      // the last segment's aggregate is never used
+
+    const int64_t L = p.seqlen;
+    const int N = p.dstate;
+    const int64_t t_seg0 = static_cast<int64_t>(seg) * p.seg_len;
+    const int64_t t_seg1 = (t_seg0 + p.seg_len < L) ? t_seg0 + p.seg_len : L;
+    const float a_l2 = p.A[h] * kLog2e;
+    const float dbias = p.delta_bias ? p.delta_bias[h] : 0.0f;
+    const int64_t bh = static_cast<int64_t>(b) * p.nheads + h;
+    const int64_t PN = static_cast<int64_t>(P) * N;
+    const int nslot = p.nseg - 1;
+    const uint16_t* Brow = p.B + static_cast<int64_t>(b) * L * N;
+    const uint16_t* Crow = p.C + static_cast<int64_t>(b) * L * N;
+
+    // State tiles of this wave: tile k = wave + kWaves j covers n in 16 (k / kTP) + [0, 16)
+    // and p in 16 (k % kTP) + [0, 16); lane element i is (n = 16 nb + 4 lg + i, p = 16 pb + l16).
+    f32x4_t st[kSt];
+#pragma unroll
+    for (int j = 0; j < kSt; ++j) {
+        const int k = wave + kWaves * j;
+        st[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (OUTPUT && seg > 0 && k < kT) {
+            const int nb = k / kTP, pb = k % kTP;
+            const float* carry = p.ws_H + (bh * nslot + seg - 1) * PN + static_cast<int64_t>(16 * pb + l16) * N;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 16 * nb + 4 * lg + i;
+                if (n < N) st[j][i] = carry[n];
+            }
+        }
+    }
+    float seg_decay = 1.0f;
+
+    // Per-thread constants of the output epilogue: each thread always handles the
+    // same 8 channels (kThreads is a multiple of kVP).
+    const int ep0 = (tid % kVP) * 8;
+    float Dp[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Dp[e] = (OUTPUT && p.D) ? p.D[h * P + ep0 + e] : 0.0f;
+
+    for (int64_t t0 = t_seg0; t0 < t_seg1; t0 += kQ) {
+        // ---- 1. stage the chunk: B (and C) rows, x transposed, per-token scalars
+        for (int i = tid; i < kQ * kVN; i += kThreads) {
+            const int row = i / kVN, n0 = (i % kVN) * 8;
+            const int64_t tg = t0 + row;
+            u32x4_t vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
+            if (tg < t_seg1 && n0 < N) {
+                vb = *reinterpret_cast<const u32x4_t*>(Brow + tg * N + n0);
+                if (OUTPUT) vc = *reinterpret_cast<const u32x4_t*>(Crow + tg * N + n0);
+            }
+            *reinterpret_cast<u32x4_t*>(sB + row * SN + n0) = vb;
+            if (OUTPUT) *reinterpret_cast<u32x4_t*>(sC + row * SN + n0) = vc;
+        }
+        for (int i = tid; i < kQ * kVP; i += kThreads) {
+            const int row = i / kVP, p0 = (i % kVP) * 8;
+            const int64_t tg = t0 + row;
+            u32x4_t vx = {0u, 0u, 0u, 0u};
+            if (tg < t_seg1)
+                vx = *reinterpret_cast<const u32x4_t*>(p.u + (static_cast<int64_t>(b) * L + tg) * p.dim + h * P + p0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sXT[(p0 + 2 * j) * SQ + row] = static_cast<uint16_t>(vx[j] & 0xffffu);
+                sXT[(p0 + 2 * j + 1) * SQ + row] = static_cast<uint16_t>(vx[j] >> 16);
+            }
+        }
+        if (wave == 0) {
+            // Lane = token of the chunk.  Tokens past the segment end are identity
+            // steps (dt = 0) with zero B, C and x rows.
+            const int64_t tg = t0 + lane;
+            const bool valid = tg < t_seg1;
+            float dt = 0.0f;
+            bool reset = false;
+            if (valid) {
+                const int64_t row = static_cast<int64_t>(b) * L + tg;
+                float v = bf16_to_f32(p.delta[row * p.nheads + h]) + dbias;
+                if constexpr (SOFTPLUS) v = softplus_f(v);
+                dt = v;
+                reset = tg == 0 || (p.doc_start != nullptr && p.doc_start[row] != 0);
+            }
+            float cs = dt * a_l2;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(cs, off);
+                if (lane >= off) cs += o;
+            }
+            const uint64_t rmask = __ballot(reset);
+            const int sg = __popcll(rmask & ((2ull << lane) - 1ull));
+            const int sg_end = __popcll(rmask);
+            const float cs_end = __shfl(cs, 63);
+            sDt[lane] = dt;
+            sCs[lane] = cs;
+            sSeg[lane] = sg;
+            sW[lane] = (sg == sg_end) ? exp2_fast(cs_end - cs) * dt : 0.0f;
+            sScale[lane] = (sg == 0) ? exp2_fast(cs) : 0.0f;
+        }
+        __syncthreads();
+
+        // ---- 2. M = mask(C B^T), the chunk-entry state as bf16, dt-weighted B^T
+        if constexpr (OUTPUT) {
+            const int ti = wave >> 1;
+            const int kread = 2 * (ti / 2 + 1);            // column tiles of M read for row tile ti
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int tj = (wave & 1) + 2 * jj;
+                if (tj >= kread) continue;
+                f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (tj <= ti) {
+#pragma unroll
+                    for (int kb = 0; kb < NP / 32; ++kb)
+                        g = mma(frag(sC + (16 * ti + l16) * SN + 32 * kb + 8 * lg),
+                                frag(sB + (16 * tj + l16) * SN + 32 * kb + 8 * lg), g);
+                }
+                const int s = 16 * tj + l16;
+                const float cs_s = sCs[s], dt_s = sDt[s];
+                const int sg_s = sSeg[s];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * ti + 4 * lg + i;
+                    float m = 0.0f;
+                    if (s <= t && sSeg[t] == sg_s) m = g[i] * exp2_fast(sCs[t] - cs_s) * dt_s;
+                    sM[t * SQ + s] = f32_to_bf16(m);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kSt; ++j) {
+                const int k = wave + kWaves * j;
+                if (k < kT) {
+                    const int nb = k / kTP, pb = k % kTP;
+                    const u32x2_t v = {pack2(st[j][0], st[j][1]), pack2(st[j][2], st[j][3])};
+                    *reinterpret_cast<u32x2_t*>(sHT + (16 * pb + l16) * SN + 16 * nb + 4 * lg) = v;
+                }
+            }
+        }
+        for (int i = tid; i < kQ * kVN; i += kThreads) {
+            const int s = i / kVN, n0 = (i % kVN) * 8;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sB + s * SN + n0);
+            const float w = sW[s];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sBw[(n0 + 2 * j) * SQ + s] = f32_to_bf16(lo_bf16(v[j]) * w);
+                sBw[(n0 + 2 * j + 1) * SQ + s] = f32_to_bf16(hi_bf16(v[j]) * w);
+            }
+        }
+        __syncthreads();
+
+        // ---- 3. products: Y = scale (C H_in) + M x;  H = g H + (dt-weighted B)^T x
+        const float g_chunk = sScale[kQ - 1];
+        f32x4_t y[kYw];
+        if constexpr (OUTPUT) {
+#pragma unroll
+            for (int j = 0; j < kYw; ++j) {
+                const int k = wave + kWaves * j;
+                y[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                if (k < kTY) {
+                    const int ti = k / kTP, tp = k % kTP;
+#pragma unroll
+                    for (int kb = 0; kb < NP / 32; ++kb)
+                        y[j] = mma(frag(sC + (16 * ti + l16) * SN + 32 * kb + 8 * lg),
+                                   frag(sHT + (16 * tp + l16) * SN + 32 * kb + 8 * lg), y[j]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[j][i] *= sScale[16 * ti + 4 * lg + i];
+                    for (int kb = 0; kb <= ti / 2; ++kb)
+                        y[j] = mma(frag(sM + (16 * ti + l16) * SQ + 32 * kb + 8 * lg),
+                                   frag(sXT + (16 * tp + l16) * SQ + 32 * kb + 8 * lg), y[j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kSt; ++j) {
+            const int k = wave + kWaves * j;
+            if (k < kT) {
+                const int nb = k / kTP, pb = k % kTP;
+                st[j] *= g_chunk;
+#pragma unroll
+                for (int kb = 0; kb < kQ / 32; ++kb)
+                    st[j] = mma(frag(sBw + (16 * nb + l16) * SQ + 32 * kb + 8 * lg),
+                                frag(sXT + (16 * pb + l16) * SQ + 32 * kb + 8 * lg), st[j]);
+            }
+        }
+        seg_decay *= g_chunk;
+
+        // ---- 4. outputs: Y through LDS (it reuses the B rows), then coalesced rows
+        if constexpr (OUTPUT) {
+#pragma unroll
+            for (int j = 0; j < kYw; ++j) {
+                const int k = wave + kWaves * j;
+                if (k < kTY) {
+                    const int ti = k / kTP, tp = k % kTP;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sY[(16 * ti + 4 * lg + i) * SY + 16 * tp + l16] = y[j][i];
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < kQ * kVP; i += kThreads) {
+                const int row = i / kVP;
+                const int64_t tg = t0 + row;
+                if (tg >= t_seg1) continue;
+                const int64_t off = (static_cast<int64_t>(b) * L + tg) * p.dim + h * P + ep0;
+                const u32x4_t vx = *reinterpret_cast<const u32x4_t*>(p.u + off);
+                u32x4_t vz = {0u, 0u, 0u, 0u};
+                if constexpr (HAS_Z) vz = *reinterpret_cast<const u32x4_t*>(p.z + off);
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xv = (e & 1) ? hi_bf16(vx[e / 2]) : lo_bf16(vx[e / 2]);
+                    float yv = __builtin_fmaf(Dp[e], xv, sY[row * SY + ep0 + e]);
+                    if constexpr (HAS_Z) yv *= silu_f((e & 1) ? hi_bf16(vz[e / 2]) : lo_bf16(vz[e / 2]));
+                    o[e] = yv;
+                }
+                const u32x4_t vo = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+                *reinterpret_cast<u32x4_t*>(p.out + off) = vo;
+            }
+        }
+        __syncthreads();            // the next chunk overwrites every LDS tile
+    }
+
+#pragma unroll
+    for (int j = 0; j < kSt; ++j) {
+        const int k = wave + kWaves * j;
+        if (k >= kT) continue;
+        const int nb = k / kTP, pb = k % kTP;
+        const int pp = 16 * pb + l16;
+        float* dst;
+        if constexpr (OUTPUT) {
+            if (seg != p.nseg - 1 || p.final_state == nullptr) continue;
+            dst = p.final_state + (static_cast<int64_t>(b) * p.dim + h * P + pp) * N;
+        } else {
+            dst = p.ws_H + (bh * nslot + seg) * PN + static_cast<int64_t>(pp) * N;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = 16 * nb + 4 * lg + i;
+            if (n < N) dst[n] = st[j][i];
+        }
+    }
+    if (!OUTPUT && tid == 0) p.ws_G[bh * nslot + seg] = seg_decay;
+}
+
+// Pass 2: carry_{k+1} = G_k carry_k + H_k over the segments of each (row, head),
+// written over H_k (which then holds the state entering segment k + 1).
+__global__ __launch_bounds__(256) void ssd_carry_kernel(float* __restrict__ ws_H, const float* __restrict__ ws_G,
+                                                        int64_t nbh, int nslot, int64_t PN) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= nbh * PN) return;
+    const int64_t bh = i / PN, e = i % PN;
+    float c = 0.0f;
+    for (int k = 0; k < nslot; ++k) {
+        float* hp = ws_H + (bh * nslot + k) * PN + e;
+        c = __builtin_fmaf(ws_G[bh * nslot + k], c, *hp);
+        *hp = c;
+    }
+}
+
+struct SsdPlan {
+    int nseg;
+    int64_t seg_len;
+};
+
+SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int nheads) {
+    SsdPlan s{1, kQ};
+    if (seqlen <= 0) return s;
+    const int64_t bh = batch * nheads;
+    const int64_t nchunks = (seqlen + kQ - 1) / kQ;
+    int64_t want = bh > 0 ? (kTargetBlocks + bh - 1) / bh : 1;
+    if (want > nchunks) want = nchunks;
+    if (want < 1) want = 1;
+    const int64_t per_seg = (nchunks + want - 1) / want;
+    s.seg_len = per_seg * kQ;
+    s.nseg = static_cast<int>((seqlen + s.seg_len - 1) / s.seg_len);
+    return s;
+}
+
+template <int NP, int P, bool OUTPUT, bool HAS_Z>
+void launch_chunk(const SsdParams& p, bool softplus, unsigned blocks, hipStream_t stream) {
+    if (softplus)
+        hipLaunchKernelGGL((ssd_chunk_kernel<NP, P, OUTPUT, HAS_Z, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((ssd_chunk_kernel<NP, P, OUTPUT, HAS_Z, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+}
+
+template <int NP, int P>
+hipError_t launch_ssd_typed(const ScanArgs& a, const SsdPlan& plan) {
+    SsdParams p;
+    p.u = static_cast<const uint16_t*>(a.u);
+    p.delta = static_cast<const uint16_t*>(a.delta);
+    p.A = a.A;
+    p.B = static_cast<const uint16_t*>(a.B);
+    p.C = static_cast<const uint16_t*>(a.C);
+    p.D = a.D;
+    p.z = static_cast<const uint16_t*>(a.z);
+    p.delta_bias = a.delta_bias;
+    p.doc_start = a.doc_start;
+    p.out = static_cast<uint16_t*>(a.out);
+    p.final_state = a.final_state;
+    const int64_t nbh = a.batch * a.nheads;
+    const int nslot = plan.nseg - 1;
+    const int64_t PN = static_cast<int64_t>(P) * a.dstate;
+    p.ws_H = a.ws;
+    p.ws_G = a.ws ? a.ws + nbh * nslot * PN : nullptr;
+    p.seqlen = a.seqlen;
+    p.seg_len = plan.seg_len;
+    p.dim = static_cast<int>(a.dim);
+    p.nheads = a.nheads;
+    p.dstate = static_cast<int>(a.dstate);
+    p.nseg = plan.nseg;
+    p.nbatch = static_cast<int>(a.batch);
+
+    const unsigned blocks = static_cast<unsigned>(nbh * plan.nseg);
+    if (nslot > 0) {
+        launch_chunk<NP, P, false, false>(p, a.softplus, blocks, a.stream);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t count = nbh * PN;
+        hipLaunchKernelGGL(ssd_carry_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0,
+                           a.stream, p.ws_H, p.ws_G, nbh, nslot, PN);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.z) launch_chunk<NP, P, true, true>(p, a.softplus, blocks, a.stream);
+    else launch_chunk<NP, P, true, false>(p, a.softplus, blocks, a.stream);
+    return hipGetLastError();
+}
+
+template <int NP>
+hipError_t launch_ssd_np(const ScanArgs& a, const SsdPlan& plan) {
+    switch (a.dim / a.nheads) {
+        case 32: return launch_ssd_typed<NP, 32>(a, plan);
+        case 64: return launch_ssd_typed<NP, 64>(a, plan);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool ssd_supported(int64_t dim, int64_t dstate, int nheads) {
+    if (nheads <= 0 || dim % nheads != 0) return false;
+    const int64_t P = dim / nheads;
+    return (P == 32 || P == 64) && dstate % 8 == 0 && dstate >= 8 && dstate <= 128;
+}
+
+size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads) {
+    const SsdPlan plan = plan_ssd(batch, seqlen, nheads);
+    if (plan.nseg <= 1) return 0;
+    const int64_t nbh = batch * nheads;
+    const int64_t slots = nbh * (plan.nseg - 1);
+    return static_cast<size_t>(slots * (dim / nheads) * dstate + slots) * sizeof(float);
+}
+
+hipError_t launch_ssd(const ScanArgs& a) {
+    const SsdPlan plan = plan_ssd(a.batch, a.seqlen, a.nheads);
+    if (a.dstate <= 32) return launch_ssd_np<32>(a, plan);
+    if (a.dstate <= 64) return launch_ssd_np<64>(a, plan);
+    return launch_ssd_np<128>(a, plan);
+}
+
+}  // namespace mamba

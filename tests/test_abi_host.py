@@ -93,6 +93,17 @@ def test_workspace_query(lib):
     assert ws_bytes(lib, dims(nheads=24, dstate=128))[0] == _lib.MAMBA_OK
     assert ws_bytes(lib, dims(dtype=3))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
     assert ws_bytes(lib, dims(dstate=0))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    # scalar-A heads with bf16 I/O: headdim 32 or 64, a multiple of 8 states up to 128
+    assert ws_bytes(lib, dims(nheads=32, dstate=128))[0] == _lib.MAMBA_ERR_UNSUPPORTED      # headdim 48
+    assert ws_bytes(lib, dims(nheads=24, dstate=12))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    assert ws_bytes(lib, dims(nheads=24, dstate=136))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    assert ws_bytes(lib, dims(nheads=24, dstate=24))[0] == _lib.MAMBA_OK
+    assert ws_bytes(lib, dims(nheads=32, dstate=128, dtype=0))[0] == _lib.MAMBA_OK           # f32: recurrent form
+    assert ws_bytes(lib, dims(nheads=24, dstate=24, dtype=0))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    st, n = ws_bytes(lib, dims(nheads=24, dstate=128, seqlen=64))
+    assert st == _lib.MAMBA_OK and n == 0                 # one chunk: no carries
+    st, n = ws_bytes(lib, dims(nheads=24, dstate=128, seqlen=32768))
+    assert st == _lib.MAMBA_OK and n > 0
     assert lib.mamba_selective_scan_workspace_bytes(None, None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
 
 
@@ -112,6 +123,9 @@ def test_scan_validation(lib):
     assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=3)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert scan(lib, out=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT           # out overlaps u
     assert scan(lib, fs=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT        # final_state overlaps out
+    heads = dims(batch=1, seqlen=64, dim=64, nheads=2, dstate=16)
+    assert scan(lib, d=heads, u=FAKE + 8) == _lib.MAMBA_ERR_MISALIGNED       # bf16 heads: 16-byte vectors
+    assert scan(lib, d=heads, C=FAKE * 5 + 8) == _lib.MAMBA_ERR_MISALIGNED
     # a multi-chunk shape without workspace, then with a too small one
     big = dims(batch=1, seqlen=100000, dim=64)
     st, need = ws_bytes(lib, big)

@@ -113,6 +113,9 @@ SCAN_CASES = [
     (1, 300, 128, 32, 4, "bf16", 70.0),      # heads, headdim 32: one wave spans two heads
     (2, 200, 128, 64, 2, "f32", 50.0),
     (1, 260, 192, 128, 3, "bf16", 80.0),
+    (1, 333, 64, 8, 2, "bf16", 40.0),        # heads: headdim 32, 8 states (padded to 32 in the products)
+    (2, 450, 128, 24, 2, "bf16", 60.0),      # heads: 24 states
+    (1, 200, 64, 128, 2, "bf16", 30.0),      # heads: headdim 32, 128 states
 ]
 
 
@@ -146,6 +149,17 @@ def test_scan_documents_at_chunk_edges(ssm):
     for t in (63, 64, 65, 127, 128, 192, 256, 320, 399):
         inp.doc_start[0, t] = 1
     inp.doc_start[1, 64::64] = 1
+    scan_case(ssm, inp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_heads_documents_at_chunk_edges(ssm, dtype):
+    """Scalar-A heads: starts on either side of the 64-token chunk edges, a row with
+    a start on every token, and a row with none."""
+    inp = make_custom(3, 400, 128, 32, nheads=2, dtype=dtype, docs=None, seed=310)
+    for t in (1, 62, 63, 64, 65, 127, 128, 129, 255, 256, 320, 399):
+        inp.doc_start[0, t] = 1
+    inp.doc_start[1, :] = 1
     scan_case(ssm, inp)
 
 
