@@ -85,6 +85,13 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load of the wave, which would stall the next chunk's
+// prefetch at each barrier; here the wave waits for its own LDS operations
+// (lgkmcnt) and then meets the others.  The "memory" clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -180,36 +187,89 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
     }
     float seg_decay = 1.0f;
 
-    // Per-thread constants of the output epilogue: each thread always handles the
-    // same 8 channels (kThreads is a multiple of kVP).
-    const int ep0 = (tid % kVP) * 8;
+    // Global data of one chunk, held in registers one chunk ahead so that its
+    // loads overlap the current chunk's products.
+    //   B, C rows: vector i = tid + kThreads k is (row i / kVN, states 8 (i % kVN) ..)
+    //   x, z:      vector tid is (token tid % 64, channels 8 (tid / 64) ..); the same
+    //              thread later writes that token's 8 outputs.  Tokens run along the
+    //              lanes so that the transposed 2-byte LDS writes of x hit distinct banks.
+    //   wave 0:    lane = token: raw delta and the document-start flag.
+    constexpr int kBV = (kQ * kVN + kThreads - 1) / kThreads;
+    const bool x_thread = tid < kQ * kVP;
+    const int x_row = tid % kQ;
+    const int x_p0 = (tid / kQ) * 8;
     float Dp[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Dp[e] = (OUTPUT && p.D) ? p.D[h * P + ep0 + e] : 0.0f;
+    for (int e = 0; e < 8; ++e) Dp[e] = (OUTPUT && p.D && x_thread) ? p.D[h * P + x_p0 + e] : 0.0f;
 
+    // Every prefetch load is unconditional (row and state indices clamped into
+    // range) and nothing inspects its value until the chunk is staged, so no wait
+    // for it is needed before then; rows past the segment end and padded states
+    // are zeroed while staging.
+    u32x4_t pb_[kBV], pc_[kBV], px_, pz_;
+    uint32_t pdelta = 0, pflag = 0;
+    auto fetch = [&](int64_t c0) {
+#pragma unroll
+        for (int k = 0; k < kBV; ++k) {
+            const int i = tid + kThreads * k;
+            if (i < kQ * kVN) {
+                const int row = i / kVN, n0 = (i % kVN) * 8;
+                const int64_t tg = (c0 + row < t_seg1) ? c0 + row : t_seg1 - 1;
+                const int nc = n0 < N ? n0 : N - 8;
+                pb_[k] = *reinterpret_cast<const u32x4_t*>(Brow + tg * N + nc);
+                if (OUTPUT) pc_[k] = *reinterpret_cast<const u32x4_t*>(Crow + tg * N + nc);
+            }
+        }
+        if (x_thread) {
+            const int64_t tx = (c0 + x_row < t_seg1) ? c0 + x_row : t_seg1 - 1;
+            const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
+            px_ = *reinterpret_cast<const u32x4_t*>(p.u + off);
+            if (OUTPUT && HAS_Z) pz_ = *reinterpret_cast<const u32x4_t*>(p.z + off);
+        }
+        if (wave == 0) {
+            const int64_t tg = (c0 + lane < t_seg1) ? c0 + lane : t_seg1 - 1;
+            const int64_t row = static_cast<int64_t>(b) * L + tg;
+            pdelta = p.delta[row * p.nheads + h];
+            if (p.doc_start != nullptr) pflag = p.doc_start[row];
+        }
+    };
+
+    // Let the loads above (carry, D) land before the chunk loop: otherwise the wait
+    // for them sits inside the loop and also drains every chunk's prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (t_seg0 < t_seg1) fetch(t_seg0);
     for (int64_t t0 = t_seg0; t0 < t_seg1; t0 += kQ) {
         // ---- 1. stage the chunk: B (and C) rows, x transposed, per-token scalars
-        for (int i = tid; i < kQ * kVN; i += kThreads) {
-            const int row = i / kVN, n0 = (i % kVN) * 8;
-            const int64_t tg = t0 + row;
-            u32x4_t vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
-            if (tg < t_seg1 && n0 < N) {
-                vb = *reinterpret_cast<const u32x4_t*>(Brow + tg * N + n0);
-                if (OUTPUT) vc = *reinterpret_cast<const u32x4_t*>(Crow + tg * N + n0);
+        const u32x4_t kZero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < kBV; ++k) {
+            const int i = tid + kThreads * k;
+            if (i < kQ * kVN) {
+                const int row = i / kVN, n0 = (i % kVN) * 8;
+                const bool keep = t0 + row < t_seg1 && n0 < N;
+                *reinterpret_cast<u32x4_t*>(sB + row * SN + n0) = keep ? pb_[k] : kZero;
+                if (OUTPUT) *reinterpret_cast<u32x4_t*>(sC + row * SN + n0) = keep ? pc_[k] : kZero;
             }
-            *reinterpret_cast<u32x4_t*>(sB + row * SN + n0) = vb;
-            if (OUTPUT) *reinterpret_cast<u32x4_t*>(sC + row * SN + n0) = vc;
         }
-        for (int i = tid; i < kQ * kVP; i += kThreads) {
-            const int row = i / kVP, p0 = (i % kVP) * 8;
-            const int64_t tg = t0 + row;
-            u32x4_t vx = {0u, 0u, 0u, 0u};
-            if (tg < t_seg1)
-                vx = *reinterpret_cast<const u32x4_t*>(p.u + (static_cast<int64_t>(b) * L + tg) * p.dim + h * P + p0);
+        const bool x_valid = t0 + x_row < t_seg1;
+        u32x4_t cx = kZero;
+        float gate[8];           // silu(z), taken now so the epilogue waits on no load
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gate[e] = 1.0f;
+        if (x_thread) {
+            cx = x_valid ? px_ : kZero;
+            // Pin cx here: the epilogue then reads a value defined at this point
+            // rather than the load itself, whose wait would drain the next prefetch.
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(cx[j]));
+            if constexpr (OUTPUT && HAS_Z) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) gate[e] = silu_f((e & 1) ? hi_bf16(pz_[e / 2]) : lo_bf16(pz_[e / 2]));
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                sXT[(p0 + 2 * j) * SQ + row] = static_cast<uint16_t>(vx[j] & 0xffffu);
-                sXT[(p0 + 2 * j + 1) * SQ + row] = static_cast<uint16_t>(vx[j] >> 16);
+                sXT[(x_p0 + 2 * j) * SQ + x_row] = static_cast<uint16_t>(cx[j] & 0xffffu);
+                sXT[(x_p0 + 2 * j + 1) * SQ + x_row] = static_cast<uint16_t>(cx[j] >> 16);
             }
         }
         if (wave == 0) {
@@ -218,14 +278,11 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
             const int64_t tg = t0 + lane;
             const bool valid = tg < t_seg1;
             float dt = 0.0f;
-            bool reset = false;
             if (valid) {
-                const int64_t row = static_cast<int64_t>(b) * L + tg;
-                float v = bf16_to_f32(p.delta[row * p.nheads + h]) + dbias;
-                if constexpr (SOFTPLUS) v = softplus_f(v);
-                dt = v;
-                reset = tg == 0 || (p.doc_start != nullptr && p.doc_start[row] != 0);
+                dt = bf16_to_f32(static_cast<uint16_t>(pdelta)) + dbias;
+                if constexpr (SOFTPLUS) dt = softplus_f(dt);
             }
+            const bool reset = valid && (tg == 0 || pflag != 0);
             float cs = dt * a_l2;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -242,7 +299,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
             sW[lane] = (sg == sg_end) ? exp2_fast(cs_end - cs) * dt : 0.0f;
             sScale[lane] = (sg == 0) ? exp2_fast(cs) : 0.0f;
         }
-        __syncthreads();
+        if (t0 + kQ < t_seg1) fetch(t0 + kQ);
+        lds_barrier();
 
         // ---- 2. M = mask(C B^T), the chunk-entry state as bf16, dt-weighted B^T
         if constexpr (OUTPUT) {
@@ -280,8 +338,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
                 }
             }
         }
+        // dt-weighted B^T: tokens along the lanes, so the 2-byte transposed writes
+        // land on consecutive addresses.
         for (int i = tid; i < kQ * kVN; i += kThreads) {
-            const int s = i / kVN, n0 = (i % kVN) * 8;
+            const int s = i % kQ, n0 = (i / kQ) * 8;
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sB + s * SN + n0);
             const float w = sW[s];
 #pragma unroll
@@ -290,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
                 sBw[(n0 + 2 * j + 1) * SQ + s] = f32_to_bf16(hi_bf16(v[j]) * w);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 3. products: Y = scale (C H_in) + M x;  H = g H + (dt-weighted B)^T x
         const float g_chunk = sScale[kQ - 1];
@@ -328,7 +388,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
         }
         seg_decay *= g_chunk;
 
-        // ---- 4. outputs: Y through LDS (it reuses the B rows), then coalesced rows
+        // ---- 4. outputs: Y through LDS (it reuses the B rows); each thread finishes
+        //         the 8 channels of one token whose x and z it fetched
         if constexpr (OUTPUT) {
 #pragma unroll
             for (int j = 0; j < kYw; ++j) {
@@ -339,28 +400,21 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
                     for (int i = 0; i < 4; ++i) sY[(16 * ti + 4 * lg + i) * SY + 16 * tp + l16] = y[j][i];
                 }
             }
-            __syncthreads();
-            for (int i = tid; i < kQ * kVP; i += kThreads) {
-                const int row = i / kVP;
-                const int64_t tg = t0 + row;
-                if (tg >= t_seg1) continue;
-                const int64_t off = (static_cast<int64_t>(b) * L + tg) * p.dim + h * P + ep0;
-                const u32x4_t vx = *reinterpret_cast<const u32x4_t*>(p.u + off);
-                u32x4_t vz = {0u, 0u, 0u, 0u};
-                if constexpr (HAS_Z) vz = *reinterpret_cast<const u32x4_t*>(p.z + off);
+            lds_barrier();
+            const int64_t tx = t0 + x_row;
+            if (x_thread && tx < t_seg1) {
+                const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
                 float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float xv = (e & 1) ? hi_bf16(vx[e / 2]) : lo_bf16(vx[e / 2]);
-                    float yv = __builtin_fmaf(Dp[e], xv, sY[row * SY + ep0 + e]);
-                    if constexpr (HAS_Z) yv *= silu_f((e & 1) ? hi_bf16(vz[e / 2]) : lo_bf16(vz[e / 2]));
-                    o[e] = yv;
+                    const float xv = (e & 1) ? hi_bf16(cx[e / 2]) : lo_bf16(cx[e / 2]);
+                    o[e] = __builtin_fmaf(Dp[e], xv, sY[x_row * SY + x_p0 + e]) * gate[e];
                 }
                 const u32x4_t vo = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
                 *reinterpret_cast<u32x4_t*>(p.out + off) = vo;
             }
         }
-        __syncthreads();            // the next chunk overwrites every LDS tile
+        lds_barrier();            // the next chunk overwrites every LDS tile
     }
 
 #pragma unroll
