@@ -22,14 +22,19 @@
 // and fp32 accumulation.  The state H of a head lives in fp32 MFMA accumulators
 // across all chunks of a segment.
 //
-// Parallelism: one workgroup (8 waves) per (row, head, segment of L).  Segments
-// are joined like the chunks of the per-channel scan: pass 1 computes every
-// segment's end state from zero and its total decay, pass 2 carries the states
-// across segments, pass 3 recomputes each segment from its carry and writes the
-// outputs.  Workgroups of the same (row, segment) read the same B and C rows, so
-// the block index is remapped to keep all heads of one (row, segment) on one XCD
-// (the dispatcher deals consecutive workgroups round-robin to the 8 XCDs, each
-// with its own L2).
+// Parallelism: one workgroup (8 waves) per (row, head, segment of L).
+// Segments are joined like the chunks of the per-channel scan: pass 1 computes
+// every segment's end state from zero and its total decay, pass 2 carries the
+// states across segments, pass 3 recomputes each segment from its carry and
+// writes the outputs.  Workgroups of the same (row, segment) read the same B and
+// C rows, so the block index is remapped to keep all heads of one (row, segment)
+// on one XCD (the dispatcher deals consecutive workgroups round-robin to the 8
+// XCDs, each with its own L2).
+//
+// Work of wave w in a chunk: half of output row tile w / 2 (tokens 16 (w / 2) ..
+// + 15, channel half w % 2), half of the C B^T tiles of that row, and state
+// tiles k = w, w + 8, ...  Its C rows come straight from global memory into MFMA
+// fragments; B, x and the per-token scalars are shared through LDS.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -44,6 +49,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kQ = 64;                  // tokens per chunk
 constexpr int kWaves = 8;
+constexpr int kRowW = kWaves / 4;       // waves sharing one 16-token output row tile
 constexpr int kThreads = 64 * kWaves;
 constexpr int64_t kTargetBlocks = 768;  // workgroups per pass (three per CU)
 constexpr int kXcds = 8;
@@ -92,6 +98,11 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Makes v a value defined here, so later uses do not wait on the load it came
+// from (a wait there would also drain every load issued after it).
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(u32x4_t& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -101,16 +112,15 @@ template <int NP, int P, bool OUTPUT>
 struct SsdLds {
     static constexpr int SN = NP + 8;              // [*][NP] bf16 tiles
     static constexpr int SQ = kQ + 8;              // [*][Q] bf16 tiles
-    static constexpr int SY = P + 4;               // fp32 Y tile
+    static constexpr int SY = P / kRowW + 4;       // per-wave fp32 output tile [16][SY]
     static constexpr int kBBytes = kQ * SN * 2;
-    static constexpr int kYBytes = OUTPUT ? kQ * SY * 4 : 0;
-    static constexpr int oC = 0;                                   // C rows [t][n]
-    static constexpr int oB = oC + (OUTPUT ? kQ * SN * 2 : 0);     // B rows [s][n], later Y [t][p] fp32
-    static constexpr int oBw = oB + (kBBytes > kYBytes ? kBBytes : kYBytes);  // weighted B^T [n][s]
-    static constexpr int oXT = oBw + NP * SQ * 2;                  // x^T [p][s]
-    static constexpr int oM = oXT + P * SQ * 2;                    // M [t][s]
-    static constexpr int oHT = oM + (OUTPUT ? kQ * SQ * 2 : 0);    // chunk-entry state^T [p][n]
-    static constexpr int oTok = oHT + (OUTPUT ? P * SN * 2 : 0);   // per-token scalars
+    static constexpr int kYBytes = OUTPUT ? kWaves * 16 * SY * 4 : 0;
+    static constexpr int oB = 0;                                    // B rows [s][n]; later the output tiles
+    static constexpr int oBw = oB + (kBBytes > kYBytes ? kBBytes : kYBytes);   // dt-weighted B^T [n][s]
+    static constexpr int oXT = oBw + NP * SQ * 2;                   // x^T [p][s]
+    static constexpr int oM = oXT + P * SQ * 2;                     // M [t][s]
+    static constexpr int oHT = oM + (OUTPUT ? kQ * SQ * 2 : 0);     // chunk-entry state^T [p][n]
+    static constexpr int oTok = oHT + (OUTPUT ? P * SN * 2 : 0);    // per-token scalars
     static constexpr int kBytes = oTok + 5 * kQ * 4;
 };
 
@@ -121,15 +131,16 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
     constexpr int kTN = NP / 16, kTP = P / 16;
     constexpr int kT = kTN * kTP;                          // state tiles
     constexpr int kSt = (kT + kWaves - 1) / kWaves;        // state tiles per wave
-    constexpr int kTY = (kQ / 16) * kTP;                   // output tiles
-    constexpr int kYw = (kTY + kWaves - 1) / kWaves;
-    constexpr int kVN = NP / 8;                            // 16-byte vectors per B/C row
-    constexpr int kVP = P / 8;                             // 16-byte vectors per x row
+    constexpr int kKB = NP / 32;                           // K blocks over the states
+    constexpr int kVN = NP / 8;                            // 16-byte vectors per B row
+    constexpr int kBV = (kQ * kVN + kThreads - 1) / kThreads;
+    constexpr int kPW = P / kRowW;                         // channels of a wave's output tile part
+    constexpr int kTPW = kPW / 16;                         // its 16-channel tiles
+    constexpr int kLPR = kPW / 8;                          // lanes per token row (8 channels each)
+    constexpr int kBwTasks = (kQ / 2) * kVN;               // (token pair, 8 states) tasks
 
     __shared__ __attribute__((aligned(16))) unsigned char lds[Lay::kBytes];
-    uint16_t* sC = reinterpret_cast<uint16_t*>(lds + Lay::oC);
     uint16_t* sB = reinterpret_cast<uint16_t*>(lds + Lay::oB);
-    float* sY = reinterpret_cast<float*>(lds + Lay::oB);
     uint16_t* sBw = reinterpret_cast<uint16_t*>(lds + Lay::oBw);
     uint16_t* sXT = reinterpret_cast<uint16_t*>(lds + Lay::oXT);
     uint16_t* sM = reinterpret_cast<uint16_t*>(lds + Lay::oM);
@@ -145,6 +156,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
     const int wave = tid >> 6;
     const int l16 = lane & 15;
     const int lg = lane >> 4;
+    float* sYw = reinterpret_cast<float*>(lds + Lay::oB) + wave * 16 * SY;   // this wave's output tile
 
     // Workgroup -> (row, segment, head); all heads of a (row, segment) share an XCD.
     const int total = p.nbatch * p.nheads * p.nseg;
@@ -187,26 +199,23 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
     }
     float seg_decay = 1.0f;
 
-    // Global data of one chunk, held in registers one chunk ahead so that its
-    // loads overlap the current chunk's products.
-    //   B, C rows: vector i = tid + kThreads k is (row i / kVN, states 8 (i % kVN) ..)
-    //   x, z:      vector tid is (token tid % 64, channels 8 (tid / 64) ..); the same
-    //              thread later writes that token's 8 outputs.  Tokens run along the
-    //              lanes so that the transposed 2-byte LDS writes of x hit distinct banks.
-    //   wave 0:    lane = token: raw delta and the document-start flag.
-    constexpr int kBV = (kQ * kVN + kThreads - 1) / kThreads;
-    const bool x_thread = tid < kQ * kVP;
-    const int x_row = tid % kQ;
-    const int x_p0 = (tid / kQ) * 8;
+    // This wave's part of the chunk: output row tile `wt` (tokens 16 wt ..), channels
+    // wp .. wp + kPW - 1.  x staging and the epilogue: lane -> token x_row, channels
+    // x_p0 .. x_p0 + 7 (lanes past 16 kLPR idle).
+    const int wt = wave / kRowW;
+    const int wp = (wave % kRowW) * kPW;
+    const bool x_lane = lane < 16 * kLPR;
+    const int x_row = 16 * wt + (x_lane ? lane / kLPR : 0);
+    const int x_p0 = wp + (lane % kLPR) * 8;
     float Dp[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Dp[e] = (OUTPUT && p.D && x_thread) ? p.D[h * P + x_p0 + e] : 0.0f;
+    for (int e = 0; e < 8; ++e) Dp[e] = (OUTPUT && p.D) ? p.D[h * P + x_p0 + e] : 0.0f;
 
-    // Every prefetch load is unconditional (row and state indices clamped into
-    // range) and nothing inspects its value until the chunk is staged, so no wait
-    // for it is needed before then; rows past the segment end and padded states
-    // are zeroed while staging.
-    u32x4_t pb_[kBV], pc_[kBV], px_, pz_;
+    // Global data of one chunk, held in registers one chunk ahead so that its
+    // loads overlap the current chunk's work.  Every load is unconditional (token
+    // and state indices clamped into range): rows past the segment end only ever
+    // meet a zero step size, and padded states are zeroed when consumed.
+    u32x4_t pb_[kBV], pc_[kKB], px_, pz_;
     uint32_t pdelta = 0, pflag = 0;
     auto fetch = [&](int64_t c0) {
 #pragma unroll
@@ -215,17 +224,21 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
             if (i < kQ * kVN) {
                 const int row = i / kVN, n0 = (i % kVN) * 8;
                 const int64_t tg = (c0 + row < t_seg1) ? c0 + row : t_seg1 - 1;
-                const int nc = n0 < N ? n0 : N - 8;
-                pb_[k] = *reinterpret_cast<const u32x4_t*>(Brow + tg * N + nc);
-                if (OUTPUT) pc_[k] = *reinterpret_cast<const u32x4_t*>(Crow + tg * N + nc);
+                pb_[k] = *reinterpret_cast<const u32x4_t*>(Brow + tg * N + (n0 < N ? n0 : N - 8));
             }
         }
-        if (x_thread) {
-            const int64_t tx = (c0 + x_row < t_seg1) ? c0 + x_row : t_seg1 - 1;
-            const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
-            px_ = *reinterpret_cast<const u32x4_t*>(p.u + off);
-            if (OUTPUT && HAS_Z) pz_ = *reinterpret_cast<const u32x4_t*>(p.z + off);
+        if constexpr (OUTPUT) {
+            const int64_t tc = (c0 + 16 * wt + l16 < t_seg1) ? c0 + 16 * wt + l16 : t_seg1 - 1;
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb) {
+                const int n0 = 32 * kb + 8 * lg;
+                pc_[kb] = *reinterpret_cast<const u32x4_t*>(Crow + tc * N + (n0 < N ? n0 : N - 8));
+            }
         }
+        const int64_t tx = (c0 + x_row < t_seg1) ? c0 + x_row : t_seg1 - 1;
+        const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
+        px_ = *reinterpret_cast<const u32x4_t*>(p.u + off);
+        if (OUTPUT && HAS_Z) pz_ = *reinterpret_cast<const u32x4_t*>(p.z + off);
         if (wave == 0) {
             const int64_t tg = (c0 + lane < t_seg1) ? c0 + lane : t_seg1 - 1;
             const int64_t row = static_cast<int64_t>(b) * L + tg;
@@ -238,34 +251,33 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
     // for them sits inside the loop and also drains every chunk's prefetch.
     __builtin_amdgcn_s_waitcnt(0);
     if (t_seg0 < t_seg1) fetch(t_seg0);
+    const u32x4_t kZero = {0u, 0u, 0u, 0u};
     for (int64_t t0 = t_seg0; t0 < t_seg1; t0 += kQ) {
-        // ---- 1. stage the chunk: B (and C) rows, x transposed, per-token scalars
-        const u32x4_t kZero = {0u, 0u, 0u, 0u};
+        // ---- 1. take the prefetched chunk: B rows to LDS, x transposed to LDS,
+        //         per-token scalars, this wave's C fragments, the gate
 #pragma unroll
         for (int k = 0; k < kBV; ++k) {
             const int i = tid + kThreads * k;
             if (i < kQ * kVN) {
                 const int row = i / kVN, n0 = (i % kVN) * 8;
-                const bool keep = t0 + row < t_seg1 && n0 < N;
-                *reinterpret_cast<u32x4_t*>(sB + row * SN + n0) = keep ? pb_[k] : kZero;
-                if (OUTPUT) *reinterpret_cast<u32x4_t*>(sC + row * SN + n0) = keep ? pc_[k] : kZero;
+                *reinterpret_cast<u32x4_t*>(sB + row * SN + n0) = (n0 < N) ? pb_[k] : kZero;
             }
         }
-        const bool x_valid = t0 + x_row < t_seg1;
-        u32x4_t cx = kZero;
-        float gate[8];           // silu(z), taken now so the epilogue waits on no load
+        u32x4_t cf[kKB];
+        if constexpr (OUTPUT) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gate[e] = 1.0f;
-        if (x_thread) {
-            cx = x_valid ? px_ : kZero;
-            // Pin cx here: the epilogue then reads a value defined at this point
-            // rather than the load itself, whose wait would drain the next prefetch.
-#pragma unroll
-            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(cx[j]));
-            if constexpr (OUTPUT && HAS_Z) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) gate[e] = silu_f((e & 1) ? hi_bf16(pz_[e / 2]) : lo_bf16(pz_[e / 2]));
+            for (int kb = 0; kb < kKB; ++kb) {
+                cf[kb] = (32 * kb + 8 * lg < N) ? pc_[kb] : kZero;
+                pin(cf[kb]);
             }
+        }
+        u32x4_t cx = px_, cz = kZero;
+        pin(cx);
+        if constexpr (OUTPUT && HAS_Z) {
+            cz = pz_;
+            pin(cz);
+        }
+        if (x_lane) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 sXT[(x_p0 + 2 * j) * SQ + x_row] = static_cast<uint16_t>(cx[j] & 0xffffu);
@@ -274,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
         }
         if (wave == 0) {
             // Lane = token of the chunk.  Tokens past the segment end are identity
-            // steps (dt = 0) with zero B, C and x rows.
+            // steps (dt = 0).
             const int64_t tg = t0 + lane;
             const bool valid = tg < t_seg1;
             float dt = 0.0f;
@@ -302,19 +314,26 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
         if (t0 + kQ < t_seg1) fetch(t0 + kQ);
         lds_barrier();
 
-        // ---- 2. M = mask(C B^T), the chunk-entry state as bf16, dt-weighted B^T
+        // ---- 2. M = mask(C B^T): this wave's share of row tile wt; the chunk-entry
+        //         state as bf16; dt-weighted B^T
         if constexpr (OUTPUT) {
-            const int ti = wave >> 1;
-            const int kread = 2 * (ti / 2 + 1);            // column tiles of M read for row tile ti
+            const int ti = wt;
+            const int kread = 2 * (ti / 2 + 1);            // column tiles of M read by row tile ti
+            float cs_t[4];
+            int sg_t[4];
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int tj = (wave & 1) + 2 * jj;
-                if (tj >= kread) continue;
+            for (int i = 0; i < 4; ++i) {
+                cs_t[i] = sCs[16 * ti + 4 * lg + i];
+                sg_t[i] = sSeg[16 * ti + 4 * lg + i];
+            }
+#pragma unroll
+            for (int tj = wave % kRowW; tj < 4; tj += kRowW) {
+                if (tj >= kread) break;
                 f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
                 if (tj <= ti) {
 #pragma unroll
-                    for (int kb = 0; kb < NP / 32; ++kb)
-                        g = mma(frag(sC + (16 * ti + l16) * SN + 32 * kb + 8 * lg),
+                    for (int kb = 0; kb < kKB; ++kb)
+                        g = mma(__builtin_bit_cast(bf16x8_t, cf[kb]),
                                 frag(sB + (16 * tj + l16) * SN + 32 * kb + 8 * lg), g);
                 }
                 const int s = 16 * tj + l16;
@@ -323,9 +342,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = 16 * ti + 4 * lg + i;
-                    float m = 0.0f;
-                    if (s <= t && sSeg[t] == sg_s) m = g[i] * exp2_fast(sCs[t] - cs_s) * dt_s;
-                    sM[t * SQ + s] = f32_to_bf16(m);
+                    // Computed for every element, then selected: for s > t the
+                    // exponent can be positive, and the select drops any inf.
+                    const float m = g[i] * exp2_fast(cs_t[i] - cs_s) * dt_s;
+                    sM[t * SQ + s] = f32_to_bf16((s <= t && sg_t[i] == sg_s) ? m : 0.0f);
                 }
             }
 #pragma unroll
@@ -338,40 +358,49 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
                 }
             }
         }
-        // dt-weighted B^T: tokens along the lanes, so the 2-byte transposed writes
-        // land on consecutive addresses.
-        for (int i = tid; i < kQ * kVN; i += kThreads) {
-            const int s = i % kQ, n0 = (i / kQ) * 8;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sB + s * SN + n0);
-            const float w = sW[s];
+        // dt-weighted B^T, two tokens per task so each write is one 32-bit word;
+        // token pairs run along the lanes, so the writes hit consecutive words.
+        for (int i = tid; i < kBwTasks; i += kThreads) {
+            const int s = 2 * (i % (kQ / 2)), n0 = (i / (kQ / 2)) * 8;
+            const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(sB + s * SN + n0);
+            const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(sB + (s + 1) * SN + n0);
+            const float w0 = sW[s], w1 = sW[s + 1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                sBw[(n0 + 2 * j) * SQ + s] = f32_to_bf16(lo_bf16(v[j]) * w);
-                sBw[(n0 + 2 * j + 1) * SQ + s] = f32_to_bf16(hi_bf16(v[j]) * w);
+                *reinterpret_cast<uint32_t*>(sBw + (n0 + 2 * j) * SQ + s) =
+                    pack2(lo_bf16(v0[j]) * w0, lo_bf16(v1[j]) * w1);
+                *reinterpret_cast<uint32_t*>(sBw + (n0 + 2 * j + 1) * SQ + s) =
+                    pack2(hi_bf16(v0[j]) * w0, hi_bf16(v1[j]) * w1);
             }
         }
         lds_barrier();
 
-        // ---- 3. products: Y = scale (C H_in) + M x;  H = g H + (dt-weighted B)^T x
+        // ---- 3. products: Y = scale (C H_in) + M x for this wave's output tiles;
+        //         H = g H + (dt-weighted B)^T x for its state tiles
         const float g_chunk = sScale[kQ - 1];
-        f32x4_t y[kYw];
+        f32x4_t y[kTPW];
         if constexpr (OUTPUT) {
+            const int ti = wt;
+            float scale[4];
 #pragma unroll
-            for (int j = 0; j < kYw; ++j) {
-                const int k = wave + kWaves * j;
-                y[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                if (k < kTY) {
-                    const int ti = k / kTP, tp = k % kTP;
+            for (int i = 0; i < 4; ++i) scale[i] = sScale[16 * ti + 4 * lg + i];
 #pragma unroll
-                    for (int kb = 0; kb < NP / 32; ++kb)
-                        y[j] = mma(frag(sC + (16 * ti + l16) * SN + 32 * kb + 8 * lg),
-                                   frag(sHT + (16 * tp + l16) * SN + 32 * kb + 8 * lg), y[j]);
+            for (int tp = 0; tp < kTPW; ++tp) {
+                y[tp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) y[j][i] *= sScale[16 * ti + 4 * lg + i];
-                    for (int kb = 0; kb <= ti / 2; ++kb)
-                        y[j] = mma(frag(sM + (16 * ti + l16) * SQ + 32 * kb + 8 * lg),
-                                   frag(sXT + (16 * tp + l16) * SQ + 32 * kb + 8 * lg), y[j]);
-                }
+                for (int kb = 0; kb < kKB; ++kb)
+                    y[tp] = mma(__builtin_bit_cast(bf16x8_t, cf[kb]),
+                                frag(sHT + (wp + 16 * tp + l16) * SN + 32 * kb + 8 * lg), y[tp]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[tp][i] *= scale[i];
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb > ti / 2) break;
+                const bf16x8_t a = frag(sM + (16 * ti + l16) * SQ + 32 * kb + 8 * lg);
+#pragma unroll
+                for (int tp = 0; tp < kTPW; ++tp)
+                    y[tp] = mma(a, frag(sXT + (wp + 16 * tp + l16) * SQ + 32 * kb + 8 * lg), y[tp]);
             }
         }
 #pragma unroll
@@ -388,30 +417,30 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
         }
         seg_decay *= g_chunk;
 
-        // ---- 4. outputs: Y through LDS (it reuses the B rows); each thread finishes
-        //         the 8 channels of one token whose x and z it fetched
+        // ---- 4. outputs of this wave's tiles: they go through the wave's own LDS
+        //         area (over the B rows, which every wave is done with) to a
+        //         token-per-lane layout, then (Y + D x) silu(z) as bf16 rows
         if constexpr (OUTPUT) {
 #pragma unroll
-            for (int j = 0; j < kYw; ++j) {
-                const int k = wave + kWaves * j;
-                if (k < kTY) {
-                    const int ti = k / kTP, tp = k % kTP;
+            for (int tp = 0; tp < kTPW; ++tp)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sY[(16 * ti + 4 * lg + i) * SY + 16 * tp + l16] = y[j][i];
-                }
-            }
-            lds_barrier();
+                for (int i = 0; i < 4; ++i) sYw[(4 * lg + i) * SY + 16 * tp + l16] = y[tp][i];
             const int64_t tx = t0 + x_row;
-            if (x_thread && tx < t_seg1) {
-                const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
-                float o[8];
+            if (x_lane && tx < t_seg1) {
+                const float* yr = sYw + (x_row - 16 * wt) * SY + (x_p0 - wp);
+                uint32_t o[4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float xv = (e & 1) ? hi_bf16(cx[e / 2]) : lo_bf16(cx[e / 2]);
-                    o[e] = __builtin_fmaf(Dp[e], xv, sY[x_row * SY + x_p0 + e]) * gate[e];
+                for (int j = 0; j < 4; ++j) {
+                    float y0 = __builtin_fmaf(Dp[2 * j], lo_bf16(cx[j]), yr[2 * j]);
+                    float y1 = __builtin_fmaf(Dp[2 * j + 1], hi_bf16(cx[j]), yr[2 * j + 1]);
+                    if constexpr (HAS_Z) {
+                        y0 *= silu_f(lo_bf16(cz[j]));
+                        y1 *= silu_f(hi_bf16(cz[j]));
+                    }
+                    o[j] = pack2(y0, y1);
                 }
-                const u32x4_t vo = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
-                *reinterpret_cast<u32x4_t*>(p.out + off) = vo;
+                const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
+                *reinterpret_cast<u32x4_t*>(p.out + off) = u32x4_t{o[0], o[1], o[2], o[3]};
             }
         }
         lds_barrier();            // the next chunk overwrites every LDS tile
