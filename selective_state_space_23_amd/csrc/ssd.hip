@@ -51,8 +51,14 @@ constexpr int kQ = 64;                  // tokens per chunk
 constexpr int kWaves = 8;
 constexpr int kRowW = kWaves / 4;       // waves sharing one 16-token output row tile
 constexpr int kThreads = 64 * kWaves;
-constexpr int64_t kTargetBlocks = 768;  // workgroups per pass (three per CU)
+#ifndef MAMBA_SSD_TARGET_BLOCKS
+#define MAMBA_SSD_TARGET_BLOCKS 768
+#endif
+constexpr int64_t kTargetBlocks = MAMBA_SSD_TARGET_BLOCKS;  // workgroups per pass
 constexpr int kXcds = 8;
+#ifndef MAMBA_SSD_WAVES_PER_EU
+#define MAMBA_SSD_WAVES_PER_EU 2        // up to 256 VGPRs: one 8-wave workgroup per CU
+#endif
 
 struct SsdParams {
     const uint16_t* u;
@@ -103,6 +109,15 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void pin(u32x4_t& v) { asm volatile("" : "+v"(v)); }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    constexpr int kRsrcWord3 = 0x00020000;        // gfx9 data format: 32-bit, raw access
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
+}
+
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -125,7 +140,8 @@ struct SsdLds {
 };
 
 template <int NP, int P, bool OUTPUT, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_SSD_WAVES_PER_EU))) void ssd_chunk_kernel(
+    const SsdParams p) {
     using Lay = SsdLds<NP, P, OUTPUT>;
     constexpr int SN = Lay::SN, SQ = Lay::SQ, SY = Lay::SY;
     constexpr int kTN = NP / 16, kTP = P / 16;
@@ -217,33 +233,38 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(const SsdParams p) 
     // meet a zero step size, and padded states are zeroed when consumed.
     u32x4_t pb_[kBV], pc_[kKB], px_, pz_;
     uint32_t pdelta = 0, pflag = 0;
+    // Buffer resources per row: wave-uniform base and size in SGPRs, 32-bit byte
+    // offsets per lane (a row of any tensor is below 2 GiB, checked on the host).
+    // A load past a resource's end returns zeros.
+    const int64_t arow = L * p.dim;
+    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Brow, L * N * 2);
+    const __amdgpu_buffer_rsrc_t rsC = make_rsrc(Crow, L * N * 2);
+    const __amdgpu_buffer_rsrc_t rsU = make_rsrc(p.u + b * arow, arow * 2);
+    const __amdgpu_buffer_rsrc_t rsZ = make_rsrc(HAS_Z ? p.z + b * arow : p.u, arow * 2);
+    const __amdgpu_buffer_rsrc_t rsDl = make_rsrc(p.delta + b * L * p.nheads, L * p.nheads * 2);
+    const __amdgpu_buffer_rsrc_t rsDs = make_rsrc(p.doc_start ? p.doc_start + b * L : nullptr, p.doc_start ? L : 0);
+    const int xcol = h * P + x_p0;
     auto fetch = [&](int64_t c0) {
+        const int c0i = static_cast<int>(c0);
 #pragma unroll
         for (int k = 0; k < kBV; ++k) {
             const int i = tid + kThreads * k;
             if (i < kQ * kVN) {
                 const int row = i / kVN, n0 = (i % kVN) * 8;
-                const int64_t tg = (c0 + row < t_seg1) ? c0 + row : t_seg1 - 1;
-                pb_[k] = *reinterpret_cast<const u32x4_t*>(Brow + tg * N + (n0 < N ? n0 : N - 8));
+                pb_[k] = load16(rsB, ((c0i + row) * N + n0) * 2);
             }
         }
         if constexpr (OUTPUT) {
-            const int64_t tc = (c0 + 16 * wt + l16 < t_seg1) ? c0 + 16 * wt + l16 : t_seg1 - 1;
+            const int cbase = ((c0i + 16 * wt + l16) * N + 8 * lg) * 2;
 #pragma unroll
-            for (int kb = 0; kb < kKB; ++kb) {
-                const int n0 = 32 * kb + 8 * lg;
-                pc_[kb] = *reinterpret_cast<const u32x4_t*>(Crow + tc * N + (n0 < N ? n0 : N - 8));
-            }
+            for (int kb = 0; kb < kKB; ++kb) pc_[kb] = load16(rsC, cbase + 64 * kb);
         }
-        const int64_t tx = (c0 + x_row < t_seg1) ? c0 + x_row : t_seg1 - 1;
-        const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
-        px_ = *reinterpret_cast<const u32x4_t*>(p.u + off);
-        if (OUTPUT && HAS_Z) pz_ = *reinterpret_cast<const u32x4_t*>(p.z + off);
+        const int xoff = ((c0i + x_row) * p.dim + xcol) * 2;
+        px_ = load16(rsU, xoff);
+        if (OUTPUT && HAS_Z) pz_ = load16(rsZ, xoff);
         if (wave == 0) {
-            const int64_t tg = (c0 + lane < t_seg1) ? c0 + lane : t_seg1 - 1;
-            const int64_t row = static_cast<int64_t>(b) * L + tg;
-            pdelta = p.delta[row * p.nheads + h];
-            if (p.doc_start != nullptr) pflag = p.doc_start[row];
+            pdelta = __builtin_amdgcn_raw_buffer_load_b16(rsDl, ((c0i + lane) * p.nheads + h) * 2, 0, 0);
+            pflag = __builtin_amdgcn_raw_buffer_load_b8(rsDs, c0i + lane, 0, 0);
         }
     };
 
