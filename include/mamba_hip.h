@@ -123,10 +123,19 @@ int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* 
  *              bytes, 256-byte aligned; contents on entry are ignored, and it is
  *              scratch for chunk carries during the call.  May be NULL when the
  *              required size is 0.
- * Supported: ngroups == 1; N in {4, 8, 16} with nheads == 0; N in {16, 32, 64,
- * 128} with nheads > 0.  Others return MAMBA_ERR_UNSUPPORTED.
+ * Supported (others return MAMBA_ERR_UNSUPPORTED):
+ *   ngroups == 1, and (L + 64) * max(D, N) * 4 < 2^31 (a batch row of any
+ *   tensor is addressed with 32-bit offsets);
+ *   nheads == 0: N in {4, 8, 16};
+ *   nheads > 0, float32: N in {16, 32, 64, 128} (recurrent form, fp32 throughout);
+ *   nheads > 0, bf16: head size D / H in {32, 64} and N a multiple of 8 up to
+ *   128 (chunked matrix-product form: bf16 operands, fp32 accumulation and
+ *   state; Mamba skill page, "Mamba-2: Structured State Space Duality (SSD)").
  * Alignment: activations aligned to their element size; B and C rows must be
- * 4-byte aligned (N even for bf16).  B, L or D of 0 is a no-op. */
+ * 4-byte aligned (N even for bf16); with nheads > 0 and bf16, u, z, out, B and
+ * C must be 16-byte aligned.  Otherwise MAMBA_ERR_MISALIGNED.
+ * B, L or D of 0 is a no-op.
+ * Repeated calls with the same arguments give bitwise identical results. */
 int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims,
                              const void* u, const void* delta, const float* A,
                              const void* B, const void* C, const float* D,

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 
 #include "launch.hpp"
@@ -43,6 +44,10 @@ int check_dims(const mamba_scan_dims_t* d) {
     if (!mul_ok(d->batch, d->seqlen, d->dim, &n)) return MAMBA_ERR_INVALID_ARGUMENT;
     if (!mul_ok(d->batch, d->seqlen, d->dstate, &n)) return MAMBA_ERR_INVALID_ARGUMENT;
     if (d->ngroups != 1) return MAMBA_ERR_UNSUPPORTED;
+    // The scan kernels address one batch row of a tensor with 32-bit byte offsets
+    // (up to 64 tokens past the row end, which read as zeros).
+    const int64_t widest = d->dim > d->dstate ? d->dim : d->dstate;
+    if ((d->seqlen + 64) * widest * 4 > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
     if (!mamba::scan_supported(d->dim, d->dstate, d->nheads, d->dtype == MAMBA_DTYPE_BF16)) return MAMBA_ERR_UNSUPPORTED;
     return MAMBA_OK;
 }

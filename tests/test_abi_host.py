@@ -92,6 +92,8 @@ def test_workspace_query(lib):
     assert ws_bytes(lib, dims(nheads=7))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT     # 1536 % 7
     assert ws_bytes(lib, dims(nheads=24, dstate=128))[0] == _lib.MAMBA_OK
     assert ws_bytes(lib, dims(dtype=3))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert ws_bytes(lib, dims(seqlen=400000))[0] == _lib.MAMBA_ERR_UNSUPPORTED      # a row above 2 GiB at 4 B
+    assert ws_bytes(lib, dims(batch=1, seqlen=65536, dim=5120))[0] == _lib.MAMBA_OK
     assert ws_bytes(lib, dims(dstate=0))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
     # scalar-A heads with bf16 I/O: headdim 32 or 64, a multiple of 8 states up to 128
     assert ws_bytes(lib, dims(nheads=32, dstate=128))[0] == _lib.MAMBA_ERR_UNSUPPORTED      # headdim 48
