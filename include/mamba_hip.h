@@ -116,6 +116,12 @@ int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* 
  *   z          (B, L, D) or NULL (no gate).
  *   delta_bias (D|H,) float32 or NULL (zero).
  *   doc_start  (B, L) uint8 or NULL.
+ *   initial_state (B, D, N) float32 or NULL: the state before token 0 of each
+ *              row (e.g. the final_state of the preceding stretch of the same
+ *              rows).  With it, token 0 starts a new document only where
+ *              doc_start[b, 0] is set; without it, token 0 always does and the
+ *              state starts at zero.  Must not overlap out, final_state or the
+ *              workspace.
  *   out        (B, L, D)         y_t * silu(z_t), y_t = C_t . h_t + D u_t.
  *   final_state (B, D, N) float32 or NULL: h after token L-1 (the state of the
  *                                last document of each row).
@@ -140,8 +146,44 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims,
                              const void* u, const void* delta, const float* A,
                              const void* B, const void* C, const float* D,
                              const void* z, const float* delta_bias,
-                             const uint8_t* doc_start, void* out, float* final_state,
+                             const uint8_t* doc_start, const float* initial_state,
+                             void* out, float* final_state,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- One-token decode (Mamba skill page, "Dual Computation Modes": the
+ * recurrent mode used for generation).  A prefill with mamba_causal_conv1d_fwd
+ * and mamba_selective_scan_fwd followed by these steps gives the same outputs as
+ * one long call: the conv window holds the last three inputs x (not u) of each
+ * channel, the scan state is final_state. */
+
+/* Causal conv1d for one token per row.
+ *   x          (B, D)        input at this token, dtype `dtype`.
+ *   conv_state (B, D, 3)     same dtype, in place: (x_{t-3}, x_{t-2}, x_{t-1}) on
+ *                            entry, (x_{t-2}, x_{t-1}, x_t) on return (zeros
+ *                            before a row's first token).
+ *   weight (D, 4), bias (D,) or NULL: as mamba_causal_conv1d_fwd.
+ *   reset      (B,) uint8 or NULL: nonzero where the token starts a new document
+ *              (the window is cleared first).
+ *   out        (B, D)        SiLU(conv) (or the plain conv with apply_silu = 0).
+ * Supported: width == 4.  No argument may overlap out. */
+int mamba_causal_conv1d_update(const void* x, void* conv_state, const float* weight, const float* bias,
+                               const uint8_t* reset, void* out, int64_t batch, int64_t dim, int32_t width,
+                               int32_t dtype, int32_t apply_silu, void* stream);
+
+/* Selective-scan recurrence for one token per row.
+ *   dims       as mamba_selective_scan_fwd with seqlen == 1.
+ *   state      (B, D, N) float32, 16-byte aligned, updated in place:
+ *              h <- exp(dt A) h + dt u B.
+ *   u, z, out  (B, D); delta (B, D|H); B, C (B, N); A, D, delta_bias as
+ *              mamba_selective_scan_fwd.
+ *   reset      (B,) uint8 or NULL: nonzero where the token starts a new document
+ *              (the state is zeroed first).
+ *   out        = (C . h + D u) silu(z).
+ * Supported: N in {4, 8, 16, 32, 64, 128}, either A layout, ngroups == 1. */
+int mamba_selective_state_update(const mamba_scan_dims_t* dims, float* state, const void* u,
+                                 const void* delta, const float* A, const void* B, const void* C,
+                                 const float* D, const void* z, const float* delta_bias,
+                                 const uint8_t* reset, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,10 @@ missing or the tensors are not on a GPU the calls raise.
 
     u = causal_conv1d_fwd(x, weight, bias, doc_start)                  # (B, L, D)
     out, h = selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, doc_start)
+
+    # decode, one token per row, continuing the prefill above
+    u_t = causal_conv1d_update(x_t, conv_state, weight, bias)          # (B, D)
+    out_t = selective_state_update(h, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias)
 """
 
 from __future__ import annotations
@@ -21,6 +25,8 @@ __all__ = [
     "causal_conv1d_fwd",
     "selective_scan_fwd",
     "scan_workspace_bytes",
+    "causal_conv1d_update",
+    "selective_state_update",
     "MambaError",
     "MambaArgumentError",
     "library_path",
@@ -120,14 +126,17 @@ def scan_workspace_bytes(batch, seqlen, dim, dstate, nheads=0, dtype="bf16") -> 
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, doc_start=None,
-                       delta_softplus: bool = True, out=None, final_state=True, workspace=None):
+                       delta_softplus: bool = True, out=None, final_state=True, workspace=None,
+                       initial_state=None):
     """Selective scan forward; see mamba_selective_scan_fwd.
 
     u, z (B, L, D); delta (B, L, D) with A (D, N), or delta (B, L, H) with A (H,);
     B, C (B, L, N); D (D,), delta_bias (D,) or (H,), float32.  ``final_state``:
     True to allocate and return it, False/None to skip, or a (B, D, N) float32
     tensor to fill.  ``workspace``: optional uint8 device tensor of at least
-    scan_workspace_bytes(...) bytes.  Returns (out, final_state or None)."""
+    scan_workspace_bytes(...) bytes.  ``initial_state``: optional (B, D, N) float32
+    state before token 0 (token 0 then resets only where doc_start[:, 0] is set).
+    Returns (out, final_state or None)."""
     torch = _torch()
     dev = _check_device(u)
     if u.dim() != 3:
@@ -165,8 +174,68 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, doc_s
         _ptr(z, "z", dev, u.dtype, (Bt, L, Dm)),
         _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)),
         _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(initial_state, "initial_state", dev, torch.float32, (Bt, Dm, N)),
         _ptr(out, "out", dev, u.dtype, (Bt, L, Dm)),
         _ptr(final_state, "final_state", dev, torch.float32, (Bt, Dm, N)),
         ws_ptr, ws_bytes, _stream(dev))
     _lib.check(st, "mamba_selective_scan_fwd")
     return out, final_state
+
+
+def causal_conv1d_update(x, conv_state, weight, bias=None, reset=None, apply_silu: bool = True, out=None):
+    """Causal conv1d (width 4) + SiLU for one token per row; see mamba_causal_conv1d_update.
+
+    x (B, D); conv_state (B, D, 3) of x's dtype, updated in place (the last three
+    inputs of each channel); weight (D, 4) float32; bias (D,); reset (B,)
+    uint8/bool.  Returns out (B, D)."""
+    torch = _torch()
+    dev = _check_device(x)
+    if x.dim() != 2:
+        raise ValueError("x must be (B, D)")
+    Bt, Dm = x.shape
+    if weight.dim() == 3:
+        weight = weight.reshape(weight.shape[0], weight.shape[-1])
+    W = weight.shape[-1]
+    if reset is not None and reset.dtype == torch.bool:
+        reset = reset.to(torch.uint8)
+    if out is None:
+        out = torch.empty_like(x)
+    st = _lib.load().mamba_causal_conv1d_update(
+        _ptr(x, "x", dev), _ptr(conv_state, "conv_state", dev, x.dtype, (Bt, Dm, W - 1)),
+        _ptr(weight, "weight", dev, torch.float32, (Dm, W)), _ptr(bias, "bias", dev, torch.float32, (Dm,)),
+        _ptr(reset, "reset", dev, torch.uint8, (Bt,)), _ptr(out, "out", dev, x.dtype, (Bt, Dm)),
+        Bt, Dm, W, _dtype_code(x), int(bool(apply_silu)), _stream(dev))
+    _lib.check(st, "mamba_causal_conv1d_update")
+    return out
+
+
+def selective_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, reset=None,
+                           delta_softplus: bool = True, out=None):
+    """One recurrence step per row; see mamba_selective_state_update.
+
+    state (B, D, N) float32, updated in place; u, z (B, D); delta (B, D) with A
+    (D, N) or (B, H) with A (H,); B, C (B, N); reset (B,) uint8/bool.  Returns
+    out (B, D)."""
+    torch = _torch()
+    dev = _check_device(u)
+    if u.dim() != 2:
+        raise ValueError("u must be (B, D)")
+    Bt, Dm = u.shape
+    N = B.shape[-1]
+    nheads = A.shape[0] if A.dim() == 1 else 0
+    nd = nheads if nheads else Dm
+    if reset is not None and reset.dtype == torch.bool:
+        reset = reset.to(torch.uint8)
+    if out is None:
+        out = torch.empty_like(u)
+    dims = _scan_dims(Bt, 1, Dm, N, nheads, _dtype_code(u), delta_softplus)
+    st = _lib.load().mamba_selective_state_update(
+        ctypes.byref(dims), _ptr(state, "state", dev, torch.float32, (Bt, Dm, N)),
+        _ptr(u, "u", dev, u.dtype, (Bt, Dm)), _ptr(delta, "delta", dev, u.dtype, (Bt, nd)),
+        _ptr(A, "A", dev, torch.float32, (nheads,) if nheads else (Dm, N)),
+        _ptr(B, "B", dev, u.dtype, (Bt, N)), _ptr(C, "C", dev, u.dtype, (Bt, N)),
+        _ptr(D, "D", dev, torch.float32, (Dm,)), _ptr(z, "z", dev, u.dtype, (Bt, Dm)),
+        _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)), _ptr(reset, "reset", dev, torch.uint8, (Bt,)),
+        _ptr(out, "out", dev, u.dtype, (Bt, Dm)), _stream(dev))
+    _lib.check(st, "mamba_selective_state_update")
+    return out

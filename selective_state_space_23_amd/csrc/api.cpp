@@ -112,8 +112,9 @@ int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* 
 
 int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
                              const void* B, const void* C, const float* D, const void* z,
-                             const float* delta_bias, const uint8_t* doc_start, void* out, float* final_state,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             const float* delta_bias, const uint8_t* doc_start, const float* initial_state,
+                             void* out, float* final_state, void* workspace, size_t workspace_bytes,
+                             void* stream) {
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
     const int64_t Bt = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
@@ -130,7 +131,7 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
         (!aligned(u, 16) || !aligned(out, 16) || (z && !aligned(z, 16)) || !aligned(B, 16) || !aligned(C, 16)))
         return MAMBA_ERR_MISALIGNED;
     if (!aligned(A, 4) || (D && !aligned(D, 4)) || (delta_bias && !aligned(delta_bias, 4)) ||
-        (final_state && !aligned(final_state, 4)))
+        (final_state && !aligned(final_state, 4)) || (initial_state && !aligned(initial_state, 4)))
         return MAMBA_ERR_MISALIGNED;
 
     const size_t act = static_cast<size_t>(Bt * L * Dm) * esz;
@@ -138,10 +139,11 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
     const size_t bc = static_cast<size_t>(Bt * L * N) * esz;
     const size_t fsb = static_cast<size_t>(Bt * Dm * N) * 4;
     const size_t abytes = static_cast<size_t>(dims->nheads ? dims->nheads : Dm * N) * 4;
-    const void* ins[] = {u, delta, B, C, z, A, D, delta_bias, doc_start};
+    const void* ins[] = {u, delta, B, C, z, A, D, delta_bias, doc_start, initial_state};
     const size_t insz[] = {act, dlt, bc, bc, act, abytes, static_cast<size_t>(Dm) * 4,
-                           static_cast<size_t>(nd) * 4, static_cast<size_t>(Bt * L)};
-    for (int i = 0; i < 9; ++i) {
+                           static_cast<size_t>(nd) * 4, static_cast<size_t>(Bt * L), fsb};
+    constexpr int kIns = 10;
+    for (int i = 0; i < kIns; ++i) {
         if (overlap(ins[i], insz[i], out, act)) return MAMBA_ERR_INVALID_ARGUMENT;
         if (overlap(ins[i], insz[i], final_state, fsb)) return MAMBA_ERR_INVALID_ARGUMENT;
     }
@@ -151,7 +153,7 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;
-        for (int i = 0; i < 9; ++i)
+        for (int i = 0; i < kIns; ++i)
             if (overlap(ins[i], insz[i], workspace, need)) return MAMBA_ERR_INVALID_ARGUMENT;
         if (overlap(out, act, workspace, need) || overlap(final_state, fsb, workspace, need))
             return MAMBA_ERR_INVALID_ARGUMENT;
@@ -159,7 +161,8 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
 
     mamba::ScanArgs a;
     a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
-    a.delta_bias = delta_bias; a.doc_start = doc_start; a.out = out; a.final_state = final_state;
+    a.delta_bias = delta_bias; a.doc_start = doc_start; a.initial_state = initial_state;
+    a.out = out; a.final_state = final_state;
     a.ws = static_cast<float*>(workspace);
     a.batch = Bt; a.seqlen = L; a.dim = Dm; a.dstate = N;
     a.nheads = dims->nheads;
@@ -167,6 +170,71 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
     a.softplus = dims->delta_softplus != 0;
     a.stream = static_cast<hipStream_t>(stream);
     return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+int mamba_causal_conv1d_update(const void* x, void* conv_state, const float* weight, const float* bias,
+                               const uint8_t* reset, void* out, int64_t batch, int64_t dim, int32_t width,
+                               int32_t dtype, int32_t apply_silu, void* stream) {
+    if (batch < 0 || dim < 0 || batch > 65535 || dim > kMaxDim) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (width != 4) return MAMBA_ERR_UNSUPPORTED;
+    if (batch * dim == 0) return MAMBA_OK;
+    if (!x || !conv_state || !weight || !out) return MAMBA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(conv_state, esz) || !aligned(out, esz) || !aligned(weight, 4) ||
+        (bias && !aligned(bias, 4)))
+        return MAMBA_ERR_MISALIGNED;
+    const size_t act = static_cast<size_t>(batch * dim) * esz;
+    if (overlap(x, act, out, act) || overlap(conv_state, act * 3, out, act) || overlap(x, act, conv_state, act * 3) ||
+        overlap(weight, dim * 16, out, act) || overlap(bias, dim * 4, out, act) ||
+        overlap(reset, batch, out, act) || overlap(weight, dim * 16, conv_state, act * 3))
+        return MAMBA_ERR_INVALID_ARGUMENT;
+    mamba::ConvUpdateArgs a;
+    a.x = x; a.conv_state = conv_state; a.weight = weight; a.bias = bias; a.reset = reset; a.out = out;
+    a.batch = batch; a.dim = dim;
+    a.bf16 = dtype == MAMBA_DTYPE_BF16;
+    a.apply_silu = apply_silu != 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    return mamba::launch_conv1d_update(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+int mamba_selective_state_update(const mamba_scan_dims_t* dims, float* state, const void* u, const void* delta,
+                                 const float* A, const void* B, const void* C, const float* D, const void* z,
+                                 const float* delta_bias, const uint8_t* reset, void* out, void* stream) {
+    if (!dims) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (dims->batch < 0 || dims->dim < 0 || dims->dstate < 1 || dims->nheads < 0 || dims->batch > 65535 ||
+        dims->dim > kMaxDim || dims->seqlen != 1)
+        return MAMBA_ERR_INVALID_ARGUMENT;
+    if (dims->dtype != MAMBA_DTYPE_F32 && dims->dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (dims->nheads > 0 && dims->dim % dims->nheads != 0) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (dims->ngroups != 1 || !mamba::state_update_supported(dims->dstate)) return MAMBA_ERR_UNSUPPORTED;
+    const int64_t Bt = dims->batch, Dm = dims->dim, N = dims->dstate;
+    if (Bt * Dm == 0) return MAMBA_OK;
+    if (!state || !u || !delta || !A || !B || !C || !out) return MAMBA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(state, 16) || !aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) ||
+        !aligned(out, esz) || (z && !aligned(z, esz)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+        (delta_bias && !aligned(delta_bias, 4)))
+        return MAMBA_ERR_MISALIGNED;
+    const int64_t nd = dims->nheads ? dims->nheads : Dm;
+    const size_t act = static_cast<size_t>(Bt * Dm) * esz;
+    const size_t sb = static_cast<size_t>(Bt * Dm * N) * 4;
+    const void* ins[] = {u, delta, A, B, C, D, z, delta_bias, reset};
+    const size_t insz[] = {act, static_cast<size_t>(Bt * nd) * esz,
+                           static_cast<size_t>(dims->nheads ? dims->nheads : Dm * N) * 4,
+                           static_cast<size_t>(Bt * N) * esz, static_cast<size_t>(Bt * N) * esz,
+                           static_cast<size_t>(Dm) * 4, act, static_cast<size_t>(nd) * 4, static_cast<size_t>(Bt)};
+    for (int i = 0; i < 9; ++i)
+        if (overlap(ins[i], insz[i], out, act) || overlap(ins[i], insz[i], state, sb)) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (overlap(out, act, state, sb)) return MAMBA_ERR_INVALID_ARGUMENT;
+    mamba::StateUpdateArgs a;
+    a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
+    a.delta_bias = delta_bias; a.reset = reset; a.out = out;
+    a.batch = Bt; a.dim = Dm; a.dstate = N; a.nheads = dims->nheads;
+    a.bf16 = dims->dtype == MAMBA_DTYPE_BF16;
+    a.softplus = dims->delta_softplus != 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    return mamba::launch_state_update(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
 }  // extern "C"

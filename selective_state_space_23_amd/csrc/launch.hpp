@@ -32,9 +32,10 @@ struct ScanArgs {
     const void* z;
     const float* delta_bias;
     const uint8_t* doc_start;
+    const float* initial_state;   // (B, D, N) or null
     void* out;
     float* final_state;
-    float* ws;          // chunk carries, see scan_workspace_floats
+    float* ws;          // chunk carries, see scan_workspace_bytes
     int64_t batch, seqlen, dim, dstate;
     int nheads;         // 0: per-channel A (D, N); > 0: scalar A per head
     bool bf16;
@@ -52,6 +53,43 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim);
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16);
 bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16);
 hipError_t launch_selective_scan(const ScanArgs& a);
+
+// One-token decode steps (decode.hip).
+struct ConvUpdateArgs {
+    const void* x;          // (B, D)
+    void* conv_state;       // (B, D, 3), I/O dtype: x_{t-3}, x_{t-2}, x_{t-1}
+    const float* weight;    // (D, 4)
+    const float* bias;      // (D,) or null
+    const uint8_t* reset;   // (B,) or null
+    void* out;              // (B, D)
+    int64_t batch, dim;
+    bool bf16;
+    bool apply_silu;
+    hipStream_t stream;
+};
+
+struct StateUpdateArgs {
+    float* state;           // (B, D, N) float32, in place
+    const void* u;          // (B, D)
+    const void* delta;      // (B, D) or (B, H)
+    const float* A;         // (D, N) or (H,)
+    const void* B;          // (B, N)
+    const void* C;          // (B, N)
+    const float* D;
+    const void* z;
+    const float* delta_bias;
+    const uint8_t* reset;   // (B,) or null
+    void* out;              // (B, D)
+    int64_t batch, dim, dstate;
+    int nheads;
+    bool bf16;
+    bool softplus;
+    hipStream_t stream;
+};
+
+hipError_t launch_conv1d_update(const ConvUpdateArgs& a);
+bool state_update_supported(int64_t dstate);
+hipError_t launch_state_update(const StateUpdateArgs& a);
 
 // Scalar-A heads with bf16 I/O: the chunked matrix-core form (ssd.hip).
 bool ssd_supported(int64_t dim, int64_t dstate, int nheads);

@@ -60,6 +60,7 @@ struct ScanKParams {
     const void* z;
     const float* delta_bias;
     const uint8_t* doc_start;
+    const float* initial_state;   // (B, D, N) or null: state before token 0
     void* out;
     float* final_state;
     float* ws_P;        // [nchunks-1][B][D][N]: pass 1 P, then pass 2 carries
@@ -162,8 +163,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     const int64_t slot_stride = static_cast<int64_t>(p.nbatch) * p.dim * N;
     const int64_t my_slot = (b * p.dim + dc) * N;
     float h[N];
-    if (OUTPUT && c > 0) {
-        const float* carry = p.ws_P + (c - 1) * slot_stride + my_slot;
+    if (OUTPUT && (c > 0 || p.initial_state != nullptr)) {
+        const float* carry = c > 0 ? p.ws_P + (c - 1) * slot_stride + my_slot : p.initial_state + my_slot;
 #pragma unroll
         for (int n = 0; n < N; ++n) h[n] = carry[n];
     } else {
@@ -297,7 +298,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
         {
             const int64_t tl = w0 + lane;
             bool st = false;
-            if (tl < t_end) st = (tl == 0) || (ds_row != nullptr && ds_row[tl] != 0);
+            // Token 0 starts a document unless the row continues an initial state.
+            if (tl < t_end) st = (tl == 0 && p.initial_state == nullptr) || (ds_row != nullptr && ds_row[tl] != 0);
             starts = __ballot(st);
         }
         __syncthreads();                 // every wave is done with the previous window
@@ -334,12 +336,14 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
 }
 
 // Pass 2: carry_{c+1} = P_c * carry_c + H_c for every (b, d, n), written over
-// ws_P[c] (ws_P[c] then holds the state entering chunk c + 1).
+// ws_P[c] (ws_P[c] then holds the state entering chunk c + 1); carry_0 is the
+// initial state (or zero).
 __global__ __launch_bounds__(256) void scan_carry_kernel(float* __restrict__ ws_P, const float* __restrict__ ws_H,
-                                                         int64_t count, int64_t nslots) {
+                                                         const float* __restrict__ init, int64_t count,
+                                                         int64_t nslots) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= count) return;
-    float carry = 0.0f;
+    float carry = init != nullptr ? init[i] : 0.0f;
     int64_t c = 0;
     for (; c + 4 <= nslots; c += 4) {
         float P[4], H[4];
@@ -364,7 +368,8 @@ template <typename T, int N, bool HEADS>
 hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     ScanKParams p;
     p.u = a.u; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
-    p.delta_bias = a.delta_bias; p.doc_start = a.doc_start; p.out = a.out; p.final_state = a.final_state;
+    p.delta_bias = a.delta_bias; p.doc_start = a.doc_start; p.initial_state = a.initial_state;
+    p.out = a.out; p.final_state = a.final_state;
     const int64_t count = a.batch * a.dim * N;
     const int64_t nslots = plan.nchunks - 1;
     p.ws_P = a.ws;
@@ -389,7 +394,8 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         dim3 g2(static_cast<unsigned>((count + 255) / 256));
-        hipLaunchKernelGGL(scan_carry_kernel, g2, dim3(256), 0, a.stream, p.ws_P, p.ws_H, count, nslots);
+        hipLaunchKernelGGL(scan_carry_kernel, g2, dim3(256), 0, a.stream, p.ws_P, p.ws_H, a.initial_state, count,
+                           nslots);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -70,6 +70,7 @@ struct SsdParams {
     const uint16_t* z;
     const float* delta_bias;
     const uint8_t* doc_start;
+    const float* initial_state;   // (B, D, N) or null: state before token 0
     uint16_t* out;
     float* final_state;
     float* ws_H;        // [B*H][nseg-1][P][N]: segment end states, then carries
@@ -203,9 +204,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
     for (int j = 0; j < kSt; ++j) {
         const int k = wave + kWaves * j;
         st[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (OUTPUT && seg > 0 && k < kT) {
+        if (OUTPUT && (seg > 0 || p.initial_state != nullptr) && k < kT) {
             const int nb = k / kTP, pb = k % kTP;
-            const float* carry = p.ws_H + (bh * nslot + seg - 1) * PN + static_cast<int64_t>(16 * pb + l16) * N;
+            const float* carry = (seg > 0 ? p.ws_H + (bh * nslot + seg - 1) * PN : p.initial_state + bh * PN) +
+                                 static_cast<int64_t>(16 * pb + l16) * N;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int n = 16 * nb + 4 * lg + i;
@@ -315,7 +317,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
                 dt = bf16_to_f32(static_cast<uint16_t>(pdelta)) + dbias;
                 if constexpr (SOFTPLUS) dt = softplus_f(dt);
             }
-            const bool reset = valid && (tg == 0 || pflag != 0);
+            // Token 0 starts a document unless the row continues an initial state.
+            const bool reset = valid && ((tg == 0 && p.initial_state == nullptr) || pflag != 0);
             float cs = dt * a_l2;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -490,13 +493,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
 }
 
 // Pass 2: carry_{k+1} = G_k carry_k + H_k over the segments of each (row, head),
-// written over H_k (which then holds the state entering segment k + 1).
+// written over H_k (which then holds the state entering segment k + 1); carry_0
+// is the initial state (or zero).  The (B, D, N) initial state of head h of row b
+// is the contiguous block (b H + h) P N .. + P N, laid out like H_k.
 __global__ __launch_bounds__(256) void ssd_carry_kernel(float* __restrict__ ws_H, const float* __restrict__ ws_G,
-                                                        int64_t nbh, int nslot, int64_t PN) {
+                                                        const float* __restrict__ init, int64_t nbh, int nslot,
+                                                        int64_t PN) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= nbh * PN) return;
     const int64_t bh = i / PN, e = i % PN;
-    float c = 0.0f;
+    float c = init != nullptr ? init[i] : 0.0f;
     for (int k = 0; k < nslot; ++k) {
         float* hp = ws_H + (bh * nslot + k) * PN + e;
         c = __builtin_fmaf(ws_G[bh * nslot + k], c, *hp);
@@ -543,6 +549,7 @@ hipError_t launch_ssd_typed(const ScanArgs& a, const SsdPlan& plan) {
     p.z = static_cast<const uint16_t*>(a.z);
     p.delta_bias = a.delta_bias;
     p.doc_start = a.doc_start;
+    p.initial_state = a.initial_state;
     p.out = static_cast<uint16_t*>(a.out);
     p.final_state = a.final_state;
     const int64_t nbh = a.batch * a.nheads;
@@ -565,7 +572,7 @@ hipError_t launch_ssd_typed(const ScanArgs& a, const SsdPlan& plan) {
         if (e != hipSuccess) return e;
         const int64_t count = nbh * PN;
         hipLaunchKernelGGL(ssd_carry_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0,
-                           a.stream, p.ws_H, p.ws_G, nbh, nslot, PN);
+                           a.stream, p.ws_H, p.ws_G, a.initial_state, nbh, nslot, PN);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

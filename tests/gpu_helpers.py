@@ -106,6 +106,7 @@ def oracle_scan(inp, u, channels, **kw):
     use_D = kw.pop("use_D", True)
     use_bias = kw.pop("use_bias", True)
     softplus = kw.pop("softplus", True)
+    init = kw.pop("initial_state", None)
     return oracle.selective_scan(u, delta, A, inp.B, inp.C, inp.D[ch] if use_D else None,
                                  inp.z[:, :, ch] if use_z else None, bias if use_bias else None, softplus,
-                                 inp.doc_start)
+                                 inp.doc_start, initial_state=None if init is None else init[:, ch, :])

@@ -110,9 +110,10 @@ def test_workspace_query(lib):
 
 
 def scan(lib, d=None, u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None, bias=None,
-         ds=None, out=FAKE * 6, fs=None, ws=None, wsb=0):
+         ds=None, init=None, out=FAKE * 6, fs=None, ws=None, wsb=0):
     d = d or dims(batch=1, seqlen=64, dim=64)
-    return lib.mamba_selective_scan_fwd(ctypes.byref(d), u, delta, A, B, C, D, z, bias, ds, out, fs, ws, wsb, None)
+    return lib.mamba_selective_scan_fwd(ctypes.byref(d), u, delta, A, B, C, D, z, bias, ds, init, out, fs, ws, wsb,
+                                        None)
 
 
 def test_scan_validation(lib):
@@ -125,6 +126,8 @@ def test_scan_validation(lib):
     assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=3)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert scan(lib, out=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT           # out overlaps u
     assert scan(lib, fs=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT        # final_state overlaps out
+    assert scan(lib, fs=FAKE * 8, init=FAKE * 8) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # initial = final state
+    assert scan(lib, init=FAKE * 8 + 2) == _lib.MAMBA_ERR_MISALIGNED
     heads = dims(batch=1, seqlen=64, dim=64, nheads=2, dstate=16)
     assert scan(lib, d=heads, u=FAKE + 8) == _lib.MAMBA_ERR_MISALIGNED       # bf16 heads: 16-byte vectors
     assert scan(lib, d=heads, C=FAKE * 5 + 8) == _lib.MAMBA_ERR_MISALIGNED
@@ -151,3 +154,34 @@ def test_python_binding_rejects_cpu_tensors():
         ssm.causal_conv1d_fwd(x, torch.zeros(16, 4))
     with pytest.raises(ValueError):
         ssm.selective_scan_fwd(x, x, torch.zeros(16, 4), torch.zeros(1, 8, 4), torch.zeros(1, 8, 4))
+
+
+def conv_update(lib, x=FAKE, cs=FAKE * 2, w=FAKE * 3, b=None, reset=None, out=FAKE * 4, B=2, D=16, W=4, dtype=1,
+                silu=1):
+    return lib.mamba_causal_conv1d_update(x, cs, w, b, reset, out, B, D, W, dtype, silu, None)
+
+
+def test_conv_update_validation(lib):
+    assert conv_update(lib, W=3) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert conv_update(lib, dtype=5) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv_update(lib, cs=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv_update(lib, x=FAKE + 1) == _lib.MAMBA_ERR_MISALIGNED
+    assert conv_update(lib, out=FAKE * 2 + 64) == _lib.MAMBA_ERR_INVALID_ARGUMENT     # inside conv_state
+    assert conv_update(lib, x=None, cs=None, w=None, out=None, B=0) == _lib.MAMBA_OK
+
+
+def state_update(lib, d=None, state=FAKE * 16, u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None,
+                 z=None, bias=None, reset=None, out=FAKE * 6):
+    d = d or dims(batch=2, seqlen=1, dim=64, dstate=16)
+    return lib.mamba_selective_state_update(ctypes.byref(d), state, u, delta, A, B, C, D, z, bias, reset, out, None)
+
+
+def test_state_update_validation(lib):
+    assert state_update(lib, d=dims(batch=2, seqlen=2, dim=64, dstate=16)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=12)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=16, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=16, nheads=3)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert state_update(lib, state=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert state_update(lib, state=FAKE * 16 + 4) == _lib.MAMBA_ERR_MISALIGNED
+    assert state_update(lib, out=FAKE * 16 + 64) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # out inside state
+    assert state_update(lib, d=dims(batch=0, seqlen=1), state=None, u=None, out=None) == _lib.MAMBA_OK

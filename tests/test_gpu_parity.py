@@ -34,10 +34,12 @@ def run_conv(ssm, dev, inp, apply_silu=True, use_bias=True, use_docs=True):
                                  dev["doc_start"] if use_docs else None, apply_silu=apply_silu)
 
 
-def run_scan(ssm, dev, u, use_z=True, use_D=True, use_bias=True, softplus=True, final_state=True):
+def run_scan(ssm, dev, u, use_z=True, use_D=True, use_bias=True, softplus=True, final_state=True,
+             initial_state=None):
     return ssm.selective_scan_fwd(u, dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"] if use_D else None,
                                   dev["z"] if use_z else None, dev["delta_bias"] if use_bias else None,
-                                  dev["doc_start"], delta_softplus=softplus, final_state=final_state)
+                                  dev["doc_start"], delta_softplus=softplus, final_state=final_state,
+                                  initial_state=initial_state)
 
 
 # ----------------------------------------------------------------------------
@@ -92,7 +94,10 @@ def scan_case(ssm, inp, **flags):
     u = oracle.causal_conv1d(inp.x, inp.conv_w, inp.conv_b, inp.doc_start)
     u32 = bf16_round(u.astype(np.float32)) if inp.dtype == "bf16" else u.astype(np.float32)
     dev = upload(inp)
-    out, fin = run_scan(ssm, dev, to_dev(u32, inp.dtype), **flags)
+    gflags = dict(flags)
+    if flags.get("initial_state") is not None:
+        gflags["initial_state"] = torch_mod().from_numpy(flags["initial_state"].astype(np.float32)).cuda()
+    out, fin = run_scan(ssm, dev, to_dev(u32, inp.dtype), **gflags)
     ch = np.arange(inp.x.shape[2])
     kw = {k: v for k, v in flags.items() if k != "final_state"}
     ref_out, ref_fin = oracle_scan(inp, u32.astype(np.float64), ch, **kw)
@@ -161,6 +166,47 @@ def test_heads_documents_at_chunk_edges(ssm, dtype):
         inp.doc_start[0, t] = 1
     inp.doc_start[1, :] = 1
     scan_case(ssm, inp)
+
+
+INIT_CASES = [
+    # (dim, dstate, nheads, dtype): both A layouts, both dtypes, and the matrix-core form
+    (96, 16, 0, "bf16"), (64, 8, 0, "f32"), (128, 32, 2, "bf16"), (128, 16, 2, "f32"), (128, 128, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", INIT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_scan_initial_state(ssm, case):
+    """A given state before token 0: row 0 continues it, row 1 starts a document at
+    token 0 (and so ignores it); lengths span one chunk and several."""
+    Dm, N, H, dt = case
+    for L in (50, 700):
+        inp = make_custom(2, L, Dm, N, nheads=H, dtype=dt, docs=120.0, seed=400 + L + N)
+        inp.doc_start[0, 0] = 0
+        inp.doc_start[1, 0] = 1
+        init = np.random.default_rng(401).normal(0.0, 0.5, size=(2, Dm, N))
+        scan_case(ssm, inp, initial_state=init)
+
+
+def test_scan_split_equals_whole(ssm):
+    """Scanning [0, L1) and then [L1, L) from the first part's final state gives the
+    whole scan's outputs and final state (the carry a sequence-parallel split uses)."""
+    torch = torch_mod()
+    for H, N in ((0, 16), (2, 64)):
+        inp = make_custom(2, 900, 128, N, nheads=H, dtype="bf16", docs=200.0, seed=402 + N)
+        u = bf16_round(oracle.causal_conv1d(inp.x, inp.conv_w, inp.conv_b, inp.doc_start).astype(np.float32))
+        ch = np.arange(128)
+        ref_out, ref_fin = oracle_scan(inp, u.astype(np.float64), ch)
+        dev = upload(inp)
+        ud = to_dev(u, "bf16")
+        L1 = 333
+        parts = []
+        fin = None
+        for sl in (slice(0, L1), slice(L1, 900)):
+            sub = {k: (v[:, sl].contiguous() if k in ("delta", "B", "C", "z", "doc_start") else v) for k, v in dev.items()}
+            o, fin = run_scan(ssm, sub, ud[:, sl].contiguous(), initial_state=fin)
+            parts.append(to_host(o))
+        assert_close(np.concatenate(parts, axis=1), ref_out, "bf16", f"split out H={H}")
+        assert_close(to_host(fin), ref_fin, "bf16", f"split final_state H={H}")
 
 
 def test_scan_A_zero_and_vanishing_step(ssm):
