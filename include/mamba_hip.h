@@ -75,6 +75,10 @@ const char* mamba_status_string(int status);
  *             with the singleton group dimension dropped).
  *   bias      (D,) float32 or NULL (zero).
  *   doc_start (B, L) uint8 or NULL.
+ *   conv_state (B, D, 3) `dtype` or NULL: the inputs x[-3], x[-2], x[-1] before
+ *             token 0 of each row (the window mamba_causal_conv1d_update keeps).
+ *             With it, token 0 starts a new document only where doc_start[b, 0]
+ *             is set; without it, token 0 always does (taps before it read zero).
  *   out       (B, L, D), `dtype`: act(bias + sum_j weight[., width-1-j] x[t-j]),
  *             taps before the start of the token's document read zero;
  *             act = SiLU if apply_silu else identity.
@@ -83,7 +87,7 @@ const char* mamba_status_string(int status);
  * multiple of 16 bytes' worth of elements select the vectorised kernel).
  * Returns MAMBA_OK, or an error before any launch.  B, L or D of 0 is a no-op. */
 int mamba_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
-                            const uint8_t* doc_start, void* out,
+                            const uint8_t* doc_start, const void* conv_state, void* out,
                             int64_t batch, int64_t seqlen, int64_t dim, int32_t width,
                             int32_t dtype, int32_t apply_silu, void* stream);
 
@@ -149,6 +153,21 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims,
                              const uint8_t* doc_start, const float* initial_state,
                              void* out, float* final_state,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Conv1d (width 4, SiLU) and selective scan in one call: the whole forward path
+ * of the mixer core.  Same arguments and results as mamba_causal_conv1d_fwd
+ * (x, conv_weight, conv_bias, doc_start, conv_state; apply_silu = 1) followed by
+ * mamba_selective_scan_fwd (dims, delta ... final_state, workspace sized by
+ * mamba_selective_scan_workspace_bytes) on its output; the conv output is also
+ * written to `u` (B, L, D).  With per-channel A the convolution runs inside the
+ * scan's first pass, which saves the conv's separate pass over x and u.
+ * conv_state and initial_state are normally given together (a continuation). */
+int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const float* conv_weight,
+                        const float* conv_bias, const void* conv_state, const void* delta,
+                        const float* A, const void* B, const void* C, const float* D,
+                        const void* z, const float* delta_bias, const uint8_t* doc_start,
+                        const float* initial_state, void* u, void* out, float* final_state,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- One-token decode (Mamba skill page, "Dual Computation Modes": the
  * recurrent mode used for generation).  A prefill with mamba_causal_conv1d_fwd

@@ -25,6 +25,7 @@ __all__ = [
     "causal_conv1d_fwd",
     "selective_scan_fwd",
     "scan_workspace_bytes",
+    "conv_scan_fwd",
     "causal_conv1d_update",
     "selective_state_update",
     "MambaError",
@@ -84,11 +85,13 @@ def _check_device(x):
     return x.device
 
 
-def causal_conv1d_fwd(x, weight, bias=None, doc_start=None, apply_silu: bool = True, out=None):
+def causal_conv1d_fwd(x, weight, bias=None, doc_start=None, apply_silu: bool = True, out=None, conv_state=None):
     """Depthwise causal conv1d (width 4) + SiLU; see mamba_causal_conv1d_fwd.
 
     x (B, L, D) float32/bfloat16; weight (D, 4) or (D, 1, 4) float32; bias (D,)
-    float32; doc_start (B, L) uint8/bool.  Returns out (B, L, D), x's dtype."""
+    float32; doc_start (B, L) uint8/bool; conv_state (B, D, 3) of x's dtype: the
+    inputs before token 0 (token 0 then starts a document only where doc_start
+    says so).  Returns out (B, L, D), x's dtype."""
     torch = _torch()
     dev = _check_device(x)
     if x.dim() != 3:
@@ -105,6 +108,7 @@ def causal_conv1d_fwd(x, weight, bias=None, doc_start=None, apply_silu: bool = T
         _ptr(x, "x", dev), _ptr(weight, "weight", dev, torch.float32, (Dm, W)),
         _ptr(bias, "bias", dev, torch.float32, (Dm,)),
         _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(conv_state, "conv_state", dev, x.dtype, (Bt, Dm, W - 1)),
         _ptr(out, "out", dev, x.dtype, (Bt, L, Dm)), Bt, L, Dm, W, _dtype_code(x), int(bool(apply_silu)),
         _stream(dev))
     _lib.check(st, "mamba_causal_conv1d_fwd")
@@ -180,6 +184,66 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, doc_s
         ws_ptr, ws_bytes, _stream(dev))
     _lib.check(st, "mamba_selective_scan_fwd")
     return out, final_state
+
+
+def conv_scan_fwd(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, delta_bias=None, doc_start=None,
+                  delta_softplus: bool = True, initial_state=None, conv_state=None, u=None, out=None,
+                  final_state=True, workspace=None):
+    """Conv1d (width 4) + SiLU and the selective scan in one call; see mamba_conv_scan_fwd.
+
+    Arguments as causal_conv1d_fwd (x, conv_weight, conv_bias, doc_start,
+    conv_state) and selective_scan_fwd (the rest).  ``u``: optional (B, L, D)
+    tensor that receives the conv output.  Returns (u, out, final_state or None)."""
+    torch = _torch()
+    dev = _check_device(x)
+    if x.dim() != 3:
+        raise ValueError("x must be (B, L, D)")
+    Bt, L, Dm = x.shape
+    N = B.shape[-1]
+    if conv_weight.dim() == 3:
+        conv_weight = conv_weight.reshape(conv_weight.shape[0], conv_weight.shape[-1])
+    nheads = A.shape[0] if A.dim() == 1 else 0
+    nd = nheads if nheads else Dm
+    if doc_start is not None and doc_start.dtype == torch.bool:
+        doc_start = doc_start.to(torch.uint8)
+    if u is None:
+        u = torch.empty_like(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if final_state is True:
+        final_state = torch.empty((Bt, Dm, N), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    dims = _scan_dims(Bt, L, Dm, N, nheads, _dtype_code(x), delta_softplus)
+    lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.mamba_selective_scan_workspace_bytes(ctypes.byref(dims), ctypes.byref(need)),
+               "mamba_selective_scan_workspace_bytes")
+    if need.value and workspace is None:
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace, "workspace", dev, torch.uint8) if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    st = lib.mamba_conv_scan_fwd(
+        ctypes.byref(dims),
+        _ptr(x, "x", dev, x.dtype, (Bt, L, Dm)),
+        _ptr(conv_weight, "conv_weight", dev, torch.float32, (Dm, 4)),
+        _ptr(conv_bias, "conv_bias", dev, torch.float32, (Dm,)),
+        _ptr(conv_state, "conv_state", dev, x.dtype, (Bt, Dm, 3)),
+        _ptr(delta, "delta", dev, x.dtype, (Bt, L, nd)),
+        _ptr(A, "A", dev, torch.float32, (nheads,) if nheads else (Dm, N)),
+        _ptr(B, "B", dev, x.dtype, (Bt, L, N)),
+        _ptr(C, "C", dev, x.dtype, (Bt, L, N)),
+        _ptr(D, "D", dev, torch.float32, (Dm,)),
+        _ptr(z, "z", dev, x.dtype, (Bt, L, Dm)),
+        _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)),
+        _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(initial_state, "initial_state", dev, torch.float32, (Bt, Dm, N)),
+        _ptr(u, "u", dev, x.dtype, (Bt, L, Dm)),
+        _ptr(out, "out", dev, x.dtype, (Bt, L, Dm)),
+        _ptr(final_state, "final_state", dev, torch.float32, (Bt, Dm, N)),
+        ws_ptr, ws_bytes, _stream(dev))
+    _lib.check(st, "mamba_conv_scan_fwd")
+    return u, out, final_state
 
 
 def causal_conv1d_update(x, conv_state, weight, bias=None, reset=None, apply_silu: bool = True, out=None):

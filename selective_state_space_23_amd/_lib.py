@@ -24,6 +24,7 @@ EXPORTED = (
     "mamba_causal_conv1d_fwd",
     "mamba_selective_scan_workspace_bytes",
     "mamba_selective_scan_fwd",
+    "mamba_conv_scan_fwd",
     "mamba_causal_conv1d_update",
     "mamba_selective_state_update",
 )
@@ -74,13 +75,15 @@ def load() -> ctypes.CDLL:
     lib.mamba_version.restype = ctypes.c_int
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     lib.mamba_status_string.restype = ctypes.c_char_p
-    lib.mamba_causal_conv1d_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.mamba_causal_conv1d_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
     lib.mamba_causal_conv1d_fwd.restype = ctypes.c_int
     lib.mamba_selective_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(sz)]
     lib.mamba_selective_scan_workspace_bytes.restype = ctypes.c_int
     lib.mamba_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              vp, vp, vp, sz, vp]
     lib.mamba_selective_scan_fwd.restype = ctypes.c_int
+    lib.mamba_conv_scan_fwd.argtypes = [ctypes.POINTER(ScanDims)] + [vp] * 17 + [sz, vp]
+    lib.mamba_conv_scan_fwd.restype = ctypes.c_int
     lib.mamba_causal_conv1d_update.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp]
     lib.mamba_causal_conv1d_update.restype = ctypes.c_int
     lib.mamba_selective_state_update.argtypes = [ctypes.POINTER(ScanDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,

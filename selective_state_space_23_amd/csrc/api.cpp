@@ -52,73 +52,63 @@ int check_dims(const mamba_scan_dims_t* d) {
     return MAMBA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int mamba_version(void) { return (0 << 16) | (1 << 8) | 0; }
-
-const char* mamba_status_string(int status) {
-    switch (status) {
-        case MAMBA_OK: return "ok";
-        case MAMBA_ERR_INVALID_ARGUMENT: return "invalid argument";
-        case MAMBA_ERR_UNSUPPORTED: return "unsupported configuration";
-        case MAMBA_ERR_MISALIGNED: return "misaligned pointer";
-        case MAMBA_ERR_WORKSPACE: return "workspace missing or too small";
-        case MAMBA_ERR_HIP: return "HIP launch failed";
-        default: return "unknown status";
-    }
-}
-
-int mamba_causal_conv1d_fwd(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
-                            void* out, int64_t batch, int64_t seqlen, int64_t dim, int32_t width, int32_t dtype,
-                            int32_t apply_silu, void* stream) {
+// Checks of one conv1d call (shared by the conv and the fused conv + scan entry
+// points); fills `a` on success.
+int check_conv(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
+               const void* conv_state, void* out, int64_t batch, int64_t seqlen, int64_t dim, int32_t width,
+               int32_t dtype, int32_t apply_silu, void* stream, mamba::ConvArgs* a, bool* empty) {
+    *empty = false;
     if (batch < 0 || seqlen < 0 || dim < 0) return MAMBA_ERR_INVALID_ARGUMENT;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARGUMENT;
     if (width != 4) return MAMBA_ERR_UNSUPPORTED;
     int64_t n;
     if (!mul_ok(batch, seqlen, dim, &n) || dim > kMaxDim || batch > 65535) return MAMBA_ERR_INVALID_ARGUMENT;
     if (seqlen > kMaxSeqlen) return MAMBA_ERR_UNSUPPORTED;
-    if (n == 0) return MAMBA_OK;
+    if (n == 0) {
+        *empty = true;
+        return MAMBA_OK;
+    }
     if (!x || !weight || !out) return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
-    if (!aligned(x, esz) || !aligned(out, esz) || !aligned(weight, 4) || (bias && !aligned(bias, 4)))
+    if (!aligned(x, esz) || !aligned(out, esz) || !aligned(weight, 4) || (bias && !aligned(bias, 4)) ||
+        (conv_state && !aligned(conv_state, esz)))
         return MAMBA_ERR_MISALIGNED;
     const size_t bytes = static_cast<size_t>(n) * esz;
+    const size_t hist = static_cast<size_t>(batch * dim * 3) * esz;
     if (overlap(x, bytes, out, bytes) || overlap(weight, dim * 16, out, bytes) ||
-        overlap(bias, dim * 4, out, bytes) || overlap(doc_start, batch * seqlen, out, bytes))
+        overlap(bias, dim * 4, out, bytes) || overlap(doc_start, batch * seqlen, out, bytes) ||
+        overlap(conv_state, hist, out, bytes))
         return MAMBA_ERR_INVALID_ARGUMENT;
 
-    mamba::ConvArgs a;
-    a.x = x; a.weight = weight; a.bias = bias; a.doc_start = doc_start; a.out = out;
-    a.batch = batch; a.seqlen = seqlen; a.dim = dim;
-    a.bf16 = dtype == MAMBA_DTYPE_BF16;
-    const int64_t vec = a.bf16 ? 8 : 4;
-    a.vectorized = (dim % vec) == 0 && aligned(x, 16) && aligned(out, 16);
-    a.apply_silu = apply_silu != 0;
-    a.stream = static_cast<hipStream_t>(stream);
-    return mamba::launch_causal_conv1d(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
-}
-
-int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes) {
-    if (!bytes) return MAMBA_ERR_INVALID_ARGUMENT;
-    *bytes = 0;
-    const int st = check_dims(dims);
-    if (st != MAMBA_OK) return st;
-    *bytes = mamba::scan_workspace_bytes(dims->batch, dims->seqlen, dims->dim, dims->dstate, dims->nheads,
-                                         dims->dtype == MAMBA_DTYPE_BF16);
+    a->x = x; a->weight = weight; a->bias = bias; a->doc_start = doc_start; a->conv_state = conv_state;
+    a->out = out;
+    a->batch = batch; a->seqlen = seqlen; a->dim = dim;
+    a->bf16 = dtype == MAMBA_DTYPE_BF16;
+    const int64_t vec = a->bf16 ? 8 : 4;
+    a->vectorized = (dim % vec) == 0 && aligned(x, 16) && aligned(out, 16);
+    a->apply_silu = apply_silu != 0;
+    a->stream = static_cast<hipStream_t>(stream);
     return MAMBA_OK;
 }
 
-int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
-                             const void* B, const void* C, const float* D, const void* z,
-                             const float* delta_bias, const uint8_t* doc_start, const float* initial_state,
-                             void* out, float* final_state, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+// Checks of one selective-scan call (shared by the scan and the fused conv + scan
+// entry points); fills `a` on success.  For the fused call (nextra > 0) u is
+// written too, and `extra` lists its further read-only inputs (conv input,
+// weights, history; byte sizes in extra_sz): neither may overlap what else the
+// call reads or writes.
+int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A, const void* B,
+               const void* C, const float* D, const void* z, const float* delta_bias, const uint8_t* doc_start,
+               const float* initial_state, void* out, float* final_state, void* workspace, size_t workspace_bytes,
+               void* stream, const void* const* extra, const size_t* extra_sz, int nextra, mamba::ScanArgs* a,
+               bool* empty) {
+    *empty = false;
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
     const int64_t Bt = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
-    if (Bt * L * Dm == 0) return MAMBA_OK;
+    if (Bt * L * Dm == 0) {
+        *empty = true;
+        return MAMBA_OK;
+    }
     if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
     const int64_t nd = dims->nheads ? dims->nheads : Dm;
@@ -148,6 +138,13 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
         if (overlap(ins[i], insz[i], final_state, fsb)) return MAMBA_ERR_INVALID_ARGUMENT;
     }
     if (overlap(out, act, final_state, fsb)) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (nextra > 0) {
+        for (int i = 1; i < kIns; ++i)           // u is written: it may not overlap the scan's inputs
+            if (overlap(ins[i], insz[i], u, act)) return MAMBA_ERR_INVALID_ARGUMENT;
+        for (int i = 0; i < nextra; ++i)
+            if (overlap(extra[i], extra_sz[i], out, act) || overlap(extra[i], extra_sz[i], final_state, fsb))
+                return MAMBA_ERR_INVALID_ARGUMENT;
+    }
 
     const size_t need = mamba::scan_workspace_bytes(Bt, L, Dm, N, dims->nheads, dims->dtype == MAMBA_DTYPE_BF16);
     if (need > 0) {
@@ -157,18 +154,105 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
             if (overlap(ins[i], insz[i], workspace, need)) return MAMBA_ERR_INVALID_ARGUMENT;
         if (overlap(out, act, workspace, need) || overlap(final_state, fsb, workspace, need))
             return MAMBA_ERR_INVALID_ARGUMENT;
+        for (int i = 0; i < nextra; ++i)
+            if (overlap(extra[i], extra_sz[i], workspace, need)) return MAMBA_ERR_INVALID_ARGUMENT;
     }
 
+    a->u = u; a->delta = delta; a->A = A; a->B = B; a->C = C; a->D = D; a->z = z;
+    a->delta_bias = delta_bias; a->doc_start = doc_start; a->initial_state = initial_state;
+    a->out = out; a->final_state = final_state;
+    a->ws = static_cast<float*>(workspace);
+    a->batch = Bt; a->seqlen = L; a->dim = Dm; a->dstate = N;
+    a->nheads = dims->nheads;
+    a->bf16 = dims->dtype == MAMBA_DTYPE_BF16;
+    a->softplus = dims->delta_softplus != 0;
+    a->stream = static_cast<hipStream_t>(stream);
+    return MAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char* mamba_status_string(int status) {
+    switch (status) {
+        case MAMBA_OK: return "ok";
+        case MAMBA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MAMBA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MAMBA_ERR_MISALIGNED: return "misaligned pointer";
+        case MAMBA_ERR_WORKSPACE: return "workspace missing or too small";
+        case MAMBA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int mamba_causal_conv1d_fwd(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
+                            const void* conv_state, void* out, int64_t batch, int64_t seqlen, int64_t dim,
+                            int32_t width, int32_t dtype, int32_t apply_silu, void* stream) {
+    mamba::ConvArgs a;
+    bool empty;
+    const int st = check_conv(x, weight, bias, doc_start, conv_state, out, batch, seqlen, dim, width, dtype,
+                              apply_silu, stream, &a, &empty);
+    if (st != MAMBA_OK || empty) return st;
+    return mamba::launch_causal_conv1d(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+
+int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes) {
+    if (!bytes) return MAMBA_ERR_INVALID_ARGUMENT;
+    *bytes = 0;
+    const int st = check_dims(dims);
+    if (st != MAMBA_OK) return st;
+    *bytes = mamba::scan_workspace_bytes(dims->batch, dims->seqlen, dims->dim, dims->dstate, dims->nheads,
+                                         dims->dtype == MAMBA_DTYPE_BF16);
+    return MAMBA_OK;
+}
+
+int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, const uint8_t* doc_start, const float* initial_state,
+                             void* out, float* final_state, void* workspace, size_t workspace_bytes,
+                             void* stream) {
     mamba::ScanArgs a;
-    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
-    a.delta_bias = delta_bias; a.doc_start = doc_start; a.initial_state = initial_state;
-    a.out = out; a.final_state = final_state;
-    a.ws = static_cast<float*>(workspace);
-    a.batch = Bt; a.seqlen = L; a.dim = Dm; a.dstate = N;
-    a.nheads = dims->nheads;
-    a.bf16 = dims->dtype == MAMBA_DTYPE_BF16;
-    a.softplus = dims->delta_softplus != 0;
-    a.stream = static_cast<hipStream_t>(stream);
+    bool empty;
+    const int st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out,
+                              final_state, workspace, workspace_bytes, stream, nullptr, nullptr, 0, &a, &empty);
+    if (st != MAMBA_OK || empty) return st;
+    return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const float* conv_weight,
+                        const float* conv_bias, const void* conv_state, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+                        const uint8_t* doc_start, const float* initial_state, void* u, void* out, float* final_state,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    const int sd = check_dims(dims);
+    if (sd != MAMBA_OK) return sd;
+    // The conv history is a continuation of the state: without an initial state
+    // token 0 starts a document for both, and the history is not used.
+    if (!initial_state) conv_state = nullptr;
+    mamba::ConvArgs ca;
+    bool empty;
+    int st = check_conv(x, conv_weight, conv_bias, doc_start, conv_state, u, dims->batch, dims->seqlen, dims->dim, 4,
+                        dims->dtype, 1, stream, &ca, &empty);
+    if (st != MAMBA_OK || empty) return st;
+    // u is written by the conv and read by the scan: it may overlap nothing else.
+    const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+    const size_t act = static_cast<size_t>(dims->batch * dims->seqlen * dims->dim) * esz;
+    const void* conv_in[] = {x, conv_weight, conv_bias, conv_state};
+    const size_t conv_sz[] = {act, static_cast<size_t>(dims->dim) * 16, static_cast<size_t>(dims->dim) * 4,
+                              static_cast<size_t>(dims->batch * dims->dim * 3) * esz};
+    mamba::ScanArgs a;
+    st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out, final_state, workspace,
+                    workspace_bytes, stream, conv_in, conv_sz, 4, &a, &empty);
+    if (st != MAMBA_OK || empty) return st;
+    if (dims->nheads == 0) {
+        a.conv_x = x; a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state;
+        return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+    }
+    if (mamba::launch_causal_conv1d(ca) != hipSuccess) return MAMBA_ERR_HIP;
     return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 

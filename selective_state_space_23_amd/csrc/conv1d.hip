@@ -73,7 +73,8 @@ template <typename T> struct VecIO<T, 1> {
 template <typename T, int VEC, bool SILU>
 __global__ __launch_bounds__(kConvBlock) void causal_conv1d_w4_kernel(
     const void* __restrict__ x, const float* __restrict__ weight, const float* __restrict__ bias,
-    const uint8_t* __restrict__ doc_start, void* __restrict__ out, int64_t seqlen, int dim) {
+    const uint8_t* __restrict__ doc_start, const void* __restrict__ conv_state, void* __restrict__ out,
+    int64_t seqlen, int dim) {
     const int ngroups = (dim + VEC - 1) / VEC;   // VEC == 1 when dim % VEC != 0
     const int g = blockIdx.x * kConvBlock + threadIdx.x;
     const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kConvTile;
@@ -81,12 +82,13 @@ __global__ __launch_bounds__(kConvBlock) void causal_conv1d_w4_kernel(
     const int64_t row = b * seqlen;
 
     // Document starts of tokens t0-3 .. t0+kConvTile-1 as one wave-uniform mask:
-    // bit i <-> token t0 - 3 + i.  Token 0 of the row always starts a document.
+    // bit i <-> token t0 - 3 + i.  Token 0 of the row starts a document unless the
+    // row continues a given history (conv_state).
     const int lane = threadIdx.x & 63;
     const int64_t tl = t0 - 3 + lane;
     bool is_start = false;
     if (lane < kConvTile + 3 && tl >= 0 && tl < seqlen)
-        is_start = (tl == 0) || (doc_start != nullptr && doc_start[row + tl] != 0);
+        is_start = (tl == 0 && conv_state == nullptr) || (doc_start != nullptr && doc_start[row + tl] != 0);
     const uint64_t starts = __ballot(is_start);
     if (g >= ngroups) return;
 
@@ -106,9 +108,15 @@ __global__ __launch_bounds__(kConvBlock) void causal_conv1d_w4_kernel(
 #pragma unroll
     for (int k = 0; k < 3; ++k) {            // replay the halo tokens t0-3 .. t0-1
         const int64_t t = t0 - 3 + k;
-        if (t < 0) continue;
         float xv[VEC];
-        VecIO<T, VEC>::load(x, (row + t) * dim + d0, xv);
+        if (t >= 0) {
+            VecIO<T, VEC>::load(x, (row + t) * dim + d0, xv);
+        } else if (conv_state != nullptr) {  // (B, D, 3): x_{-3}, x_{-2}, x_{-1} of each channel
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) xv[i] = Elem<T>::load(conv_state, (b * dim + d0 + i) * 3 + (3 + t));
+        } else {
+            continue;
+        }
         const bool reset = (starts >> k) & 1ull;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
@@ -150,10 +158,12 @@ hipError_t launch_conv_vec(const ConvArgs& a) {
               static_cast<unsigned>(a.batch));
     if (a.apply_silu)
         hipLaunchKernelGGL((causal_conv1d_w4_kernel<T, VEC, true>), grid, dim3(kConvBlock), 0, a.stream,
-                           a.x, a.weight, a.bias, a.doc_start, a.out, a.seqlen, static_cast<int>(a.dim));
+                           a.x, a.weight, a.bias, a.doc_start, a.conv_state, a.out, a.seqlen,
+                           static_cast<int>(a.dim));
     else
         hipLaunchKernelGGL((causal_conv1d_w4_kernel<T, VEC, false>), grid, dim3(kConvBlock), 0, a.stream,
-                           a.x, a.weight, a.bias, a.doc_start, a.out, a.seqlen, static_cast<int>(a.dim));
+                           a.x, a.weight, a.bias, a.doc_start, a.conv_state, a.out, a.seqlen,
+                           static_cast<int>(a.dim));
     return hipGetLastError();
 }
 

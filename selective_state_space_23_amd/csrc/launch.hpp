@@ -12,6 +12,7 @@ struct ConvArgs {
     const float* weight;
     const float* bias;
     const uint8_t* doc_start;
+    const void* conv_state;   // (B, D, 3) history before token 0, or null
     void* out;
     int64_t batch, seqlen, dim;
     bool bf16;
@@ -36,6 +37,12 @@ struct ScanArgs {
     void* out;
     float* final_state;
     float* ws;          // chunk carries, see scan_workspace_bytes
+    // Fused conv1d (width 4, SiLU): when conv_x is set, u is an output: the scan
+    // computes u = SiLU(conv(conv_x)) itself (per-channel A) and stores it there.
+    const void* conv_x = nullptr;
+    const float* conv_w = nullptr;
+    const float* conv_b = nullptr;
+    const void* conv_state = nullptr;   // (B, D, 3) history before token 0, or null
     int64_t batch, seqlen, dim, dstate;
     int nheads;         // 0: per-channel A (D, N); > 0: scalar A per head
     bool bf16;

@@ -49,6 +49,7 @@ constexpr int kScanBlock = 256;    // 4 independent waves, 256 consecutive chann
 #define MAMBA_SCAN_WAVES_PER_EU 4
 #endif
 constexpr int kGroup = MAMBA_SCAN_GROUP;   // tokens whose activations are fetched together
+constexpr int kNoStore = 0x7fffff00;       // buffer offset past any resource: the access is dropped
 
 struct ScanKParams {
     const void* u;
@@ -65,6 +66,12 @@ struct ScanKParams {
     float* final_state;
     float* ws_P;        // [nchunks-1][B][D][N]: pass 1 P, then pass 2 carries
     float* ws_H;        // [nchunks-1][B][D][N]: pass 1 H
+    const void* conv_x;       // fused conv (pass 1): its input x (B, L, D)
+    const float* conv_w;      // (D, 4)
+    const float* conv_b;      // (D,) or null
+    const void* conv_state;   // (B, D, 3) or null
+    void* u_out;              // (B, L, D): pass 1 stores u here
+    int64_t nslots;           // chunks with an aggregate slot (nchunks - 1)
     int64_t seqlen;
     int64_t chunk_len;
     int dim;
@@ -110,9 +117,17 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, int byte_of
 //     fetched while the current group computes: two register sets in ping-pong,
 //     so no loaded register is ever copied (a copy would wait on the load);
 //   - addresses are a wave-uniform 64-bit row base plus a 32-bit element offset.
-template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS>
+//
+// CONV (pass 1 only): the activations loaded are the conv input x, and each lane
+// forms u = SiLU(bias + w . (x[t-3], x[t-2], x[t-1], x[t])) itself from a 3-token
+// history in registers (cleared at document starts, primed from the tokens
+// before the chunk), stores u (rounded to T) for pass 3 and scans with it.  The
+// arithmetic and its order are those of the standalone conv kernel, so u is
+// bitwise the same.
+template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS, bool CONV = false>
 __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMBA_SCAN_WAVES_PER_EU))) void scan_chunk_kernel(
     const ScanKParams p) {
+    static_assert(!CONV || (!OUTPUT && !HEADS), "the conv runs in the aggregate pass of the per-channel scan");
     constexpr int G = kGroup;
     constexpr int kWin = 64;                                   // tokens per staged window
     constexpr int kRows = OUTPUT ? 2 : 1;                      // B and C, or B only
@@ -138,12 +153,14 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     // for the per-lane activations: t * width + channel fits in 31 bits.
     constexpr int kEsz = static_cast<int>(sizeof(T));
     const int64_t act_row = L * p.dim;
-    const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(static_cast<const T*>(p.u) + b * act_row, act_row * kEsz);
+    const __amdgpu_buffer_rsrc_t u_rs =
+        make_rsrc(static_cast<const T*>(CONV ? p.conv_x : p.u) + b * act_row, act_row * kEsz);
+    const __amdgpu_buffer_rsrc_t uo_rs =
+        make_rsrc(static_cast<T*>(CONV ? p.u_out : p.out) + b * act_row, act_row * kEsz);
     const __amdgpu_buffer_rsrc_t dl_rs =
         make_rsrc(static_cast<const T*>(p.delta) + b * L * nd, L * nd * kEsz);
     const __amdgpu_buffer_rsrc_t z_rs =
         make_rsrc(HAS_Z ? static_cast<const T*>(p.z) + b * act_row : static_cast<const T*>(p.u), act_row * kEsz);
-    const __amdgpu_buffer_rsrc_t out_rs = make_rsrc(static_cast<T*>(p.out) + b * act_row, act_row * kEsz);
     const T* B_row = static_cast<const T*>(p.B) + b * L * N;
     const T* C_row = static_cast<const T*>(p.C) + b * L * N;
     const uint8_t* ds_row = p.doc_start ? p.doc_start + b * L : nullptr;
@@ -173,6 +190,29 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     }
     float sum_dt = 0.0f;          // pass 1: sum of dt since the chunk start
     bool any_reset = false;       // pass 1: a document starts inside the chunk
+
+    // Fused conv: weights and the input history x[t-1], x[t-2], x[t-3] as seen by
+    // the chunk's first token (taps before its document start read zero).
+    float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f, xh1 = 0.0f, xh2 = 0.0f, xh3 = 0.0f;
+    if constexpr (CONV) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cw[j] = p.conv_w[static_cast<int64_t>(dc) * 4 + j];
+        cb = p.conv_b ? p.conv_b[dc] : 0.0f;
+        auto hist = [&](int k) -> float {              // x[t_begin - k]
+            const int64_t t = t_begin - k;
+            if (t >= 0) return buf_load<T>(u_rs, static_cast<int>((t * p.dim + dc) * kEsz));
+            if (p.conv_state == nullptr) return 0.0f;
+            return Elem<T>::load(p.conv_state, (b * p.dim + dc) * 3 + (3 - k));
+        };
+        auto starts_at = [&](int64_t t) -> bool {      // same rule as the window mask
+            if (t < 0) return false;
+            return (t == 0 && p.initial_state == nullptr) || (ds_row != nullptr && ds_row[t] != 0);
+        };
+        const bool s1 = starts_at(t_begin - 1), s2 = starts_at(t_begin - 2);
+        xh1 = hist(1);
+        xh2 = s1 ? 0.0f : hist(2);
+        xh3 = (s1 || s2) ? 0.0f : hist(3);
+    }
 
     auto load_group = [&](int64_t g0, float (&uu)[G], float (&dl)[G], float (&zz)[G]) {
 #pragma unroll
@@ -247,7 +287,26 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             float dt = cd[k] + dbias;
             if constexpr (SOFTPLUS) dt = softplus_f(dt);
             dt = valid ? dt : 0.0f;
-            const float w = dt * cu[k];
+            float uk = cu[k];
+            if constexpr (CONV) {
+                const float xt = cu[k];
+                xh1 = reset ? 0.0f : xh1;
+                xh2 = reset ? 0.0f : xh2;
+                xh3 = reset ? 0.0f : xh3;
+                float acc = __builtin_fmaf(cw[3], xt, cb);
+                acc = __builtin_fmaf(cw[2], xh1, acc);
+                acc = __builtin_fmaf(cw[1], xh2, acc);
+                acc = __builtin_fmaf(cw[0], xh3, acc);
+                uk = silu_f(acc);
+                if constexpr (sizeof(T) == 2) uk = bf16_to_f32(f32_to_bf16(uk));   // the u pass 3 reads back
+                // Branchless: a store past the resource's end is dropped by the
+                // hardware, and a branch here would double the register footprint.
+                buf_store<T>(uo_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, uk);
+                xh3 = xh2;
+                xh2 = xh1;
+                xh1 = xt;
+            }
+            const float w = dt * uk;
             float y0 = 0.0f, y1 = 0.0f, y2 = 0.0f, y3 = 0.0f;
             float a_head = 0.0f;
             if constexpr (HEADS) a_head = exp2_fast(__builtin_fmaf(dt, Al2[0], r));
@@ -278,7 +337,7 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             if constexpr (OUTPUT) {
                 float y = ((y0 + y1) + (y2 + y3)) + Dd * cu[k];
                 if constexpr (HAS_Z) y *= silu_f(cz[k]);
-                if (active && valid) buf_store<T>(out_rs, (static_cast<int>(t) * p.dim + d) * kEsz, y);
+                if (active && valid) buf_store<T>(uo_rs, (static_cast<int>(t) * p.dim + d) * kEsz, y);
             } else {
                 sum_dt += dt;
             }
@@ -322,6 +381,7 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             for (int n = 0; n < N; ++n) fs[n] = h[n];
         }
     } else {
+        if (c >= p.nslots) return;          // the last chunk's aggregate is never used
         float* P = p.ws_P + c * slot_stride + my_slot;
         float* H = p.ws_H + c * slot_stride + my_slot;
 #pragma unroll
@@ -381,16 +441,35 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     p.headdim = a.nheads ? static_cast<int>(a.dim / a.nheads) : 0;
     p.nbatch = static_cast<int>(a.batch);
     p.softplus = a.softplus ? 1 : 0;
+    p.conv_x = a.conv_x; p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.conv_state = a.conv_state;
+    p.u_out = a.conv_x ? const_cast<void*>(a.u) : nullptr;
+    p.nslots = nslots;
 
     const unsigned gx = static_cast<unsigned>((a.dim + kScanBlock - 1) / kScanBlock);
+    if constexpr (!HEADS) {
+        if (a.conv_x != nullptr) {
+            // Fused conv: pass 1 runs on every chunk (the last one only to produce u).
+            dim3 g1(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
+            if (a.softplus)
+                hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, true, true>), g1, dim3(kScanBlock),
+                                   0, a.stream, p);
+            else
+                hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, false, true>), g1,
+                                   dim3(kScanBlock), 0, a.stream, p);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
     if (nslots > 0) {
-        dim3 g1(gx, static_cast<unsigned>(nslots), static_cast<unsigned>(a.batch));
-        if (a.softplus)
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, true>), g1, dim3(kScanBlock), 0,
-                               a.stream, p);
-        else
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, false>), g1, dim3(kScanBlock), 0,
-                               a.stream, p);
+        if (a.conv_x == nullptr) {
+            dim3 g1(gx, static_cast<unsigned>(nslots), static_cast<unsigned>(a.batch));
+            if (a.softplus)
+                hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, true>), g1, dim3(kScanBlock), 0,
+                                   a.stream, p);
+            else
+                hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, false>), g1, dim3(kScanBlock), 0,
+                                   a.stream, p);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         dim3 g2(static_cast<unsigned>((count + 255) / 256));

@@ -50,8 +50,8 @@ def test_status_strings(lib):
 FAKE = 0x10000  # a non-null address never dereferenced: every call below fails validation first
 
 
-def conv(lib, x=FAKE, w=FAKE, b=None, ds=None, out=FAKE * 4, B=1, L=8, D=16, W=4, dtype=1, silu=1):
-    return lib.mamba_causal_conv1d_fwd(x, w, b, ds, out, B, L, D, W, dtype, silu, None)
+def conv(lib, x=FAKE, w=FAKE, b=None, ds=None, cs=None, out=FAKE * 4, B=1, L=8, D=16, W=4, dtype=1, silu=1):
+    return lib.mamba_causal_conv1d_fwd(x, w, b, ds, cs, out, B, L, D, W, dtype, silu, None)
 
 
 def test_conv_validation(lib):
@@ -65,6 +65,8 @@ def test_conv_validation(lib):
     assert conv(lib, out=FAKE * 4 + 2, dtype=0) == _lib.MAMBA_ERR_MISALIGNED
     assert conv(lib, out=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # aliases x
     assert conv(lib, L=10 ** 7) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert conv(lib, cs=FAKE * 4 + 64) == _lib.MAMBA_ERR_INVALID_ARGUMENT       # history inside out
+    assert conv(lib, cs=FAKE * 8 + 1) == _lib.MAMBA_ERR_MISALIGNED
     # empty shapes are a no-op, even with null pointers
     assert conv(lib, x=None, w=None, out=None, B=0) == _lib.MAMBA_OK
     assert conv(lib, x=None, w=None, out=None, L=0) == _lib.MAMBA_OK
@@ -185,3 +187,21 @@ def test_state_update_validation(lib):
     assert state_update(lib, state=FAKE * 16 + 4) == _lib.MAMBA_ERR_MISALIGNED
     assert state_update(lib, out=FAKE * 16 + 64) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # out inside state
     assert state_update(lib, d=dims(batch=0, seqlen=1), state=None, u=None, out=None) == _lib.MAMBA_OK
+
+
+def conv_scan(lib, d=None, x=FAKE * 7, cw=FAKE * 8, cb=None, cs=None, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4,
+              C=FAKE * 5, D=None, z=None, bias=None, ds=None, init=None, u=FAKE, out=FAKE * 6, fs=None, ws=None, wsb=0):
+    d = d or dims(batch=1, seqlen=64, dim=64)
+    return lib.mamba_conv_scan_fwd(ctypes.byref(d), x, cw, cb, cs, delta, A, B, C, D, z, bias, ds, init, u, out, fs,
+                                   ws, wsb, None)
+
+
+def test_conv_scan_validation(lib):
+    assert conv_scan(lib, x=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv_scan(lib, u=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert conv_scan(lib, x=FAKE * 7 + 1) == _lib.MAMBA_ERR_MISALIGNED
+    assert conv_scan(lib, u=FAKE * 7) == _lib.MAMBA_ERR_INVALID_ARGUMENT        # u aliases x
+    assert conv_scan(lib, u=FAKE * 2) == _lib.MAMBA_ERR_INVALID_ARGUMENT        # u aliases delta
+    assert conv_scan(lib, cw=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT       # weights inside out
+    assert conv_scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=5)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert conv_scan(lib, d=dims(batch=0), x=None, u=None, out=None) == _lib.MAMBA_OK

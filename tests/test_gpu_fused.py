@@ -1,0 +1,123 @@
+"""GPU parity of the fused conv + scan entry point (and of the conv history input)
+against the fp64 oracle pipeline.  The fused call must also reproduce, bit for
+bit, the u of the standalone conv kernel (the same arithmetic in the same order)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_custom, make_inputs
+
+from gpu_helpers import assert_close, oracle_pipeline, to_dev, to_host, torch_mod, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (they fail instead of skipping)")
+    import selective_state_space_23_amd as mod
+    mod._lib.load()
+    return mod
+
+
+def fused(ssm, dev, **kw):
+    return ssm.conv_scan_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["delta"], dev["A"], dev["B"], dev["C"],
+                             dev["D"], dev["z"], dev["delta_bias"], dev["doc_start"], **kw)
+
+
+def conv_window(x, doc_start, t):
+    """x[t-3 .. t-1] of each channel, zero before the latest document start at or
+    before t-1 (the history a continuation at token t sees)."""
+    Bt, _, Dm = x.shape
+    w = np.zeros((Bt, Dm, 3), dtype=np.float32)
+    for b in range(Bt):
+        first = 0
+        for s in range(max(t - 3, 0), t):
+            if doc_start[b, s]:
+                first = s
+        for k, s in enumerate(range(t - 3, t)):
+            if s >= first and s >= 0:
+                w[b, :, k] = x[b, s]
+    return w
+
+
+CASES = [
+    # (batch, seqlen, dim, dstate, nheads, dtype, docs)
+    (2, 1000, 100, 16, 0, "bf16", 150.0),     # ragged D, many chunks
+    (1, 500, 72, 4, 0, "f32", 60.0),
+    (2, 130, 64, 8, 0, "bf16", 20.0),         # a few chunks with a tail
+    (3, 50, 64, 16, 0, "bf16", 9.0),          # one chunk: no carry pass
+    (1, 300, 128, 64, 2, "bf16", 70.0),       # heads: conv kernel, then the matrix-core scan
+    (2, 200, 128, 32, 2, "f32", 50.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_conv_scan_parity(ssm, case):
+    torch = torch_mod()
+    Bt, L, Dm, N, H, dt, docs = case
+    inp = make_custom(Bt, L, Dm, N, nheads=H, dtype=dt, docs=docs, seed=700 + L + Dm)
+    inp.conv_b[:] = np.linspace(-0.3, 0.3, Dm).astype(np.float32)
+    dev = upload(inp)
+    u, out, fin = fused(ssm, dev)
+    u_conv = ssm.causal_conv1d_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["doc_start"])
+    assert torch.equal(u, u_conv), "fused conv differs from the conv kernel"
+    ch = np.arange(Dm)
+    u_ref, out_ref, fin_ref = oracle_pipeline(inp, ch)
+    u_exact = oracle.causal_conv1d(inp.x, inp.conv_w, inp.conv_b, inp.doc_start)
+    assert_close(to_host(u), u_exact, dt, f"fused u {case}")
+    assert_close(to_host(out), out_ref, dt, f"fused out {case}")
+    assert_close(to_host(fin), fin_ref, dt, f"fused final_state {case}")
+
+
+@pytest.mark.parametrize("H,N", [(0, 16), (2, 64)])
+def test_conv_scan_continuation(ssm, H, N):
+    """[0, L1) and then [L1, L) with the first part's final state and conv window
+    give the whole sequence's results; one row has a document starting right
+    before the split, inside the handed-over window."""
+    torch = torch_mod()
+    L, L1, Dm = 800, 457, 128
+    inp = make_custom(2, L, Dm, N, nheads=H, dtype="bf16", docs=150.0, seed=710 + N)
+    inp.doc_start[0, L1 - 1] = 1
+    inp.doc_start[1, L1 - 2:L1 + 1] = 0
+    dev = upload(inp)
+    ch = np.arange(Dm)
+    _, out_ref, fin_ref = oracle_pipeline(inp, ch)
+    cut = ("x", "z", "delta", "B", "C", "doc_start")
+    first = {k: (v[:, :L1].contiguous() if k in cut else v) for k, v in dev.items()}
+    second = {k: (v[:, L1:].contiguous() if k in cut else v) for k, v in dev.items()}
+    _, o1, f1 = fused(ssm, first)
+    window = to_dev(conv_window(inp.x, inp.doc_start, L1), "bf16")
+    _, o2, f2 = fused(ssm, second, initial_state=f1, conv_state=window)
+    assert_close(np.concatenate([to_host(o1), to_host(o2)], axis=1), out_ref, "bf16", "continued out")
+    assert_close(to_host(f2), fin_ref, "bf16", "continued final_state")
+    # the conv alone with the same history
+    u2 = ssm.causal_conv1d_fwd(second["x"], dev["conv_w"], dev["conv_b"], second["doc_start"], conv_state=window)
+    u_exact = oracle.causal_conv1d(inp.x, inp.conv_w, inp.conv_b, inp.doc_start)[:, L1:]
+    assert_close(to_host(u2), u_exact, "bf16", "conv with history")
+
+
+SAMPLES = {"packed_32k": [0, 5, 63, 64, 700, 1535], "heads_32k": [0, 64, 700, 1535], "m130_2k": [0, 777, 1535]}
+
+
+@pytest.mark.parametrize("name", list(SAMPLES))
+def test_conv_scan_workload(ssm, name):
+    inp = make_inputs(name)
+    ch = np.array(SAMPLES[name])
+    print(f"[fused] {name} shape={inp.shape}", flush=True)
+    dev = upload(inp)
+    u, out, fin = fused(ssm, dev)
+    torch = torch_mod()
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(ch).to(u.device)
+    u_g, out_g, fin_g = to_host(u.index_select(2, idx)), to_host(out.index_select(2, idx)), to_host(
+        fin.index_select(1, idx))
+    del dev, u, out, fin
+    _, out_ref, fin_ref = oracle_pipeline(inp, ch)
+    u_exact = oracle.causal_conv1d(inp.x[:, :, ch], inp.conv_w[ch], inp.conv_b[ch], inp.doc_start)
+    assert_close(u_g, u_exact, inp.dtype, f"{name} u")
+    assert_close(out_g, out_ref, inp.dtype, f"{name} out")
+    assert_close(fin_g, fin_ref, inp.dtype, f"{name} final_state")
