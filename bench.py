@@ -7,10 +7,11 @@ discretisation, the recurrence, C.h + D.u readout, SiLU(z) gate, per-document
 resets, final state).  Inputs are generated on the host with the seeded recipe
 of `workloads`, uploaded once, and are resident in HBM before timing starts.
 
-Prints one JSON line.  `value` is tokens/s of the step (conv + scan).  Extra
-objects: `roofline` for the dominant kernel (live HIP-event timing), the HBM
-roofline of the conv + scan pair, per-kernel timings and `cpu_baseline` (the fp64
-oracle timed on this host on a bounded sample).
+Prints one JSON line.  `value` is tokens/s of the step (conv + scan; by default
+one fused mamba_conv_scan_fwd call).  Extra objects: `roofline` for the timed
+call (live HIP-event timing), the HBM roofline of the conv + scan pair, a device
+copy probe, and `cpu_baseline` (the fp64 oracle timed on this host on a bounded
+sample).
 """
 
 from __future__ import annotations
@@ -27,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "selective-scan fwd tokens/s + % HBM roofline, B=2 L=32K D=1536 N=16 bf16"
 HBM_PEAK_GBS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
 def scan_bytes(B, L, D, N, nheads, esz):
@@ -59,6 +61,19 @@ def scan_alu_flop_eq(B, L, D, N, nheads):
     else:
         slots = el * 3 + B * L * D * 13 + B * L * nheads * (13 + 4 + 1)
     return 2.0 * slots
+
+
+def ssd_mfma_flops(B, L, D, N, H, q=64):
+    """bf16 MFMA flops the chunked matrix form of scalar-A heads issues per call:
+    per 64-token chunk and head, the causal C B^T tiles (10 of the 16 16x16 tiles,
+    K = N), M x over the causal K range (K = 32, 32, 64, 64 for the four 16-row
+    tiles), C H_in (Q x N x P) and the state update (N x Q x P) in the output pass,
+    and the state update again in the aggregate pass."""
+    P = D // H
+    npad = -(-N // 32) * 32
+    per_chunk = (10 * 16 * 16 * npad + 16 * P * (32 + 32 + 64 + 64) + q * npad * P + npad * P * q) * 2
+    per_chunk += npad * P * q * 2
+    return B * H * (-(-L // q)) * per_chunk
 
 
 def conv_alu_flop_eq(B, L, D):
@@ -132,13 +147,15 @@ def cpu_baseline(inp, tokens_per_row):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="packed_32k",
                     help="workload name from workloads.CONFIGS (default: the 32K packed bf16 shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768, help="oracle sample: tokens per row")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the device copy probe (0: skip)")
+    ap.add_argument("--path", choices=("fused", "split"), default="fused",
+                    help="fused: one mamba_conv_scan_fwd call per step; split: conv call, then scan call")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -175,14 +192,22 @@ def main():
     fin = torch.empty((B, D, N), dtype=torch.float32, device=dev)
     ws = torch.empty(max(ssm.scan_workspace_bytes(B, L, D, N, H, inp.dtype), 1), dtype=torch.uint8, device=dev)
 
+    fused = args.path == "fused"
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        ssm.causal_conv1d_fwd(t["x"], t["conv_w"], t["conv_b"], t["doc_start"], out=u)
-        if ev is not None:
-            ev[1].record()
-        ssm.selective_scan_fwd(u, t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
-                               t["doc_start"], out=out, final_state=fin, workspace=ws)
+        if fused:
+            ssm.conv_scan_fwd(t["x"], t["conv_w"], t["conv_b"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                              t["delta_bias"], t["doc_start"], u=u, out=out, final_state=fin, workspace=ws)
+            if ev is not None:
+                ev[1].record()
+        else:
+            ssm.causal_conv1d_fwd(t["x"], t["conv_w"], t["conv_b"], t["doc_start"], out=u)
+            if ev is not None:
+                ev[1].record()
+            ssm.selective_scan_fwd(u, t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                                   t["doc_start"], out=out, final_state=fin, workspace=ws)
         if ev is not None:
             ev[2].record()
 
@@ -198,21 +223,47 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    conv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    # HIP events on torch's current stream, which is the stream the binding
+    # passes to every launch of the library.
+    call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
+    first_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
 
     probe = copy_probe(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
     csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
-    traffic = recorded_traffic(os.path.join(ROOT, "profiles", f"scan_{args.config}_hbm_traffic.txt"),
-                               [os.path.join(csrc, f) for f in ("scan.hip", "launch.hpp", "device_common.hpp")])
+    traffic = recorded_traffic(
+        os.path.join(ROOT, "profiles", f"{args.path}_{args.config}_hbm_traffic.txt"),
+        [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))])
 
     tokens = B * L
     sb = scan_bytes(B, L, D, N, H, esz)
     cb = conv_bytes(B, L, D, esz)
     scan_flops = scan_alu_flop_eq(B, L, D, N, H)
-    scan_tflops = scan_flops / (scan_ms * 1e-3) / 1e12
-    scan_gbs = sb / (scan_ms * 1e-3) / 1e9
-    pair_gbs = (sb + cb) / ((conv_ms + scan_ms) * 1e-3) / 1e9
+    conv_flops = conv_alu_flop_eq(B, L, D)
+    if fused:
+        kernel = ("mamba_conv_scan_fwd, one call: conv + aggregate pass, carry pass, output pass"
+                  if H == 0 else "mamba_conv_scan_fwd, one call: conv, aggregate pass, carry pass, output pass")
+        dom_ms, dom_flops, dom_bytes = call_ms, scan_flops + conv_flops, sb + cb
+        timings = {"call_ms": call_ms}
+    else:
+        kernel = "mamba_selective_scan_fwd, one call: aggregate pass, carry pass, output pass"
+        dom_ms, dom_flops, dom_bytes = call_ms - first_ms, scan_flops, sb
+        timings = {"conv_ms": first_ms, "scan_ms": call_ms - first_ms}
+    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    pair_gbs = (sb + cb) / (call_ms * 1e-3) / 1e9
+    if H > 0 and inp.dtype == "bf16":
+        # Scalar-A heads run as bf16 matrix products: the chunked form's flops go to
+        # the matrix cores and the call is judged against HBM (its MFMA share beside).
+        mf = ssd_mfma_flops(B, L, D, N, H)
+        roof = {"kernel": kernel, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                "mfma_flops": mf, "mfma_TFLOPs": mf / (dom_ms * 1e-3) / 1e12,
+                "mfma_frac": mf / (dom_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, "avg_ms": dom_ms}
+    else:
+        roof = {"kernel": kernel, "bound": "alu", "achieved": dom_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": dom_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic,
+                "algorithmic_flop_eq": dom_flops, "algorithmic_bytes": dom_bytes, "hbm_achieved_GBs": dom_gbs,
+                "hbm_frac": dom_gbs / HBM_PEAK_GBS, "avg_ms": dom_ms}
     result = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -227,26 +278,12 @@ def main():
         "dtype": "bf16" if inp.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": args.config, "batch": B, "seqlen": L, "dim": D, "dstate": N, "nheads": H,
-                   "d_conv": 4, "doc_mean_len": spec["docs"], "io_dtype": inp.dtype, "state_dtype": "f32"},
-        "roofline": {
-            "kernel": "selective_scan_fwd (all launches of one call)",
-            "bound": "alu",
-            "achieved": scan_tflops,
-            "peak": FP32_VECTOR_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS,
-            "traffic": traffic,
-            "hbm_achieved_GBs": scan_gbs,
-            "hbm_frac": scan_gbs / HBM_PEAK_GBS,
-            "algorithmic_bytes": sb,
-            "algorithmic_flop_eq": scan_flops,
-            "avg_ms": scan_ms,
-        },
-        "hbm_roofline_pair": {
-            "achieved": pair_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pair_gbs / HBM_PEAK_GBS,
-            "algorithmic_bytes": sb + cb, "conv_ms": conv_ms, "scan_ms": scan_ms,
-            "conv_GBs": cb / (conv_ms * 1e-3) / 1e9,
-        },
+                   "d_conv": 4, "doc_mean_len": spec["docs"], "io_dtype": inp.dtype, "state_dtype": "f32",
+                   "path": args.path},
+        "roofline": roof,
+        "hbm_roofline_pair": dict(
+            {"achieved": pair_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pair_gbs / HBM_PEAK_GBS,
+             "algorithmic_bytes": sb + cb, "conv_bytes": cb, "scan_bytes": sb}, **timings),
         "copy_probe": None if probe is None else dict(
             probe, pair_frac_of_copy=pair_gbs / probe["GBs"], kernel="hipMemcpyAsync device-to-device"),
     }
