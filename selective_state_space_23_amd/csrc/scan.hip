@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 xh1 = xt;
             }
             const float w = dt * uk;
-            float y0 = 0.0f, y1 = 0.0f, y2 = 0.0f, y3 = 0.0f;
+            float y0 = 0.0f, y1 = 0.0f;          // two partial sums of C . h
             float a_head = 0.0f;
             if constexpr (HEADS) a_head = exp2_fast(__builtin_fmaf(dt, Al2[0], r));
             const float4* Bq = reinterpret_cast<const float4*>(smem + (off + k) * N);
@@ -327,15 +327,13 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                     else a = exp2_fast(__builtin_fmaf(dt, Al2[n], r));
                     h[n] = __builtin_fmaf(a, h[n], w * bb[j]);
                     if constexpr (OUTPUT) {
-                        if (j == 0) y0 = __builtin_fmaf(cc[j], h[n], y0);
-                        else if (j == 1) y1 = __builtin_fmaf(cc[j], h[n], y1);
-                        else if (j == 2) y2 = __builtin_fmaf(cc[j], h[n], y2);
-                        else y3 = __builtin_fmaf(cc[j], h[n], y3);
+                        if (j == 0 || j == 2) y0 = __builtin_fmaf(cc[j], h[n], y0);
+                        else y1 = __builtin_fmaf(cc[j], h[n], y1);
                     }
                 }
             }
             if constexpr (OUTPUT) {
-                float y = ((y0 + y1) + (y2 + y3)) + Dd * cu[k];
+                float y = (y0 + y1) + Dd * cu[k];
                 if constexpr (HAS_Z) y *= silu_f(cz[k]);
                 if (active && valid) buf_store<T>(uo_rs, (static_cast<int>(t) * p.dim + d) * kEsz, y);
             } else {
