@@ -71,6 +71,7 @@ struct ScanKParams {
     const float* conv_b;      // (D,) or null
     const void* conv_state;   // (B, D, 3) or null
     void* u_out;              // (B, L, D): pass 1 stores u here
+    void* dt_ws;              // (B, L, D), I/O dtype: step sizes from pass 1 for pass 3 (per-channel A)
     int64_t nslots;           // chunks with an aggregate slot (nchunks - 1)
     int64_t seqlen;
     int64_t chunk_len;
@@ -157,8 +158,13 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
         make_rsrc(static_cast<const T*>(CONV ? p.conv_x : p.u) + b * act_row, act_row * kEsz);
     const __amdgpu_buffer_rsrc_t uo_rs =
         make_rsrc(static_cast<T*>(CONV ? p.u_out : p.out) + b * act_row, act_row * kEsz);
+    // Per-channel A: pass 1 stores dt (rounded to T) and pass 3 reads it back
+    // instead of recomputing the softplus; both passes use the same rounded dt.
+    constexpr bool kDtWs = !HEADS;
     const __amdgpu_buffer_rsrc_t dl_rs =
-        make_rsrc(static_cast<const T*>(p.delta) + b * L * nd, L * nd * kEsz);
+        make_rsrc(static_cast<const T*>((kDtWs && OUTPUT) ? p.dt_ws : p.delta) + b * L * nd, L * nd * kEsz);
+    const __amdgpu_buffer_rsrc_t dto_rs =
+        make_rsrc(static_cast<T*>(kDtWs ? p.dt_ws : p.out) + b * act_row, kDtWs ? act_row * kEsz : 0);
     const __amdgpu_buffer_rsrc_t z_rs =
         make_rsrc(HAS_Z ? static_cast<const T*>(p.z) + b * act_row : static_cast<const T*>(p.u), act_row * kEsz);
     const T* B_row = static_cast<const T*>(p.B) + b * L * N;
@@ -284,8 +290,17 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 any_reset = any_reset || reset;
                 sum_dt = reset ? 0.0f : sum_dt;
             }
-            float dt = cd[k] + dbias;
-            if constexpr (SOFTPLUS) dt = softplus_f(dt);
+            float dt;
+            if constexpr (kDtWs && OUTPUT) {
+                dt = cd[k];                                   // stored by pass 1
+            } else {
+                dt = cd[k] + dbias;
+                if constexpr (SOFTPLUS) dt = softplus_f(dt);
+                if constexpr (kDtWs) {
+                    if constexpr (sizeof(T) == 2) dt = bf16_to_f32(f32_to_bf16(dt));
+                    buf_store<T>(dto_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, dt);
+                }
+            }
             dt = valid ? dt : 0.0f;
             float uk = cu[k];
             if constexpr (CONV) {
@@ -422,6 +437,16 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(float* __restrict__ ws_
     }
 }
 
+// Byte offset of the step-size array in the per-channel scan's workspace: after
+// the two carry arrays, rounded up to 256 bytes.
+size_t dt_ws_offset(int64_t batch, int64_t dim, int64_t dstate, const ScanPlan& plan) {
+    const size_t carries =
+        plan.nchunks > 1
+            ? static_cast<size_t>(2 * (plan.nchunks - 1)) * static_cast<size_t>(batch * dim * dstate) * sizeof(float)
+            : 0;
+    return (carries + 255) / 256 * 256;
+}
+
 template <typename T, int N, bool HEADS>
 hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     ScanKParams p;
@@ -432,6 +457,7 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     const int64_t nslots = plan.nchunks - 1;
     p.ws_P = a.ws;
     p.ws_H = a.ws ? a.ws + nslots * count : nullptr;
+    p.dt_ws = (!HEADS && a.ws) ? reinterpret_cast<char*>(a.ws) + dt_ws_offset(a.batch, a.dim, N, plan) : nullptr;
     p.seqlen = a.seqlen;
     p.chunk_len = plan.chunk_len;
     p.dim = static_cast<int>(a.dim);
@@ -458,8 +484,20 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
             if (e != hipSuccess) return e;
         }
     }
+    if (!HEADS && a.conv_x == nullptr) {
+        // Pass 1 runs on every chunk: the last one only to store its step sizes.
+        dim3 g1(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
+        if (a.softplus)
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, true>), g1, dim3(kScanBlock), 0,
+                               a.stream, p);
+        else
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, false>), g1, dim3(kScanBlock), 0,
+                               a.stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (nslots > 0) {
-        if (a.conv_x == nullptr) {
+        if (HEADS && a.conv_x == nullptr) {
             dim3 g1(gx, static_cast<unsigned>(nslots), static_cast<unsigned>(a.batch));
             if (a.softplus)
                 hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, true>), g1, dim3(kScanBlock), 0,
@@ -544,8 +582,14 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim) {
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16) {
     if (nheads > 0 && bf16) return ssd_workspace_bytes(batch, seqlen, dim, dstate, nheads);
     const ScanPlan plan = plan_scan(batch, seqlen, dim);
-    if (plan.nchunks <= 1) return 0;
-    return static_cast<size_t>(2 * (plan.nchunks - 1)) * static_cast<size_t>(batch * dim * dstate) * sizeof(float);
+    const size_t carries =
+        plan.nchunks > 1
+            ? static_cast<size_t>(2 * (plan.nchunks - 1)) * static_cast<size_t>(batch * dim * dstate) * sizeof(float)
+            : 0;
+    if (nheads > 0) return carries;
+    // Per-channel A: the step sizes pass 1 hands to pass 3 follow the carries.
+    return dt_ws_offset(batch, dim, dstate, plan) +
+           static_cast<size_t>(batch * seqlen * dim) * (bf16 ? 2 : 4);
 }
 
 hipError_t launch_selective_scan(const ScanArgs& a) {
