@@ -563,15 +563,18 @@ bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16) {
     return dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128;
 }
 
-// Chunks are sized so that pass 3 launches roughly 4096+ waves (four or more per
-// SIMD on 256 CUs) while keeping the carry workspace small.
+// Chunks are sized so that each pass launches roughly 4096 or more waves (four
+// or more per SIMD on 256 CUs) while keeping the carry workspace small.
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim) {
     const int64_t chains = batch * ((dim + 63) / 64);
     int64_t want_chunks = chains > 0 ? (MAMBA_SCAN_TARGET_WAVES + chains - 1) / chains : 1;
     if (want_chunks < 1) want_chunks = 1;
     int64_t len = (seqlen + want_chunks - 1) / want_chunks;
-    int64_t chunk = 64;
-    while (chunk < len) chunk *= 2;
+    // The largest power of two not above that length: rounding up instead left
+    // wide rows (one row of 5120 channels) at 2.5 waves per SIMD and 20% slower.
+    // Below 128 tokens per chunk the per-chunk overhead wins (2K-token rows).
+    int64_t chunk = 128;
+    while (chunk * 2 <= len) chunk *= 2;
     if (chunk > 4096) chunk = 4096;
     ScanPlan p;
     p.chunk_len = chunk;

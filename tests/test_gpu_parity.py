@@ -110,7 +110,7 @@ def scan_case(ssm, inp, **flags):
 SCAN_CASES = [
     # (batch, seqlen, dim, dstate, nheads, dtype, docs)
     (1, 64, 16, 4, 0, "f32", None),
-    (2, 1000, 100, 16, 0, "bf16", 150.0),    # 16 chunks of 64 with a 40-token tail, ragged D
+    (2, 1000, 100, 16, 0, "bf16", 150.0),    # 7 chunks of 128 with a 104-token tail, ragged D
     (2, 777, 64, 8, 0, "bf16", 90.0),
     (1, 500, 70, 4, 0, "f32", 60.0),
     (3, 257, 130, 16, 0, "f32", 40.0),
