@@ -131,13 +131,17 @@ struct SsdLds {
     static constexpr int SY = P / kRowW + 4;       // per-wave fp32 output tile [16][SY]
     static constexpr int kBBytes = kQ * SN * 2;
     static constexpr int kYBytes = OUTPUT ? kWaves * 16 * SY * 4 : 0;
-    static constexpr int oB = 0;                                    // B rows [s][n]; later the output tiles
-    static constexpr int oBw = oB + (kBBytes > kYBytes ? kBBytes : kYBytes);   // dt-weighted B^T [n][s]
-    static constexpr int oXT = oBw + NP * SQ * 2;                   // x^T [p][s]
-    static constexpr int oM = oXT + P * SQ * 2;                     // M [t][s]
+    // B rows, x^T and the per-token scalars are double-buffered by chunk parity:
+    // the next chunk is staged while slower waves still read the current one, so
+    // no barrier is needed between chunks.
+    static constexpr int kBRegion = kBBytes > kYBytes ? kBBytes : kYBytes;
+    static constexpr int oB = 0;                                    // 2 x B rows [s][n]; later the output tiles
+    static constexpr int oBw = oB + 2 * kBRegion;                   // dt-weighted B^T [n][s]
+    static constexpr int oXT = oBw + NP * SQ * 2;                   // 2 x x^T [p][s]
+    static constexpr int oM = oXT + 2 * P * SQ * 2;                 // M [t][s]
     static constexpr int oHT = oM + (OUTPUT ? kQ * SQ * 2 : 0);     // chunk-entry state^T [p][n]
-    static constexpr int oTok = oHT + (OUTPUT ? P * SN * 2 : 0);    // per-token scalars
-    static constexpr int kBytes = oTok + 5 * kQ * 4;
+    static constexpr int oTok = oHT + (OUTPUT ? P * SN * 2 : 0);    // 2 x per-token scalars
+    static constexpr int kBytes = oTok + 2 * 5 * kQ * 4;
 };
 
 template <int NP, int P, bool OUTPUT, bool HAS_Z, bool SOFTPLUS>
@@ -157,23 +161,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
     constexpr int kBwTasks = (kQ / 2) * kVN;               // (token pair, 8 states) tasks
 
     __shared__ __attribute__((aligned(16))) unsigned char lds[Lay::kBytes];
-    uint16_t* sB = reinterpret_cast<uint16_t*>(lds + Lay::oB);
+    uint16_t* sB0 = reinterpret_cast<uint16_t*>(lds + Lay::oB);
     uint16_t* sBw = reinterpret_cast<uint16_t*>(lds + Lay::oBw);
-    uint16_t* sXT = reinterpret_cast<uint16_t*>(lds + Lay::oXT);
+    uint16_t* sXT0 = reinterpret_cast<uint16_t*>(lds + Lay::oXT);
     uint16_t* sM = reinterpret_cast<uint16_t*>(lds + Lay::oM);
     uint16_t* sHT = reinterpret_cast<uint16_t*>(lds + Lay::oHT);
-    float* sDt = reinterpret_cast<float*>(lds + Lay::oTok);
-    float* sCs = sDt + kQ;
-    float* sW = sCs + kQ;
-    float* sScale = sW + kQ;
-    int* sSeg = reinterpret_cast<int*>(sScale + kQ);
+    float* sTok0 = reinterpret_cast<float*>(lds + Lay::oTok);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l16 = lane & 15;
     const int lg = lane >> 4;
-    float* sYw = reinterpret_cast<float*>(lds + Lay::oB) + wave * 16 * SY;   // this wave's output tile
+
 
     // Workgroup -> (row, segment, head); all heads of a (row, segment) share an XCD.
     const int total = p.nbatch * p.nheads * p.nseg;
@@ -276,6 +276,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
     if (t_seg0 < t_seg1) fetch(t_seg0);
     const u32x4_t kZero = {0u, 0u, 0u, 0u};
     for (int64_t t0 = t_seg0; t0 < t_seg1; t0 += kQ) {
+        const int par = static_cast<int>(((t0 - t_seg0) / kQ) & 1);
+        uint16_t* sB = sB0 + par * (Lay::kBRegion / 2);
+        uint16_t* sXT = sXT0 + par * P * SQ;
+        float* sDt = sTok0 + par * 5 * kQ;
+        float* sCs = sDt + kQ;
+        float* sW = sCs + kQ;
+        float* sScale = sW + kQ;
+        int* sSeg = reinterpret_cast<int*>(sScale + kQ);
+        float* sYw = reinterpret_cast<float*>(sB) + wave * 16 * SY;   // this wave's output tile (over B rows)
         // ---- 1. take the prefetched chunk: B rows to LDS, x transposed to LDS,
         //         per-token scalars, this wave's C fragments, the gate
 #pragma unroll
@@ -467,7 +476,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
                 *reinterpret_cast<u32x4_t*>(p.out + off) = u32x4_t{o[0], o[1], o[2], o[3]};
             }
         }
-        lds_barrier();            // the next chunk overwrites every LDS tile
     }
 
 #pragma unroll
