@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the Mamba selective-scan forward path.
+"""fp64 CPU oracle for the Mamba selective-scan forward path (and its gradients).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package; the library and its
@@ -18,3 +18,4 @@ from .mamba_oracle import (  # noqa: F401
     softplus,
     ssd_matrix_scan,
 )
+from .mamba_grad import selective_scan_bwd  # noqa: F401

@@ -1,0 +1,100 @@
+"""Plain fp64 gradients of the selective scan (reverse mode of the sequential
+recurrence).
+
+TEST INFRASTRUCTURE ONLY, like the rest of `oracle/`: the library never imports
+it.  The forward is the one of `mamba_oracle.selective_scan` ("Mamba & State
+Space Models (SSMs)" skill page: the S6 block diagram and code, "Core Concept"
+for the D term; axolotl "FLA Mamba and Mamba2": per-document restart); the
+gradients are that forward's adjoint, written step by step backwards in time.
+Per channel d and state n, with a_t = exp(dt_t A[n]) (0 at a document start),
+h_t = a_t h_{t-1} + dt_t u_t B_t[n], y_t = C_t . h_t + D u_t, out_t = y_t silu(z_t):
+
+    dy_t    = dout_t silu(z_t),        dz_t = dout_t y_t silu'(z_t)
+    g_t     = dL/dh_t = C_t dy_t + a_{t+1} g_{t+1}          (g_L = 0)
+    dC_t   += dy_t h_t                (summed over channels)
+    dB_t   += g_t dt_t u_t            (summed over channels)
+    du_t    = dy_t D + sum_n g_t[n] dt_t B_t[n]
+    ddt_t   = sum_n g_t[n] (u_t B_t[n] + A[n] a_t[n] h_{t-1}[n])   (second term 0 at a start)
+    dA[n]  += g_t[n] dt_t a_t[n] h_{t-1}[n]
+    dD     += dy_t u_t
+    ddelta_t = ddt_t softplus'(delta_t + bias) = ddt_t sigmoid(delta_t + bias)
+    dbias  += ddelta_t
+
+Pinned by central finite differences of `selective_scan` (tests/test_oracle_pins.py).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .mamba_oracle import _f64, doc_segment_start, sigmoid, silu
+
+
+def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
+                       doc_start=None):
+    """Gradients of sum(dout * out) for the per-channel-A selective scan (A of shape
+    (D, N), no initial state).  Returns a dict with du, ddelta, dA, dB, dC and,
+    when the input is given, dD, dz, ddelta_bias (all float64)."""
+    u = _f64(u)
+    dl = _f64(delta)
+    Am = _f64(A)
+    Bm = _f64(B)
+    Cm = _f64(C)
+    go = _f64(dout)
+    Bt, L, Dm = u.shape
+    N = Bm.shape[-1]
+    bias = np.zeros(Dm) if delta_bias is None else _f64(delta_bias)
+    pre = dl + bias[None, None, :]
+    dt = np.log1p(np.exp(-np.abs(pre))) + np.maximum(pre, 0.0) if delta_softplus else pre
+    Dv = np.zeros(Dm) if D is None else _f64(D)
+    zz = None if z is None else _f64(z)
+    starts = doc_segment_start(doc_start, Bt, L, first_is_start=True) == np.arange(L)[None, :]
+
+    # Forward, keeping every state and decay (the oracle can afford it).
+    a = np.empty((Bt, L, Dm, N))
+    h = np.empty((Bt, L, Dm, N))
+    hprev = np.zeros((Bt, Dm, N))
+    for t in range(L):
+        at = np.exp(dt[:, t, :, None] * Am[None, :, :])
+        at[starts[:, t]] = 0.0
+        a[:, t] = at
+        hprev = at * hprev + (dt[:, t, :] * u[:, t, :])[:, :, None] * Bm[:, t, None, :]
+        h[:, t] = hprev
+    y = np.einsum("bldn,bln->bld", h, Cm) + Dv[None, None, :] * u
+
+    if zz is not None:
+        sg = sigmoid(zz)
+        dy = go * silu(zz)
+        dz = go * y * sg * (1.0 + zz * (1.0 - sg))
+    else:
+        dy = go
+        dz = None
+
+    du = dy * Dv[None, None, :]
+    ddt = np.zeros((Bt, L, Dm))
+    dA = np.zeros((Dm, N))
+    dB = np.zeros((Bt, L, N))
+    dC = np.einsum("bld,bldn->bln", dy, h)
+    g = np.zeros((Bt, Dm, N))
+    for t in range(L - 1, -1, -1):
+        if t + 1 < L:
+            g = a[:, t + 1] * g
+        else:
+            g = np.zeros((Bt, Dm, N))
+        g = g + Cm[:, t, None, :] * dy[:, t, :, None]
+        h_before = h[:, t - 1] if t > 0 else np.zeros((Bt, Dm, N))
+        q = a[:, t] * h_before                                     # 0 at a start
+        dB[:, t] = np.einsum("bdn,bd->bn", g, dt[:, t] * u[:, t])
+        du[:, t] += np.einsum("bdn,bn->bd", g, Bm[:, t]) * dt[:, t]
+        ddt[:, t] = np.einsum("bdn,bn->bd", g, Bm[:, t]) * u[:, t] + np.einsum("bdn,dn->bd", g * q, Am)
+        dA += np.einsum("bdn,bd->dn", g * q, dt[:, t])
+
+    ddelta = ddt * sigmoid(pre) if delta_softplus else ddt
+    grads = {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC}
+    if D is not None:
+        grads["dD"] = np.einsum("bld,bld->d", dy, u)
+    if zz is not None:
+        grads["dz"] = dz
+    if delta_bias is not None:
+        grads["ddelta_bias"] = ddelta.sum(axis=(0, 1))
+    return grads

@@ -361,3 +361,58 @@ def test_pack_documents_geometric_mean():
     assert np.all(flags[:, 0] == 1)
     lengths = np.diff(np.flatnonzero(flags[0]))
     assert abs(lengths.mean() - 2048) < 0.15 * 2048
+
+
+# ----------------------------------------------------------------------------
+# Gradients: central finite differences of the forward oracle
+# ----------------------------------------------------------------------------
+def _grad_case(seed, softplus=True, with_z=True, with_D=True, with_bias=True):
+    rng = np.random.default_rng(seed)
+    Bt, L, Dm, N = 2, 11, 3, 4
+    u = rng.normal(size=(Bt, L, Dm))
+    delta = rng.normal(0.0, 0.5, size=(Bt, L, Dm)) + (0.0 if softplus else 1.0)
+    A = -np.exp(rng.normal(size=(Dm, N)))
+    B = rng.normal(size=(Bt, L, N))
+    C = rng.normal(size=(Bt, L, N))
+    D = rng.normal(size=Dm) if with_D else None
+    z = rng.normal(size=(Bt, L, Dm)) if with_z else None
+    bias = rng.normal(0.0, 0.3, size=Dm) if with_bias else None
+    ds = np.zeros((Bt, L), dtype=np.uint8)
+    ds[0, 4] = 1
+    ds[1, 1] = 1
+    ds[1, 7] = 1
+    dout = rng.normal(size=(Bt, L, Dm))
+    return dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, delta_bias=bias, delta_softplus=softplus,
+                doc_start=ds), dout
+
+
+def _loss(args, dout):
+    out, _ = oracle.selective_scan(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"],
+                                   args["z"], args["delta_bias"], args["delta_softplus"], args["doc_start"])
+    return float(np.sum(out * dout))
+
+
+@pytest.mark.parametrize("flags", [dict(), dict(softplus=False), dict(with_z=False, with_D=False, with_bias=False)],
+                         ids=str)
+def test_gradients_match_finite_differences(flags):
+    args, dout = _grad_case(11, **flags)
+    g = oracle.selective_scan_bwd(args["u"], args["delta"], args["A"], args["B"], args["C"], dout, args["D"],
+                                  args["z"], args["delta_bias"], args["delta_softplus"], args["doc_start"])
+    names = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+             "delta_bias": "ddelta_bias"}
+    eps = 1e-6
+    for arg, gname in names.items():
+        if args[arg] is None:
+            assert gname not in g
+            continue
+        x = args[arg]
+        for flat in range(x.size):
+            orig = x.flat[flat]
+            x.flat[flat] = orig + eps
+            lp = _loss(args, dout)
+            x.flat[flat] = orig - eps
+            lm = _loss(args, dout)
+            x.flat[flat] = orig
+            fd = (lp - lm) / (2 * eps)
+            an = g[gname].flat[flat]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (arg, flat, fd, an)
