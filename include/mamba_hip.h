@@ -1,7 +1,8 @@
 /*
- * mamba_hip.h -- C ABI of the MI355X (gfx950) Mamba selective-scan forward path.
+ * mamba_hip.h -- C ABI of the MI355X (gfx950) Mamba selective-scan path.
  *
- * Two operations, each one or more HIP kernel launches on the caller's stream:
+ * The two operations of the forward path, each one or more HIP kernel launches on
+ * the caller's stream:
  *
  *   mamba_causal_conv1d_fwd   depthwise causal conv1d (width 4) + optional SiLU.
  *       Defined by the "Mamba: Selective State Spaces (S6)" section of the Mamba
@@ -17,6 +18,10 @@
  *       (y = C h + D x), the S6 code (dt = softplus(dt), y * silu(z)), the
  *       "Mamba-2 (SSD)" section (scalar A per head, multi-head, headdim), and the
  *       packing paragraph (recurrent state restarts at every document start).
+ *
+ * Further entry points: the two in one call (mamba_conv_scan_fwd), one-token
+ * decode steps, and the backward pass of the per-channel scan
+ * (mamba_selective_scan_bwd), each described at its declaration below.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -168,6 +173,46 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
                         const void* z, const float* delta_bias, const uint8_t* doc_start,
                         const float* initial_state, void* u, void* out, float* final_state,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Backward pass (training) of the per-channel scan: the gradients of
+ * sum(dout * out) through mamba_selective_scan_fwd, i.e. the adjoint of the
+ * recurrence run from the row end back to token 0.  Defined by the same pages
+ * as the forward; the states are recomputed rather than stored (Mamba skill
+ * page, "Hardware-Aware Parallel Scan": recomputation in the backward pass).
+ * With a_t = exp(dt_t A) (0 at a document start), h_t the forward state and
+ * dy_t = dout_t silu(z_t), the adjoint g_t = C_t dy_t + a_{t+1} g_{t+1} gives
+ *   du_t = D dy_t + dt_t (g_t . B_t)
+ *   ddelta_t = [u_t (g_t . B_t) + sum_n A g_t a_t h_{t-1}] * sigmoid(delta_t + delta_bias)
+ *   dB_t = sum_d g_t dt_t u_t,  dC_t = sum_d dy_t h_t,  dA = sum_t dt_t g_t a_t h_{t-1}
+ *   dD = sum_t dy_t u_t,  dz_t = dout_t y_t silu'(z_t),  ddelta_bias = sum_t ddelta_t. */
+
+/* Bytes of device workspace mamba_selective_scan_bwd needs for `dims` (about
+ * B L D N * 4 / 16 + B L D * (elem size) + B L * ceil(D / 256) * 8 N bytes; 780 MB
+ * at B = 2, L = 32768, D = 1536, N = 16, bf16). */
+int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes);
+
+/* Selective scan backward.
+ *   dims, u, delta, A, B, C, D, z, delta_bias, doc_start: as the forward call
+ *              whose gradients are wanted (no initial state).
+ *   dout       (B, L, D)  gradient of the loss with respect to out.
+ *   du, ddelta (B, L, D)  written, dtype `dtype`.
+ *   dA         (D, N) float32, written.
+ *   dB, dC     (B, L, N)  written, dtype `dtype`.
+ *   dD         (D,) float32 or NULL (not computed).  Computed also when D is NULL
+ *              (the gradient at D = 0).
+ *   dz         (B, L, D); must be non-NULL exactly when z is.
+ *   ddelta_bias (D,) float32 or NULL (not computed).
+ *   workspace  at least mamba_selective_scan_bwd_workspace_bytes bytes, 256-byte
+ *              aligned, scratch (contents on entry ignored).
+ * Supported: nheads == 0, N in {4, 8, 16}, and what the forward requires; others
+ * return MAMBA_ERR_UNSUPPORTED.  Outputs must not overlap each other, the inputs
+ * or the workspace.  The sums over channels, tokens and rows run in a fixed
+ * order: repeated calls give bitwise identical results. */
+int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, const uint8_t* doc_start, const void* dout,
+                             void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                             float* ddelta_bias, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- One-token decode (Mamba skill page, "Dual Computation Modes": the
  * recurrent mode used for generation).  A prefill with mamba_causal_conv1d_fwd

@@ -8,6 +8,9 @@ missing or the tensors are not on a GPU the calls raise.
     u = causal_conv1d_fwd(x, weight, bias, doc_start)                  # (B, L, D)
     out, h = selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, doc_start)
 
+    # gradients of sum(dout * out) for per-channel A (training)
+    g = selective_scan_bwd(u, delta, A, B, C, dout, D, z, delta_bias, doc_start)
+
     # decode, one token per row, continuing the prefill above
     u_t = causal_conv1d_update(x_t, conv_state, weight, bias)          # (B, D)
     out_t = selective_state_update(h, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias)
@@ -28,6 +31,8 @@ __all__ = [
     "conv_scan_fwd",
     "causal_conv1d_update",
     "selective_state_update",
+    "selective_scan_bwd",
+    "scan_bwd_workspace_bytes",
     "MambaError",
     "MambaArgumentError",
     "library_path",
@@ -303,3 +308,67 @@ def selective_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=
         _ptr(out, "out", dev, u.dtype, (Bt, Dm)), _stream(dev))
     _lib.check(st, "mamba_selective_state_update")
     return out
+
+
+def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16") -> int:
+    code = _lib.MAMBA_DTYPE_BF16 if dtype == "bf16" else _lib.MAMBA_DTYPE_F32
+    dims = _scan_dims(batch, seqlen, dim, dstate, 0, code, True)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)),
+               "mamba_selective_scan_bwd_workspace_bytes")
+    return int(n.value)
+
+
+def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, doc_start=None,
+                       delta_softplus: bool = True, workspace=None, grads=None):
+    """Gradients of sum(dout * out) for the per-channel-A scan (A of shape (D, N));
+    see mamba_selective_scan_bwd.  Arguments as selective_scan_fwd plus ``dout``
+    (B, L, D).  Returns a dict with du, ddelta, dB, dC (u's dtype), dA (D, N)
+    float32 and, for each optional input given, dD, dz, ddelta_bias.  ``grads``:
+    optional dict of preallocated outputs with the same keys."""
+    torch = _torch()
+    dev = _check_device(u)
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be (B, L, D) and A (D, N)")
+    Bt, L, Dm = u.shape
+    N = A.shape[1]
+    code = _dtype_code(u)
+    if doc_start is not None and doc_start.dtype == torch.bool:
+        doc_start = doc_start.to(torch.uint8)
+    g = dict(grads) if grads else {}
+    f32 = torch.float32
+    shapes = {"du": ((Bt, L, Dm), u.dtype), "ddelta": ((Bt, L, Dm), u.dtype), "dA": ((Dm, N), f32),
+              "dB": ((Bt, L, N), u.dtype), "dC": ((Bt, L, N), u.dtype)}
+    if D is not None:
+        shapes["dD"] = ((Dm,), f32)
+    if z is not None:
+        shapes["dz"] = ((Bt, L, Dm), u.dtype)
+    if delta_bias is not None:
+        shapes["ddelta_bias"] = ((Dm,), f32)
+    for k, (shape, dt) in shapes.items():
+        if k not in g:
+            g[k] = torch.empty(shape, dtype=dt, device=dev)
+    dims = _scan_dims(Bt, L, Dm, N, 0, code, delta_softplus)
+    lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(need)),
+               "mamba_selective_scan_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=dev)
+    out = lambda k: _ptr(g.get(k), k, dev, shapes[k][1], shapes[k][0]) if k in shapes else None  # noqa: E731
+    st = lib.mamba_selective_scan_bwd(
+        ctypes.byref(dims),
+        _ptr(u, "u", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(delta, "delta", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(A, "A", dev, f32, (Dm, N)),
+        _ptr(B, "B", dev, u.dtype, (Bt, L, N)),
+        _ptr(C, "C", dev, u.dtype, (Bt, L, N)),
+        _ptr(D, "D", dev, f32, (Dm,)),
+        _ptr(z, "z", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(delta_bias, "delta_bias", dev, f32, (Dm,)),
+        _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(dout, "dout", dev, u.dtype, (Bt, L, Dm)),
+        out("du"), out("ddelta"), out("dA"), out("dB"), out("dC"), out("dD"), out("dz"), out("ddelta_bias"),
+        _ptr(workspace, "workspace", dev, torch.uint8), workspace.numel(), _stream(dev))
+    _lib.check(st, "mamba_selective_scan_bwd")
+    return {k: g[k] for k in shapes}

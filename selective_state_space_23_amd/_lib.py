@@ -27,6 +27,8 @@ EXPORTED = (
     "mamba_conv_scan_fwd",
     "mamba_causal_conv1d_update",
     "mamba_selective_state_update",
+    "mamba_selective_scan_bwd_workspace_bytes",
+    "mamba_selective_scan_bwd",
 )
 
 
@@ -89,6 +91,10 @@ def load() -> ctypes.CDLL:
     lib.mamba_selective_state_update.argtypes = [ctypes.POINTER(ScanDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  vp, vp]
     lib.mamba_selective_state_update.restype = ctypes.c_int
+    lib.mamba_selective_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(sz)]
+    lib.mamba_selective_scan_bwd_workspace_bytes.restype = ctypes.c_int
+    lib.mamba_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanDims)] + [vp] * 19 + [sz, vp]
+    lib.mamba_selective_scan_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 

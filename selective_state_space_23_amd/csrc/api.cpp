@@ -256,6 +256,72 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
     return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes) {
+    if (!bytes) return MAMBA_ERR_INVALID_ARGUMENT;
+    *bytes = 0;
+    const int st = check_dims(dims);
+    if (st != MAMBA_OK) return st;
+    if (!mamba::scan_bwd_supported(dims->dstate, dims->nheads)) return MAMBA_ERR_UNSUPPORTED;
+    *bytes = mamba::scan_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->dim, dims->dstate,
+                                             dims->dtype == MAMBA_DTYPE_BF16);
+    return MAMBA_OK;
+}
+
+int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+                             const uint8_t* doc_start, const void* dout, void* du, void* ddelta, float* dA, void* dB,
+                             void* dC, float* dD, void* dz, float* ddelta_bias, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    const int st = check_dims(dims);
+    if (st != MAMBA_OK) return st;
+    if (!mamba::scan_bwd_supported(dims->dstate, dims->nheads)) return MAMBA_ERR_UNSUPPORTED;
+    const int64_t Bt = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
+    if ((z == nullptr) != (dz == nullptr)) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (Bt * L * Dm == 0) return MAMBA_OK;
+    if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
+        return MAMBA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+    const void* acts[] = {u, delta, z, dout, du, ddelta, dz};
+    for (const void* t : acts)
+        if (t && !aligned(t, esz)) return MAMBA_ERR_MISALIGNED;
+    if (!aligned(B, 4) || !aligned(C, 4) || !aligned(dB, esz) || !aligned(dC, esz) || (N * esz) % 4 != 0)
+        return MAMBA_ERR_MISALIGNED;
+    const float* f32s[] = {A, D, delta_bias, dA, dD, ddelta_bias};
+    for (const float* t : f32s)
+        if (t && !aligned(t, 4)) return MAMBA_ERR_MISALIGNED;
+
+    const size_t act = static_cast<size_t>(Bt * L * Dm) * esz;
+    const size_t bc = static_cast<size_t>(Bt * L * N) * esz;
+    const size_t dn = static_cast<size_t>(Dm * N) * 4, d1 = static_cast<size_t>(Dm) * 4;
+    const void* ins[] = {u, delta, A, B, C, D, z, delta_bias, doc_start, dout};
+    const size_t insz[] = {act, act, dn, bc, bc, d1, act, d1, static_cast<size_t>(Bt * L), act};
+    const void* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias};
+    const size_t outsz[] = {act, act, dn, bc, bc, d1, act, d1};
+    const size_t need = mamba::scan_bwd_workspace_bytes(Bt, L, Dm, N, dims->dtype == MAMBA_DTYPE_BF16);
+    if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;
+    for (int o = 0; o < 8; ++o) {
+        for (int i = 0; i < 10; ++i)
+            if (overlap(outs[o], outsz[o], ins[i], insz[i])) return MAMBA_ERR_INVALID_ARGUMENT;
+        for (int k = o + 1; k < 8; ++k)
+            if (overlap(outs[o], outsz[o], outs[k], outsz[k])) return MAMBA_ERR_INVALID_ARGUMENT;
+        if (overlap(outs[o], outsz[o], workspace, need)) return MAMBA_ERR_INVALID_ARGUMENT;
+    }
+    for (int i = 0; i < 10; ++i)
+        if (overlap(ins[i], insz[i], workspace, need)) return MAMBA_ERR_INVALID_ARGUMENT;
+
+    mamba::ScanBwdArgs a;
+    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.delta_bias = delta_bias;
+    a.doc_start = doc_start; a.dout = dout;
+    a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dz = dz; a.ddelta_bias = ddelta_bias;
+    a.ws = workspace;
+    a.batch = Bt; a.seqlen = L; a.dim = Dm; a.dstate = N;
+    a.bf16 = dims->dtype == MAMBA_DTYPE_BF16;
+    a.softplus = dims->delta_softplus != 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    return mamba::launch_selective_scan_bwd(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
 int mamba_causal_conv1d_update(const void* x, void* conv_state, const float* weight, const float* bias,
                                const uint8_t* reset, void* out, int64_t batch, int64_t dim, int32_t width,
                                int32_t dtype, int32_t apply_silu, void* stream) {

@@ -61,6 +61,42 @@ size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
 bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16);
 hipError_t launch_selective_scan(const ScanArgs& a);
 
+// Passes 1 and 2 of the per-channel scan into the given buffers (each
+// (nchunks - 1) * B * D * N floats, dt_ws B * L * D floats): ws_P[c] then holds
+// the state entering chunk c + 1.  Used by the backward pass; no initial state.
+hipError_t launch_scan_chunk_carries(const ScanArgs& a, const ScanPlan& plan, float* ws_P, float* ws_H, void* dt_ws);
+
+// Backward of the per-channel scan (scan_bwd.hip).
+struct ScanBwdArgs {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* delta_bias;
+    const uint8_t* doc_start;
+    const void* dout;
+    void* du;
+    void* ddelta;
+    float* dA;
+    void* dB;
+    void* dC;
+    float* dD;            // or null
+    void* dz;             // null iff z is null
+    float* ddelta_bias;   // or null
+    void* ws;
+    int64_t batch, seqlen, dim, dstate;
+    bool bf16;
+    bool softplus;
+    hipStream_t stream;
+};
+
+bool scan_bwd_supported(int64_t dstate, int nheads);
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool bf16);
+hipError_t launch_selective_scan_bwd(const ScanBwdArgs& a);
+
 // One-token decode steps (decode.hip).
 struct ConvUpdateArgs {
     const void* x;          // (B, D)

@@ -1,0 +1,744 @@
+// Selective-scan backward pass for per-channel A (D, N), gfx950.
+//
+// What it computes: the gradients of sum(dout * out) through the forward of
+// scan.hip (Mamba skill page: S6 block diagram and code, "Core Concept" for the
+// D term; axolotl page: per-document restart), i.e. the adjoint of the
+// recurrence run backwards in time.  Per channel d and state n, with
+// a_t = exp(dt_t A[n]) (0 at a document start) and h_t the forward state:
+//   dy_t   = dout_t silu(z_t),   dz_t = dout_t y_t silu'(z_t)
+//   g_t    = C_t dy_t + a_{t+1} g_{t+1}           (adjoint of h_t; zero past the row end)
+//   dC_t  += dy_t h_t,  dB_t += g_t dt_t u_t      (sums over channels)
+//   du_t   = D dy_t + dt_t sum_n g_t B_t
+//   ddt_t  = u_t sum_n g_t B_t + sum_n A g_t a_t h_{t-1}
+//   dA    += dt_t g_t a_t h_{t-1},  dD += dy_t u_t
+//   ddelta_t = ddt_t sigmoid(delta_t + delta_bias) (softplus) or ddt_t,  ddelta_bias += ddelta_t
+// The states are recomputed, never stored per token ("Hardware-Aware Parallel
+// Scan": recomputation in the backward pass instead of keeping the (B, L, D, N)
+// trajectory).
+//
+// Parallel structure, on the forward's chunking of L:
+//   1. forward passes 1-2 (scan.hip): the state entering every chunk, and dt
+//      (float32: the step sizes are not rounded to the I/O dtype here, since
+//      the token sums dA, dD and ddelta_bias cancel and would show that rounding);
+//   2. reverse aggregate: every chunk but the first runs the adjoint recurrence
+//      backwards from zero and stores X_c = a_{t0} g_{t0} and P_c = prod of a
+//      over the chunk (0 if a document starts in it);
+//   3. reverse carry: G_c = X_{c+1} + P_{c+1} G_{c+1}, the adjoint flowing into
+//      the last token of chunk c from the right (the same associative operator
+//      as the forward carry, run from the row end);
+//   4. main pass, per chunk: one forward sweep from the chunk's state stores the
+//      state before every 16-token block (global checkpoints); then the blocks
+//      are walked last to first: recompute the block from its checkpoint keeping
+//      the state every 4 tokens, and for each 4-token piece (last first)
+//      recompute its four states and run the adjoint over them;
+//   5. fixed-order reduction of the per-block partial sums (dB, dC) and of the
+//      per-chunk partial sums (dA, dD, ddelta_bias): results are deterministic.
+//
+// Mapping: as in the forward, lanes are channels and keep their N states and
+// adjoints in VGPRs, B_t and C_t are staged in LDS per 64-token window, so du,
+// ddt and dA are per-lane sums.  dB_t and dC_t are sums over channels: each
+// wave transposes its 2N per-lane values of a token through LDS and sums
+// columns, the 4 waves' sums meet in LDS, and each block writes one partial per
+// token.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mamba {
+
+namespace {
+
+constexpr int kBlk = 256;              // 4 waves, 256 consecutive channels
+constexpr int kWaves = kBlk / 64;
+constexpr int kWin = 64;               // tokens per staged B/C window
+constexpr int kCk = 16;                // tokens per checkpoint block
+constexpr int kPiece = 4;              // tokens per innermost recompute piece
+#ifndef MAMBA_BWD_WAVES_PER_EU
+#define MAMBA_BWD_WAVES_PER_EU 2
+#endif
+
+struct BwdKParams {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* delta_bias;
+    const uint8_t* doc_start;
+    const void* dout;
+    const float* dt;         // (B, L, D) float32: step sizes from forward pass 1
+    const float* h_carry;    // [nslots][B][D][N]: state entering chunk s + 1
+    float* g_carry;          // [nslots][B][D][N]: X_{s+1}, then G_s
+    float* p_rev;            // [nslots][B][D][N]: P_{s+1}
+    float* ckpt;             // [B][nk][N][D]: state before token 16 k
+    float* part_bc;          // [B][L][nblk][2N]: per-block sums of dB_t, dC_t
+    float* part_w;           // [B][nchunks][N + 2][D]: per-chunk sums of dA, dD, ddelta_bias
+    void* du;
+    void* ddelta;
+    void* dz;
+    int64_t seqlen;
+    int64_t chunk_len;
+    int64_t nchunks;
+    int64_t nslots;
+    int64_t nk;
+    int dim;
+    int nbatch;
+    int nblk;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    constexpr int kRsrcWord3 = 0x00020000;        // gfx9 data format: 32-bit, raw access
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+template <typename T>
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+    if constexpr (sizeof(T) == 2) {
+        const uint16_t v = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, byte_off, 0, 0));
+        return bf16_to_f32(v);
+    } else {
+        return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, 0)));
+    }
+}
+
+// Element at byte offset voff + soff (soff wave-uniform).
+template <typename T>
+__device__ __forceinline__ float buf_load_s(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    if constexpr (sizeof(T) == 2) {
+        const uint16_t v = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0));
+        return bf16_to_f32(v);
+    } else {
+        return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0)));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void buf_store_s(__amdgpu_buffer_rsrc_t rs, int voff, int soff, float v) {
+    if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rs, voff, soff, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, voff, soff, 0);
+}
+
+__device__ __forceinline__ float sigmoid_f(float v) { return rcp_fast(1.0f + exp2_fast(-v * kLog2e)); }
+
+// A copy of v the compiler cannot see through.  The recompute levels evaluate the
+// same expressions on the same inputs; without this the compiler merges them back
+// into one sweep and keeps every intermediate state live (which is exactly what
+// recomputation avoids).
+__device__ __forceinline__ float opaque(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Stage rows w0 .. w0 + 63 of B (and C) into LDS as fp32 (token-major, N floats a
+// token); tokens past t_end are clamped to the last token and never read back.
+template <typename T, int N, int kRows>
+__device__ __forceinline__ void stage_rows(float* smem, const T* B_row, const T* C_row, int64_t w0, int64_t t_end,
+                                           int tid) {
+    constexpr int kWinFloats = kWin * N;
+    for (int i = tid; i < kRows * kWinFloats; i += kBlk) {
+        const int tensor = i / kWinFloats;
+        const int e = i % kWinFloats;
+        const int tok = e / N;
+        const int n = e % N;
+        const int64_t t = (w0 + tok < t_end) ? w0 + tok : t_end - 1;
+        const T* src = (tensor == 0 || kRows == 1 ? B_row : C_row) + t * N + n;
+        float v;
+        if constexpr (sizeof(T) == 2) v = bf16_to_f32(*reinterpret_cast<const uint16_t*>(src));
+        else v = *reinterpret_cast<const float*>(src);
+        smem[i] = v;
+    }
+}
+
+// Wave-uniform bit mask of the document starts among tokens w0 .. w0 + 63.
+__device__ __forceinline__ uint64_t window_starts(const uint8_t* ds_row, int64_t w0, int64_t t_end, int lane) {
+    const int64_t tl = w0 + lane;
+    bool st = false;
+    if (tl < t_end) st = tl == 0 || (ds_row != nullptr && ds_row[tl] != 0);
+    return __ballot(st);
+}
+
+// ---------------------------------------------------------------------------
+// 2. Reverse aggregate of chunk c = blockIdx.y + 1 (chunk 0 needs none).
+template <typename T, int N, bool HAS_Z>
+__global__ __launch_bounds__(kBlk) void bwd_rev_aggregate_kernel(const BwdKParams p) {
+    __shared__ float4 sC4[kWin * N / 4];
+    float* sC = reinterpret_cast<float*>(sC4);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int d = blockIdx.x * kBlk + tid;
+    const bool active = d < p.dim;
+    const int dc = active ? d : p.dim - 1;
+    const int64_t c = static_cast<int64_t>(blockIdx.y) + 1;
+    const int64_t b = blockIdx.z;
+    const int64_t L = p.seqlen;
+    const int64_t t_begin = c * p.chunk_len;
+    const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
+    constexpr int kEsz = static_cast<int>(sizeof(T));
+    const int64_t act_row = L * p.dim;
+    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(p.dt + b * act_row, act_row * 4);
+    const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, act_row * kEsz);
+    const __amdgpu_buffer_rsrc_t z_rs =
+        make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, act_row * kEsz);
+    const T* C_row = static_cast<const T*>(p.C) + b * L * N;
+    const uint8_t* ds_row = p.doc_start ? p.doc_start + b * L : nullptr;
+
+    float Al2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Al2[n] = p.A[static_cast<int64_t>(dc) * N + n] * kLog2e;
+    float gn[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) gn[n] = 0.0f;
+    float sum_dt = 0.0f;
+    bool any_reset = false;
+
+    const int64_t nwin = (t_end - t_begin + kWin - 1) / kWin;
+    for (int64_t wi = nwin - 1; wi >= 0; --wi) {
+        const int64_t w0 = t_begin + wi * kWin;
+        const uint64_t starts = window_starts(ds_row, w0, t_end, lane);
+        any_reset = any_reset || starts != 0;
+        __syncthreads();
+        stage_rows<T, N, 1>(sC, C_row, C_row, w0, t_end, tid);
+        __syncthreads();
+        const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
+        for (int64_t g0 = wend - kPiece; g0 > w0 - kPiece; g0 -= kPiece) {
+            // tokens g0 .. g0 + 3, the ones below w0 are skipped (g0 < w0 only on a ragged window)
+            float dtv[kPiece], dyv[kPiece];
+#pragma unroll
+            for (int k = 0; k < kPiece; ++k) {
+                const int64_t t = g0 + k >= w0 ? g0 + k : w0;
+                const int off = static_cast<int>((t * p.dim + dc) * kEsz);
+                dtv[k] = buf_load<float>(dt_rs, static_cast<int>((t * p.dim + dc) * 4));
+                float dy = buf_load<T>(do_rs, off);
+                if constexpr (HAS_Z) dy *= silu_f(buf_load<T>(z_rs, off));
+                dyv[k] = dy;
+            }
+#pragma unroll
+            for (int k = kPiece - 1; k >= 0; --k) {
+                const int64_t t = g0 + k;
+                if (t < w0) continue;                     // wave-uniform
+                const int o = static_cast<int>(t - w0);
+                const float r = ((starts >> o) & 1ull) ? -__builtin_inff() : 0.0f;
+                const float dt = dtv[k];
+                sum_dt += dt;
+                const float4* Cq = reinterpret_cast<const float4*>(sC + o * N);
+#pragma unroll
+                for (int q = 0; q < N / 4; ++q) {
+                    const float4 cv = Cq[q];
+                    const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int n = 4 * q + j;
+                        const float g = __builtin_fmaf(cc[j], dyv[k], gn[n]);
+                        gn[n] = exp2_fast(__builtin_fmaf(dt, Al2[n], r)) * g;
+                    }
+                }
+            }
+        }
+    }
+    if (!active) return;
+    const int64_t count = static_cast<int64_t>(p.nbatch) * p.dim * N;
+    const int64_t slot = (c - 1) * count + (b * p.dim + dc) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        p.g_carry[slot + n] = gn[n];
+        p.p_rev[slot + n] = any_reset ? 0.0f : exp2_fast(sum_dt * Al2[n]);
+    }
+}
+
+// 3. Reverse carry: slot s turns from X_{s+1} into G_s = X_{s+1} + P_{s+1} G_{s+1}
+// (G_{nchunks-1} = 0: no gradient flows in from past the row end).
+__global__ __launch_bounds__(256) void bwd_rev_carry_kernel(float* __restrict__ g_carry,
+                                                            const float* __restrict__ p_rev, int64_t count,
+                                                            int64_t nslots) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= count) return;
+    float G = 0.0f;
+    int64_t s = nslots - 1;
+    for (; s >= 3; s -= 4) {
+        float X[4], P[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            X[k] = g_carry[(s - k) * count + i];
+            P[k] = p_rev[(s - k) * count + i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            G = __builtin_fmaf(P[k], G, X[k]);
+            g_carry[(s - k) * count + i] = G;
+        }
+    }
+    for (; s >= 0; --s) {
+        G = __builtin_fmaf(p_rev[s * count + i], G, g_carry[s * count + i]);
+        g_carry[s * count + i] = G;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. Main pass over chunk blockIdx.y of row blockIdx.z.
+template <typename T, int N, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_WAVES_PER_EU))) void bwd_chunk_kernel(
+    const BwdKParams p) {
+    constexpr int V = 2 * N;               // dB_t and dC_t values of one lane
+    constexpr int kTS = V + 4;             // transposition row stride (16-byte aligned rows)
+    constexpr int kWinFloats = kWin * N;
+    constexpr bool kKeepDecay = N <= 8;
+    __shared__ float4 sBC4[2 * kWinFloats / 4];          // B then C of the window
+    __shared__ float4 sT4[kWaves * 64 * kTS / 4];        // per-wave transposition
+    __shared__ float sP[kWaves * kWin * V];              // per-wave column sums of the window
+    float* sBC = reinterpret_cast<float*>(sBC4);
+    float* sT = reinterpret_cast<float*>(sT4);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int d = blockIdx.x * kBlk + tid;
+    const bool active = d < p.dim;
+    const int dc = active ? d : p.dim - 1;
+    const int64_t c = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int64_t L = p.seqlen;
+    const int64_t t_begin = c * p.chunk_len;
+    const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
+
+    constexpr int kEsz = static_cast<int>(sizeof(T));
+    const int64_t act_row = L * p.dim;
+    const int64_t rb = act_row * kEsz;
+    const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(static_cast<const T*>(p.u) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(p.dt + b * act_row, act_row * 4);
+    const __amdgpu_buffer_rsrc_t dl_rs = make_rsrc(static_cast<const T*>(p.delta) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t du_rs = make_rsrc(static_cast<T*>(p.du) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t dd_rs = make_rsrc(static_cast<T*>(p.ddelta) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t dz_rs = make_rsrc(static_cast<T*>(HAS_Z ? p.dz : p.du) + b * act_row, rb);
+    const T* B_row = static_cast<const T*>(p.B) + b * L * N;
+    const T* C_row = static_cast<const T*>(p.C) + b * L * N;
+    const uint8_t* ds_row = p.doc_start ? p.doc_start + b * L : nullptr;
+
+    float Al2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Al2[n] = p.A[static_cast<int64_t>(dc) * N + n] * kLog2e;
+    const float dbias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
+    const float Dd = p.D ? p.D[dc] : 0.0f;
+    const int64_t count = static_cast<int64_t>(p.nbatch) * p.dim * N;
+    const int64_t my_slot = (b * p.dim + dc) * N;
+    // Checkpoint k, state n of this lane: ck_lane[(k * N + n) * dim].
+    float* ck_lane = p.ckpt + b * p.nk * N * p.dim + dc;
+
+    // Element offsets: a lane-constant byte offset plus a wave-uniform one per
+    // token (the buffer instruction's scalar offset), so per-token addresses cost
+    // no VGPRs.
+    const int lane_off = dc * kEsz;
+    const int row_bytes = p.dim * kEsz;
+    auto tok_soff = [&](int64_t t) -> int {          // clamped to the chunk's last token
+        return static_cast<int>((t < t_end ? t : t_end - 1) * row_bytes);
+    };
+
+    uint64_t starts = 0;
+    // One forward step of the token at window offset o: h <- exp(dt A) h + w B_t.
+    auto fstep = [&](float (&h)[N], float dt, float w, int o) {
+        const float r = ((starts >> o) & 1ull) ? -__builtin_inff() : 0.0f;
+        const float4* Bq = reinterpret_cast<const float4*>(sBC + o * N);
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q) {
+            const float4 bv = Bq[q];
+            const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = 4 * q + j;
+                h[n] = __builtin_fmaf(exp2_fast(__builtin_fmaf(dt, Al2[n], r)), h[n], w * bb[j]);
+            }
+        }
+        // Keep the scheduler from hoisting later tokens' LDS reads and
+        // exponentials: each token already offers N independent chains.
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // dt and u of token t: dt = 0 past the chunk end (an identity step), u = 0 on
+    // an inactive lane (its dB contributions vanish).  The values pass through
+    // opaque() so that each recompute level evaluates its own exponentials.
+    auto load_dtu = [&](int64_t t, float& dt, float& uu) {
+        const int so = tok_soff(t);
+        dt = buf_load_s<float>(dt_rs, dc * 4, so * (4 / kEsz));
+        uu = buf_load_s<T>(u_rs, lane_off, so);
+        dt = opaque(t < t_end ? dt : 0.0f);
+        uu = active ? uu : 0.0f;
+    };
+    // h <- the state after tokens t0 .. t0 + 3 (window offsets o0 ..).
+    auto advance4 = [&](float (&h)[N], int64_t t0, int o0) {
+        float dtv[kPiece], uv[kPiece];
+#pragma unroll
+        for (int k = 0; k < kPiece; ++k) load_dtu(t0 + k, dtv[k], uv[k]);
+#pragma unroll
+        for (int k = 0; k < kPiece; ++k) fstep(h, dtv[k], dtv[k] * uv[k], o0 + k);
+    };
+
+    // ---- forward sweep: checkpoint before every 16-token block
+    {
+        float h[N];
+        if (c > 0) {
+            const float* hc = p.h_carry + (c - 1) * count + my_slot;
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = hc[n];
+        } else {
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = 0.0f;
+        }
+        for (int64_t w0 = t_begin; w0 < t_end; w0 += kWin) {
+            starts = window_starts(ds_row, w0, t_end, lane);
+            __syncthreads();
+            stage_rows<T, N, 1>(sBC, B_row, C_row, w0, t_end, tid);
+            __syncthreads();
+            const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
+            for (int64_t s = w0; s < wend; s += kCk) {
+                if (active) {
+                    float* ck = ck_lane + (s / kCk) * N * p.dim;
+#pragma unroll
+                    for (int n = 0; n < N; ++n) ck[static_cast<int64_t>(n) * p.dim] = h[n];
+                }
+                const int os = static_cast<int>(s - w0);
+#pragma unroll
+                for (int k0 = 0; k0 < kCk; k0 += kPiece) advance4(h, s + k0, os + k0);
+            }
+        }
+    }
+
+    // ---- backward over the chunk, last window first
+    float gn[N];          // a_{t+1} g_{t+1}: the adjoint reaching token t from the right
+    if (c + 1 < p.nchunks) {
+        const float* gc = p.g_carry + c * count + my_slot;
+#pragma unroll
+        for (int n = 0; n < N; ++n) gn[n] = gc[n];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) gn[n] = 0.0f;
+    }
+    float dA[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) dA[n] = 0.0f;
+    float dD_acc = 0.0f, db_acc = 0.0f;
+
+    // Sum the 4 waves' column sums of window w0 and store the block's partials.
+    auto flush = [&](int64_t w0) {
+        const int64_t nvalid = (w0 + kWin < t_end) ? kWin : t_end - w0;
+        for (int e = tid; e < kWin * V; e += kBlk) {
+            const int tok = e / V;
+            const int j = e % V;
+            if (tok < nvalid) {
+                float sum = sP[tok * V + j];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) sum += sP[(w * kWin + tok) * V + j];
+                p.part_bc[((b * L + w0 + tok) * p.nblk + blockIdx.x) * V + j] = sum;
+            }
+        }
+    };
+
+    // One 4-token piece starting at s4 (window offset o4) from the state st before
+    // it: recompute the four states, then run the adjoint over them, last first.
+    auto piece = [&](int64_t s4, int o4, const float (&st)[N]) {
+        float dtv[kPiece], uv[kPiece], dov[kPiece], zv[kPiece], dlv[kPiece];
+#pragma unroll
+        for (int k = 0; k < kPiece; ++k) {
+            load_dtu(s4 + k, dtv[k], uv[k]);
+            const int so = tok_soff(s4 + k);
+            dov[k] = buf_load_s<T>(do_rs, lane_off, so);
+            zv[k] = HAS_Z ? buf_load_s<T>(z_rs, lane_off, so) : 0.0f;
+            dlv[k] = SOFTPLUS ? buf_load_s<T>(dl_rs, lane_off, so) : 0.0f;
+        }
+        float hs[kPiece][N];
+#pragma unroll
+        for (int k = 0; k < kPiece; ++k) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) hs[k][n] = k == 0 ? st[n] : hs[k - 1][n];
+            fstep(hs[k], dtv[k], dtv[k] * uv[k], o4 + k);
+        }
+        float* row = sT + (wave * 64 + lane) * kTS;
+#pragma unroll
+        for (int k = kPiece - 1; k >= 0; --k) {
+            const int64_t t = s4 + k;
+            const bool live = t < t_end && active;
+            const int o = o4 + k;
+            const float r = ((starts >> o) & 1ull) ? -__builtin_inff() : 0.0f;
+            // With N <= 8 the decays of the recompute above stay in registers; at
+            // N = 16 they are evaluated again (registers are the limit there).
+            const float dt = kKeepDecay ? dtv[k] : opaque(dtv[k]);
+            const float uu = uv[k];
+            const float w = dt * uu;
+            float sgz = 0.0f, dy = dov[k];
+            if constexpr (HAS_Z) {
+                sgz = sigmoid_f(zv[k]);
+                dy *= zv[k] * sgz;
+            }
+            dy = live ? dy : 0.0f;
+            const float4* Bq = reinterpret_cast<const float4*>(sBC + o * N);
+            const float4* Cq = reinterpret_cast<const float4*>(sBC + kWinFloats + o * N);
+            float sB = 0.0f, sq = 0.0f, y = 0.0f;
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q) {
+                const float4 bv = Bq[q];
+                const float4 cv = Cq[q];
+                const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+                const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+                float vb[4], vc[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = 4 * q + j;
+                    const float hprev = k == 0 ? st[n] : hs[k > 0 ? k - 1 : 0][n];
+                    const float a = exp2_fast(__builtin_fmaf(dt, Al2[n], r));
+                    const float g = __builtin_fmaf(cc[j], dy, gn[n]);
+                    gn[n] = a * g;
+                    const float gq = g * (a * hprev);
+                    sq = __builtin_fmaf(Al2[n], gq, sq);
+                    dA[n] = __builtin_fmaf(dt, gq, dA[n]);
+                    sB = __builtin_fmaf(g, bb[j], sB);
+                    vb[j] = g * w;
+                    vc[j] = dy * hs[k][n];
+                    if constexpr (HAS_Z) y = __builtin_fmaf(cc[j], hs[k][n], y);
+                }
+                // this lane's dB_t, dC_t terms go to its transposition row
+                reinterpret_cast<float4*>(row)[q] = make_float4(vb[0], vb[1], vb[2], vb[3]);
+                reinterpret_cast<float4*>(row + N)[q] = make_float4(vc[0], vc[1], vc[2], vc[3]);
+            }
+            const float du = __builtin_fmaf(dy, Dd, dt * sB);
+            const float ddt = __builtin_fmaf(uu, sB, sq * kLn2);
+            float ddl = ddt;
+            if constexpr (SOFTPLUS) ddl *= sigmoid_f(dlv[k] + dbias);
+            dD_acc = __builtin_fmaf(dy, uu, dD_acc);
+            db_acc += live ? ddl : 0.0f;
+            if (live) {
+                const int so = tok_soff(t);
+                buf_store_s<T>(du_rs, lane_off, so, du);
+                buf_store_s<T>(dd_rs, lane_off, so, ddl);
+                if constexpr (HAS_Z) {
+                    const float yf = __builtin_fmaf(Dd, uu, y);
+                    buf_store_s<T>(dz_rs, lane_off, so, dov[k] * yf * sgz * __builtin_fmaf(zv[k], 1.0f - sgz, 1.0f));
+                }
+            }
+            // dB_t, dC_t: sum the wave's 64 rows of 2N values column by column.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int jv = lane % V;
+            const int part = lane / V;
+            const float* col = sT + (wave * 64 + part * V) * kTS + jv;
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) sum += col[i * kTS];
+#pragma unroll
+            for (int m = V; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
+            if (lane < V) sP[(wave * kWin + o) * V + lane] = sum;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int64_t nwin = (t_end - t_begin + kWin - 1) / kWin;
+    for (int64_t wi = nwin - 1; wi >= 0; --wi) {
+        const int64_t w0 = t_begin + wi * kWin;
+        starts = window_starts(ds_row, w0, t_end, lane);
+        __syncthreads();
+        if (wi != nwin - 1) flush(w0 + kWin);
+        stage_rows<T, N, 2>(sBC, B_row, C_row, w0, t_end, tid);
+        __syncthreads();
+        const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
+        const int nblk16 = static_cast<int>((wend - w0 + kCk - 1) / kCk);
+        for (int kb = nblk16 - 1; kb >= 0; --kb) {
+            // 16-token block [s, s + 16): its checkpoint, the state before s + 8,
+            // then its four pieces last to first (pieces past the chunk end are
+            // identity steps and are skipped).
+            const int64_t s = w0 + kb * kCk;
+            const int os = kb * kCk;
+            float ck0[N], ck8[N];
+            {
+                const float* src = ck_lane + (s / kCk) * N * p.dim;
+#pragma unroll
+                for (int n = 0; n < N; ++n) ck0[n] = src[static_cast<int64_t>(n) * p.dim];
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) ck8[n] = ck0[n];
+            advance4(ck8, s, os);
+            advance4(ck8, s + 4, os + 4);
+#pragma unroll
+            for (int n = 0; n < N; ++n) ck8[n] = opaque(ck8[n]);
+            if (s + 12 < t_end) {
+                float st[N];
+#pragma unroll
+                for (int n = 0; n < N; ++n) st[n] = ck8[n];
+                advance4(st, s + 8, os + 8);
+#pragma unroll
+                for (int n = 0; n < N; ++n) st[n] = opaque(st[n]);
+                piece(s + 12, os + 12, st);
+            }
+            if (s + 8 < t_end) piece(s + 8, os + 8, ck8);
+            if (s + 4 < t_end) {
+                float st[N];
+#pragma unroll
+                for (int n = 0; n < N; ++n) st[n] = ck0[n];
+                advance4(st, s, os);
+#pragma unroll
+                for (int n = 0; n < N; ++n) st[n] = opaque(st[n]);
+                piece(s + 4, os + 4, st);
+            }
+            piece(s, os, ck0);
+        }
+    }
+    __syncthreads();
+    flush(t_begin);
+
+    if (!active) return;
+    float* pw = p.part_w + (b * p.nchunks + c) * (N + 2) * p.dim + d;
+#pragma unroll
+    for (int n = 0; n < N; ++n) pw[static_cast<int64_t>(n) * p.dim] = dA[n];
+    pw[static_cast<int64_t>(N) * p.dim] = dD_acc;
+    pw[static_cast<int64_t>(N + 1) * p.dim] = db_acc;
+}
+
+// 5a. dB[b, t, n] and dC[b, t, n]: sums of the per-block partials, in block order.
+template <typename T, int N>
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, void* dB, void* dC,
+                                                            int64_t rows, int nblk) {
+    constexpr int V = 2 * N;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= rows * V) return;
+    const int64_t row = e / V;
+    const int j = static_cast<int>(e % V);
+    const float* src = part + row * nblk * V + j;
+    float s = 0.0f;
+    for (int k = 0; k < nblk; ++k) s += src[static_cast<int64_t>(k) * V];
+    if (j < N) Elem<T>::store(dB, row * N + j, s);
+    else Elem<T>::store(dC, row * N + j - N, s);
+}
+
+// 5b. dA (D, N), dD (D,), ddelta_bias (D,): sums over rows and chunks in order.
+template <int N>
+__global__ __launch_bounds__(256) void bwd_reduce_w_kernel(const float* __restrict__ part, float* dA, float* dD,
+                                                           float* dbias, int64_t nparts, int dim) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= static_cast<int64_t>(N + 2) * dim) return;
+    const int k = static_cast<int>(e / dim);
+    const int d = static_cast<int>(e % dim);
+    const float* src = part + e;
+    float s = 0.0f;
+    for (int64_t i = 0; i < nparts; ++i) s += src[i * (N + 2) * dim];
+    if (k < N) dA[static_cast<int64_t>(d) * N + k] = s;
+    else if (k == N) { if (dD) dD[d] = s; }
+    else if (dbias) dbias[d] = s;
+}
+
+// Workspace layout (byte offsets, each region 256-byte aligned).
+struct BwdLayout {
+    size_t h_carry, h_agg, g_carry, p_rev, dt, ckpt, part_bc, part_w, total;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, const ScanPlan& plan) {
+    const size_t count = static_cast<size_t>(batch * dim * dstate);
+    const size_t slots = plan.nchunks > 1 ? static_cast<size_t>(plan.nchunks - 1) : 0;
+    const size_t carry = align256(slots * count * sizeof(float));
+    const int64_t nk = (seqlen + kCk - 1) / kCk;
+    const int64_t nblk = (dim + kBlk - 1) / kBlk;
+    BwdLayout l;
+    l.h_carry = 0;
+    l.h_agg = l.h_carry + carry;
+    l.g_carry = l.h_agg + carry;
+    l.p_rev = l.g_carry + carry;
+    l.dt = l.p_rev + carry;
+    l.ckpt = l.dt + align256(static_cast<size_t>(batch * seqlen * dim) * sizeof(float));
+    l.part_bc = l.ckpt + align256(static_cast<size_t>(batch * nk * dstate * dim) * sizeof(float));
+    l.part_w = l.part_bc + align256(static_cast<size_t>(batch * seqlen * nblk * 2 * dstate) * sizeof(float));
+    l.total = l.part_w + align256(static_cast<size_t>(batch * plan.nchunks * (dstate + 2) * dim) * sizeof(float));
+    return l;
+}
+
+template <typename T, int N>
+hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const BwdLayout& l) {
+    char* ws = static_cast<char*>(a.ws);
+    ScanArgs fa{};
+    fa.u = a.u; fa.delta = a.delta; fa.A = a.A; fa.B = a.B; fa.C = a.C; fa.delta_bias = a.delta_bias;
+    fa.doc_start = a.doc_start; fa.initial_state = nullptr;
+    fa.batch = a.batch; fa.seqlen = a.seqlen; fa.dim = a.dim; fa.dstate = N; fa.nheads = 0;
+    fa.bf16 = a.bf16; fa.softplus = a.softplus; fa.stream = a.stream;
+    hipError_t e = launch_scan_chunk_carries(fa, plan, reinterpret_cast<float*>(ws + l.h_carry),
+                                             reinterpret_cast<float*>(ws + l.h_agg), ws + l.dt);
+    if (e != hipSuccess) return e;
+
+    BwdKParams p{};
+    p.u = a.u; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
+    p.delta_bias = a.delta_bias; p.doc_start = a.doc_start; p.dout = a.dout;
+    p.dt = reinterpret_cast<const float*>(ws + l.dt);
+    p.h_carry = reinterpret_cast<const float*>(ws + l.h_carry);
+    p.g_carry = reinterpret_cast<float*>(ws + l.g_carry);
+    p.p_rev = reinterpret_cast<float*>(ws + l.p_rev);
+    p.ckpt = reinterpret_cast<float*>(ws + l.ckpt);
+    p.part_bc = reinterpret_cast<float*>(ws + l.part_bc);
+    p.part_w = reinterpret_cast<float*>(ws + l.part_w);
+    p.du = a.du; p.ddelta = a.ddelta; p.dz = a.dz;
+    p.seqlen = a.seqlen;
+    p.chunk_len = plan.chunk_len;
+    p.nchunks = plan.nchunks;
+    p.nslots = plan.nchunks - 1;
+    p.nk = (a.seqlen + kCk - 1) / kCk;
+    p.dim = static_cast<int>(a.dim);
+    p.nbatch = static_cast<int>(a.batch);
+    p.nblk = static_cast<int>((a.dim + kBlk - 1) / kBlk);
+    const unsigned gx = static_cast<unsigned>(p.nblk);
+    const int64_t count = a.batch * a.dim * N;
+
+    if (p.nslots > 0) {
+        dim3 g2(gx, static_cast<unsigned>(p.nslots), static_cast<unsigned>(a.batch));
+        if (a.z) hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, true>), g2, dim3(kBlk), 0, a.stream, p);
+        else hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, false>), g2, dim3(kBlk), 0, a.stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(bwd_rev_carry_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0,
+                           a.stream, p.g_carry, static_cast<const float*>(p.p_rev), count, p.nslots);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    dim3 g4(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
+    if (a.z) {
+        if (a.softplus) hipLaunchKernelGGL((bwd_chunk_kernel<T, N, true, true>), g4, dim3(kBlk), 0, a.stream, p);
+        else hipLaunchKernelGGL((bwd_chunk_kernel<T, N, true, false>), g4, dim3(kBlk), 0, a.stream, p);
+    } else {
+        if (a.softplus) hipLaunchKernelGGL((bwd_chunk_kernel<T, N, false, true>), g4, dim3(kBlk), 0, a.stream, p);
+        else hipLaunchKernelGGL((bwd_chunk_kernel<T, N, false, false>), g4, dim3(kBlk), 0, a.stream, p);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = a.batch * a.seqlen;
+    hipLaunchKernelGGL((bwd_reduce_bc_kernel<T, N>), dim3(static_cast<unsigned>((rows * 2 * N + 255) / 256)),
+                       dim3(256), 0, a.stream, static_cast<const float*>(p.part_bc), a.dB, a.dC, rows, p.nblk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_reduce_w_kernel<N>), dim3(static_cast<unsigned>(((N + 2) * a.dim + 255) / 256)),
+                       dim3(256), 0, a.stream, static_cast<const float*>(p.part_w), a.dA, a.dD, a.ddelta_bias,
+                       a.batch * plan.nchunks, p.dim);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool scan_bwd_supported(int64_t dstate, int nheads) {
+    return nheads == 0 && (dstate == 4 || dstate == 8 || dstate == 16);
+}
+
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool bf16) {
+    (void)bf16;   // the step sizes are float32 for either I/O dtype
+    return bwd_layout(batch, seqlen, dim, dstate, plan_scan(batch, seqlen, dim)).total;
+}
+
+hipError_t launch_selective_scan_bwd(const ScanBwdArgs& a) {
+    const ScanPlan plan = plan_scan(a.batch, a.seqlen, a.dim);
+    const BwdLayout l = bwd_layout(a.batch, a.seqlen, a.dim, a.dstate, plan);
+    switch (a.dstate) {
+        case 4: return a.bf16 ? launch_bwd_typed<bf16_t, 4>(a, plan, l) : launch_bwd_typed<float, 4>(a, plan, l);
+        case 8: return a.bf16 ? launch_bwd_typed<bf16_t, 8>(a, plan, l) : launch_bwd_typed<float, 8>(a, plan, l);
+        case 16: return a.bf16 ? launch_bwd_typed<bf16_t, 16>(a, plan, l) : launch_bwd_typed<float, 16>(a, plan, l);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mamba

@@ -206,3 +206,43 @@ def test_conv_scan_validation(lib):
     assert conv_scan(lib, cw=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT       # weights inside out
     assert conv_scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=5)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert conv_scan(lib, d=dims(batch=0), x=None, u=None, out=None) == _lib.MAMBA_OK
+
+
+def bwd(lib, d=None, u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None, bias=None,
+        ds=None, dout=FAKE * 6, du=FAKE * 7, ddelta=FAKE * 8, dA=FAKE * 9, dB=FAKE * 10, dC=FAKE * 11, dD=None,
+        dz=None, dbias=None, ws=FAKE * 64, wsb=1 << 40):
+    d = d or dims(batch=1, seqlen=64, dim=64)
+    return lib.mamba_selective_scan_bwd(ctypes.byref(d), u, delta, A, B, C, D, z, bias, ds, dout, du, ddelta, dA,
+                                        dB, dC, dD, dz, dbias, ws, wsb, None)
+
+
+def test_bwd_workspace_query(lib):
+    n = ctypes.c_size_t(7)
+    d = dims(batch=2, seqlen=32768, dim=1536, dstate=16)
+    assert lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == _lib.MAMBA_OK
+    # at least the 16-token checkpoints and the step sizes
+    assert n.value >= 2 * 2048 * 1536 * 16 * 4 + 2 * 32768 * 1536 * 2
+    for bad in (dims(nheads=24, dstate=128), dims(dstate=32)):
+        assert lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == \
+            _lib.MAMBA_ERR_UNSUPPORTED
+    assert lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(d), None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, u=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert bwd(lib, dout=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert bwd(lib, dB=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert bwd(lib, z=FAKE * 12) == _lib.MAMBA_ERR_INVALID_ARGUMENT            # z without dz
+    assert bwd(lib, dz=FAKE * 12) == _lib.MAMBA_ERR_INVALID_ARGUMENT           # dz without z
+    assert bwd(lib, du=FAKE * 7 + 1) == _lib.MAMBA_ERR_MISALIGNED
+    assert bwd(lib, dA=FAKE * 9 + 2) == _lib.MAMBA_ERR_MISALIGNED
+    assert bwd(lib, ws=FAKE * 64 + 64) == _lib.MAMBA_ERR_MISALIGNED
+    assert bwd(lib, du=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT            # du aliases dout
+    assert bwd(lib, dB=FAKE * 8) == _lib.MAMBA_ERR_INVALID_ARGUMENT            # two outputs alias
+    assert bwd(lib, ws=FAKE * 2) == _lib.MAMBA_ERR_INVALID_ARGUMENT            # workspace over delta
+    assert bwd(lib, wsb=16) == _lib.MAMBA_ERR_WORKSPACE
+    assert bwd(lib, ws=None) == _lib.MAMBA_ERR_WORKSPACE
+    assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, nheads=2)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=32)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert bwd(lib, d=dims(batch=0), u=None, dout=None) == _lib.MAMBA_OK   # empty: no-op

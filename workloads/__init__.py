@@ -7,6 +7,7 @@ it without sharing any computation.
 """
 
 from .synth import (  # noqa: F401
+    make_cotangent,
     CONFIGS,
     ScanInputs,
     bf16_bits,

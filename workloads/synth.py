@@ -189,3 +189,16 @@ def make_inputs(config, seed: Optional[int] = None, **overrides) -> ScanInputs:
     return make_custom(spec["batch"], spec["seqlen"], spec["dim"], spec["dstate"],
                        nheads=spec["nheads"], dtype=spec["dtype"], docs=spec["docs"],
                        a_noise=spec["a_noise"], seed=spec["seed"], name=config)
+
+
+def make_cotangent(batch: int, seqlen: int, dim: int, *, dtype: str = "bf16", seed: int = 0,
+                   channels=None) -> np.ndarray:
+    """A seeded gradient of the loss with respect to the scan output (B, L, D),
+    standard normal (bf16-exact for bf16), optionally zero outside `channels`."""
+    rng = np.random.default_rng(seed)
+    g = _normal(rng, (batch, seqlen, dim))
+    if channels is not None:
+        keep = np.zeros(dim, dtype=bool)
+        keep[np.asarray(channels)] = True
+        g[:, :, ~keep] = 0.0
+    return bf16_round(g) if dtype == "bf16" else g
