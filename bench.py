@@ -76,6 +76,24 @@ def ssd_mfma_flops(B, L, D, N, H, q=64):
     return B * H * (-(-L // q)) * per_chunk
 
 
+def bwd_bytes(B, L, D, N, esz):
+    """Algorithmic HBM bytes of one backward call: u, delta, z, dout, B, C and the
+    doc flags read once; du, ddelta, dz, dB, dC written once; parameters and their
+    gradients."""
+    per_token = esz * 7 * D + 4 * esz * N + 1
+    return B * L * per_token + 4 * 2 * (D * N + 3 * D)
+
+
+def bwd_alu_flop_eq(B, L, D, N):
+    """Algorithmic fp32 VALU work of the backward in flop-equivalents (slots as in
+    scan_alu_flop_eq).  Per (t, d, n): the decay (dt*A + exp = 5), the state
+    (dt*u*B, FMA = 2), the adjoint (C*dy FMA, times the decay = 2), a*h_{t-1} and
+    g*(a*h) (2), the A and dA terms (2), g.B (1), the dB and dC terms (2) and their
+    sums over channels (2) = 18 slots.  Per (t, d): softplus, its sigmoid, SiLU(z)
+    with its derivative, du, ddt, dz and the dD / ddelta_bias sums, about 48 slots."""
+    return 2.0 * (B * L * D * N * 18 + B * L * D * 48)
+
+
 def conv_alu_flop_eq(B, L, D):
     """4 FMAs + SiLU (exp, rcp, 2 ops) per (t, d) = 14 slots."""
     return 2.0 * 14 * B * L * D
@@ -154,8 +172,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768, help="oracle sample: tokens per row")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the device copy probe (0: skip)")
-    ap.add_argument("--path", choices=("fused", "split"), default="fused",
-                    help="fused: one mamba_conv_scan_fwd call per step; split: conv call, then scan call")
+    ap.add_argument("--path", choices=("fused", "split", "bwd"), default="fused",
+                    help="fused: one mamba_conv_scan_fwd call per step; split: conv call, then scan call; "
+                         "bwd: one mamba_selective_scan_bwd call per step (per-channel A workloads)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -192,6 +211,8 @@ def main():
     fin = torch.empty((B, D, N), dtype=torch.float32, device=dev)
     ws = torch.empty(max(ssm.scan_workspace_bytes(B, L, D, N, H, inp.dtype), 1), dtype=torch.uint8, device=dev)
 
+    if args.path == "bwd":
+        return bench_bwd(args, torch, np, ssm, inp, t, spec, dev)
     fused = args.path == "fused"
 
     def step(ev=None):
@@ -290,6 +311,101 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
     print(json.dumps(result), flush=True)
+
+
+METRIC_BWD = "selective-scan bwd tokens/s, B=2 L=32K D=1536 N=16 bf16"
+
+
+def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
+    """One step = one backward call (gradients of sum(dout * out) with respect to
+    u, delta, A, B, C, D, z and delta_bias), u = the workload's x."""
+    from gpu_helpers import to_dev
+    from workloads import make_cotangent
+
+    B, L, D = inp.x.shape
+    N = inp.B.shape[-1]
+    if inp.nheads:
+        print("the backward pass covers per-channel A workloads only", file=sys.stderr)
+        sys.exit(2)
+    esz = 2 if inp.dtype == "bf16" else 4
+    dout = to_dev(make_cotangent(B, L, D, dtype=inp.dtype, seed=7), inp.dtype, dev)
+    ws = torch.empty(ssm.scan_bwd_workspace_bytes(B, L, D, N, inp.dtype), dtype=torch.uint8, device=dev)
+    grads = {}
+
+    def step():
+        g = ssm.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dout, t["D"], t["z"],
+                                   t["delta_bias"], t["doc_start"], workspace=ws, grads=grads)
+        grads.update(g)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events[i][0].record()
+        step()
+        events[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    probe = copy_probe(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
+    csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
+    traffic = recorded_traffic(os.path.join(ROOT, "profiles", f"bwd_{args.config}_hbm_traffic.txt"),
+                               [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))])
+    flops = bwd_alu_flop_eq(B, L, D, N)
+    nbytes = bwd_bytes(B, L, D, N, esz)
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    gbs = nbytes / (call_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC_BWD,
+        "value": B * L / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inp.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.config, "batch": B, "seqlen": L, "dim": D, "dstate": N, "nheads": 0,
+                   "doc_mean_len": spec["docs"], "io_dtype": inp.dtype, "state_dtype": "f32", "path": "bwd"},
+        "roofline": {"kernel": "mamba_selective_scan_bwd, one call: forward aggregate and carry, reverse aggregate "
+                               "and carry, main pass, reductions",
+                     "bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic, "algorithmic_flop_eq": flops,
+                     "algorithmic_bytes": nbytes, "hbm_achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                     "avg_ms": call_ms},
+        "copy_probe": probe,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_bwd(inp, dout_seed=7, tokens_per_row=min(args.cpu_tokens, 4096))
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_bwd(inp, dout_seed, tokens_per_row):
+    """Time the fp64 oracle gradients (as they stand) on the first tokens of every row."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import make_cotangent
+
+    B, L, D = inp.x.shape
+    T = min(tokens_per_row, L)
+    sl = slice(0, T)
+    dout = make_cotangent(B, L, D, dtype=inp.dtype, seed=dout_seed)[:, sl]
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.selective_scan_bwd(inp.x[:, sl], inp.delta[:, sl], inp.A, inp.B[:, sl], inp.C[:, sl], dout,
+                                  D=inp.D, z=inp.z[:, sl], delta_bias=inp.delta_bias, doc_start=inp.doc_start[:, sl])
+        dt = time.perf_counter() - t0
+    ntok = B * T
+    return dict(value=ntok / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {T} tokens of each of the {B} rows, all {D} channels "
+                       f"({ntok} tokens, {dt:.1f} s, fp64 numpy, one thread)")
 
 
 if __name__ == "__main__":

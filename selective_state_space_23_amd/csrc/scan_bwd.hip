@@ -26,11 +26,13 @@
 //   3. reverse carry: G_c = X_{c+1} + P_{c+1} G_{c+1}, the adjoint flowing into
 //      the last token of chunk c from the right (the same associative operator
 //      as the forward carry, run from the row end);
-//   4. main pass, per chunk: one forward sweep from the chunk's state stores the
-//      state before every 16-token block (global checkpoints); then the blocks
-//      are walked last to first: recompute the block from its checkpoint keeping
-//      the state every 4 tokens, and for each 4-token piece (last first)
-//      recompute its four states and run the adjoint over them;
+//   4. main pass, per chunk: pass 1 also stored, before every 16-token block, the
+//      state reached from zero at the chunk start and the step-size sum since
+//      then, so the true state there is local + exp(A sum) * (chunk's carry).
+//      The blocks are walked last to first: from that checkpoint recompute the
+//      state before token 8, and for each 4-token piece (last first) its start
+//      state (4 more steps for the odd pieces) and its four states, then run
+//      the adjoint over them;
 //   5. fixed-order reduction of the per-block partial sums (dB, dC) and of the
 //      per-chunk partial sums (dA, dD, ddelta_bias): results are deterministic.
 //
@@ -71,7 +73,7 @@ struct BwdKParams {
     const float* h_carry;    // [nslots][B][D][N]: state entering chunk s + 1
     float* g_carry;          // [nslots][B][D][N]: X_{s+1}, then G_s
     float* p_rev;            // [nslots][B][D][N]: P_{s+1}
-    float* ckpt;             // [B][nk][N][D]: state before token 16 k
+    const float* ckpt;       // [B][nk][N + 2][D]: local checkpoints of forward pass 1
     float* part_bc;          // [B][L][nblk][2N]: per-block sums of dB_t, dC_t
     float* part_w;           // [B][nchunks][N + 2][D]: per-chunk sums of dA, dD, ddelta_bias
     void* du;
@@ -323,8 +325,8 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
     const float Dd = p.D ? p.D[dc] : 0.0f;
     const int64_t count = static_cast<int64_t>(p.nbatch) * p.dim * N;
     const int64_t my_slot = (b * p.dim + dc) * N;
-    // Checkpoint k, state n of this lane: ck_lane[(k * N + n) * dim].
-    float* ck_lane = p.ckpt + b * p.nk * N * p.dim + dc;
+    // Checkpoint k of this lane, row r: ck_lane[(k * (N + 2) + r) * dim].
+    const float* ck_lane = p.ckpt + b * p.nk * (N + 2) * p.dim + dc;
 
     // Element offsets: a lane-constant byte offset plus a wave-uniform one per
     // token (the buffer instruction's scalar offset), so per-token addresses cost
@@ -372,36 +374,6 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
 #pragma unroll
         for (int k = 0; k < kPiece; ++k) fstep(h, dtv[k], dtv[k] * uv[k], o0 + k);
     };
-
-    // ---- forward sweep: checkpoint before every 16-token block
-    {
-        float h[N];
-        if (c > 0) {
-            const float* hc = p.h_carry + (c - 1) * count + my_slot;
-#pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = hc[n];
-        } else {
-#pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = 0.0f;
-        }
-        for (int64_t w0 = t_begin; w0 < t_end; w0 += kWin) {
-            starts = window_starts(ds_row, w0, t_end, lane);
-            __syncthreads();
-            stage_rows<T, N, 1>(sBC, B_row, C_row, w0, t_end, tid);
-            __syncthreads();
-            const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
-            for (int64_t s = w0; s < wend; s += kCk) {
-                if (active) {
-                    float* ck = ck_lane + (s / kCk) * N * p.dim;
-#pragma unroll
-                    for (int n = 0; n < N; ++n) ck[static_cast<int64_t>(n) * p.dim] = h[n];
-                }
-                const int os = static_cast<int>(s - w0);
-#pragma unroll
-                for (int k0 = 0; k0 < kCk; k0 += kPiece) advance4(h, s + k0, os + k0);
-            }
-        }
-    }
 
     // ---- backward over the chunk, last window first
     float gn[N];          // a_{t+1} g_{t+1}: the adjoint reaching token t from the right
@@ -552,9 +524,19 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
             const int os = kb * kCk;
             float ck0[N], ck8[N];
             {
-                const float* src = ck_lane + (s / kCk) * N * p.dim;
+                // local checkpoint + exp(A * sum dt) * (state entering the chunk)
+                const float* src = ck_lane + (s / kCk) * (N + 2) * p.dim;
+                const float cdt = src[static_cast<int64_t>(N) * p.dim];
+                const bool fresh = c == 0 || src[static_cast<int64_t>(N + 1) * p.dim] != 0.0f;
+                const float* hin = p.h_carry + (c > 0 ? c - 1 : 0) * count + my_slot;
+                if (fresh) {
 #pragma unroll
-                for (int n = 0; n < N; ++n) ck0[n] = src[static_cast<int64_t>(n) * p.dim];
+                    for (int n = 0; n < N; ++n) ck0[n] = src[static_cast<int64_t>(n) * p.dim];
+                } else {
+#pragma unroll
+                    for (int n = 0; n < N; ++n)
+                        ck0[n] = __builtin_fmaf(exp2_fast(Al2[n] * cdt), hin[n], src[static_cast<int64_t>(n) * p.dim]);
+                }
             }
 #pragma unroll
             for (int n = 0; n < N; ++n) ck8[n] = ck0[n];
@@ -562,26 +544,22 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
             advance4(ck8, s + 4, os + 4);
 #pragma unroll
             for (int n = 0; n < N; ++n) ck8[n] = opaque(ck8[n]);
-            if (s + 12 < t_end) {
+            // Pieces last to first, one loop body (unrolling the four lets the
+            // compiler interleave them and run out of registers).
+#pragma unroll 1
+            for (int j = kCk / kPiece - 1; j >= 0; --j) {
+                const int64_t s4 = s + j * kPiece;
+                if (s4 >= t_end) continue;                 // identity steps only
                 float st[N];
 #pragma unroll
-                for (int n = 0; n < N; ++n) st[n] = ck8[n];
-                advance4(st, s + 8, os + 8);
+                for (int n = 0; n < N; ++n) st[n] = j >= 2 ? ck8[n] : ck0[n];
+                if (j & 1) {
+                    advance4(st, s4 - kPiece, os + j * kPiece - kPiece);
 #pragma unroll
-                for (int n = 0; n < N; ++n) st[n] = opaque(st[n]);
-                piece(s + 12, os + 12, st);
+                    for (int n = 0; n < N; ++n) st[n] = opaque(st[n]);
+                }
+                piece(s4, os + j * kPiece, st);
             }
-            if (s + 8 < t_end) piece(s + 8, os + 8, ck8);
-            if (s + 4 < t_end) {
-                float st[N];
-#pragma unroll
-                for (int n = 0; n < N; ++n) st[n] = ck0[n];
-                advance4(st, s, os);
-#pragma unroll
-                for (int n = 0; n < N; ++n) st[n] = opaque(st[n]);
-                piece(s + 4, os + 4, st);
-            }
-            piece(s, os, ck0);
         }
     }
     __syncthreads();
@@ -611,17 +589,33 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
     else Elem<T>::store(dC, row * N + j - N, s);
 }
 
-// 5b. dA (D, N), dD (D,), ddelta_bias (D,): sums over rows and chunks in order.
+// 5b. dA (D, N), dD (D,), ddelta_bias (D,): sums over rows and chunks.  A block
+// covers 64 outputs with 4 threads each; thread g sums the parts g, g + 4, ...
+// (two accumulators), then the 4 partial sums are added in a fixed order.
 template <int N>
 __global__ __launch_bounds__(256) void bwd_reduce_w_kernel(const float* __restrict__ part, float* dA, float* dD,
                                                            float* dbias, int64_t nparts, int dim) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= static_cast<int64_t>(N + 2) * dim) return;
+    __shared__ float red[4][64];
+    const int64_t nout = static_cast<int64_t>(N + 2) * dim;
+    const int lane = threadIdx.x & 63;
+    const int grp = threadIdx.x >> 6;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+    float s0 = 0.0f, s1 = 0.0f;
+    if (e < nout) {
+        const float* src = part + e;
+        int64_t i = grp;
+        for (; i + 4 < nparts; i += 8) {
+            s0 += src[i * nout];
+            s1 += src[(i + 4) * nout];
+        }
+        if (i < nparts) s0 += src[i * nout];
+    }
+    red[grp][lane] = s0 + s1;
+    __syncthreads();
+    if (grp != 0 || e >= nout) return;
+    const float s = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
     const int k = static_cast<int>(e / dim);
     const int d = static_cast<int>(e % dim);
-    const float* src = part + e;
-    float s = 0.0f;
-    for (int64_t i = 0; i < nparts; ++i) s += src[i * (N + 2) * dim];
     if (k < N) dA[static_cast<int64_t>(d) * N + k] = s;
     else if (k == N) { if (dD) dD[d] = s; }
     else if (dbias) dbias[d] = s;
@@ -647,7 +641,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     l.p_rev = l.g_carry + carry;
     l.dt = l.p_rev + carry;
     l.ckpt = l.dt + align256(static_cast<size_t>(batch * seqlen * dim) * sizeof(float));
-    l.part_bc = l.ckpt + align256(static_cast<size_t>(batch * nk * dstate * dim) * sizeof(float));
+    l.part_bc = l.ckpt + align256(static_cast<size_t>(batch * nk * (dstate + 2) * dim) * sizeof(float));
     l.part_w = l.part_bc + align256(static_cast<size_t>(batch * seqlen * nblk * 2 * dstate) * sizeof(float));
     l.total = l.part_w + align256(static_cast<size_t>(batch * plan.nchunks * (dstate + 2) * dim) * sizeof(float));
     return l;
@@ -662,7 +656,8 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     fa.batch = a.batch; fa.seqlen = a.seqlen; fa.dim = a.dim; fa.dstate = N; fa.nheads = 0;
     fa.bf16 = a.bf16; fa.softplus = a.softplus; fa.stream = a.stream;
     hipError_t e = launch_scan_chunk_carries(fa, plan, reinterpret_cast<float*>(ws + l.h_carry),
-                                             reinterpret_cast<float*>(ws + l.h_agg), ws + l.dt);
+                                             reinterpret_cast<float*>(ws + l.h_agg), ws + l.dt,
+                                             reinterpret_cast<float*>(ws + l.ckpt));
     if (e != hipSuccess) return e;
 
     BwdKParams p{};
@@ -672,7 +667,7 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     p.h_carry = reinterpret_cast<const float*>(ws + l.h_carry);
     p.g_carry = reinterpret_cast<float*>(ws + l.g_carry);
     p.p_rev = reinterpret_cast<float*>(ws + l.p_rev);
-    p.ckpt = reinterpret_cast<float*>(ws + l.ckpt);
+    p.ckpt = reinterpret_cast<const float*>(ws + l.ckpt);
     p.part_bc = reinterpret_cast<float*>(ws + l.part_bc);
     p.part_w = reinterpret_cast<float*>(ws + l.part_w);
     p.du = a.du; p.ddelta = a.ddelta; p.dz = a.dz;
@@ -713,7 +708,7 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
                        dim3(256), 0, a.stream, static_cast<const float*>(p.part_bc), a.dB, a.dC, rows, p.nblk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_reduce_w_kernel<N>), dim3(static_cast<unsigned>(((N + 2) * a.dim + 255) / 256)),
+    hipLaunchKernelGGL((bwd_reduce_w_kernel<N>), dim3(static_cast<unsigned>(((N + 2) * a.dim + 63) / 64)),
                        dim3(256), 0, a.stream, static_cast<const float*>(p.part_w), a.dA, a.dD, a.ddelta_bias,
                        a.batch * plan.nchunks, p.dim);
     return hipGetLastError();

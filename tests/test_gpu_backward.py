@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make_cotangent, make_custom, make_inputs
+from workloads import bf16_round, make_cotangent, make_custom, make_inputs
 
 from gpu_helpers import assert_close, to_dev, to_host, torch_mod, upload
 
@@ -88,6 +88,12 @@ def test_bwd_parity_small(ssm, case):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_bwd_optional_inputs(ssm, flags, dtype):
     inp = make_custom(2, 600, 96, 16, dtype=dtype, docs=100.0, seed=811)
+    if not flags.get("softplus", True):
+        # Without softplus, delta is the step size itself: give positive ones.
+        # (Negative steps make exp(dt A) > 1 and the states grow towards 1e36
+        # within 600 tokens, where fp32 gradient sums are ill-conditioned.)
+        pos = np.abs(inp.delta) * np.float32(0.5) + np.float32(0.001)
+        inp.delta[:] = bf16_round(pos) if dtype == "bf16" else pos
     bwd_case(ssm, inp, seed=911, **flags)
 
 
