@@ -55,7 +55,19 @@ constexpr int kWin = 64;               // tokens per staged B/C window
 constexpr int kCk = 16;                // tokens per checkpoint block
 constexpr int kPiece = 4;              // tokens per innermost recompute piece
 #ifndef MAMBA_BWD_WAVES_PER_EU
-#define MAMBA_BWD_WAVES_PER_EU 2
+#define MAMBA_BWD_WAVES_PER_EU 0        // 0: chosen per state count (bwd_waves_per_eu)
+#endif
+#ifndef MAMBA_BWD_TOKEN_BARRIER
+#define MAMBA_BWD_TOKEN_BARRIER 1
+#endif
+#ifndef MAMBA_BWD_KEEP_NL
+#define MAMBA_BWD_KEEP_NL 4      // keep the recompute's decays in registers up to this many states a lane
+#endif
+#ifndef MAMBA_BWD_G16
+#define MAMBA_BWD_G16 2          // lanes per channel at N = 16
+#endif
+#ifndef MAMBA_BWD_G8
+#define MAMBA_BWD_G8 1           // lanes per channel at N = 8
 #endif
 
 struct BwdKParams {
@@ -278,23 +290,50 @@ __global__ __launch_bounds__(256) void bwd_rev_carry_kernel(float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // 4. Main pass over chunk blockIdx.y of row blockIdx.z.
-template <typename T, int N, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_WAVES_PER_EU))) void bwd_chunk_kernel(
+//
+// G lanes share one channel, each holding NL = N / G of its states (G = 2 at
+// N = 16 halves the per-lane arrays, which is what lets 3 waves share a SIMD);
+// their partial sums over states (g.B, the A term, C.h) meet through one DPP
+// exchange per sum, and every lane of the group computes the per-token scalars.
+template <int G>
+__device__ __forceinline__ float sum_group(float v) {
+    if constexpr (G >= 2)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    if constexpr (G >= 4)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    return v;
+}
+
+// Waves per SIMD the main pass is compiled for: 3 with 8 states a lane (two
+// lanes per channel at N = 16; a few spills, measured faster than 2 without),
+// 2 otherwise.
+constexpr int bwd_waves_per_eu(int nl) { return MAMBA_BWD_WAVES_PER_EU > 0 ? MAMBA_BWD_WAVES_PER_EU : (nl == 8 ? 3 : 2); }
+
+template <typename T, int N, int G, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(N / G)))) void bwd_chunk_kernel(
     const BwdKParams p) {
-    constexpr int V = 2 * N;               // dB_t and dC_t values of one lane
+    constexpr int NL = N / G;              // states per lane
+    constexpr int CPB = kBlk / G;          // channels per block
+    constexpr int V = 2 * NL;              // dB_t and dC_t terms of one lane
     constexpr int kTS = V + 4;             // transposition row stride (16-byte aligned rows)
+    constexpr int NOUT = 2 * N;            // sums per token: dB_t, then dC_t
+    constexpr int R = 64 / NOUT;           // lanes per sum
+    constexpr int ROWS = 64 / G / R;       // rows each of them adds
     constexpr int kWinFloats = kWin * N;
-    constexpr bool kKeepDecay = N <= 8;
+    constexpr bool kKeepDecay = NL <= MAMBA_BWD_KEEP_NL;
+    static_assert(N % G == 0 && NL % 4 == 0 && 64 % NOUT == 0, "state split");
     __shared__ float4 sBC4[2 * kWinFloats / 4];          // B then C of the window
     __shared__ float4 sT4[kWaves * 64 * kTS / 4];        // per-wave transposition
-    __shared__ float sP[kWaves * kWin * V];              // per-wave column sums of the window
+    __shared__ float sP[2][kWaves * kCk * NOUT];         // per-wave sums of a 16-token block (2 buffers)
     float* sBC = reinterpret_cast<float*>(sBC4);
     float* sT = reinterpret_cast<float*>(sT4);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int d = blockIdx.x * kBlk + tid;
+    const int sub = tid % G;
+    const int n0 = sub * NL;                // first state of this lane
+    const int d = blockIdx.x * CPB + tid / G;
     const bool active = d < p.dim;
     const int dc = active ? d : p.dim - 1;
     const int64_t c = blockIdx.y;
@@ -318,14 +357,14 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
     const T* C_row = static_cast<const T*>(p.C) + b * L * N;
     const uint8_t* ds_row = p.doc_start ? p.doc_start + b * L : nullptr;
 
-    float Al2[N];
+    float Al2[NL];
 #pragma unroll
-    for (int n = 0; n < N; ++n) Al2[n] = p.A[static_cast<int64_t>(dc) * N + n] * kLog2e;
+    for (int i = 0; i < NL; ++i) Al2[i] = p.A[static_cast<int64_t>(dc) * N + n0 + i] * kLog2e;
     const float dbias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
     const float Dd = p.D ? p.D[dc] : 0.0f;
     const int64_t count = static_cast<int64_t>(p.nbatch) * p.dim * N;
-    const int64_t my_slot = (b * p.dim + dc) * N;
-    // Checkpoint k of this lane, row r: ck_lane[(k * (N + 2) + r) * dim].
+    const int64_t my_slot = (b * p.dim + dc) * N + n0;
+    // Checkpoint k of this channel, row r: ck_lane[(k * (N + 2) + r) * dim].
     const float* ck_lane = p.ckpt + b * p.nk * (N + 2) * p.dim + dc;
 
     // Element offsets: a lane-constant byte offset plus a wave-uniform one per
@@ -339,26 +378,26 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
 
     uint64_t starts = 0;
     // One forward step of the token at window offset o: h <- exp(dt A) h + w B_t.
-    auto fstep = [&](float (&h)[N], float dt, float w, int o) {
+    auto fstep = [&](float (&h)[NL], float dt, float w, int o) {
         const float r = ((starts >> o) & 1ull) ? -__builtin_inff() : 0.0f;
-        const float4* Bq = reinterpret_cast<const float4*>(sBC + o * N);
+        const float4* Bq = reinterpret_cast<const float4*>(sBC + o * N + n0);
 #pragma unroll
-        for (int q = 0; q < N / 4; ++q) {
+        for (int q = 0; q < NL / 4; ++q) {
             const float4 bv = Bq[q];
             const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int n = 4 * q + j;
-                h[n] = __builtin_fmaf(exp2_fast(__builtin_fmaf(dt, Al2[n], r)), h[n], w * bb[j]);
+                const int i = 4 * q + j;
+                h[i] = __builtin_fmaf(exp2_fast(__builtin_fmaf(dt, Al2[i], r)), h[i], w * bb[j]);
             }
         }
         // Keep the scheduler from hoisting later tokens' LDS reads and
-        // exponentials: each token already offers N independent chains.
+        // exponentials: each token already offers NL independent chains.
         __builtin_amdgcn_sched_barrier(0);
     };
     // dt and u of token t: dt = 0 past the chunk end (an identity step), u = 0 on
-    // an inactive lane (its dB contributions vanish).  The values pass through
-    // opaque() so that each recompute level evaluates its own exponentials.
+    // an inactive lane (its dB terms vanish).  The values pass through opaque()
+    // so that each recompute level evaluates its own exponentials.
     auto load_dtu = [&](int64_t t, float& dt, float& uu) {
         const int so = tok_soff(t);
         dt = buf_load_s<float>(dt_rs, dc * 4, so * (4 / kEsz));
@@ -367,7 +406,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
         uu = active ? uu : 0.0f;
     };
     // h <- the state after tokens t0 .. t0 + 3 (window offsets o0 ..).
-    auto advance4 = [&](float (&h)[N], int64_t t0, int o0) {
+    auto advance4 = [&](float (&h)[NL], int64_t t0, int o0) {
         float dtv[kPiece], uv[kPiece];
 #pragma unroll
         for (int k = 0; k < kPiece; ++k) load_dtu(t0 + k, dtv[k], uv[k]);
@@ -375,39 +414,40 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
         for (int k = 0; k < kPiece; ++k) fstep(h, dtv[k], dtv[k] * uv[k], o0 + k);
     };
 
-    // ---- backward over the chunk, last window first
-    float gn[N];          // a_{t+1} g_{t+1}: the adjoint reaching token t from the right
+    float gn[NL];         // a_{t+1} g_{t+1}: the adjoint reaching token t from the right
     if (c + 1 < p.nchunks) {
         const float* gc = p.g_carry + c * count + my_slot;
 #pragma unroll
-        for (int n = 0; n < N; ++n) gn[n] = gc[n];
+        for (int i = 0; i < NL; ++i) gn[i] = gc[i];
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) gn[n] = 0.0f;
+        for (int i = 0; i < NL; ++i) gn[i] = 0.0f;
     }
-    float dA[N];
+    float dA[NL];
 #pragma unroll
-    for (int n = 0; n < N; ++n) dA[n] = 0.0f;
+    for (int i = 0; i < NL; ++i) dA[i] = 0.0f;
     float dD_acc = 0.0f, db_acc = 0.0f;
+    int buf = 0;
 
-    // Sum the 4 waves' column sums of window w0 and store the block's partials.
-    auto flush = [&](int64_t w0) {
-        const int64_t nvalid = (w0 + kWin < t_end) ? kWin : t_end - w0;
-        for (int e = tid; e < kWin * V; e += kBlk) {
-            const int tok = e / V;
-            const int j = e % V;
+    // Sum the 4 waves' sums of 16-token block s and store the block's partials.
+    auto flush16 = [&](const float* sp, int64_t s) {
+        const int64_t nvalid = (s + kCk < t_end) ? kCk : t_end - s;
+        for (int e = tid; e < kCk * NOUT; e += kBlk) {
+            const int tok = e / NOUT;
+            const int j = e % NOUT;
             if (tok < nvalid) {
-                float sum = sP[tok * V + j];
+                float sum = sp[tok * NOUT + j];
 #pragma unroll
-                for (int w = 1; w < kWaves; ++w) sum += sP[(w * kWin + tok) * V + j];
-                p.part_bc[((b * L + w0 + tok) * p.nblk + blockIdx.x) * V + j] = sum;
+                for (int w = 1; w < kWaves; ++w) sum += sp[(w * kCk + tok) * NOUT + j];
+                p.part_bc[((b * L + s + tok) * p.nblk + blockIdx.x) * NOUT + j] = sum;
             }
         }
     };
 
-    // One 4-token piece starting at s4 (window offset o4) from the state st before
-    // it: recompute the four states, then run the adjoint over them, last first.
-    auto piece = [&](int64_t s4, int o4, const float (&st)[N]) {
+    // One 4-token piece starting at s4 (window offset o4, block offset k4) from
+    // the state st before it: recompute the four states, then run the adjoint
+    // over them, last first.
+    auto piece = [&](int64_t s4, int o4, int k4, const float (&st)[NL], float* sp) {
         float dtv[kPiece], uv[kPiece], dov[kPiece], zv[kPiece], dlv[kPiece];
 #pragma unroll
         for (int k = 0; k < kPiece; ++k) {
@@ -417,11 +457,11 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
             zv[k] = HAS_Z ? buf_load_s<T>(z_rs, lane_off, so) : 0.0f;
             dlv[k] = SOFTPLUS ? buf_load_s<T>(dl_rs, lane_off, so) : 0.0f;
         }
-        float hs[kPiece][N];
+        float hs[kPiece][NL];
 #pragma unroll
         for (int k = 0; k < kPiece; ++k) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) hs[k][n] = k == 0 ? st[n] : hs[k - 1][n];
+            for (int i = 0; i < NL; ++i) hs[k][i] = k == 0 ? st[i] : hs[k - 1][i];
             fstep(hs[k], dtv[k], dtv[k] * uv[k], o4 + k);
         }
         float* row = sT + (wave * 64 + lane) * kTS;
@@ -431,8 +471,8 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
             const bool live = t < t_end && active;
             const int o = o4 + k;
             const float r = ((starts >> o) & 1ull) ? -__builtin_inff() : 0.0f;
-            // With N <= 8 the decays of the recompute above stay in registers; at
-            // N = 16 they are evaluated again (registers are the limit there).
+            // With few states per lane the decays of the recompute above stay in
+            // registers; otherwise they are evaluated again (registers are the limit).
             const float dt = kKeepDecay ? dtv[k] : opaque(dtv[k]);
             const float uu = uv[k];
             const float w = dt * uu;
@@ -442,11 +482,11 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
                 dy *= zv[k] * sgz;
             }
             dy = live ? dy : 0.0f;
-            const float4* Bq = reinterpret_cast<const float4*>(sBC + o * N);
-            const float4* Cq = reinterpret_cast<const float4*>(sBC + kWinFloats + o * N);
+            const float4* Bq = reinterpret_cast<const float4*>(sBC + o * N + n0);
+            const float4* Cq = reinterpret_cast<const float4*>(sBC + kWinFloats + o * N + n0);
             float sB = 0.0f, sq = 0.0f, y = 0.0f;
 #pragma unroll
-            for (int q = 0; q < N / 4; ++q) {
+            for (int q = 0; q < NL / 4; ++q) {
                 const float4 bv = Bq[q];
                 const float4 cv = Cq[q];
                 const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
@@ -454,30 +494,33 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
                 float vb[4], vc[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int n = 4 * q + j;
-                    const float hprev = k == 0 ? st[n] : hs[k > 0 ? k - 1 : 0][n];
-                    const float a = exp2_fast(__builtin_fmaf(dt, Al2[n], r));
-                    const float g = __builtin_fmaf(cc[j], dy, gn[n]);
-                    gn[n] = a * g;
+                    const int i = 4 * q + j;
+                    const float hprev = k == 0 ? st[i] : hs[k > 0 ? k - 1 : 0][i];
+                    const float a = exp2_fast(__builtin_fmaf(dt, Al2[i], r));
+                    const float g = __builtin_fmaf(cc[j], dy, gn[i]);
+                    gn[i] = a * g;
                     const float gq = g * (a * hprev);
-                    sq = __builtin_fmaf(Al2[n], gq, sq);
-                    dA[n] = __builtin_fmaf(dt, gq, dA[n]);
+                    sq = __builtin_fmaf(Al2[i], gq, sq);
+                    dA[i] = __builtin_fmaf(dt, gq, dA[i]);
                     sB = __builtin_fmaf(g, bb[j], sB);
                     vb[j] = g * w;
-                    vc[j] = dy * hs[k][n];
-                    if constexpr (HAS_Z) y = __builtin_fmaf(cc[j], hs[k][n], y);
+                    vc[j] = dy * hs[k][i];
+                    if constexpr (HAS_Z) y = __builtin_fmaf(cc[j], hs[k][i], y);
                 }
                 // this lane's dB_t, dC_t terms go to its transposition row
                 reinterpret_cast<float4*>(row)[q] = make_float4(vb[0], vb[1], vb[2], vb[3]);
-                reinterpret_cast<float4*>(row + N)[q] = make_float4(vc[0], vc[1], vc[2], vc[3]);
+                reinterpret_cast<float4*>(row + NL)[q] = make_float4(vc[0], vc[1], vc[2], vc[3]);
             }
+            sB = sum_group<G>(sB);
+            sq = sum_group<G>(sq);
+            if constexpr (HAS_Z) y = sum_group<G>(y);
             const float du = __builtin_fmaf(dy, Dd, dt * sB);
             const float ddt = __builtin_fmaf(uu, sB, sq * kLn2);
             float ddl = ddt;
             if constexpr (SOFTPLUS) ddl *= sigmoid_f(dlv[k] + dbias);
             dD_acc = __builtin_fmaf(dy, uu, dD_acc);
             db_acc += live ? ddl : 0.0f;
-            if (live) {
+            if (live && sub == 0) {
                 const int so = tok_soff(t);
                 buf_store_s<T>(du_rs, lane_off, so, du);
                 buf_store_s<T>(dd_rs, lane_off, so, ddl);
@@ -486,23 +529,31 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
                     buf_store_s<T>(dz_rs, lane_off, so, dov[k] * yf * sgz * __builtin_fmaf(zv[k], 1.0f - sgz, 1.0f));
                 }
             }
-            // dB_t, dC_t: sum the wave's 64 rows of 2N values column by column.
+            // dB_t, dC_t: sum the wave's rows column by column.  Sum o covers
+            // value j of the lanes with sub-lane index h; R lanes share it.
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int jv = lane % V;
-            const int part = lane / V;
-            const float* col = sT + (wave * 64 + part * V) * kTS + jv;
+            const int os = lane % NOUT;
+            const int part = lane / NOUT;
+            const int h = os / V;
+            const int j = os % V;
+            const float* col = sT + (wave * 64 + h + G * part * ROWS) * kTS + j;
             float sum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < V; ++i) sum += col[i * kTS];
+            for (int i = 0; i < ROWS; ++i) sum += col[i * G * kTS];
 #pragma unroll
-            for (int m = V; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
-            if (lane < V) sP[(wave * kWin + o) * V + lane] = sum;
+            for (int m = NOUT; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
+            if (lane < NOUT) {
+                const int n = j < NL ? h * NL + j : N + h * NL + (j - NL);
+                sp[(wave * kCk + k4 + k) * NOUT + n] = sum;
+            }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#if MAMBA_BWD_TOKEN_BARRIER
             __builtin_amdgcn_sched_barrier(0);
+#endif
         }
     };
 
@@ -511,7 +562,6 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
         const int64_t w0 = t_begin + wi * kWin;
         starts = window_starts(ds_row, w0, t_end, lane);
         __syncthreads();
-        if (wi != nwin - 1) flush(w0 + kWin);
         stage_rows<T, N, 2>(sBC, B_row, C_row, w0, t_end, tid);
         __syncthreads();
         const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
@@ -522,7 +572,8 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
             // identity steps and are skipped).
             const int64_t s = w0 + kb * kCk;
             const int os = kb * kCk;
-            float ck0[N], ck8[N];
+            float* sp = sP[buf];
+            float ck0[NL], ck8[NL];
             {
                 // local checkpoint + exp(A * sum dt) * (state entering the chunk)
                 const float* src = ck_lane + (s / kCk) * (N + 2) * p.dim;
@@ -531,46 +582,50 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
                 const float* hin = p.h_carry + (c > 0 ? c - 1 : 0) * count + my_slot;
                 if (fresh) {
 #pragma unroll
-                    for (int n = 0; n < N; ++n) ck0[n] = src[static_cast<int64_t>(n) * p.dim];
+                    for (int i = 0; i < NL; ++i) ck0[i] = src[static_cast<int64_t>(n0 + i) * p.dim];
                 } else {
 #pragma unroll
-                    for (int n = 0; n < N; ++n)
-                        ck0[n] = __builtin_fmaf(exp2_fast(Al2[n] * cdt), hin[n], src[static_cast<int64_t>(n) * p.dim]);
+                    for (int i = 0; i < NL; ++i)
+                        ck0[i] = __builtin_fmaf(exp2_fast(Al2[i] * cdt), hin[i],
+                                                src[static_cast<int64_t>(n0 + i) * p.dim]);
                 }
             }
 #pragma unroll
-            for (int n = 0; n < N; ++n) ck8[n] = ck0[n];
+            for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];
             advance4(ck8, s, os);
             advance4(ck8, s + 4, os + 4);
 #pragma unroll
-            for (int n = 0; n < N; ++n) ck8[n] = opaque(ck8[n]);
+            for (int i = 0; i < NL; ++i) ck8[i] = opaque(ck8[i]);
             // Pieces last to first, one loop body (unrolling the four lets the
             // compiler interleave them and run out of registers).
 #pragma unroll 1
             for (int j = kCk / kPiece - 1; j >= 0; --j) {
                 const int64_t s4 = s + j * kPiece;
                 if (s4 >= t_end) continue;                 // identity steps only
-                float st[N];
+                float st[NL];
 #pragma unroll
-                for (int n = 0; n < N; ++n) st[n] = j >= 2 ? ck8[n] : ck0[n];
+                for (int i = 0; i < NL; ++i) st[i] = j >= 2 ? ck8[i] : ck0[i];
                 if (j & 1) {
                     advance4(st, s4 - kPiece, os + j * kPiece - kPiece);
 #pragma unroll
-                    for (int n = 0; n < N; ++n) st[n] = opaque(st[n]);
+                    for (int i = 0; i < NL; ++i) st[i] = opaque(st[i]);
                 }
-                piece(s4, os + j * kPiece, st);
+                piece(s4, os + j * kPiece, j * kPiece, st, sp);
             }
+            __syncthreads();
+            flush16(sp, s);
+            buf ^= 1;
         }
     }
-    __syncthreads();
-    flush(t_begin);
 
     if (!active) return;
     float* pw = p.part_w + (b * p.nchunks + c) * (N + 2) * p.dim + d;
 #pragma unroll
-    for (int n = 0; n < N; ++n) pw[static_cast<int64_t>(n) * p.dim] = dA[n];
-    pw[static_cast<int64_t>(N) * p.dim] = dD_acc;
-    pw[static_cast<int64_t>(N + 1) * p.dim] = db_acc;
+    for (int i = 0; i < NL; ++i) pw[static_cast<int64_t>(n0 + i) * p.dim] = dA[i];
+    if (sub == 0) {
+        pw[static_cast<int64_t>(N) * p.dim] = dD_acc;
+        pw[static_cast<int64_t>(N + 1) * p.dim] = db_acc;
+    }
 }
 
 // 5a. dB[b, t, n] and dC[b, t, n]: sums of the per-block partials, in block order.
@@ -621,6 +676,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_w_kernel(const float* __restri
     else if (dbias) dbias[d] = s;
 }
 
+// Lanes per channel in the main pass.
+constexpr int lanes_per_channel(int64_t n) { return n == 16 ? MAMBA_BWD_G16 : (n == 8 ? MAMBA_BWD_G8 : 1); }
+
 // Workspace layout (byte offsets, each region 256-byte aligned).
 struct BwdLayout {
     size_t h_carry, h_agg, g_carry, p_rev, dt, ckpt, part_bc, part_w, total;
@@ -633,7 +691,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     const size_t slots = plan.nchunks > 1 ? static_cast<size_t>(plan.nchunks - 1) : 0;
     const size_t carry = align256(slots * count * sizeof(float));
     const int64_t nk = (seqlen + kCk - 1) / kCk;
-    const int64_t nblk = (dim + kBlk - 1) / kBlk;
+    const int64_t cpb = kBlk / lanes_per_channel(dstate);
+    const int64_t nblk = (dim + cpb - 1) / cpb;
     BwdLayout l;
     l.h_carry = 0;
     l.h_agg = l.h_carry + carry;
@@ -678,8 +737,10 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     p.nk = (a.seqlen + kCk - 1) / kCk;
     p.dim = static_cast<int>(a.dim);
     p.nbatch = static_cast<int>(a.batch);
-    p.nblk = static_cast<int>((a.dim + kBlk - 1) / kBlk);
-    const unsigned gx = static_cast<unsigned>(p.nblk);
+    constexpr int G = lanes_per_channel(N);
+    constexpr int CPB = kBlk / G;
+    p.nblk = static_cast<int>((a.dim + CPB - 1) / CPB);
+    const unsigned gx = static_cast<unsigned>((a.dim + kBlk - 1) / kBlk);
     const int64_t count = a.batch * a.dim * N;
 
     if (p.nslots > 0) {
@@ -693,13 +754,13 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dim3 g4(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
+    dim3 g4(static_cast<unsigned>(p.nblk), static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
     if (a.z) {
-        if (a.softplus) hipLaunchKernelGGL((bwd_chunk_kernel<T, N, true, true>), g4, dim3(kBlk), 0, a.stream, p);
-        else hipLaunchKernelGGL((bwd_chunk_kernel<T, N, true, false>), g4, dim3(kBlk), 0, a.stream, p);
+        if (a.softplus) hipLaunchKernelGGL((bwd_chunk_kernel<T, N, G, true, true>), g4, dim3(kBlk), 0, a.stream, p);
+        else hipLaunchKernelGGL((bwd_chunk_kernel<T, N, G, true, false>), g4, dim3(kBlk), 0, a.stream, p);
     } else {
-        if (a.softplus) hipLaunchKernelGGL((bwd_chunk_kernel<T, N, false, true>), g4, dim3(kBlk), 0, a.stream, p);
-        else hipLaunchKernelGGL((bwd_chunk_kernel<T, N, false, false>), g4, dim3(kBlk), 0, a.stream, p);
+        if (a.softplus) hipLaunchKernelGGL((bwd_chunk_kernel<T, N, G, false, true>), g4, dim3(kBlk), 0, a.stream, p);
+        else hipLaunchKernelGGL((bwd_chunk_kernel<T, N, G, false, false>), g4, dim3(kBlk), 0, a.stream, p);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
