@@ -18,4 +18,4 @@ from .mamba_oracle import (  # noqa: F401
     softplus,
     ssd_matrix_scan,
 )
-from .mamba_grad import selective_scan_bwd  # noqa: F401
+from .mamba_grad import causal_conv1d_bwd, selective_scan_bwd  # noqa: F401

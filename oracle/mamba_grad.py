@@ -1,5 +1,5 @@
 """Plain fp64 gradients of the selective scan (reverse mode of the sequential
-recurrence).
+recurrence) and of the causal conv1d in front of it.
 
 TEST INFRASTRUCTURE ONLY, like the rest of `oracle/`: the library never imports
 it.  The forward is the one of `mamba_oracle.selective_scan` ("Mamba & State
@@ -98,3 +98,44 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     if delta_bias is not None:
         grads["ddelta_bias"] = ddelta.sum(axis=(0, 1))
     return grads
+
+
+def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu=True):
+    """Gradients of sum(du * u) for u = causal_conv1d(x, weight, bias, doc_start,
+    apply_silu) ([S] S6 code: Conv1d with left padding W-1, first L outputs, SiLU;
+    [A] packing: taps before the token's document start are zero).  With
+    acc_t = bias + sum_j w[W-1-j] x_{t-j} over the taps inside t's document and
+    dacc_t = du_t silu'(acc_t) (du_t without SiLU):
+        dx_s      = sum_j dacc_{s+j} w[W-1-j]   over the j with s inside (s+j)'s document
+        dw[W-1-j] = sum_t dacc_t x_{t-j}        over the same taps
+        dbias     = sum_t dacc_t
+    Returns dx (B, L, D), dweight (D, W) and dbias (D,), float64."""
+    x = _f64(x)
+    w = _f64(weight)
+    g = _f64(du)
+    Bt, L, Dm = x.shape
+    W = w.shape[1]
+    seg = doc_segment_start(doc_start, Bt, L)
+    t = np.arange(L)
+    acc = np.zeros((Bt, L, Dm))
+    if bias is not None:
+        acc += _f64(bias)[None, None, :]
+    taps = []
+    for j in range(W):
+        xs = np.zeros_like(x)
+        xs[:, j:, :] = x[:, :L - j, :]
+        valid = ((t - j)[None, :] >= seg)[..., None]      # tap j of token t is inside its document
+        taps.append((xs, valid))
+        acc += np.where(valid, xs, 0.0) * w[:, W - 1 - j][None, None, :]
+    if apply_silu:
+        sg = sigmoid(acc)
+        dacc = g * sg * (1.0 + acc * (1.0 - sg))
+    else:
+        dacc = g
+    dx = np.zeros_like(x)
+    dw = np.zeros((Dm, W))
+    for j, (xs, valid) in enumerate(taps):
+        contrib = np.where(valid, dacc, 0.0)                # d acc_t / d x_{t-j} = w[W-1-j] on valid taps
+        dx[:, :L - j, :] += contrib[:, j:, :] * w[:, W - 1 - j][None, None, :]
+        dw[:, W - 1 - j] = np.einsum("bld,bld->d", contrib, xs)
+    return dx, dw, dacc.sum(axis=(0, 1))

@@ -416,3 +416,52 @@ def test_gradients_match_finite_differences(flags):
             fd = (lp - lm) / (2 * eps)
             an = g[gname].flat[flat]
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (arg, flat, fd, an)
+
+
+@pytest.mark.parametrize("silu_on,docs", [(True, True), (False, True), (True, False)], ids=str)
+def test_conv_gradients_match_finite_differences(silu_on, docs):
+    """oracle.causal_conv1d_bwd against central differences of oracle.causal_conv1d:
+    every element of x, the weights and the bias, in rows with document starts at
+    and inside the first taps (so the zeroed taps are exercised)."""
+    rng = np.random.default_rng(12)
+    Bt, L, Dm, W = 2, 11, 3, 4
+    x = rng.standard_normal((Bt, L, Dm))
+    w = rng.uniform(-0.7, 0.7, (Dm, W))
+    bias = rng.uniform(-0.3, 0.3, Dm)
+    ds = np.zeros((Bt, L), dtype=np.uint8)
+    if docs:
+        ds[0, [2, 3, 7]] = 1
+        ds[1, [5, 10]] = 1
+    du = rng.standard_normal((Bt, L, Dm))
+    dx, dw, db = oracle.causal_conv1d_bwd(x, w, du, bias, ds if docs else None, apply_silu=silu_on)
+
+    def loss():
+        return float(np.sum(oracle.causal_conv1d(x, w, bias, ds if docs else None, apply_silu=silu_on) * du))
+
+    eps = 1e-6
+    for arr, grad in ((x, dx), (w, dw), (bias, db)):
+        for flat in range(arr.size):
+            orig = arr.flat[flat]
+            arr.flat[flat] = orig + eps
+            lp = loss()
+            arr.flat[flat] = orig - eps
+            lm = loss()
+            arr.flat[flat] = orig
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad.flat[flat]) <= 1e-6 * max(1.0, abs(fd)), (flat, fd, grad.flat[flat])
+
+
+def test_conv_gradient_of_one_hot_weights():
+    """With w = e_3 (the current token only) and no SiLU the conv is the identity:
+    dx = du and dw[:, 3] = sum_t du x (closed form), in every document."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((2, 9, 4))
+    du = rng.standard_normal((2, 9, 4))
+    w = np.zeros((4, 4))
+    w[:, 3] = 1.0
+    ds = np.zeros((2, 9), dtype=np.uint8)
+    ds[0, 4] = 1
+    dx, dw, db = oracle.causal_conv1d_bwd(x, w, du, None, ds, apply_silu=False)
+    assert np.allclose(dx, du, rtol=0, atol=1e-15)
+    assert np.allclose(dw[:, 3], np.einsum("bld,bld->d", du, x), rtol=1e-14, atol=1e-14)
+    assert np.allclose(db, du.sum(axis=(0, 1)), rtol=1e-14, atol=1e-14)
