@@ -20,8 +20,9 @@
  *       packing paragraph (recurrent state restarts at every document start).
  *
  * Further entry points: the two in one call (mamba_conv_scan_fwd), one-token
- * decode steps, and the backward pass of the per-channel scan
- * (mamba_selective_scan_bwd), each described at its declaration below.
+ * decode steps, and the backward passes of the conv and of the per-channel scan
+ * (mamba_causal_conv1d_bwd, mamba_selective_scan_bwd), each described at its
+ * declaration below.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -173,6 +174,35 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
                         const void* z, const float* delta_bias, const uint8_t* doc_start,
                         const float* initial_state, void* u, void* out, float* final_state,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Backward pass (training) of the conv: the gradients of sum(du * u)
+ * through mamba_causal_conv1d_fwd (same pages and sections as the forward).
+ * With acc_t = bias + sum_j w[3-j] x_{t-j} over the taps inside token t's
+ * document and dacc_t = du_t silu'(acc_t) (du_t when apply_silu == 0):
+ *   dx_s = sum_j dacc_{s+j} w[3-j] over the j with s inside (s+j)'s document,
+ *   dweight[:, 3-j] = sum_t dacc_t x_{t-j} over the same taps, dbias = sum_t dacc_t.
+ * Chained after mamba_selective_scan_bwd (whose du it takes) it completes the
+ * mixer core's backward: dx of x, the conv's weight and bias gradients. */
+
+/* Bytes of device workspace mamba_causal_conv1d_bwd needs (per-tile partial
+ * sums of the weight gradients: 20 bytes per channel per 48 tokens). */
+int mamba_causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, size_t* bytes);
+
+/* Conv backward.
+ *   x, weight, bias, doc_start, apply_silu, width, dtype: as the forward call
+ *              (no history before token 0: conv_state is not supported here).
+ *   du         (B, L, D)  gradient of the loss with respect to the conv output.
+ *   dx         (B, L, D)  written.
+ *   dweight    (D, 4) float32, written.
+ *   dbias      (D,) float32 or NULL (not computed).
+ *   workspace  at least mamba_causal_conv1d_bwd_workspace_bytes bytes, 256-byte
+ *              aligned, scratch.
+ * Outputs must not overlap each other, the inputs or the workspace.  Sums run
+ * in a fixed order (repeated calls give identical results). */
+int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
+                            const void* du, void* dx, float* dweight, float* dbias, int64_t batch, int64_t seqlen,
+                            int64_t dim, int32_t width, int32_t dtype, int32_t apply_silu, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ---- Backward pass (training) of the per-channel scan: the gradients of
  * sum(dout * out) through mamba_selective_scan_fwd, i.e. the adjoint of the

@@ -8,8 +8,9 @@ missing or the tensors are not on a GPU the calls raise.
     u = causal_conv1d_fwd(x, weight, bias, doc_start)                  # (B, L, D)
     out, h = selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, doc_start)
 
-    # gradients of sum(dout * out) for per-channel A (training)
+    # gradients of sum(dout * out) for per-channel A (training), then through the conv
     g = selective_scan_bwd(u, delta, A, B, C, dout, D, z, delta_bias, doc_start)
+    dx, dweight, dbias = causal_conv1d_bwd(x, weight, g["du"], bias, doc_start)
 
     # decode, one token per row, continuing the prefill above
     u_t = causal_conv1d_update(x_t, conv_state, weight, bias)          # (B, D)
@@ -33,6 +34,7 @@ __all__ = [
     "selective_state_update",
     "selective_scan_bwd",
     "scan_bwd_workspace_bytes",
+    "causal_conv1d_bwd",
     "MambaError",
     "MambaArgumentError",
     "library_path",
@@ -372,3 +374,42 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         _ptr(workspace, "workspace", dev, torch.uint8), workspace.numel(), _stream(dev))
     _lib.check(st, "mamba_selective_scan_bwd")
     return {k: g[k] for k in shapes}
+
+
+def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu: bool = True, workspace=None,
+                      dx=None, dweight=None, dbias=None):
+    """Gradients of sum(du * u) for u = causal_conv1d_fwd(x, weight, bias, doc_start,
+    apply_silu); see mamba_causal_conv1d_bwd.  Returns (dx, dweight (D, 4) float32,
+    dbias (D,) float32 or None when bias is None)."""
+    torch = _torch()
+    dev = _check_device(x)
+    if x.dim() != 3:
+        raise ValueError("x must be (B, L, D)")
+    Bt, L, Dm = x.shape
+    if weight.dim() == 3:
+        weight = weight.reshape(weight.shape[0], weight.shape[-1])
+    W = weight.shape[-1]
+    if doc_start is not None and doc_start.dtype == torch.bool:
+        doc_start = doc_start.to(torch.uint8)
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dweight is None:
+        dweight = torch.empty((Dm, W), dtype=torch.float32, device=dev)
+    if dbias is None and bias is not None:
+        dbias = torch.empty((Dm,), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.mamba_causal_conv1d_bwd_workspace_bytes(Bt, L, Dm, ctypes.byref(need)),
+               "mamba_causal_conv1d_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=dev)
+    st = lib.mamba_causal_conv1d_bwd(
+        _ptr(x, "x", dev), _ptr(weight, "weight", dev, torch.float32, (Dm, W)),
+        _ptr(bias, "bias", dev, torch.float32, (Dm,)),
+        _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(du, "du", dev, x.dtype, (Bt, L, Dm)), _ptr(dx, "dx", dev, x.dtype, (Bt, L, Dm)),
+        _ptr(dweight, "dweight", dev, torch.float32, (Dm, W)), _ptr(dbias, "dbias", dev, torch.float32, (Dm,)),
+        Bt, L, Dm, W, _dtype_code(x), int(bool(apply_silu)),
+        _ptr(workspace, "workspace", dev, torch.uint8), workspace.numel(), _stream(dev))
+    _lib.check(st, "mamba_causal_conv1d_bwd")
+    return dx, dweight, dbias

@@ -256,6 +256,59 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
     return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+int mamba_causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, size_t* bytes) {
+    if (!bytes) return MAMBA_ERR_INVALID_ARGUMENT;
+    *bytes = 0;
+    int64_t n;
+    if (!mul_ok(batch, seqlen, dim, &n) || dim > kMaxDim || batch > 65535) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (seqlen > kMaxSeqlen) return MAMBA_ERR_UNSUPPORTED;
+    *bytes = mamba::conv_bwd_workspace_bytes(batch, seqlen, dim);
+    return MAMBA_OK;
+}
+
+int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
+                            const void* du, void* dx, float* dweight, float* dbias, int64_t batch, int64_t seqlen,
+                            int64_t dim, int32_t width, int32_t dtype, int32_t apply_silu, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (batch < 0 || seqlen < 0 || dim < 0) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (width != 4) return MAMBA_ERR_UNSUPPORTED;
+    int64_t n;
+    if (!mul_ok(batch, seqlen, dim, &n) || dim > kMaxDim || batch > 65535) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (seqlen > kMaxSeqlen) return MAMBA_ERR_UNSUPPORTED;
+    if (n == 0) return MAMBA_OK;
+    if (!x || !weight || !du || !dx || !dweight) return MAMBA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(du, esz) || !aligned(dx, esz) || !aligned(weight, 4) || !aligned(dweight, 4) ||
+        (bias && !aligned(bias, 4)) || (dbias && !aligned(dbias, 4)))
+        return MAMBA_ERR_MISALIGNED;
+    const size_t act = static_cast<size_t>(n) * esz;
+    const size_t need = mamba::conv_bwd_workspace_bytes(batch, seqlen, dim);
+    if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;
+    const void* ins[] = {x, weight, bias, doc_start, du};
+    const size_t insz[] = {act, static_cast<size_t>(dim) * 16, static_cast<size_t>(dim) * 4,
+                           static_cast<size_t>(batch * seqlen), act};
+    const void* outs[] = {dx, dweight, dbias, workspace};
+    const size_t outsz[] = {act, static_cast<size_t>(dim) * 16, static_cast<size_t>(dim) * 4, need};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 5; ++i)
+            if (overlap(outs[o], outsz[o], ins[i], insz[i])) return MAMBA_ERR_INVALID_ARGUMENT;
+        for (int k = o + 1; k < 4; ++k)
+            if (overlap(outs[o], outsz[o], outs[k], outsz[k])) return MAMBA_ERR_INVALID_ARGUMENT;
+    }
+    mamba::ConvBwdArgs a;
+    a.x = x; a.weight = weight; a.bias = bias; a.doc_start = doc_start; a.du = du; a.dx = dx;
+    a.dweight = dweight; a.dbias = dbias; a.ws = static_cast<float*>(workspace);
+    a.batch = batch; a.seqlen = seqlen; a.dim = dim;
+    a.bf16 = dtype == MAMBA_DTYPE_BF16;
+    const int64_t vec = a.bf16 ? 8 : 4;
+    a.vectorized = (dim % vec) == 0 && aligned(x, 16) && aligned(du, 16) && aligned(dx, 16);
+    a.apply_silu = apply_silu != 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    return mamba::launch_causal_conv1d_bwd(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
 int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes) {
     if (!bytes) return MAMBA_ERR_INVALID_ARGUMENT;
     *bytes = 0;

@@ -1,0 +1,212 @@
+// Backward pass of the depthwise causal conv1d (width 4) + SiLU, gfx950.
+//
+// What it computes: the gradients of sum(du * u) through the forward of
+// conv1d.hip ("Mamba: Selective State Spaces (S6)" section of the Mamba skill
+// page; axolotl page: the conv state restarts at every document start).  With
+// acc_t = bias + sum_j w[3-j] x_{t-j} over the taps inside token t's document
+// and dacc_t = du_t silu'(acc_t) (du_t without SiLU):
+//     dx_s      = sum_{j=0..3} dacc_{s+j} w[3-j]   over the j with s inside (s+j)'s document
+//     dw[3-j]   = sum_t dacc_t x_{t-j}             over the same taps
+//     dbias     = sum_t dacc_t
+//
+// Mapping: as the forward, each thread owns VEC consecutive channels and a
+// tile of 48 tokens.  It walks the tile and the 3 tokens after it once,
+// recomputing acc from a 3-token history (cleared at document starts, primed
+// from the 3 tokens before the tile) and keeping the not yet complete dx of the
+// last 4 tokens in a shift register: token t adds dacc_t w[3-j] to dx_{t-j} for
+// the taps that stay inside its document, and dx_{t-3} is then final.  dw and
+// dbias are summed over the tile's own tokens into per-tile partials, which a
+// second kernel adds in a fixed order.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mamba {
+
+namespace {
+
+constexpr int kTile = 48;          // tokens per thread; kTile + 6 <= 64 for one ballot
+constexpr int kBlock = 256;
+
+template <typename T, int VEC, bool SILU>
+__global__ __launch_bounds__(kBlock) void conv1d_bwd_kernel(
+    const void* __restrict__ x, const float* __restrict__ weight, const float* __restrict__ bias,
+    const uint8_t* __restrict__ doc_start, const void* __restrict__ du, void* __restrict__ dx,
+    float* __restrict__ part, int64_t seqlen, int dim) {
+    const int ngroups = (dim + VEC - 1) / VEC;
+    const int grp = blockIdx.x * kBlock + threadIdx.x;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kTile;
+    const int64_t b = blockIdx.z;
+    const int64_t row = b * seqlen;
+
+    // Document starts of tokens t0-3 .. t0+kTile+2: bit i <-> token t0 - 3 + i.
+    const int lane = threadIdx.x & 63;
+    const int64_t tl = t0 - 3 + lane;
+    bool is_start = false;
+    if (lane < kTile + 6 && tl >= 0 && tl < seqlen)
+        is_start = tl == 0 || (doc_start != nullptr && doc_start[row + tl] != 0);
+    const uint64_t starts = __ballot(is_start);
+    if (grp >= ngroups) return;
+
+    const int d0 = grp * VEC;
+    float w0[VEC], w1[VEC], w2[VEC], w3[VEC], bs[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+        const float* wr = weight + 4 * (d0 + i);
+        w0[i] = wr[0]; w1[i] = wr[1]; w2[i] = wr[2]; w3[i] = wr[3];
+        bs[i] = bias ? bias[d0 + i] : 0.0f;
+    }
+
+    // History x_{t-1}, x_{t-2}, x_{t-3} restricted to token t's document.
+    float h1[VEC], h2[VEC], h3[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int64_t t = t0 - 3 + k;
+        if (t < 0) continue;
+        float xv[VEC];
+        VecIO<T, VEC>::load(x, (row + t) * dim + d0, xv);
+        const bool reset = (starts >> k) & 1ull;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            h3[i] = reset ? 0.0f : h2[i];
+            h2[i] = reset ? 0.0f : h1[i];
+            h1[i] = xv[i];
+        }
+    }
+
+    // p0..p3: the running dx of tokens t, t-1, t-2, t-3.
+    float p1[VEC], p2[VEC], p3[VEC];
+    float gw0[VEC], gw1[VEC], gw2[VEC], gw3[VEC], gb[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+        p1[i] = p2[i] = p3[i] = 0.0f;
+        gw0[i] = gw1[i] = gw2[i] = gw3[i] = gb[i] = 0.0f;
+    }
+    // Tokens since the latest document start before t0, capped at 3 (the row's
+    // token 0 is a start, so tiles at the row start need no special case).
+    int since = 3;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if ((starts >> k) & 1ull) since = 3 - k;
+    const int64_t own_end = (t0 + kTile < seqlen) ? t0 + kTile : seqlen;
+    for (int64_t t = t0; t < own_end + 3; ++t) {
+        const bool in_row = t < seqlen;
+        float xv[VEC], gv[VEC];
+        if (in_row) {
+            VecIO<T, VEC>::load(x, (row + t) * dim + d0, xv);
+            VecIO<T, VEC>::load(du, (row + t) * dim + d0, gv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) xv[i] = gv[i] = 0.0f;
+        }
+        if (in_row && ((starts >> (t - t0 + 3)) & 1ull)) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
+            since = 0;
+        }
+        const bool own = t < own_end;
+        const float m1 = since >= 1 ? 1.0f : 0.0f;
+        const float m2 = since >= 2 ? 1.0f : 0.0f;
+        const float m3 = since >= 3 ? 1.0f : 0.0f;
+        float out[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            float acc = __builtin_fmaf(w3[i], xv[i], bs[i]);
+            acc = __builtin_fmaf(w2[i], h1[i], acc);
+            acc = __builtin_fmaf(w1[i], h2[i], acc);
+            acc = __builtin_fmaf(w0[i], h3[i], acc);
+            float g = gv[i];
+            if constexpr (SILU) {
+                const float sg = rcp_fast(1.0f + exp2_fast(-acc * kLog2e));
+                g *= sg * __builtin_fmaf(acc, 1.0f - sg, 1.0f);
+            }
+            if (own) {
+                gb[i] += g;
+                gw3[i] = __builtin_fmaf(g, xv[i], gw3[i]);
+                gw2[i] = __builtin_fmaf(g, h1[i], gw2[i]);
+                gw1[i] = __builtin_fmaf(g, h2[i], gw1[i]);
+                gw0[i] = __builtin_fmaf(g, h3[i], gw0[i]);
+            }
+            // dx_{t-3} is complete after token t's tap; shift the others along.
+            out[i] = __builtin_fmaf(g * m3, w0[i], p3[i]);
+            p3[i] = __builtin_fmaf(g * m2, w1[i], p2[i]);
+            p2[i] = __builtin_fmaf(g * m1, w2[i], p1[i]);
+            p1[i] = g * w3[i];
+            h3[i] = h2[i];
+            h2[i] = h1[i];
+            h1[i] = xv[i];
+        }
+        since = since < 3 ? since + 1 : 3;
+        const int64_t s = t - 3;
+        if (s >= t0 && s < own_end) VecIO<T, VEC>::store(dx, (row + s) * dim + d0, out);
+    }
+    // Per-tile partials: [b][tile][5][D] (dw columns 0..3, then dbias).
+    const int64_t ntiles = gridDim.y;
+    float* pt = part + ((b * ntiles + blockIdx.y) * 5) * dim + d0;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+        if (d0 + i >= dim) break;
+        pt[i] = gw0[i];
+        pt[dim + i] = gw1[i];
+        pt[2 * dim + i] = gw2[i];
+        pt[3 * dim + i] = gw3[i];
+        pt[4 * dim + i] = gb[i];
+    }
+}
+
+// dweight (D, 4) and dbias (D,): sums of the per-tile partials.  16 threads per
+// output each add every 16th part; their sums are added in a fixed order.
+__global__ __launch_bounds__(256) void conv1d_bwd_reduce_kernel(const float* __restrict__ part, float* dweight,
+                                                                float* dbias, int64_t nparts, int dim) {
+    __shared__ float red[16][16];
+    const int64_t nout = 5 * static_cast<int64_t>(dim);
+    const int o = threadIdx.x & 15;
+    const int g = threadIdx.x >> 4;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 16 + o;
+    float s = 0.0f;
+    if (e < nout)
+        for (int64_t i = g; i < nparts; i += 16) s += part[i * nout + e];
+    red[g][o] = s;
+    __syncthreads();
+    if (g != 0 || e >= nout) return;
+    float tot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tot += red[k][o];
+    const int k = static_cast<int>(e / dim);
+    const int d = static_cast<int>(e % dim);
+    if (k < 4) dweight[static_cast<int64_t>(d) * 4 + k] = tot;
+    else if (dbias) dbias[d] = tot;
+}
+
+template <typename T, int VEC>
+hipError_t launch_conv_bwd_vec(const ConvBwdArgs& a) {
+    const int ngroups = static_cast<int>((a.dim + VEC - 1) / VEC);
+    const int64_t ntiles = (a.seqlen + kTile - 1) / kTile;
+    dim3 grid((ngroups + kBlock - 1) / kBlock, static_cast<unsigned>(ntiles), static_cast<unsigned>(a.batch));
+    if (a.apply_silu)
+        hipLaunchKernelGGL((conv1d_bwd_kernel<T, VEC, true>), grid, dim3(kBlock), 0, a.stream, a.x, a.weight,
+                           a.bias, a.doc_start, a.du, a.dx, a.ws, a.seqlen, static_cast<int>(a.dim));
+    else
+        hipLaunchKernelGGL((conv1d_bwd_kernel<T, VEC, false>), grid, dim3(kBlock), 0, a.stream, a.x, a.weight,
+                           a.bias, a.doc_start, a.du, a.dx, a.ws, a.seqlen, static_cast<int>(a.dim));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(conv1d_bwd_reduce_kernel, dim3(static_cast<unsigned>((5 * a.dim + 15) / 16)), dim3(256), 0,
+                       a.stream, static_cast<const float*>(a.ws), a.dweight, a.dbias, a.batch * ntiles,
+                       static_cast<int>(a.dim));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t conv_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim) {
+    return static_cast<size_t>(batch * ((seqlen + kTile - 1) / kTile) * 5 * dim) * sizeof(float);
+}
+
+hipError_t launch_causal_conv1d_bwd(const ConvBwdArgs& a) {
+    if (a.bf16) return a.vectorized ? launch_conv_bwd_vec<bf16_t, 8>(a) : launch_conv_bwd_vec<bf16_t, 1>(a);
+    return a.vectorized ? launch_conv_bwd_vec<float, 4>(a) : launch_conv_bwd_vec<float, 1>(a);
+}
+
+}  // namespace mamba

@@ -54,6 +54,52 @@ template <> struct Elem<bf16_t> {
     }
 };
 
+// VEC consecutive elements of one token row as floats: 16-byte vectors (8 bf16 or
+// 4 f32 channels) or single elements (ragged D, unaligned buffers).
+template <typename T, int VEC> struct VecIO;
+
+// bf16, 8 channels = 16 bytes
+template <> struct VecIO<bf16_t, 8> {
+    __device__ __forceinline__ static void load(const void* base, int64_t off, float (&v)[8]) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ __forceinline__ static void store(void* base, int64_t off, const float (&v)[8]) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+                   (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+};
+
+// f32, 4 channels = 16 bytes
+template <> struct VecIO<float, 4> {
+    __device__ __forceinline__ static void load(const void* base, int64_t off, float (&v)[4]) {
+        const float4 raw = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+        v[0] = raw.x; v[1] = raw.y; v[2] = raw.z; v[3] = raw.w;
+    }
+    __device__ __forceinline__ static void store(void* base, int64_t off, const float (&v)[4]) {
+        *reinterpret_cast<float4*>(static_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+// Any type, 1 channel (ragged D or unaligned buffers).
+template <typename T> struct VecIO<T, 1> {
+    __device__ __forceinline__ static void load(const void* base, int64_t off, float (&v)[1]) {
+        v[0] = Elem<T>::load(base, off);
+    }
+    __device__ __forceinline__ static void store(void* base, int64_t off, const float (&v)[1]) {
+        Elem<T>::store(base, off, v[0]);
+    }
+};
+
 // SiLU(v) = v * sigmoid(v) = v / (1 + 2^(-v log2 e)).  For very negative v the
 // exponential overflows to +inf and the reciprocal gives 0, so the result is -0.
 __device__ __forceinline__ float silu_f(float v) {

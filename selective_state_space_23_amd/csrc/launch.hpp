@@ -23,6 +23,27 @@ struct ConvArgs {
 
 hipError_t launch_causal_conv1d(const ConvArgs& a);
 
+// Backward of the conv (conv1d_bwd.hip): dx, dweight, dbias from du.
+struct ConvBwdArgs {
+    const void* x;
+    const float* weight;
+    const float* bias;        // or null
+    const uint8_t* doc_start;
+    const void* du;
+    void* dx;
+    float* dweight;           // (D, 4)
+    float* dbias;             // (D,) or null
+    float* ws;                // conv_bwd_workspace_bytes
+    int64_t batch, seqlen, dim;
+    bool bf16;
+    bool vectorized;          // 16-byte accesses: dim and pointers aligned
+    bool apply_silu;
+    hipStream_t stream;
+};
+
+size_t conv_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim);
+hipError_t launch_causal_conv1d_bwd(const ConvBwdArgs& a);
+
 struct ScanArgs {
     const void* u;
     const void* delta;

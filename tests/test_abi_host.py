@@ -246,3 +246,26 @@ def test_bwd_validation(lib):
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=32)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=0), u=None, dout=None) == _lib.MAMBA_OK   # empty: no-op
+
+
+def test_conv_bwd_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.mamba_causal_conv1d_bwd_workspace_bytes(2, 32768, 1536, ctypes.byref(n)) == _lib.MAMBA_OK
+    assert n.value == 2 * 683 * 5 * 1536 * 4
+    assert lib.mamba_causal_conv1d_bwd_workspace_bytes(-1, 8, 8, ctypes.byref(n)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+
+    def cb(x=FAKE, w=FAKE * 2, b=None, ds=None, du=FAKE * 3, dx=FAKE * 4, dw=FAKE * 5, db=None, B=1, L=64, D=16,
+           W=4, dtype=1, silu=1, ws=FAKE * 8, wsb=1 << 30):
+        return lib.mamba_causal_conv1d_bwd(x, w, b, ds, du, dx, dw, db, B, L, D, W, dtype, silu, ws, wsb, None)
+
+    assert cb(W=3) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert cb(dtype=5) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert cb(du=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert cb(dw=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert cb(dx=FAKE * 4 + 1) == _lib.MAMBA_ERR_MISALIGNED
+    assert cb(ws=FAKE * 8 + 4) == _lib.MAMBA_ERR_MISALIGNED
+    assert cb(wsb=4) == _lib.MAMBA_ERR_WORKSPACE
+    assert cb(dx=FAKE * 3) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # dx aliases du
+    assert cb(dw=FAKE * 4) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # dweight inside dx
+    assert cb(ws=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT              # workspace over x
+    assert cb(B=0, x=None, du=None) == _lib.MAMBA_OK                  # empty: no-op

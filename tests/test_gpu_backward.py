@@ -152,3 +152,94 @@ def test_bwd_workload(ssm, name):
     ref = oracle_bwd(inp, dout, channels=ch)
     for k in sorted(ref):
         assert_close(sub[k], ref[k], inp.dtype, f"{name} {k}")
+
+
+# ----------------------------------------------------------------------------
+# conv1d backward, alone and chained after the scan backward
+# ----------------------------------------------------------------------------
+CONV_BWD_CASES = [
+    # (batch, seqlen, dim, dtype, docs)
+    (2, 200, 64, "bf16", 20.0),       # 16-byte vectors, several 48-token tiles
+    (2, 131, 37, "bf16", 9.0),        # ragged D: one channel a thread
+    (1, 100, 36, "f32", 7.0),         # ragged D for f32 vectors
+    (3, 1, 24, "bf16", None),         # one token
+    (2, 3, 24, "bf16", 2.0),          # fewer tokens than the conv width
+    (1, 1000, 1536, "bf16", 64.0),
+    (2, 500, 64, "f32", None),
+]
+
+
+def conv_bwd_case(ssm, inp, du, silu=True, bias=True, channels=None):
+    dev = upload(inp)
+    got = ssm.causal_conv1d_bwd(dev["x"], dev["conv_w"], to_dev(du, inp.dtype), dev["conv_b"] if bias else None,
+                                dev["doc_start"], apply_silu=silu)
+    ch = np.arange(inp.x.shape[2]) if channels is None else np.asarray(channels)
+    ref = oracle.causal_conv1d_bwd(inp.x[:, :, ch], inp.conv_w[ch], du[:, :, ch], inp.conv_b[ch] if bias else None,
+                                   inp.doc_start, apply_silu=silu)
+    idx = torch_mod().from_numpy(ch).to(got[0].device)
+    assert_close(to_host(got[0].index_select(2, idx)), ref[0], inp.dtype, "dx")
+    assert_close(to_host(got[1].index_select(0, idx)), ref[1], inp.dtype, "dweight")
+    if bias:
+        assert_close(to_host(got[2].index_select(0, idx)), ref[2], inp.dtype, "dbias")
+    else:
+        assert got[2] is None
+
+
+@pytest.mark.parametrize("case", CONV_BWD_CASES, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("silu,bias", [(True, True), (False, False)])
+def test_conv_bwd_parity(ssm, case, silu, bias):
+    Bt, L, Dm, dt, docs = case
+    inp = make_custom(Bt, L, Dm, 4, dtype=dt, docs=docs, seed=830 + L + Dm)
+    inp.conv_b[:] = np.linspace(-0.3, 0.3, Dm).astype(np.float32)
+    du = make_cotangent(Bt, L, Dm, dtype=dt, seed=930 + L)
+    conv_bwd_case(ssm, inp, du, silu, bias)
+
+
+def test_conv_bwd_documents_at_tile_edges(ssm):
+    """Document starts on, one before and one after the 48-token tile edges, and
+    within the 3 tokens that a tile reads past its end."""
+    L = 300
+    inp = make_custom(2, L, 64, 4, dtype="f32", docs=None, seed=831)
+    inp.doc_start[:] = 0
+    for t in (47, 48, 49, 50, 51, 95, 96, 97, 143, 144, 145, 146, 147, 149, 191, 299):
+        inp.doc_start[0, t] = 1
+    for t in range(1, L, 3):
+        inp.doc_start[1, t] = 1
+    du = make_cotangent(2, L, 64, dtype="f32", seed=931)
+    conv_bwd_case(ssm, inp, du)
+
+
+def test_conv_bwd_workload(ssm):
+    inp = make_inputs("packed_32k")
+    Bt, L, Dm = inp.x.shape
+    print(f"[conv bwd] packed_32k shape={inp.x.shape}", flush=True)
+    du = make_cotangent(Bt, L, Dm, dtype=inp.dtype, seed=932)
+    conv_bwd_case(ssm, inp, du, channels=[0, 7, 8, 700, 1535])
+
+
+def test_mixer_core_backward_chain(ssm):
+    """conv forward -> scan backward -> conv backward on the GPU against the same
+    chain in the oracle: dx, the conv's weight and bias gradients, and the scan's
+    parameter gradients of the whole conv + scan forward."""
+    inp = make_custom(2, 700, 96, 16, dtype="bf16", docs=120.0, seed=833)
+    inp.conv_b[:] = np.linspace(-0.2, 0.2, 96).astype(np.float32)
+    Bt, L, Dm = inp.x.shape
+    dout = make_cotangent(Bt, L, Dm, dtype="bf16", seed=933)
+    dev = upload(inp)
+    u = ssm.causal_conv1d_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["doc_start"])
+    g = ssm.selective_scan_bwd(u, dev["delta"], dev["A"], dev["B"], dev["C"], to_dev(dout, "bf16"), dev["D"],
+                               dev["z"], dev["delta_bias"], dev["doc_start"])
+    dx, dw, db = ssm.causal_conv1d_bwd(dev["x"], dev["conv_w"], g["du"], dev["conv_b"], dev["doc_start"])
+    # oracle: u is stored in bf16 by the forward, which the scan then reads
+    u_ref = bf16_round(oracle.causal_conv1d(inp.x, inp.conv_w, inp.conv_b, inp.doc_start).astype(np.float32))
+    gr = oracle.selective_scan_bwd(u_ref, inp.delta, inp.A, inp.B, inp.C, dout, D=inp.D, z=inp.z,
+                                   delta_bias=inp.delta_bias, doc_start=inp.doc_start)
+    # and du is stored in bf16 between the two backward calls: the same boundary
+    # rounding (the weight gradients sum ~1400 tokens of du and would show it)
+    du_r = bf16_round(gr["du"].astype(np.float32))
+    dx_r, dw_r, db_r = oracle.causal_conv1d_bwd(inp.x, inp.conv_w, du_r, inp.conv_b, inp.doc_start)
+    assert_close(to_host(dx), dx_r, "bf16", "chain dx")
+    assert_close(to_host(dw), dw_r, "bf16", "chain dweight")
+    assert_close(to_host(db), db_r, "bf16", "chain dbias")
+    for k in ("dA", "dB", "dC", "dD", "dz", "ddelta", "ddelta_bias"):
+        assert_close(to_host(g[k]), gr[k], "bf16", f"chain {k}")
