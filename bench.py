@@ -84,6 +84,12 @@ def bwd_bytes(B, L, D, N, esz):
     return B * L * per_token + 4 * 2 * (D * N + 3 * D)
 
 
+def conv_bwd_bytes(B, L, D, esz):
+    """Algorithmic HBM bytes of one conv backward call: x and du read, dx written,
+    doc flags, weights and their gradients."""
+    return B * L * (3 * esz * D + 1) + D * 10 * 4
+
+
 def bwd_alu_flop_eq(B, L, D, N):
     """Algorithmic fp32 VALU work of the backward in flop-equivalents (slots as in
     scan_alu_flop_eq).  Per (t, d, n): the decay (dt*A + exp = 5), the state
@@ -313,12 +319,14 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-METRIC_BWD = "selective-scan bwd tokens/s, B=2 L=32K D=1536 N=16 bf16"
+METRIC_BWD = "conv + selective-scan bwd tokens/s, B=2 L=32K D=1536 N=16 bf16"
 
 
 def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
-    """One step = one backward call (gradients of sum(dout * out) with respect to
-    u, delta, A, B, C, D, z and delta_bias), u = the workload's x."""
+    """One step = the mixer core's backward: mamba_selective_scan_bwd (gradients of
+    sum(dout * out) with respect to u, delta, A, B, C, D, z and delta_bias, u being
+    the conv output the forward stores) then mamba_causal_conv1d_bwd (dx and the
+    conv's weight and bias gradients from du)."""
     from gpu_helpers import to_dev
     from workloads import make_cotangent
 
@@ -332,30 +340,45 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
     ws = torch.empty(ssm.scan_bwd_workspace_bytes(B, L, D, N, inp.dtype), dtype=torch.uint8, device=dev)
     grads = {}
 
-    def step():
-        g = ssm.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dout, t["D"], t["z"],
+    # u as the forward leaves it (the conv output, stored in the I/O dtype)
+    u = ssm.causal_conv1d_fwd(t["x"], t["conv_w"], t["conv_b"], t["doc_start"])
+    ws_conv = torch.empty(ssm.conv_bwd_workspace_bytes(B, L, D), dtype=torch.uint8, device=dev)
+    conv_grads = {}
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        g = ssm.selective_scan_bwd(u, t["delta"], t["A"], t["B"], t["C"], dout, t["D"], t["z"],
                                    t["delta_bias"], t["doc_start"], workspace=ws, grads=grads)
         grads.update(g)
+        if ev is not None:
+            ev[1].record()
+        dx, dw, db = ssm.causal_conv1d_bwd(t["x"], t["conv_w"], grads["du"], t["conv_b"], t["doc_start"],
+                                           workspace=ws_conv, dx=conv_grads.get("dx"),
+                                           dweight=conv_grads.get("dw"), dbias=conv_grads.get("db"))
+        conv_grads.update(dx=dx, dw=dw, db=db)
+        if ev is not None:
+            ev[2].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        events[i][0].record()
-        step()
-        events[i][1].record()
+        step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    conv_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     probe = copy_probe(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
     csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
     traffic = recorded_traffic(os.path.join(ROOT, "profiles", f"bwd_{args.config}_hbm_traffic.txt"),
                                [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))])
     flops = bwd_alu_flop_eq(B, L, D, N)
     nbytes = bwd_bytes(B, L, D, N, esz)
+    cbytes = conv_bwd_bytes(B, L, D, esz)
     tflops = flops / (call_ms * 1e-3) / 1e12
     gbs = nbytes / (call_ms * 1e-3) / 1e9
     result = {
@@ -373,6 +396,9 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
         "data": "synthetic",
         "config": {"workload": args.config, "batch": B, "seqlen": L, "dim": D, "dstate": N, "nheads": 0,
                    "doc_mean_len": spec["docs"], "io_dtype": inp.dtype, "state_dtype": "f32", "path": "bwd"},
+        "timings": {"scan_bwd_ms": call_ms, "conv_bwd_ms": conv_ms,
+                    "conv_bwd_hbm_GBs": cbytes / (conv_ms * 1e-3) / 1e9,
+                    "conv_bwd_hbm_frac": cbytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "roofline": {"kernel": "mamba_selective_scan_bwd, one call: forward aggregate and carry, reverse aggregate "
                                "and carry, main pass, reductions",
                      "bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -387,7 +413,8 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
 
 
 def cpu_baseline_bwd(inp, dout_seed, tokens_per_row):
-    """Time the fp64 oracle gradients (as they stand) on the first tokens of every row."""
+    """Time the fp64 oracle gradients (scan, then conv; as they stand) on the first
+    tokens of every row."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -399,8 +426,10 @@ def cpu_baseline_bwd(inp, dout_seed, tokens_per_row):
     dout = make_cotangent(B, L, D, dtype=inp.dtype, seed=dout_seed)[:, sl]
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        oracle.selective_scan_bwd(inp.x[:, sl], inp.delta[:, sl], inp.A, inp.B[:, sl], inp.C[:, sl], dout,
-                                  D=inp.D, z=inp.z[:, sl], delta_bias=inp.delta_bias, doc_start=inp.doc_start[:, sl])
+        g = oracle.selective_scan_bwd(inp.x[:, sl], inp.delta[:, sl], inp.A, inp.B[:, sl], inp.C[:, sl], dout,
+                                      D=inp.D, z=inp.z[:, sl], delta_bias=inp.delta_bias,
+                                      doc_start=inp.doc_start[:, sl])
+        oracle.causal_conv1d_bwd(inp.x[:, sl], inp.conv_w, g["du"], inp.conv_b, inp.doc_start[:, sl])
         dt = time.perf_counter() - t0
     ntok = B * T
     return dict(value=ntok / dt, unit="tokens/s", cores=1, kind="oracle",

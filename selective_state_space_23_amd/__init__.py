@@ -35,6 +35,7 @@ __all__ = [
     "selective_scan_bwd",
     "scan_bwd_workspace_bytes",
     "causal_conv1d_bwd",
+    "conv_bwd_workspace_bytes",
     "MambaError",
     "MambaArgumentError",
     "library_path",
@@ -374,6 +375,13 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         _ptr(workspace, "workspace", dev, torch.uint8), workspace.numel(), _stream(dev))
     _lib.check(st, "mamba_selective_scan_bwd")
     return {k: g[k] for k in shapes}
+
+
+def conv_bwd_workspace_bytes(batch, seqlen, dim) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().mamba_causal_conv1d_bwd_workspace_bytes(batch, seqlen, dim, ctypes.byref(n)),
+               "mamba_causal_conv1d_bwd_workspace_bytes")
+    return int(n.value)
 
 
 def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu: bool = True, workspace=None,

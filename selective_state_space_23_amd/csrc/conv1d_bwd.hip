@@ -90,16 +90,27 @@ __global__ __launch_bounds__(kBlock) void conv1d_bwd_kernel(
     for (int k = 0; k < 3; ++k)
         if ((starts >> k) & 1ull) since = 3 - k;
     const int64_t own_end = (t0 + kTile < seqlen) ? t0 + kTile : seqlen;
-    for (int64_t t = t0; t < own_end + 3; ++t) {
-        const bool in_row = t < seqlen;
-        float xv[VEC], gv[VEC];
-        if (in_row) {
+    // x and du of the next token are fetched while the current one computes.
+    auto fetch = [&](int64_t t, float (&xv)[VEC], float (&gv)[VEC]) {
+        if (t < seqlen) {
             VecIO<T, VEC>::load(x, (row + t) * dim + d0, xv);
             VecIO<T, VEC>::load(du, (row + t) * dim + d0, gv);
         } else {
 #pragma unroll
             for (int i = 0; i < VEC; ++i) xv[i] = gv[i] = 0.0f;
         }
+    };
+    float xn[VEC], gn[VEC];
+    fetch(t0, xn, gn);
+    for (int64_t t = t0; t < own_end + 3; ++t) {
+        const bool in_row = t < seqlen;
+        float xv[VEC], gv[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            xv[i] = xn[i];
+            gv[i] = gn[i];
+        }
+        fetch(t + 1, xn, gn);
         if (in_row && ((starts >> (t - t0 + 3)) & 1ull)) {
 #pragma unroll
             for (int i = 0; i < VEC; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
@@ -155,24 +166,33 @@ __global__ __launch_bounds__(kBlock) void conv1d_bwd_kernel(
     }
 }
 
-// dweight (D, 4) and dbias (D,): sums of the per-tile partials.  16 threads per
-// output each add every 16th part; their sums are added in a fixed order.
-__global__ __launch_bounds__(256) void conv1d_bwd_reduce_kernel(const float* __restrict__ part, float* dweight,
-                                                                float* dbias, int64_t nparts, int dim) {
-    __shared__ float red[16][16];
+// dweight (D, 4) and dbias (D,): sums of the per-tile partials.  A block of 1024
+// threads covers 64 consecutive outputs (coalesced 256-byte rows) with 16
+// threads each; thread g adds the parts g, g + 16, ... with two accumulators,
+// and the 16 sums are added in a fixed order.
+__global__ __launch_bounds__(1024) void conv1d_bwd_reduce_kernel(const float* __restrict__ part, float* dweight,
+                                                                 float* dbias, int64_t nparts, int dim) {
+    constexpr int kGroups = 16;
+    __shared__ float red[kGroups][64];
     const int64_t nout = 5 * static_cast<int64_t>(dim);
-    const int o = threadIdx.x & 15;
-    const int g = threadIdx.x >> 4;
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 16 + o;
-    float s = 0.0f;
-    if (e < nout)
-        for (int64_t i = g; i < nparts; i += 16) s += part[i * nout + e];
-    red[g][o] = s;
+    const int o = threadIdx.x & 63;
+    const int g = threadIdx.x >> 6;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 64 + o;
+    float s0 = 0.0f, s1 = 0.0f;
+    if (e < nout) {
+        int64_t i = g;
+        for (; i + kGroups < nparts; i += 2 * kGroups) {
+            s0 += part[i * nout + e];
+            s1 += part[(i + kGroups) * nout + e];
+        }
+        if (i < nparts) s0 += part[i * nout + e];
+    }
+    red[g][o] = s0 + s1;
     __syncthreads();
     if (g != 0 || e >= nout) return;
     float tot = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) tot += red[k][o];
+    for (int k = 0; k < kGroups; ++k) tot += red[k][o];
     const int k = static_cast<int>(e / dim);
     const int d = static_cast<int>(e % dim);
     if (k < 4) dweight[static_cast<int64_t>(d) * 4 + k] = tot;
@@ -192,7 +212,7 @@ hipError_t launch_conv_bwd_vec(const ConvBwdArgs& a) {
                            a.bias, a.doc_start, a.du, a.dx, a.ws, a.seqlen, static_cast<int>(a.dim));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(conv1d_bwd_reduce_kernel, dim3(static_cast<unsigned>((5 * a.dim + 15) / 16)), dim3(256), 0,
+    hipLaunchKernelGGL(conv1d_bwd_reduce_kernel, dim3(static_cast<unsigned>((5 * a.dim + 63) / 64)), dim3(1024), 0,
                        a.stream, static_cast<const float*>(a.ws), a.dweight, a.dbias, a.batch * ntiles,
                        static_cast<int>(a.dim));
     return hipGetLastError();
@@ -204,8 +224,10 @@ size_t conv_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim) {
     return static_cast<size_t>(batch * ((seqlen + kTile - 1) / kTile) * 5 * dim) * sizeof(float);
 }
 
+// Vectors of 4 channels for either dtype (8 bf16 channels a thread need ~170
+// VGPRs for the history, pending-dx and gradient registers: 2 waves per SIMD).
 hipError_t launch_causal_conv1d_bwd(const ConvBwdArgs& a) {
-    if (a.bf16) return a.vectorized ? launch_conv_bwd_vec<bf16_t, 8>(a) : launch_conv_bwd_vec<bf16_t, 1>(a);
+    if (a.bf16) return a.vectorized ? launch_conv_bwd_vec<bf16_t, 4>(a) : launch_conv_bwd_vec<bf16_t, 1>(a);
     return a.vectorized ? launch_conv_bwd_vec<float, 4>(a) : launch_conv_bwd_vec<float, 1>(a);
 }
 

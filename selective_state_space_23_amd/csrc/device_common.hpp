@@ -55,7 +55,8 @@ template <> struct Elem<bf16_t> {
 };
 
 // VEC consecutive elements of one token row as floats: 16-byte vectors (8 bf16 or
-// 4 f32 channels) or single elements (ragged D, unaligned buffers).
+// 4 f32 channels), 8-byte vectors (4 bf16 channels) or single elements (ragged
+// D, unaligned buffers).
 template <typename T, int VEC> struct VecIO;
 
 // bf16, 8 channels = 16 bytes
@@ -76,6 +77,22 @@ template <> struct VecIO<bf16_t, 8> {
             w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
                    (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+};
+
+// bf16, 4 channels = 8 bytes
+template <> struct VecIO<bf16_t, 4> {
+    __device__ __forceinline__ static void load(const void* base, int64_t off, float (&v)[4]) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+        v[0] = __uint_as_float(raw.x << 16);
+        v[1] = __uint_as_float(raw.x & 0xffff0000u);
+        v[2] = __uint_as_float(raw.y << 16);
+        v[3] = __uint_as_float(raw.y & 0xffff0000u);
+    }
+    __device__ __forceinline__ static void store(void* base, int64_t off, const float (&v)[4]) {
+        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = make_uint2(lo, hi);
     }
 };
 
