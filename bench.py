@@ -125,6 +125,12 @@ def copy_probe(torch, dev, mib=1024, reps=5):
     return {"bytes_per_copy": 2 * n, "ms": ms, "GBs": 2 * n / (ms * 1e-3) / 1e9}
 
 
+# The kernel sources each timed path is compiled from: a recorded FETCH/WRITE
+# profile counts only while these files are unchanged.
+FWD_SOURCES = ["device_common.hpp", "launch.hpp", "conv1d.hip", "scan.hip", "ssd.hip"]
+BWD_SOURCES = ["device_common.hpp", "launch.hpp", "scan.hip", "scan_bwd.hip", "conv1d_bwd.hip"]
+
+
 def recorded_traffic(path, source_files):
     """HBM bytes per scan call from the committed FETCH_SIZE / WRITE_SIZE profile, or None
     when the kernel sources have changed since those counters were taken."""
@@ -259,7 +265,7 @@ def main():
     csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
     traffic = recorded_traffic(
         os.path.join(ROOT, "profiles", f"{args.path}_{args.config}_hbm_traffic.txt"),
-        [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))])
+        [os.path.join(csrc, f) for f in FWD_SOURCES])
 
     tokens = B * L
     sb = scan_bytes(B, L, D, N, H, esz)
@@ -375,7 +381,7 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
     probe = copy_probe(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
     csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
     traffic = recorded_traffic(os.path.join(ROOT, "profiles", f"bwd_{args.config}_hbm_traffic.txt"),
-                               [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))])
+                               [os.path.join(csrc, f) for f in BWD_SOURCES])
     flops = bwd_alu_flop_eq(B, L, D, N)
     nbytes = bwd_bytes(B, L, D, N, esz)
     cbytes = conv_bwd_bytes(B, L, D, esz)
