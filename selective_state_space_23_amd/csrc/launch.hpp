@@ -84,11 +84,11 @@ hipError_t launch_selective_scan(const ScanArgs& a);
 
 // Passes 1 and 2 of the per-channel scan into the given buffers (ws_P, ws_H each
 // (nchunks - 1) * B * D * N floats, dt_ws B * L * D floats, ckpt
-// B * ceil(L / 16) * (N + 2) * D floats): ws_P[c] then holds the state entering
-// chunk c + 1, ckpt the local state before every 16-token block.  Used by the
-// backward pass; no initial state.
+// B * ceil(L / 2^ck_shift) * (N + 2) * D floats): ws_P[c] then holds the state
+// entering chunk c + 1, ckpt the local state before every block of 2^ck_shift
+// tokens (ck_shift in 2..6).  Used by the backward pass; no initial state.
 hipError_t launch_scan_chunk_carries(const ScanArgs& a, const ScanPlan& plan, float* ws_P, float* ws_H, void* dt_ws,
-                                     float* ckpt);
+                                     float* ckpt, int ck_shift);
 
 // Backward of the per-channel scan (scan_bwd.hip).
 struct ScanBwdArgs {

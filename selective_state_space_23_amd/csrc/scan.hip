@@ -74,7 +74,8 @@ struct ScanKParams {
     void* dt_ws;              // (B, L, D), I/O dtype: step sizes from pass 1 for pass 3 (per-channel A)
     int64_t nslots;           // chunks with an aggregate slot (nchunks - 1)
     float* ckpt;              // DT32 only: [B][nk][N + 2][D] local checkpoints, see scan_chunk_kernel
-    int64_t nk;               // 16-token blocks per row
+    int64_t nk;               // checkpoints per row
+    int ck_shift;             // log2 of the tokens between checkpoints (3 or 4)
     int64_t seqlen;
     int64_t chunk_len;
     int dim;
@@ -130,7 +131,8 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, int byte_of
 //
 // DT32 (pass 1 for the backward pass only): dt is stored as float32 and used
 // unrounded, so the backward's recomputation sees the exact step sizes; and
-// before every 16-token block k of the chunk the pass stores a local checkpoint:
+// before every block k of 2^ck_shift tokens of the chunk the pass stores a local
+// checkpoint:
 // rows 0..N-1 of ckpt[b][k] the state reached from zero at the chunk start, row
 // N the sum of dt since the chunk start (or since the latest document start),
 // row N + 1 one if a document started since the chunk start.  The true state
@@ -290,8 +292,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     auto compute_group = [&](int64_t g0, const float (&cu)[G], const float (&cd)[G], const float (&cz)[G]) {
         const int off = static_cast<int>((g0 - t_begin) & (kWin - 1));
         if constexpr (DT32) {
-            if (((g0 - t_begin) & 15) == 0 && g0 < t_end && active) {
-                float* ck = p.ckpt + ((b * p.nk + g0 / 16) * (N + 2)) * p.dim + d;
+            if (((g0 - t_begin) & ((1 << p.ck_shift) - 1)) == 0 && g0 < t_end && active) {
+                float* ck = p.ckpt + ((b * p.nk + (g0 >> p.ck_shift)) * (N + 2)) * p.dim + d;
 #pragma unroll
                 for (int n = 0; n < N; ++n) ck[static_cast<int64_t>(n) * p.dim] = h[n];
                 ck[static_cast<int64_t>(N) * p.dim] = sum_dt;
@@ -585,7 +587,7 @@ hipError_t launch_heads_f32(const ScanArgs& a, const ScanPlan& plan) {
 // block (see DT32 above).  The backward pass starts from these.
 template <typename T, int N>
 hipError_t launch_carries_typed(const ScanArgs& a, const ScanPlan& plan, float* ws_P, float* ws_H, void* dt_ws,
-                                float* ckpt) {
+                                float* ckpt, int ck_shift) {
     ScanKParams p{};
     p.u = a.u; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = nullptr; p.z = nullptr;
     p.delta_bias = a.delta_bias; p.doc_start = a.doc_start; p.initial_state = nullptr;
@@ -593,7 +595,8 @@ hipError_t launch_carries_typed(const ScanArgs& a, const ScanPlan& plan, float* 
     const int64_t count = a.batch * a.dim * N;
     const int64_t nslots = plan.nchunks - 1;
     p.ws_P = ws_P; p.ws_H = ws_H; p.dt_ws = dt_ws; p.ckpt = ckpt;
-    p.nk = (a.seqlen + 15) / 16;
+    p.ck_shift = ck_shift;
+    p.nk = (a.seqlen + (1 << ck_shift) - 1) >> ck_shift;
     p.seqlen = a.seqlen; p.chunk_len = plan.chunk_len; p.dim = static_cast<int>(a.dim);
     p.nheads = 0; p.headdim = 0; p.nbatch = static_cast<int>(a.batch); p.softplus = a.softplus ? 1 : 0;
     p.nslots = nslots;
@@ -615,15 +618,15 @@ hipError_t launch_carries_typed(const ScanArgs& a, const ScanPlan& plan, float* 
 }  // namespace
 
 hipError_t launch_scan_chunk_carries(const ScanArgs& a, const ScanPlan& plan, float* ws_P, float* ws_H,
-                                     void* dt_ws, float* ckpt) {
-    if (a.nheads != 0 || a.initial_state != nullptr) return hipErrorInvalidValue;
+                                     void* dt_ws, float* ckpt, int ck_shift) {
+    if (a.nheads != 0 || a.initial_state != nullptr || ck_shift < 2 || ck_shift > 6) return hipErrorInvalidValue;
     switch (a.dstate) {
-        case 4: return a.bf16 ? launch_carries_typed<bf16_t, 4>(a, plan, ws_P, ws_H, dt_ws, ckpt)
-                              : launch_carries_typed<float, 4>(a, plan, ws_P, ws_H, dt_ws, ckpt);
-        case 8: return a.bf16 ? launch_carries_typed<bf16_t, 8>(a, plan, ws_P, ws_H, dt_ws, ckpt)
-                              : launch_carries_typed<float, 8>(a, plan, ws_P, ws_H, dt_ws, ckpt);
-        case 16: return a.bf16 ? launch_carries_typed<bf16_t, 16>(a, plan, ws_P, ws_H, dt_ws, ckpt)
-                               : launch_carries_typed<float, 16>(a, plan, ws_P, ws_H, dt_ws, ckpt);
+        case 4: return a.bf16 ? launch_carries_typed<bf16_t, 4>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift)
+                              : launch_carries_typed<float, 4>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift);
+        case 8: return a.bf16 ? launch_carries_typed<bf16_t, 8>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift)
+                              : launch_carries_typed<float, 8>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift);
+        case 16: return a.bf16 ? launch_carries_typed<bf16_t, 16>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift)
+                               : launch_carries_typed<float, 16>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift);
         default: return hipErrorInvalidValue;
     }
 }

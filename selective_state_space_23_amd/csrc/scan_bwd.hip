@@ -52,7 +52,12 @@ namespace {
 constexpr int kBlk = 256;              // 4 waves, 256 consecutive channels
 constexpr int kWaves = kBlk / 64;
 constexpr int kWin = 64;               // tokens per staged B/C window
-constexpr int kCk = 16;                // tokens per checkpoint block
+constexpr int kCk = 16;                // tokens per block of the main pass
+#ifndef MAMBA_BWD_CK_SHIFT
+#define MAMBA_BWD_CK_SHIFT 4           // checkpoints every 16 tokens (3, every 8, measured 4% slower)
+#endif
+constexpr int kCkShift = MAMBA_BWD_CK_SHIFT;
+constexpr int kCkEvery = 1 << kCkShift;
 constexpr int kPiece = 4;              // tokens per innermost recompute piece
 #ifndef MAMBA_BWD_WAVES_PER_EU
 #define MAMBA_BWD_WAVES_PER_EU 0        // 0: chosen per state count (bwd_waves_per_eu)
@@ -574,28 +579,36 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
             const int os = kb * kCk;
             float* sp = sP[buf];
             float ck0[NL], ck8[NL];
-            {
-                // local checkpoint + exp(A * sum dt) * (state entering the chunk)
-                const float* src = ck_lane + (s / kCk) * (N + 2) * p.dim;
+            // local checkpoint + exp(A * sum dt) * (state entering the chunk)
+            auto load_ck = [&](int64_t t, float (&h)[NL]) {
+                const float* src = ck_lane + (t >> kCkShift) * (N + 2) * p.dim;
                 const float cdt = src[static_cast<int64_t>(N) * p.dim];
                 const bool fresh = c == 0 || src[static_cast<int64_t>(N + 1) * p.dim] != 0.0f;
                 const float* hin = p.h_carry + (c > 0 ? c - 1 : 0) * count + my_slot;
                 if (fresh) {
 #pragma unroll
-                    for (int i = 0; i < NL; ++i) ck0[i] = src[static_cast<int64_t>(n0 + i) * p.dim];
+                    for (int i = 0; i < NL; ++i) h[i] = src[static_cast<int64_t>(n0 + i) * p.dim];
                 } else {
 #pragma unroll
                     for (int i = 0; i < NL; ++i)
-                        ck0[i] = __builtin_fmaf(exp2_fast(Al2[i] * cdt), hin[i],
-                                                src[static_cast<int64_t>(n0 + i) * p.dim]);
+                        h[i] = __builtin_fmaf(exp2_fast(Al2[i] * cdt), hin[i], src[static_cast<int64_t>(n0 + i) * p.dim]);
                 }
+            };
+            load_ck(s, ck0);
+            if constexpr (kCkEvery == 8) {
+                if (s + 8 < t_end) load_ck(s + 8, ck8);
+                else {
+#pragma unroll
+                    for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];   // unused: pieces 2, 3 are past the end
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];
+                advance4(ck8, s, os);
+                advance4(ck8, s + 4, os + 4);
+#pragma unroll
+                for (int i = 0; i < NL; ++i) ck8[i] = opaque(ck8[i]);
             }
-#pragma unroll
-            for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];
-            advance4(ck8, s, os);
-            advance4(ck8, s + 4, os + 4);
-#pragma unroll
-            for (int i = 0; i < NL; ++i) ck8[i] = opaque(ck8[i]);
             // Pieces last to first, one loop body (unrolling the four lets the
             // compiler interleave them and run out of registers).
 #pragma unroll 1
@@ -690,7 +703,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     const size_t count = static_cast<size_t>(batch * dim * dstate);
     const size_t slots = plan.nchunks > 1 ? static_cast<size_t>(plan.nchunks - 1) : 0;
     const size_t carry = align256(slots * count * sizeof(float));
-    const int64_t nk = (seqlen + kCk - 1) / kCk;
+    const int64_t nk = (seqlen + kCkEvery - 1) / kCkEvery;
     const int64_t cpb = kBlk / lanes_per_channel(dstate);
     const int64_t nblk = (dim + cpb - 1) / cpb;
     BwdLayout l;
@@ -716,7 +729,7 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     fa.bf16 = a.bf16; fa.softplus = a.softplus; fa.stream = a.stream;
     hipError_t e = launch_scan_chunk_carries(fa, plan, reinterpret_cast<float*>(ws + l.h_carry),
                                              reinterpret_cast<float*>(ws + l.h_agg), ws + l.dt,
-                                             reinterpret_cast<float*>(ws + l.ckpt));
+                                             reinterpret_cast<float*>(ws + l.ckpt), kCkShift);
     if (e != hipSuccess) return e;
 
     BwdKParams p{};
@@ -734,7 +747,7 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     p.chunk_len = plan.chunk_len;
     p.nchunks = plan.nchunks;
     p.nslots = plan.nchunks - 1;
-    p.nk = (a.seqlen + kCk - 1) / kCk;
+    p.nk = (a.seqlen + kCkEvery - 1) / kCkEvery;
     p.dim = static_cast<int>(a.dim);
     p.nbatch = static_cast<int>(a.batch);
     constexpr int G = lanes_per_channel(N);
