@@ -177,9 +177,11 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     constexpr bool kDtWs = !HEADS;
     const __amdgpu_buffer_rsrc_t dl_rs =
         make_rsrc(static_cast<const T*>((kDtWs && OUTPUT) ? p.dt_ws : p.delta) + b * L * nd, L * nd * kEsz);
+    // (DT32 with a null dt_ws: an empty resource, so the dt stores are dropped.)
     constexpr int kDtEsz = DT32 ? 4 : kEsz;
+    const bool dt_out = kDtWs && p.dt_ws != nullptr;
     const __amdgpu_buffer_rsrc_t dto_rs = make_rsrc(
-        static_cast<char*>(kDtWs ? p.dt_ws : p.out) + b * act_row * kDtEsz, kDtWs ? act_row * kDtEsz : 0);
+        dt_out ? static_cast<char*>(p.dt_ws) + b * act_row * kDtEsz : nullptr, dt_out ? act_row * kDtEsz : 0);
     const __amdgpu_buffer_rsrc_t z_rs =
         make_rsrc(HAS_Z ? static_cast<const T*>(p.z) + b * act_row : static_cast<const T*>(p.u), act_row * kEsz);
     const T* B_row = static_cast<const T*>(p.B) + b * L * N;

@@ -65,6 +65,9 @@ constexpr int kPiece = 4;              // tokens per innermost recompute piece
 #ifndef MAMBA_BWD_TOKEN_BARRIER
 #define MAMBA_BWD_TOKEN_BARRIER 1
 #endif
+#ifndef MAMBA_BWD_DT_WS
+#define MAMBA_BWD_DT_WS 1        // 1: pass 1 stores dt (fp32) for the later passes; 0: they recompute it from delta (6% slower)
+#endif
 #ifndef MAMBA_BWD_KEEP_NL
 #define MAMBA_BWD_KEEP_NL 4      // keep the recompute's decays in registers up to this many states a lane
 #endif
@@ -179,7 +182,15 @@ __device__ __forceinline__ uint64_t window_starts(const uint8_t* ds_row, int64_t
 
 // ---------------------------------------------------------------------------
 // 2. Reverse aggregate of chunk c = blockIdx.y + 1 (chunk 0 needs none).
-template <typename T, int N, bool HAS_Z>
+// dt of a token from its raw delta (the same fp32 arithmetic as the forward's
+// pass 1, so the value is bitwise the one pass 1 used).
+template <bool SOFTPLUS>
+__device__ __forceinline__ float step_size(float delta, float bias) {
+    const float v = delta + bias;
+    return SOFTPLUS ? softplus_f(v) : v;
+}
+
+template <typename T, int N, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(kBlk) void bwd_rev_aggregate_kernel(const BwdKParams p) {
     __shared__ float4 sC4[kWin * N / 4];
     float* sC = reinterpret_cast<float*>(sC4);
@@ -195,7 +206,10 @@ __global__ __launch_bounds__(kBlk) void bwd_rev_aggregate_kernel(const BwdKParam
     const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
     constexpr int kEsz = static_cast<int>(sizeof(T));
     const int64_t act_row = L * p.dim;
-    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(p.dt + b * act_row, act_row * 4);
+    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(MAMBA_BWD_DT_WS ? p.dt + b * act_row : nullptr,
+                                                   MAMBA_BWD_DT_WS ? act_row * 4 : 0);
+    const __amdgpu_buffer_rsrc_t dl_rs = make_rsrc(static_cast<const T*>(p.delta) + b * act_row, act_row * kEsz);
+    const float dbias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
     const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, act_row * kEsz);
     const __amdgpu_buffer_rsrc_t z_rs =
         make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, act_row * kEsz);
@@ -227,7 +241,8 @@ __global__ __launch_bounds__(kBlk) void bwd_rev_aggregate_kernel(const BwdKParam
             for (int k = 0; k < kPiece; ++k) {
                 const int64_t t = g0 + k >= w0 ? g0 + k : w0;
                 const int off = static_cast<int>((t * p.dim + dc) * kEsz);
-                dtv[k] = buf_load<float>(dt_rs, static_cast<int>((t * p.dim + dc) * 4));
+                if constexpr (MAMBA_BWD_DT_WS) dtv[k] = buf_load<float>(dt_rs, static_cast<int>((t * p.dim + dc) * 4));
+                else dtv[k] = step_size<SOFTPLUS>(buf_load<T>(dl_rs, off), dbias);
                 float dy = buf_load<T>(do_rs, off);
                 if constexpr (HAS_Z) dy *= silu_f(buf_load<T>(z_rs, off));
                 dyv[k] = dy;
@@ -351,7 +366,8 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
     const int64_t act_row = L * p.dim;
     const int64_t rb = act_row * kEsz;
     const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(static_cast<const T*>(p.u) + b * act_row, rb);
-    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(p.dt + b * act_row, act_row * 4);
+    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(MAMBA_BWD_DT_WS ? p.dt + b * act_row : nullptr,
+                                                   MAMBA_BWD_DT_WS ? act_row * 4 : 0);
     const __amdgpu_buffer_rsrc_t dl_rs = make_rsrc(static_cast<const T*>(p.delta) + b * act_row, rb);
     const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, rb);
     const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, rb);
@@ -405,7 +421,8 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
     // so that each recompute level evaluates its own exponentials.
     auto load_dtu = [&](int64_t t, float& dt, float& uu) {
         const int so = tok_soff(t);
-        dt = buf_load_s<float>(dt_rs, dc * 4, so * (4 / kEsz));
+        if constexpr (MAMBA_BWD_DT_WS) dt = buf_load_s<float>(dt_rs, dc * 4, so * (4 / kEsz));
+        else dt = step_size<SOFTPLUS>(buf_load_s<T>(dl_rs, lane_off, so), dbias);
         uu = buf_load_s<T>(u_rs, lane_off, so);
         dt = opaque(t < t_end ? dt : 0.0f);
         uu = active ? uu : 0.0f;
@@ -712,7 +729,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     l.g_carry = l.h_agg + carry;
     l.p_rev = l.g_carry + carry;
     l.dt = l.p_rev + carry;
-    l.ckpt = l.dt + align256(static_cast<size_t>(batch * seqlen * dim) * sizeof(float));
+    l.ckpt = l.dt + (MAMBA_BWD_DT_WS ? align256(static_cast<size_t>(batch * seqlen * dim) * sizeof(float)) : 0);
     l.part_bc = l.ckpt + align256(static_cast<size_t>(batch * nk * (dstate + 2) * dim) * sizeof(float));
     l.part_w = l.part_bc + align256(static_cast<size_t>(batch * seqlen * nblk * 2 * dstate) * sizeof(float));
     l.total = l.part_w + align256(static_cast<size_t>(batch * plan.nchunks * (dstate + 2) * dim) * sizeof(float));
@@ -728,7 +745,7 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     fa.batch = a.batch; fa.seqlen = a.seqlen; fa.dim = a.dim; fa.dstate = N; fa.nheads = 0;
     fa.bf16 = a.bf16; fa.softplus = a.softplus; fa.stream = a.stream;
     hipError_t e = launch_scan_chunk_carries(fa, plan, reinterpret_cast<float*>(ws + l.h_carry),
-                                             reinterpret_cast<float*>(ws + l.h_agg), ws + l.dt,
+                                             reinterpret_cast<float*>(ws + l.h_agg), MAMBA_BWD_DT_WS ? ws + l.dt : nullptr,
                                              reinterpret_cast<float*>(ws + l.ckpt), kCkShift);
     if (e != hipSuccess) return e;
 
@@ -758,8 +775,13 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
 
     if (p.nslots > 0) {
         dim3 g2(gx, static_cast<unsigned>(p.nslots), static_cast<unsigned>(a.batch));
-        if (a.z) hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, true>), g2, dim3(kBlk), 0, a.stream, p);
-        else hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, false>), g2, dim3(kBlk), 0, a.stream, p);
+        if (a.z) {
+            if (a.softplus) hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, true, true>), g2, dim3(kBlk), 0, a.stream, p);
+            else hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, true, false>), g2, dim3(kBlk), 0, a.stream, p);
+        } else {
+            if (a.softplus) hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, false, true>), g2, dim3(kBlk), 0, a.stream, p);
+            else hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, false, false>), g2, dim3(kBlk), 0, a.stream, p);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(bwd_rev_carry_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0,
