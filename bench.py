@@ -184,9 +184,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768, help="oracle sample: tokens per row")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the device copy probe (0: skip)")
-    ap.add_argument("--path", choices=("fused", "split", "bwd"), default="fused",
+    ap.add_argument("--path", choices=("fused", "split", "bwd", "decode"), default="fused",
                     help="fused: one mamba_conv_scan_fwd call per step; split: conv call, then scan call; "
-                         "bwd: one mamba_selective_scan_bwd call per step (per-channel A workloads)")
+                         "bwd: scan backward then conv backward (per-channel A workloads); "
+                         "decode: one token per row (conv window update + recurrence step)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -225,6 +226,8 @@ def main():
 
     if args.path == "bwd":
         return bench_bwd(args, torch, np, ssm, inp, t, spec, dev)
+    if args.path == "decode":
+        return bench_decode(args, torch, np, ssm, inp, t, spec, dev)
     fused = args.path == "fused"
 
     def step(ev=None):
@@ -326,6 +329,123 @@ def main():
 
 
 METRIC_BWD = "conv + selective-scan bwd tokens/s, B=2 L=32K D=1536 N=16 bf16"
+
+
+def bench_decode(args, torch, np, ssm, inp, t, spec, dev, tokens=64, graphs_per_run=None):
+    """One step = one token for every row: mamba_conv_state_update (the conv
+    window update and the recurrence step in one launch) on the workload's rows
+    and channels, state and window updated in place.  The timed loop replays a
+    HIP graph that holds `tokens` consecutive steps (the steps are launch-bound);
+    the eager rate (Python marshalling included) and the two-launch step
+    (mamba_causal_conv1d_update, then mamba_selective_state_update) are reported
+    beside it."""
+    B, L, D = inp.x.shape
+    N = inp.B.shape[-1]
+    H = inp.nheads
+    esz = 2 if inp.dtype == "bf16" else 4
+    T = min(tokens, L)
+    # per-step inputs as (T, B, ...) so every step's slice is contiguous
+    xs = t["x"][:, :T].transpose(0, 1).contiguous()
+    zs = t["z"][:, :T].transpose(0, 1).contiguous()
+    dls = t["delta"][:, :T].transpose(0, 1).contiguous()
+    Bs = t["B"][:, :T].transpose(0, 1).contiguous()
+    Cs = t["C"][:, :T].transpose(0, 1).contiguous()
+    rs = t["doc_start"][:, :T].transpose(0, 1).contiguous()
+    rs[0].fill_(1)
+    state = torch.zeros((B, D, N), dtype=torch.float32, device=dev)
+    cstate = torch.zeros((B, D, 3), dtype=t["x"].dtype, device=dev)
+    us = torch.empty((T, B, D), dtype=t["x"].dtype, device=dev)
+    outs = torch.empty((T, B, D), dtype=t["x"].dtype, device=dev)
+
+    def steps_two():
+        for k in range(T):
+            ssm.causal_conv1d_update(xs[k], cstate, t["conv_w"], t["conv_b"], reset=rs[k], out=us[k])
+            ssm.selective_state_update(state, us[k], dls[k], t["A"], Bs[k], Cs[k], t["D"], zs[k], t["delta_bias"],
+                                       reset=rs[k], out=outs[k])
+
+    def steps():
+        for k in range(T):
+            ssm.conv_state_update(xs[k], cstate, t["conv_w"], t["conv_b"], state, dls[k], t["A"], Bs[k], Cs[k],
+                                  t["D"], zs[k], t["delta_bias"], reset=rs[k], out=outs[k])
+
+    def graph_of(fn):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()                     # warm-up on the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
+    for _ in range(3):
+        steps()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        steps()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / (5 * T)
+
+    # the two-launch step, for comparison
+    g2 = graph_of(steps_two)
+    for _ in range(args.warmup):
+        g2.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(max(args.steps, 1)):
+        g2.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    two_us = e0.elapsed_time(e1) * 1e3 / (max(args.steps, 1) * T)
+
+    g = graph_of(steps)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 1)
+    e0.record()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = e0.elapsed_time(e1) * 1e3 / (reps * T)
+    ms_per_step = wall * 1e3 / (reps * T)
+    # algorithmic bytes of one step: state and conv window read and written,
+    # the token's x, delta, z, B, C read, u and out written, the parameters read
+    nd = H if H else D
+    nbytes = (2 * B * D * N * 4 + 2 * B * D * 3 * esz + B * (3 * D + nd + 2 * N) * esz + 2 * B * D * esz
+              + 4 * ((H if H else D * N) + 2 * D + nd + 4 * D) + B)
+    gbs = nbytes / (step_us * 1e-6) / 1e9
+    result = {
+        "metric": f"selective-scan decode tokens/s, B={B} D={D} N={N} {inp.dtype} (one token per row per step)",
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": reps * T,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inp.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.config, "batch": B, "dim": D, "dstate": N, "nheads": H, "io_dtype": inp.dtype,
+                   "path": "decode", "tokens_per_graph": T},
+        "timings": {"graph_step_us": step_us, "eager_step_us": eager_us, "two_launch_graph_step_us": two_us},
+        "roofline": {"kernel": "one decode step: mamba_conv_state_update, one launch (HIP graph replay)",
+                     "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": nbytes,
+                     "avg_ms": step_us * 1e-3,
+                     "note": "launch-bound: one launch of a few microseconds per token"},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):

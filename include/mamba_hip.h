@@ -279,6 +279,22 @@ int mamba_selective_state_update(const mamba_scan_dims_t* dims, float* state, co
                                  const float* D, const void* z, const float* delta_bias,
                                  const uint8_t* reset, void* out, void* stream);
 
+/* Both decode steps in one launch: mamba_causal_conv1d_update (width 4,
+ * apply_silu = 1) followed by mamba_selective_state_update on its output, with
+ * identical results (u is rounded to the I/O dtype between the two, as the
+ * separate steps store it).
+ *   dims, state, delta, A, B, C, D, z, delta_bias, reset, out: as
+ *              mamba_selective_state_update.
+ *   x          (B, D)     the token's conv input.
+ *   conv_state (B, D, 3)  the window, I/O dtype, updated in place.
+ *   conv_weight (D, 4), conv_bias (D,) or NULL: float32.
+ *   u_out      (B, D) or NULL: the conv output, when the caller wants it.
+ * The window and u_out may overlap nothing else of the call. */
+int mamba_conv_state_update(const mamba_scan_dims_t* dims, const void* x, void* conv_state, const float* conv_weight,
+                            const float* conv_bias, float* state, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z, const float* delta_bias,
+                            const uint8_t* reset, void* u_out, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,8 @@ missing or the tensors are not on a GPU the calls raise.
     # decode, one token per row, continuing the prefill above
     u_t = causal_conv1d_update(x_t, conv_state, weight, bias)          # (B, D)
     out_t = selective_state_update(h, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias)
+    # or both in one launch
+    out_t = conv_state_update(x_t, conv_state, weight, bias, h, delta_t, A, B_t, C_t, D, z_t, delta_bias)
 """
 
 from __future__ import annotations
@@ -32,6 +34,7 @@ __all__ = [
     "conv_scan_fwd",
     "causal_conv1d_update",
     "selective_state_update",
+    "conv_state_update",
     "selective_scan_bwd",
     "scan_bwd_workspace_bytes",
     "causal_conv1d_bwd",
@@ -320,6 +323,40 @@ def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16") -> int:
     _lib.check(_lib.load().mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)),
                "mamba_selective_scan_bwd_workspace_bytes")
     return int(n.value)
+
+
+def conv_state_update(x, conv_state, conv_weight, conv_bias, state, delta, A, B, C, D=None, z=None, delta_bias=None,
+                      reset=None, delta_softplus: bool = True, out=None, u_out=None):
+    """Both decode steps in one launch; see mamba_conv_state_update.  x (B, D);
+    conv_state (B, D, 3) and state (B, D, N) updated in place; the rest as
+    selective_state_update.  Returns out (B, D) (u is written to u_out if given)."""
+    torch = _torch()
+    dev = _check_device(x)
+    if x.dim() != 2:
+        raise ValueError("x must be (B, D)")
+    Bt, Dm = x.shape
+    N = B.shape[-1]
+    nheads = A.shape[0] if A.dim() == 1 else 0
+    nd = nheads if nheads else Dm
+    if conv_weight.dim() == 3:
+        conv_weight = conv_weight.reshape(conv_weight.shape[0], conv_weight.shape[-1])
+    if reset is not None and reset.dtype == torch.bool:
+        reset = reset.to(torch.uint8)
+    if out is None:
+        out = torch.empty_like(x)
+    dims = _scan_dims(Bt, 1, Dm, N, nheads, _dtype_code(x), delta_softplus)
+    st = _lib.load().mamba_conv_state_update(
+        ctypes.byref(dims), _ptr(x, "x", dev), _ptr(conv_state, "conv_state", dev, x.dtype, (Bt, Dm, 3)),
+        _ptr(conv_weight, "conv_weight", dev, torch.float32, (Dm, 4)),
+        _ptr(conv_bias, "conv_bias", dev, torch.float32, (Dm,)),
+        _ptr(state, "state", dev, torch.float32, (Bt, Dm, N)), _ptr(delta, "delta", dev, x.dtype, (Bt, nd)),
+        _ptr(A, "A", dev, torch.float32, (nheads,) if nheads else (Dm, N)),
+        _ptr(B, "B", dev, x.dtype, (Bt, N)), _ptr(C, "C", dev, x.dtype, (Bt, N)),
+        _ptr(D, "D", dev, torch.float32, (Dm,)), _ptr(z, "z", dev, x.dtype, (Bt, Dm)),
+        _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)), _ptr(reset, "reset", dev, torch.uint8, (Bt,)),
+        _ptr(u_out, "u_out", dev, x.dtype, (Bt, Dm)), _ptr(out, "out", dev, x.dtype, (Bt, Dm)), _stream(dev))
+    _lib.check(st, "mamba_conv_state_update")
+    return out
 
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, doc_start=None,

@@ -31,6 +31,7 @@ EXPORTED = (
     "mamba_selective_scan_bwd",
     "mamba_causal_conv1d_bwd_workspace_bytes",
     "mamba_causal_conv1d_bwd",
+    "mamba_conv_state_update",
 )
 
 
@@ -101,6 +102,8 @@ def load() -> ctypes.CDLL:
     lib.mamba_causal_conv1d_bwd_workspace_bytes.restype = ctypes.c_int
     lib.mamba_causal_conv1d_bwd.argtypes = [vp] * 8 + [i64, i64, i64, i32, i32, i32, vp, sz, vp]
     lib.mamba_causal_conv1d_bwd.restype = ctypes.c_int
+    lib.mamba_conv_state_update.argtypes = [ctypes.POINTER(ScanDims)] + [vp] * 16
+    lib.mamba_conv_state_update.restype = ctypes.c_int
     _lib = lib
     return lib
 

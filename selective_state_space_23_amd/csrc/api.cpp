@@ -401,9 +401,16 @@ int mamba_causal_conv1d_update(const void* x, void* conv_state, const float* wei
     return mamba::launch_conv1d_update(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
-int mamba_selective_state_update(const mamba_scan_dims_t* dims, float* state, const void* u, const void* delta,
-                                 const float* A, const void* B, const void* C, const float* D, const void* z,
-                                 const float* delta_bias, const uint8_t* reset, void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of one decode recurrence step (shared by the plain and the fused entry
+// points); `u` is the step's input (x for the fused step).  Fills `a`.
+int check_state_update(const mamba_scan_dims_t* dims, float* state, const void* u, const void* delta, const float* A,
+                       const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+                       const uint8_t* reset, void* out, void* stream, mamba::StateUpdateArgs* a, bool* empty) {
+    *empty = false;
     if (!dims) return MAMBA_ERR_INVALID_ARGUMENT;
     if (dims->batch < 0 || dims->dim < 0 || dims->dstate < 1 || dims->nheads < 0 || dims->batch > 65535 ||
         dims->dim > kMaxDim || dims->seqlen != 1)
@@ -412,7 +419,10 @@ int mamba_selective_state_update(const mamba_scan_dims_t* dims, float* state, co
     if (dims->nheads > 0 && dims->dim % dims->nheads != 0) return MAMBA_ERR_INVALID_ARGUMENT;
     if (dims->ngroups != 1 || !mamba::state_update_supported(dims->dstate)) return MAMBA_ERR_UNSUPPORTED;
     const int64_t Bt = dims->batch, Dm = dims->dim, N = dims->dstate;
-    if (Bt * Dm == 0) return MAMBA_OK;
+    if (Bt * Dm == 0) {
+        *empty = true;
+        return MAMBA_OK;
+    }
     if (!state || !u || !delta || !A || !B || !C || !out) return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
     if (!aligned(state, 16) || !aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) ||
@@ -430,13 +440,60 @@ int mamba_selective_state_update(const mamba_scan_dims_t* dims, float* state, co
     for (int i = 0; i < 9; ++i)
         if (overlap(ins[i], insz[i], out, act) || overlap(ins[i], insz[i], state, sb)) return MAMBA_ERR_INVALID_ARGUMENT;
     if (overlap(out, act, state, sb)) return MAMBA_ERR_INVALID_ARGUMENT;
+    a->state = state; a->u = u; a->delta = delta; a->A = A; a->B = B; a->C = C; a->D = D; a->z = z;
+    a->delta_bias = delta_bias; a->reset = reset; a->out = out;
+    a->batch = Bt; a->dim = Dm; a->dstate = N; a->nheads = dims->nheads;
+    a->bf16 = dims->dtype == MAMBA_DTYPE_BF16;
+    a->softplus = dims->delta_softplus != 0;
+    a->stream = static_cast<hipStream_t>(stream);
+    return MAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba_selective_state_update(const mamba_scan_dims_t* dims, float* state, const void* u, const void* delta,
+                                 const float* A, const void* B, const void* C, const float* D, const void* z,
+                                 const float* delta_bias, const uint8_t* reset, void* out, void* stream) {
     mamba::StateUpdateArgs a;
-    a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
-    a.delta_bias = delta_bias; a.reset = reset; a.out = out;
-    a.batch = Bt; a.dim = Dm; a.dstate = N; a.nheads = dims->nheads;
-    a.bf16 = dims->dtype == MAMBA_DTYPE_BF16;
-    a.softplus = dims->delta_softplus != 0;
-    a.stream = static_cast<hipStream_t>(stream);
+    bool empty;
+    const int st = check_state_update(dims, state, u, delta, A, B, C, D, z, delta_bias, reset, out, stream, &a, &empty);
+    if (st != MAMBA_OK || empty) return st;
+    return mamba::launch_state_update(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+int mamba_conv_state_update(const mamba_scan_dims_t* dims, const void* x, void* conv_state, const float* conv_weight,
+                            const float* conv_bias, float* state, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z, const float* delta_bias,
+                            const uint8_t* reset, void* u_out, void* out, void* stream) {
+    mamba::StateUpdateArgs a;
+    bool empty;
+    const int st = check_state_update(dims, state, x, delta, A, B, C, D, z, delta_bias, reset, out, stream, &a, &empty);
+    if (st != MAMBA_OK || empty) return st;
+    if (!conv_state || !conv_weight) return MAMBA_ERR_INVALID_ARGUMENT;
+    const int64_t Bt = dims->batch, Dm = dims->dim;
+    const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(conv_state, esz) || !aligned(conv_weight, 4) || (conv_bias && !aligned(conv_bias, 4)) ||
+        (u_out && !aligned(u_out, esz)))
+        return MAMBA_ERR_MISALIGNED;
+    const size_t act = static_cast<size_t>(Bt * Dm) * esz;
+    const size_t win = act * 3;
+    const size_t sb = static_cast<size_t>(Bt * Dm * dims->dstate) * 4;
+    // the window and u are written: neither may overlap anything else of the call
+    const int64_t nd = dims->nheads ? dims->nheads : Dm;
+    const void* others[] = {x, delta, A, B, C, D, z, delta_bias, reset, conv_weight, conv_bias, state, out};
+    const size_t osz[] = {act, static_cast<size_t>(Bt * nd) * esz,
+                          static_cast<size_t>(dims->nheads ? dims->nheads : Dm * dims->dstate) * 4,
+                          static_cast<size_t>(Bt * dims->dstate) * esz, static_cast<size_t>(Bt * dims->dstate) * esz,
+                          static_cast<size_t>(Dm) * 4, act, static_cast<size_t>(nd) * 4, static_cast<size_t>(Bt),
+                          static_cast<size_t>(Dm) * 16, static_cast<size_t>(Dm) * 4, sb, act};
+    for (int i = 0; i < 13; ++i)
+        if (overlap(conv_state, win, others[i], osz[i]) || overlap(u_out, act, others[i], osz[i]))
+            return MAMBA_ERR_INVALID_ARGUMENT;
+    if (overlap(conv_state, win, u_out, act)) return MAMBA_ERR_INVALID_ARGUMENT;
+    a.u = nullptr;
+    a.conv_x = x; a.conv_state = conv_state; a.conv_w = conv_weight; a.conv_b = conv_bias; a.u_out = u_out;
     return mamba::launch_state_update(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 

@@ -8,6 +8,7 @@
 //        a reset (document start at this token) clears the window first.
 // scan:  dt = softplus(delta + delta_bias);  h <- exp(dt A) h + dt u B  (h <- 0
 //        first on a reset);  out = (C . h + D u) silu(z).
+// Both in one launch: the scan step forms u with the conv step's arithmetic.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -44,7 +45,10 @@ __global__ __launch_bounds__(256) void conv1d_update_kernel(const void* __restri
 // G = N / 4 consecutive lanes own one (row, channel): four states each, so the
 // state row of a channel is read and written as contiguous 16-byte pieces and
 // C . h is a sum over the G lanes (xor shuffles inside the group).
-template <typename T, int G, bool HEADS>
+// CONV: the conv step runs first in the same launch; every lane of the group
+// forms u from the window (rounded to T, as the separate conv step stores it)
+// and the group's first lane writes the window back.
+template <typename T, int G, bool HEADS, bool CONV>
 __global__ __launch_bounds__(256) void state_update_kernel(const StateUpdateArgs a) {
     constexpr int N = 4 * G;
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -59,9 +63,31 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StateUpdateArgs
 
     float dt = Elem<T>::load(a.delta, b * nd + dsel) + (a.delta_bias != nullptr ? a.delta_bias[dsel] : 0.0f);
     if (a.softplus) dt = softplus_f(dt);
-    const float u = Elem<T>::load(a.u, cc);
-    const float w = dt * u;
     const bool clear = a.reset != nullptr && a.reset[b] != 0;
+    float u;
+    if constexpr (CONV) {
+        float s[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) s[k] = clear ? 0.0f : Elem<T>::load(a.conv_state, cc * 3 + k);
+        const float xt = Elem<T>::load(a.conv_x, cc);
+        const float* cw = a.conv_w + d * 4;
+        float acc = a.conv_b != nullptr ? a.conv_b[d] : 0.0f;
+        acc = __builtin_fmaf(cw[0], s[0], acc);
+        acc = __builtin_fmaf(cw[1], s[1], acc);
+        acc = __builtin_fmaf(cw[2], s[2], acc);
+        acc = __builtin_fmaf(cw[3], xt, acc);
+        u = silu_f(acc);
+        if constexpr (sizeof(T) == 2) u = bf16_to_f32(f32_to_bf16(u));
+        if (live && q == 0) {
+            Elem<T>::store(a.conv_state, cc * 3 + 0, s[1]);
+            Elem<T>::store(a.conv_state, cc * 3 + 1, s[2]);
+            Elem<T>::store(a.conv_state, cc * 3 + 2, xt);
+            if (a.u_out != nullptr) Elem<T>::store(a.u_out, cc, u);
+        }
+    } else {
+        u = Elem<T>::load(a.u, cc);
+    }
+    const float w = dt * u;
 
     float4 h = clear ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : reinterpret_cast<const float4*>(a.state)[cc * G + q];
     float hv[4] = {h.x, h.y, h.z, h.w};
@@ -85,21 +111,26 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StateUpdateArgs
     }
 }
 
-template <typename T, bool HEADS>
+template <typename T, bool HEADS, bool CONV>
 hipError_t launch_state_update_typed(const StateUpdateArgs& a) {
     const int G = static_cast<int>(a.dstate / 4);
     const int64_t threads = a.batch * a.dim * G;
     const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
     switch (G) {
-        case 1: hipLaunchKernelGGL((state_update_kernel<T, 1, HEADS>), grid, dim3(256), 0, a.stream, a); break;
-        case 2: hipLaunchKernelGGL((state_update_kernel<T, 2, HEADS>), grid, dim3(256), 0, a.stream, a); break;
-        case 4: hipLaunchKernelGGL((state_update_kernel<T, 4, HEADS>), grid, dim3(256), 0, a.stream, a); break;
-        case 8: hipLaunchKernelGGL((state_update_kernel<T, 8, HEADS>), grid, dim3(256), 0, a.stream, a); break;
-        case 16: hipLaunchKernelGGL((state_update_kernel<T, 16, HEADS>), grid, dim3(256), 0, a.stream, a); break;
-        case 32: hipLaunchKernelGGL((state_update_kernel<T, 32, HEADS>), grid, dim3(256), 0, a.stream, a); break;
+        case 1: hipLaunchKernelGGL((state_update_kernel<T, 1, HEADS, CONV>), grid, dim3(256), 0, a.stream, a); break;
+        case 2: hipLaunchKernelGGL((state_update_kernel<T, 2, HEADS, CONV>), grid, dim3(256), 0, a.stream, a); break;
+        case 4: hipLaunchKernelGGL((state_update_kernel<T, 4, HEADS, CONV>), grid, dim3(256), 0, a.stream, a); break;
+        case 8: hipLaunchKernelGGL((state_update_kernel<T, 8, HEADS, CONV>), grid, dim3(256), 0, a.stream, a); break;
+        case 16: hipLaunchKernelGGL((state_update_kernel<T, 16, HEADS, CONV>), grid, dim3(256), 0, a.stream, a); break;
+        case 32: hipLaunchKernelGGL((state_update_kernel<T, 32, HEADS, CONV>), grid, dim3(256), 0, a.stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <typename T, bool HEADS>
+hipError_t launch_state_update_conv(const StateUpdateArgs& a) {
+    return a.conv_x != nullptr ? launch_state_update_typed<T, HEADS, true>(a) : launch_state_update_typed<T, HEADS, false>(a);
 }
 
 }  // namespace
@@ -109,8 +140,8 @@ bool state_update_supported(int64_t dstate) {
 }
 
 hipError_t launch_state_update(const StateUpdateArgs& a) {
-    if (a.bf16) return a.nheads ? launch_state_update_typed<bf16_t, true>(a) : launch_state_update_typed<bf16_t, false>(a);
-    return a.nheads ? launch_state_update_typed<float, true>(a) : launch_state_update_typed<float, false>(a);
+    if (a.bf16) return a.nheads ? launch_state_update_conv<bf16_t, true>(a) : launch_state_update_conv<bf16_t, false>(a);
+    return a.nheads ? launch_state_update_conv<float, true>(a) : launch_state_update_conv<float, false>(a);
 }
 
 hipError_t launch_conv1d_update(const ConvUpdateArgs& a) {

@@ -152,6 +152,13 @@ struct StateUpdateArgs {
     bool bf16;
     bool softplus;
     hipStream_t stream;
+    // Fused conv step (conv_x set): u is formed from conv_x and the window, which
+    // is updated in place; u is also written to u_out when that is not null.
+    const void* conv_x = nullptr;      // (B, D)
+    void* conv_state = nullptr;        // (B, D, 3), I/O dtype
+    const float* conv_w = nullptr;     // (D, 4)
+    const float* conv_b = nullptr;     // (D,) or null
+    void* u_out = nullptr;             // (B, D) or null
 };
 
 hipError_t launch_conv1d_update(const ConvUpdateArgs& a);

@@ -269,3 +269,22 @@ def test_conv_bwd_validation(lib):
     assert cb(dw=FAKE * 4) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # dweight inside dx
     assert cb(ws=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT              # workspace over x
     assert cb(B=0, x=None, du=None) == _lib.MAMBA_OK                  # empty: no-op
+
+
+def test_conv_state_update_validation(lib):
+    def csu(d=None, x=FAKE, cs=FAKE * 2, cw=FAKE * 3, cb=None, st=FAKE * 4, dl=FAKE * 5, A=FAKE * 6, B=FAKE * 7,
+            C=FAKE * 8, D=None, z=None, bias=None, rs=None, uo=None, out=FAKE * 9):
+        d = d or dims(batch=2, seqlen=1, dim=64)
+        return lib.mamba_conv_state_update(ctypes.byref(d), x, cs, cw, cb, st, dl, A, B, C, D, z, bias, rs, uo, out,
+                                           None)
+
+    assert csu(cs=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert csu(cw=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert csu(x=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert csu(d=dims(batch=2, seqlen=2, dim=64)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert csu(d=dims(batch=2, seqlen=1, dim=64, dstate=5)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert csu(st=FAKE * 4 + 8) == _lib.MAMBA_ERR_MISALIGNED
+    assert csu(cs=FAKE * 2 + 1) == _lib.MAMBA_ERR_MISALIGNED
+    assert csu(cs=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT              # window over x
+    assert csu(uo=FAKE * 9) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # u_out over out
+    assert csu(d=dims(batch=0, seqlen=1), x=None) == _lib.MAMBA_OK      # empty: no-op

@@ -95,3 +95,90 @@ def test_prefill_then_decode(ssm, case):
     assert_close(to_host(out_pre), ref_out[:, :L0], dt, f"prefill out {case}")
     assert_close(got, ref_out[:, L0:], dt, f"decode out {case}")
     assert_close(to_host(state), ref_fin, dt, f"decode state {case}")
+
+
+def test_decode_graph_replays_match_eager(ssm):
+    """Decode steps captured in a HIP graph (as bench.py --path decode replays
+    them): every replay, with eager work and synchronisations between replays,
+    gives the eager outputs and states bit for bit."""
+    torch = torch_mod()
+    inp = make_custom(2, 40, 96, 16, dtype="bf16", docs=9.0, seed=321)
+    dev = upload(inp)
+    T = 12
+    xs = dev["x"][:, :T].transpose(0, 1).contiguous()
+    zs = dev["z"][:, :T].transpose(0, 1).contiguous()
+    dls = dev["delta"][:, :T].transpose(0, 1).contiguous()
+    Bs = dev["B"][:, :T].transpose(0, 1).contiguous()
+    Cs = dev["C"][:, :T].transpose(0, 1).contiguous()
+    rs = dev["doc_start"][:, :T].transpose(0, 1).contiguous()
+    rs[0].fill_(1)
+    state = torch.zeros((2, 96, 16), dtype=torch.float32, device="cuda")
+    cstate = torch.zeros((2, 96, 3), dtype=torch.bfloat16, device="cuda")
+    us = torch.empty((T, 2, 96), dtype=torch.bfloat16, device="cuda")
+    outs = torch.empty_like(us)
+
+    def steps():
+        for k in range(T):
+            ssm.causal_conv1d_update(xs[k], cstate, dev["conv_w"], dev["conv_b"], reset=rs[k], out=us[k])
+            ssm.selective_state_update(state, us[k], dls[k], dev["A"], Bs[k], Cs[k], dev["D"], zs[k],
+                                       dev["delta_bias"], reset=rs[k], out=outs[k])
+
+    # eager reference from a fixed starting state
+    start_state = torch.randn((2, 96, 16), dtype=torch.float32, device="cuda") * 0.1
+    start_conv = (torch.randn((2, 96, 3), device="cuda") * 0.5).to(torch.bfloat16)
+    state.copy_(start_state)
+    cstate.copy_(start_conv)
+    steps()
+    ref_out, ref_state, ref_conv = outs.clone(), state.clone(), cstate.clone()
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        steps()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            steps()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        state.copy_(start_state)
+        cstate.copy_(start_conv)
+        outs.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, ref_out), f"replay {rep}: outputs"
+        assert torch.equal(state, ref_state), f"replay {rep}: state"
+        assert torch.equal(cstate, ref_conv), f"replay {rep}: conv window"
+        _ = (outs.float() * 2).sum().item()      # eager work between replays
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fused_decode_step_matches_two_steps(ssm, case):
+    """mamba_conv_state_update (one launch) gives, bit for bit, the outputs, u,
+    states and conv windows of mamba_causal_conv1d_update followed by
+    mamba_selective_state_update, over steps with document starts."""
+    torch = torch_mod()
+    Dm, N, H, dt = case
+    inp = make_custom(2, 30, Dm, N, nheads=H, dtype=dt, docs=7.0, seed=400 + Dm + N)
+    dev = upload(inp)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    st1 = torch.randn((2, Dm, N), dtype=torch.float32, device="cuda") * 0.1
+    cs1 = (torch.randn((2, Dm, 3), device="cuda") * 0.5).to(tdt)
+    st2, cs2 = st1.clone(), cs1.clone()
+    for t in range(30):
+        reset = dev["doc_start"][:, t].contiguous()
+        args = (dev["delta"][:, t].contiguous(), dev["A"], dev["B"][:, t].contiguous(), dev["C"][:, t].contiguous(),
+                dev["D"], dev["z"][:, t].contiguous(), dev["delta_bias"])
+        x_t = dev["x"][:, t].contiguous()
+        u1 = ssm.causal_conv1d_update(x_t, cs1, dev["conv_w"], dev["conv_b"], reset=reset)
+        o1 = ssm.selective_state_update(st1, u1, *args, reset=reset)
+        u2 = torch.empty_like(u1)
+        o2 = ssm.conv_state_update(x_t, cs2, dev["conv_w"], dev["conv_b"], st2, *args, reset=reset, u_out=u2)
+        torch.cuda.synchronize()
+        assert torch.equal(u1, u2), f"u at token {t}"
+        assert torch.equal(o1, o2), f"out at token {t}"
+        assert torch.equal(st1, st2), f"state at token {t}"
+        assert torch.equal(cs1, cs2), f"conv window at token {t}"
