@@ -82,14 +82,6 @@ size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
 bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16);
 hipError_t launch_selective_scan(const ScanArgs& a);
 
-// Passes 1 and 2 of the per-channel scan into the given buffers (ws_P, ws_H each
-// (nchunks - 1) * B * D * N floats, dt_ws B * L * D floats, ckpt
-// B * ceil(L / 2^ck_shift) * (N + 2) * D floats): ws_P[c] then holds the state
-// entering chunk c + 1, ckpt the local state before every block of 2^ck_shift
-// tokens (ck_shift in 2..6).  Used by the backward pass; no initial state.
-hipError_t launch_scan_chunk_carries(const ScanArgs& a, const ScanPlan& plan, float* ws_P, float* ws_H, void* dt_ws,
-                                     float* ckpt, int ck_shift);
-
 // Backward of the per-channel scan (scan_bwd.hip).
 struct ScanBwdArgs {
     const void* u;

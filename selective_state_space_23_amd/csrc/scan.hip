@@ -73,9 +73,6 @@ struct ScanKParams {
     void* u_out;              // (B, L, D): pass 1 stores u here
     void* dt_ws;              // (B, L, D), I/O dtype: step sizes from pass 1 for pass 3 (per-channel A)
     int64_t nslots;           // chunks with an aggregate slot (nchunks - 1)
-    float* ckpt;              // DT32 only: [B][nk][N + 2][D] local checkpoints, see scan_chunk_kernel
-    int64_t nk;               // checkpoints per row
-    int ck_shift;             // log2 of the tokens between checkpoints (3 or 4)
     int64_t seqlen;
     int64_t chunk_len;
     int dim;
@@ -128,21 +125,10 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, int byte_of
 // before the chunk), stores u (rounded to T) for pass 3 and scans with it.  The
 // arithmetic and its order are those of the standalone conv kernel, so u is
 // bitwise the same.
-//
-// DT32 (pass 1 for the backward pass only): dt is stored as float32 and used
-// unrounded, so the backward's recomputation sees the exact step sizes; and
-// before every block k of 2^ck_shift tokens of the chunk the pass stores a local
-// checkpoint:
-// rows 0..N-1 of ckpt[b][k] the state reached from zero at the chunk start, row
-// N the sum of dt since the chunk start (or since the latest document start),
-// row N + 1 one if a document started since the chunk start.  The true state
-// there is then local + exp(A * sum) * (state entering the chunk), or local
-// alone after a document start.
-template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS, bool CONV = false, bool DT32 = false>
+template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS, bool CONV = false>
 __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMBA_SCAN_WAVES_PER_EU))) void scan_chunk_kernel(
     const ScanKParams p) {
     static_assert(!CONV || (!OUTPUT && !HEADS), "the conv runs in the aggregate pass of the per-channel scan");
-    static_assert(!DT32 || (!OUTPUT && !HEADS && !CONV), "float32 step sizes are a pass-1 option");
     constexpr int G = kGroup;
     constexpr int kWin = 64;                                   // tokens per staged window
     constexpr int kRows = OUTPUT ? 2 : 1;                      // B and C, or B only
@@ -177,11 +163,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     constexpr bool kDtWs = !HEADS;
     const __amdgpu_buffer_rsrc_t dl_rs =
         make_rsrc(static_cast<const T*>((kDtWs && OUTPUT) ? p.dt_ws : p.delta) + b * L * nd, L * nd * kEsz);
-    // (DT32 with a null dt_ws: an empty resource, so the dt stores are dropped.)
-    constexpr int kDtEsz = DT32 ? 4 : kEsz;
-    const bool dt_out = kDtWs && p.dt_ws != nullptr;
-    const __amdgpu_buffer_rsrc_t dto_rs = make_rsrc(
-        dt_out ? static_cast<char*>(p.dt_ws) + b * act_row * kDtEsz : nullptr, dt_out ? act_row * kDtEsz : 0);
+    const __amdgpu_buffer_rsrc_t dto_rs =
+        make_rsrc(static_cast<T*>(kDtWs ? p.dt_ws : p.out) + b * act_row, kDtWs ? act_row * kEsz : 0);
     const __amdgpu_buffer_rsrc_t z_rs =
         make_rsrc(HAS_Z ? static_cast<const T*>(p.z) + b * act_row : static_cast<const T*>(p.u), act_row * kEsz);
     const T* B_row = static_cast<const T*>(p.B) + b * L * N;
@@ -293,15 +276,6 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     uint64_t starts = 0;
     auto compute_group = [&](int64_t g0, const float (&cu)[G], const float (&cd)[G], const float (&cz)[G]) {
         const int off = static_cast<int>((g0 - t_begin) & (kWin - 1));
-        if constexpr (DT32) {
-            if (((g0 - t_begin) & ((1 << p.ck_shift) - 1)) == 0 && g0 < t_end && active) {
-                float* ck = p.ckpt + ((b * p.nk + (g0 >> p.ck_shift)) * (N + 2)) * p.dim + d;
-#pragma unroll
-                for (int n = 0; n < N; ++n) ck[static_cast<int64_t>(n) * p.dim] = h[n];
-                ck[static_cast<int64_t>(N) * p.dim] = sum_dt;
-                ck[static_cast<int64_t>(N + 1) * p.dim] = any_reset ? 1.0f : 0.0f;
-            }
-        }
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             // Tokens past the chunk end run as identity steps (dt = 0: decay 1, no
@@ -322,9 +296,7 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             } else {
                 dt = cd[k] + dbias;
                 if constexpr (SOFTPLUS) dt = softplus_f(dt);
-                if constexpr (DT32) {
-                    buf_store<float>(dto_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * 4 : kNoStore, dt);
-                } else if constexpr (kDtWs) {
+                if constexpr (kDtWs) {
                     if constexpr (sizeof(T) == 2) dt = bf16_to_f32(f32_to_bf16(dt));
                     buf_store<T>(dto_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, dt);
                 }
@@ -583,55 +555,7 @@ hipError_t launch_heads_f32(const ScanArgs& a, const ScanPlan& plan) {
     }
 }
 
-// Passes 1 and 2 alone for per-channel A, into caller-chosen buffers: after it,
-// ws_P[c] holds the state entering chunk c + 1, dt_ws the step sizes (float32,
-// unrounded) of every token and ckpt the local checkpoints of every 16-token
-// block (see DT32 above).  The backward pass starts from these.
-template <typename T, int N>
-hipError_t launch_carries_typed(const ScanArgs& a, const ScanPlan& plan, float* ws_P, float* ws_H, void* dt_ws,
-                                float* ckpt, int ck_shift) {
-    ScanKParams p{};
-    p.u = a.u; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = nullptr; p.z = nullptr;
-    p.delta_bias = a.delta_bias; p.doc_start = a.doc_start; p.initial_state = nullptr;
-    p.out = nullptr; p.final_state = nullptr;
-    const int64_t count = a.batch * a.dim * N;
-    const int64_t nslots = plan.nchunks - 1;
-    p.ws_P = ws_P; p.ws_H = ws_H; p.dt_ws = dt_ws; p.ckpt = ckpt;
-    p.ck_shift = ck_shift;
-    p.nk = (a.seqlen + (1 << ck_shift) - 1) >> ck_shift;
-    p.seqlen = a.seqlen; p.chunk_len = plan.chunk_len; p.dim = static_cast<int>(a.dim);
-    p.nheads = 0; p.headdim = 0; p.nbatch = static_cast<int>(a.batch); p.softplus = a.softplus ? 1 : 0;
-    p.nslots = nslots;
-    const unsigned gx = static_cast<unsigned>((a.dim + kScanBlock - 1) / kScanBlock);
-    dim3 g1(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
-    if (a.softplus)
-        hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, true, false, true>), g1, dim3(kScanBlock), 0,
-                           a.stream, p);
-    else
-        hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, false, false, true>), g1, dim3(kScanBlock),
-                           0, a.stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || nslots == 0) return e;
-    hipLaunchKernelGGL(scan_carry_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, a.stream,
-                       ws_P, ws_H, static_cast<const float*>(nullptr), count, nslots);
-    return hipGetLastError();
-}
-
 }  // namespace
-
-hipError_t launch_scan_chunk_carries(const ScanArgs& a, const ScanPlan& plan, float* ws_P, float* ws_H,
-                                     void* dt_ws, float* ckpt, int ck_shift) {
-    if (a.nheads != 0 || a.initial_state != nullptr || ck_shift < 2 || ck_shift > 6) return hipErrorInvalidValue;
-    switch (a.dstate) {
-        case 4: return a.bf16 ? launch_carries_typed<bf16_t, 4>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift)
-                              : launch_carries_typed<float, 4>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift);
-        case 8: return a.bf16 ? launch_carries_typed<bf16_t, 8>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift)
-                              : launch_carries_typed<float, 8>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift);
-        case 16: return a.bf16 ? launch_carries_typed<bf16_t, 16>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift)
-                               : launch_carries_typed<float, 16>(a, plan, ws_P, ws_H, dt_ws, ckpt, ck_shift);
-        default: return hipErrorInvalidValue;
-    }
-}
 
 bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16) {
     if (nheads == 0) return dstate == 4 || dstate == 8 || dstate == 16;

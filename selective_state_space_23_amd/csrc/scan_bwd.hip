@@ -17,18 +17,23 @@
 // trajectory).
 //
 // Parallel structure, on the forward's chunking of L:
-//   1. forward passes 1-2 (scan.hip): the state entering every chunk, and dt
-//      (float32: the step sizes are not rounded to the I/O dtype here, since
-//      the token sums dA, dD and ddelta_bias cancel and would show that rounding);
-//   2. reverse aggregate: every chunk but the first runs the adjoint recurrence
-//      backwards from zero and stores X_c = a_{t0} g_{t0} and P_c = prod of a
-//      over the chunk (0 if a document starts in it);
-//   3. reverse carry: G_c = X_{c+1} + P_{c+1} G_{c+1}, the adjoint flowing into
-//      the last token of chunk c from the right (the same associative operator
-//      as the forward carry, run from the row end);
-//   4. main pass, per chunk: pass 1 also stored, before every 16-token block, the
-//      state reached from zero at the chunk start and the step-size sum since
-//      then, so the true state there is local + exp(A sum) * (chunk's carry).
+//   1. aggregate pass, one forward sweep per chunk from a zero state: stores dt
+//      (float32: the step sizes are not rounded to the I/O dtype here, since the
+//      token sums dA, dD and ddelta_bias cancel and would show that rounding),
+//      a checkpoint before every 16-token block (the local state, the step-size
+//      sum since the chunk start and whether a document started since), and per
+//      chunk the local end state H_c, R_c = prod of a over the chunk (0 if a
+//      document starts in it) and X_c = a_{t0} g_{t0} of the chunk's own
+//      adjoint.  X_c needs no reverse sweep: unrolled, it is the sum over the
+//      chunk's tokens of (a_{t0} ... a_t) C_t dy_t, a running product and a
+//      running sum carried forward;
+//   2. forward carry: the state entering chunk c + 1 is R_c carry_c + H_c;
+//   3. reverse carry: G_c = X_{c+1} + R_{c+1} G_{c+1}, the adjoint flowing into
+//      the last token of chunk c from the right (the same associative operator,
+//      run from the row end);
+//   4. main pass, per chunk: the true state before a block is the checkpoint
+//      plus exp(A sum) * (chunk's carry), or the checkpoint alone if a document
+//      started since the chunk start.
 //      The blocks are walked last to first: from that checkpoint recompute the
 //      state before token 8, and for each 4-token piece (last first) its start
 //      state (4 more steps for the odd pieces) and its four states, then run
@@ -53,20 +58,13 @@ constexpr int kBlk = 256;              // 4 waves, 256 consecutive channels
 constexpr int kWaves = kBlk / 64;
 constexpr int kWin = 64;               // tokens per staged B/C window
 constexpr int kCk = 16;                // tokens per block of the main pass
-#ifndef MAMBA_BWD_CK_SHIFT
-#define MAMBA_BWD_CK_SHIFT 4           // checkpoints every 16 tokens (3, every 8, measured 4% slower)
-#endif
-constexpr int kCkShift = MAMBA_BWD_CK_SHIFT;
-constexpr int kCkEvery = 1 << kCkShift;
+constexpr int kCkShift = 4;            // a checkpoint before every block: log2(kCk)
 constexpr int kPiece = 4;              // tokens per innermost recompute piece
 #ifndef MAMBA_BWD_WAVES_PER_EU
 #define MAMBA_BWD_WAVES_PER_EU 0        // 0: chosen per state count (bwd_waves_per_eu)
 #endif
 #ifndef MAMBA_BWD_TOKEN_BARRIER
 #define MAMBA_BWD_TOKEN_BARRIER 1
-#endif
-#ifndef MAMBA_BWD_DT_WS
-#define MAMBA_BWD_DT_WS 1        // 1: pass 1 stores dt (fp32) for the later passes; 0: they recompute it from delta (6% slower)
 #endif
 #ifndef MAMBA_BWD_KEEP_NL
 #define MAMBA_BWD_KEEP_NL 4      // keep the recompute's decays in registers up to this many states a lane
@@ -89,11 +87,15 @@ struct BwdKParams {
     const float* delta_bias;
     const uint8_t* doc_start;
     const void* dout;
-    const float* dt;         // (B, L, D) float32: step sizes from forward pass 1
+    const float* dt;         // (B, L, D) float32: step sizes from the aggregate pass
+    float* dt_out;           // the same array, written by the aggregate pass
+    float* h_agg_P;          // [nslots][B][D][N]: R_s, then (forward carry) the state entering chunk s + 1
+    float* h_agg_H;          // [nslots][B][D][N]: H_s
+    float* ckpt_out;         // checkpoints, written by the aggregate pass
     const float* h_carry;    // [nslots][B][D][N]: state entering chunk s + 1
     float* g_carry;          // [nslots][B][D][N]: X_{s+1}, then G_s
     float* p_rev;            // [nslots][B][D][N]: P_{s+1}
-    const float* ckpt;       // [B][nk][N + 2][D]: local checkpoints of forward pass 1
+    const float* ckpt;       // [B][nk][N + 2][D]: local checkpoints of the aggregate pass
     float* part_bc;          // [B][L][nblk][2N]: per-block sums of dB_t, dC_t
     float* part_w;           // [B][nchunks][N + 2][D]: per-chunk sums of dA, dD, ddelta_bias
     void* du;
@@ -181,102 +183,205 @@ __device__ __forceinline__ uint64_t window_starts(const uint8_t* ds_row, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// 2. Reverse aggregate of chunk c = blockIdx.y + 1 (chunk 0 needs none).
-// dt of a token from its raw delta (the same fp32 arithmetic as the forward's
-// pass 1, so the value is bitwise the one pass 1 used).
+// dt of a token from its raw delta (the fp32 arithmetic of the forward pass).
 template <bool SOFTPLUS>
 __device__ __forceinline__ float step_size(float delta, float bias) {
     const float v = delta + bias;
     return SOFTPLUS ? softplus_f(v) : v;
 }
 
+// 1. One forward sweep of chunk blockIdx.y of row blockIdx.z from a zero state
+// (lanes are channels, N states in VGPRs, B and C of a 64-token window in LDS).
+// It yields, with one exponential per element:
+//   - dt (fp32) of every token, read by the later passes;
+//   - before every 16-token block a local checkpoint: the state reached from zero
+//     at the chunk start, the step-size sum since then (since the latest
+//     document start), and whether a document started;
+//   - the forward aggregate: the end state H_c and R_c = prod of a over the chunk
+//     (exactly 0 once a document starts);
+//   - the reverse aggregate X_c = a_{t0} g_{t0} of the adjoint g run backwards
+//     from zero over the chunk.  Unrolled, X_c = sum_t R_t C_t dy_t with
+//     R_t = prod_{s = t0 .. t} a_s: a forward running sum over the same decays
+//     (three multiply-adds per element, no exponential).
 template <typename T, int N, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kBlk) void bwd_rev_aggregate_kernel(const BwdKParams p) {
-    __shared__ float4 sC4[kWin * N / 4];
-    float* sC = reinterpret_cast<float*>(sC4);
+#ifndef MAMBA_BWD_AGG_WAVES_PER_EU
+#define MAMBA_BWD_AGG_WAVES_PER_EU 3
+#endif
+__global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_AGG_WAVES_PER_EU))) void bwd_aggregate_kernel(
+    const BwdKParams p) {
+    constexpr int kWinFloats = kWin * N;
+    __shared__ float4 sBC4[2 * kWinFloats / 4];
+    float* sBC = reinterpret_cast<float*>(sBC4);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int d = blockIdx.x * kBlk + tid;
     const bool active = d < p.dim;
     const int dc = active ? d : p.dim - 1;
-    const int64_t c = static_cast<int64_t>(blockIdx.y) + 1;
+    const int64_t c = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int64_t L = p.seqlen;
     const int64_t t_begin = c * p.chunk_len;
     const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
     constexpr int kEsz = static_cast<int>(sizeof(T));
     const int64_t act_row = L * p.dim;
-    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(MAMBA_BWD_DT_WS ? p.dt + b * act_row : nullptr,
-                                                   MAMBA_BWD_DT_WS ? act_row * 4 : 0);
-    const __amdgpu_buffer_rsrc_t dl_rs = make_rsrc(static_cast<const T*>(p.delta) + b * act_row, act_row * kEsz);
-    const float dbias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
-    const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, act_row * kEsz);
-    const __amdgpu_buffer_rsrc_t z_rs =
-        make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, act_row * kEsz);
+    const int64_t rb = act_row * kEsz;
+    const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(static_cast<const T*>(p.u) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t dl_rs = make_rsrc(static_cast<const T*>(p.delta) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, rb);
+    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(p.dt_out + b * act_row, act_row * 4);
+    const T* B_row = static_cast<const T*>(p.B) + b * L * N;
     const T* C_row = static_cast<const T*>(p.C) + b * L * N;
     const uint8_t* ds_row = p.doc_start ? p.doc_start + b * L : nullptr;
 
     float Al2[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) Al2[n] = p.A[static_cast<int64_t>(dc) * N + n] * kLog2e;
-    float gn[N];
+    const float dbias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
+    const int lane_off = dc * kEsz;
+    const int row_bytes = p.dim * kEsz;
+    float h[N], R[N], X[N];
 #pragma unroll
-    for (int n = 0; n < N; ++n) gn[n] = 0.0f;
+    for (int n = 0; n < N; ++n) {
+        h[n] = 0.0f;
+        R[n] = 1.0f;
+        X[n] = 0.0f;
+    }
     float sum_dt = 0.0f;
     bool any_reset = false;
+    float* ck_row = p.ckpt_out + b * p.nk * (N + 2) * p.dim;
 
-    const int64_t nwin = (t_end - t_begin + kWin - 1) / kWin;
-    for (int64_t wi = nwin - 1; wi >= 0; --wi) {
-        const int64_t w0 = t_begin + wi * kWin;
-        const uint64_t starts = window_starts(ds_row, w0, t_end, lane);
-        any_reset = any_reset || starts != 0;
-        __syncthreads();
-        stage_rows<T, N, 1>(sC, C_row, C_row, w0, t_end, tid);
-        __syncthreads();
-        const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
-        for (int64_t g0 = wend - kPiece; g0 > w0 - kPiece; g0 -= kPiece) {
-            // tokens g0 .. g0 + 3, the ones below w0 are skipped (g0 < w0 only on a ragged window)
-            float dtv[kPiece], dyv[kPiece];
+    // u, delta, dout, z of tokens g0 .. g0 + 3 (clamped to the chunk's last token).
+    auto fetch = [&](int64_t g0, float (&uu)[kPiece], float (&dl)[kPiece], float (&go)[kPiece],
+                     float (&zz)[kPiece]) {
 #pragma unroll
-            for (int k = 0; k < kPiece; ++k) {
-                const int64_t t = g0 + k >= w0 ? g0 + k : w0;
-                const int off = static_cast<int>((t * p.dim + dc) * kEsz);
-                if constexpr (MAMBA_BWD_DT_WS) dtv[k] = buf_load<float>(dt_rs, static_cast<int>((t * p.dim + dc) * 4));
-                else dtv[k] = step_size<SOFTPLUS>(buf_load<T>(dl_rs, off), dbias);
-                float dy = buf_load<T>(do_rs, off);
-                if constexpr (HAS_Z) dy *= silu_f(buf_load<T>(z_rs, off));
-                dyv[k] = dy;
-            }
+        for (int k = 0; k < kPiece; ++k) {
+            const int64_t t = g0 + k < t_end ? g0 + k : t_end - 1;
+            const int so = static_cast<int>(t * row_bytes);
+            uu[k] = buf_load_s<T>(u_rs, lane_off, so);
+            dl[k] = buf_load_s<T>(dl_rs, lane_off, so);
+            go[k] = buf_load_s<T>(do_rs, lane_off, so);
+            zz[k] = HAS_Z ? buf_load_s<T>(z_rs, lane_off, so) : 0.0f;
+        }
+    };
+    uint64_t starts = 0;
+    auto steps = [&](int64_t g0, int64_t w0, const float (&uu)[kPiece], const float (&dl)[kPiece],
+                     const float (&go)[kPiece], const float (&zz)[kPiece]) {
+        // Stores take the clamped channel and token: a lane past the last channel
+        // (or a token past the chunk end) repeats the value of the lane (token) it
+        // was clamped to, so no store needs a branch inside the token loop.
+        if (((g0 - t_begin) & (kCk - 1)) == 0 && g0 < t_end) {
+            // One resource per checkpoint: wave-uniform base, row offsets in soffset.
+            const __amdgpu_buffer_rsrc_t ck_rs =
+                make_rsrc(ck_row + (g0 >> kCkShift) * (N + 2) * p.dim, (N + 2) * p.dim * 4);
 #pragma unroll
-            for (int k = kPiece - 1; k >= 0; --k) {
-                const int64_t t = g0 + k;
-                if (t < w0) continue;                     // wave-uniform
-                const int o = static_cast<int>(t - w0);
-                const float r = ((starts >> o) & 1ull) ? -__builtin_inff() : 0.0f;
-                const float dt = dtv[k];
-                sum_dt += dt;
-                const float4* Cq = reinterpret_cast<const float4*>(sC + o * N);
+            for (int n = 0; n < N; ++n) buf_store_s<float>(ck_rs, dc * 4, n * p.dim * 4, h[n]);
+            buf_store_s<float>(ck_rs, dc * 4, N * p.dim * 4, sum_dt);
+            buf_store_s<float>(ck_rs, dc * 4, (N + 1) * p.dim * 4, any_reset ? 1.0f : 0.0f);
+        }
 #pragma unroll
-                for (int q = 0; q < N / 4; ++q) {
-                    const float4 cv = Cq[q];
-                    const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+        for (int k = 0; k < kPiece; ++k) {
+            const int64_t t = g0 + k;
+            const bool valid = t < t_end;
+            const int o = static_cast<int>(t - w0);
+            const bool reset = (starts >> o) & 1ull;
+            const float r = reset ? -__builtin_inff() : 0.0f;
+            float dt = step_size<SOFTPLUS>(dl[k], dbias);
+            buf_store_s<float>(dt_rs, dc * 4, static_cast<int>((valid ? t : t_end - 1) * p.dim * 4), dt);
+            dt = valid ? dt : 0.0f;
+            float dy = go[k];
+            if constexpr (HAS_Z) dy *= silu_f(zz[k]);
+            dy = valid ? dy : 0.0f;
+            any_reset = any_reset || reset;
+            sum_dt = reset ? 0.0f : sum_dt;
+            const float w = dt * uu[k];
+            const float4* Bq = reinterpret_cast<const float4*>(sBC + o * N);
+            const float4* Cq = reinterpret_cast<const float4*>(sBC + kWinFloats + o * N);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int n = 4 * q + j;
-                        const float g = __builtin_fmaf(cc[j], dyv[k], gn[n]);
-                        gn[n] = exp2_fast(__builtin_fmaf(dt, Al2[n], r)) * g;
-                    }
+            for (int q = 0; q < N / 4; ++q) {
+                const float4 bv = Bq[q];
+                const float4 cv = Cq[q];
+                const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+                const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = 4 * q + j;
+                    const float a = exp2_fast(__builtin_fmaf(dt, Al2[n], r));
+                    h[n] = __builtin_fmaf(a, h[n], w * bb[j]);
+                    R[n] *= a;
+                    X[n] = __builtin_fmaf(R[n], cc[j] * dy, X[n]);
                 }
             }
+            // Keep each token's R and X updates in that token (the compiler
+            // otherwise defers them over the group and spills the decays).
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                R[n] = opaque(R[n]);
+                X[n] = opaque(X[n]);
+            }
+            sum_dt += dt;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    float au[kPiece], ad[kPiece], ao[kPiece], az[kPiece], bu[kPiece], bd[kPiece], bo[kPiece], bz[kPiece];
+    fetch(t_begin, au, ad, ao, az);
+    for (int64_t w0 = t_begin; w0 < t_end; w0 += kWin) {
+        starts = window_starts(ds_row, w0, t_end, lane);
+        __syncthreads();
+        stage_rows<T, N, 2>(sBC, B_row, C_row, w0, t_end, tid);
+        __syncthreads();
+        const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
+        for (int64_t g0 = w0; g0 < wend; g0 += 2 * kPiece) {
+            fetch(g0 + kPiece, bu, bd, bo, bz);
+            steps(g0, w0, au, ad, ao, az);
+            fetch(g0 + 2 * kPiece, au, ad, ao, az);
+            steps(g0 + kPiece, w0, bu, bd, bo, bz);
         }
     }
     if (!active) return;
     const int64_t count = static_cast<int64_t>(p.nbatch) * p.dim * N;
-    const int64_t slot = (c - 1) * count + (b * p.dim + dc) * N;
+    const int64_t my_slot = (b * p.dim + d) * N;
+    if (c < p.nslots) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        p.g_carry[slot + n] = gn[n];
-        p.p_rev[slot + n] = any_reset ? 0.0f : exp2_fast(sum_dt * Al2[n]);
+        for (int n = 0; n < N; ++n) {
+            p.h_agg_P[c * count + my_slot + n] = R[n];
+            p.h_agg_H[c * count + my_slot + n] = h[n];
+        }
+    }
+    if (c > 0) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            p.g_carry[(c - 1) * count + my_slot + n] = X[n];
+            p.p_rev[(c - 1) * count + my_slot + n] = R[n];
+        }
+    }
+}
+
+// 2. Forward carry: slot s turns from R_s into the state entering chunk s + 1,
+// carry_{s+1} = R_s carry_s + H_s (carry_0 = 0: no initial state).
+__global__ __launch_bounds__(256) void bwd_fwd_carry_kernel(float* __restrict__ ws_P, const float* __restrict__ ws_H,
+                                                            int64_t count, int64_t nslots) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= count) return;
+    float carry = 0.0f;
+    int64_t s = 0;
+    for (; s + 4 <= nslots; s += 4) {
+        float P[4], H[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            P[k] = ws_P[(s + k) * count + i];
+            H[k] = ws_H[(s + k) * count + i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            carry = __builtin_fmaf(P[k], carry, H[k]);
+            ws_P[(s + k) * count + i] = carry;
+        }
+    }
+    for (; s < nslots; ++s) {
+        carry = __builtin_fmaf(ws_P[s * count + i], carry, ws_H[s * count + i]);
+        ws_P[s * count + i] = carry;
     }
 }
 
@@ -366,8 +471,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
     const int64_t act_row = L * p.dim;
     const int64_t rb = act_row * kEsz;
     const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(static_cast<const T*>(p.u) + b * act_row, rb);
-    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(MAMBA_BWD_DT_WS ? p.dt + b * act_row : nullptr,
-                                                   MAMBA_BWD_DT_WS ? act_row * 4 : 0);
+    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(p.dt + b * act_row, act_row * 4);
     const __amdgpu_buffer_rsrc_t dl_rs = make_rsrc(static_cast<const T*>(p.delta) + b * act_row, rb);
     const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, rb);
     const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, rb);
@@ -421,8 +525,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
     // so that each recompute level evaluates its own exponentials.
     auto load_dtu = [&](int64_t t, float& dt, float& uu) {
         const int so = tok_soff(t);
-        if constexpr (MAMBA_BWD_DT_WS) dt = buf_load_s<float>(dt_rs, dc * 4, so * (4 / kEsz));
-        else dt = step_size<SOFTPLUS>(buf_load_s<T>(dl_rs, lane_off, so), dbias);
+        dt = buf_load_s<float>(dt_rs, dc * 4, so * (4 / kEsz));
         uu = buf_load_s<T>(u_rs, lane_off, so);
         dt = opaque(t < t_end ? dt : 0.0f);
         uu = active ? uu : 0.0f;
@@ -612,20 +715,12 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
                 }
             };
             load_ck(s, ck0);
-            if constexpr (kCkEvery == 8) {
-                if (s + 8 < t_end) load_ck(s + 8, ck8);
-                else {
 #pragma unroll
-                    for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];   // unused: pieces 2, 3 are past the end
-                }
-            } else {
+            for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];
+            advance4(ck8, s, os);
+            advance4(ck8, s + 4, os + 4);
 #pragma unroll
-                for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];
-                advance4(ck8, s, os);
-                advance4(ck8, s + 4, os + 4);
-#pragma unroll
-                for (int i = 0; i < NL; ++i) ck8[i] = opaque(ck8[i]);
-            }
+            for (int i = 0; i < NL; ++i) ck8[i] = opaque(ck8[i]);
             // Pieces last to first, one loop body (unrolling the four lets the
             // compiler interleave them and run out of registers).
 #pragma unroll 1
@@ -720,7 +815,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     const size_t count = static_cast<size_t>(batch * dim * dstate);
     const size_t slots = plan.nchunks > 1 ? static_cast<size_t>(plan.nchunks - 1) : 0;
     const size_t carry = align256(slots * count * sizeof(float));
-    const int64_t nk = (seqlen + kCkEvery - 1) / kCkEvery;
+    const int64_t nk = (seqlen + kCk - 1) / kCk;
     const int64_t cpb = kBlk / lanes_per_channel(dstate);
     const int64_t nblk = (dim + cpb - 1) / cpb;
     BwdLayout l;
@@ -729,7 +824,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     l.g_carry = l.h_agg + carry;
     l.p_rev = l.g_carry + carry;
     l.dt = l.p_rev + carry;
-    l.ckpt = l.dt + (MAMBA_BWD_DT_WS ? align256(static_cast<size_t>(batch * seqlen * dim) * sizeof(float)) : 0);
+    l.ckpt = l.dt + align256(static_cast<size_t>(batch * seqlen * dim) * sizeof(float));
     l.part_bc = l.ckpt + align256(static_cast<size_t>(batch * nk * (dstate + 2) * dim) * sizeof(float));
     l.part_w = l.part_bc + align256(static_cast<size_t>(batch * seqlen * nblk * 2 * dstate) * sizeof(float));
     l.total = l.part_w + align256(static_cast<size_t>(batch * plan.nchunks * (dstate + 2) * dim) * sizeof(float));
@@ -739,20 +834,14 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
 template <typename T, int N>
 hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const BwdLayout& l) {
     char* ws = static_cast<char*>(a.ws);
-    ScanArgs fa{};
-    fa.u = a.u; fa.delta = a.delta; fa.A = a.A; fa.B = a.B; fa.C = a.C; fa.delta_bias = a.delta_bias;
-    fa.doc_start = a.doc_start; fa.initial_state = nullptr;
-    fa.batch = a.batch; fa.seqlen = a.seqlen; fa.dim = a.dim; fa.dstate = N; fa.nheads = 0;
-    fa.bf16 = a.bf16; fa.softplus = a.softplus; fa.stream = a.stream;
-    hipError_t e = launch_scan_chunk_carries(fa, plan, reinterpret_cast<float*>(ws + l.h_carry),
-                                             reinterpret_cast<float*>(ws + l.h_agg), MAMBA_BWD_DT_WS ? ws + l.dt : nullptr,
-                                             reinterpret_cast<float*>(ws + l.ckpt), kCkShift);
-    if (e != hipSuccess) return e;
-
     BwdKParams p{};
     p.u = a.u; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
     p.delta_bias = a.delta_bias; p.doc_start = a.doc_start; p.dout = a.dout;
     p.dt = reinterpret_cast<const float*>(ws + l.dt);
+    p.dt_out = reinterpret_cast<float*>(ws + l.dt);
+    p.h_agg_P = reinterpret_cast<float*>(ws + l.h_carry);
+    p.h_agg_H = reinterpret_cast<float*>(ws + l.h_agg);
+    p.ckpt_out = reinterpret_cast<float*>(ws + l.ckpt);
     p.h_carry = reinterpret_cast<const float*>(ws + l.h_carry);
     p.g_carry = reinterpret_cast<float*>(ws + l.g_carry);
     p.p_rev = reinterpret_cast<float*>(ws + l.p_rev);
@@ -764,7 +853,7 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     p.chunk_len = plan.chunk_len;
     p.nchunks = plan.nchunks;
     p.nslots = plan.nchunks - 1;
-    p.nk = (a.seqlen + kCkEvery - 1) / kCkEvery;
+    p.nk = (a.seqlen + kCk - 1) / kCk;
     p.dim = static_cast<int>(a.dim);
     p.nbatch = static_cast<int>(a.batch);
     constexpr int G = lanes_per_channel(N);
@@ -773,19 +862,24 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     const unsigned gx = static_cast<unsigned>((a.dim + kBlk - 1) / kBlk);
     const int64_t count = a.batch * a.dim * N;
 
+    dim3 g1(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
+    if (a.z) {
+        if (a.softplus) hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, true, true>), g1, dim3(kBlk), 0, a.stream, p);
+        else hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, true, false>), g1, dim3(kBlk), 0, a.stream, p);
+    } else {
+        if (a.softplus) hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, false, true>), g1, dim3(kBlk), 0, a.stream, p);
+        else hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, false, false>), g1, dim3(kBlk), 0, a.stream, p);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (p.nslots > 0) {
-        dim3 g2(gx, static_cast<unsigned>(p.nslots), static_cast<unsigned>(a.batch));
-        if (a.z) {
-            if (a.softplus) hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, true, true>), g2, dim3(kBlk), 0, a.stream, p);
-            else hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, true, false>), g2, dim3(kBlk), 0, a.stream, p);
-        } else {
-            if (a.softplus) hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, false, true>), g2, dim3(kBlk), 0, a.stream, p);
-            else hipLaunchKernelGGL((bwd_rev_aggregate_kernel<T, N, false, false>), g2, dim3(kBlk), 0, a.stream, p);
-        }
+        const dim3 gc(static_cast<unsigned>((count + 255) / 256));
+        hipLaunchKernelGGL(bwd_fwd_carry_kernel, gc, dim3(256), 0, a.stream, p.h_agg_P,
+                           static_cast<const float*>(p.h_agg_H), count, p.nslots);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_rev_carry_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0,
-                           a.stream, p.g_carry, static_cast<const float*>(p.p_rev), count, p.nslots);
+        hipLaunchKernelGGL(bwd_rev_carry_kernel, gc, dim3(256), 0, a.stream, p.g_carry, static_cast<const float*>(p.p_rev),
+                           count, p.nslots);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
