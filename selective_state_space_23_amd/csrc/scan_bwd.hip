@@ -429,6 +429,73 @@ __device__ __forceinline__ float sum_group(float v) {
     return v;
 }
 
+// Sums over lanes without LDS: V values per lane (v[i], v[i + V/2] are dB and dC
+// terms of one state), added over the lanes that differ in bits 1..5 of the lane
+// index, and over bit 0 too unless HALVES (then lanes l and l ^ 1 hold different
+// state halves of one channel and stay apart).  Each step pairs lanes that differ
+// in one bit: each keeps half of its values and receives the partner's partial
+// sums of that half, so the exchanges halve with every step (the permlane swaps
+// of bits 5 and 4 deliver both halves at once).  Lane l ends with the total of
+// value (l >> 2) & 15 (V = 16) or (l >> 3) & 7 (V = 8) of its half.
+// v_permlane32_swap exchanges lanes 32..63 of a with lanes 0..31 of b, so a + b
+// afterwards holds value a summed over lane pairs (l, l + 32) in the low half
+// and value b in the high half; v_permlane16_swap does the same for odd and even
+// 16-lane rows.  Written as asm because the compiler's builtins for them lose
+// the second result (both results come back in one register); the s_nop before
+// gives the VALU-write-to-permlane-read distance the compiler cannot see through
+// asm, the one after covers the read of the results.
+__device__ __forceinline__ float swap_add32(float a, float b) {
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 0" : "+v"(a), "+v"(b));
+    return a + b;
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 0" : "+v"(a), "+v"(b));
+    return a + b;
+}
+__device__ __forceinline__ float dpp_f(float v, int ctrl_is_ror8) {
+    return __builtin_bit_cast(float, ctrl_is_ror8
+        ? __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)     // lane ^ 8 (row_ror:8)
+        : __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));    // lane ^ 2 (quad_perm 2,3,0,1)
+}
+__device__ __forceinline__ float xor4_f(float v, bool hi) {           // the value of lane ^ 4
+    const int a = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x104, 0xF, 0xF, false);   // lane + 4
+    const int b = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, false);   // lane - 4
+    return __builtin_bit_cast(float, hi ? b : a);
+}
+// Steps for bits 5 and 4 on one group of values; used per group of 4 states as
+// the values are produced (w[i] = the bit-5 sums, filled in 4 at a time).
+template <int V, bool HALVES>
+__device__ __forceinline__ float lane_sum_finish(const float (&w)[V / 2], int lane) {
+    constexpr int V2 = V / 4;
+    float x[V2];
+#pragma unroll
+    for (int i = 0; i < V2; ++i) x[i] = swap_add16(w[i], w[i + V2]);
+    const bool b3 = lane & 8, b2 = lane & 4;
+    float z;
+    if constexpr (V2 == 4) {
+        float y[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float keep = b3 ? x[i + 2] : x[i];
+            const float send = b3 ? x[i] : x[i + 2];
+            y[i] = keep + dpp_f(send, 1);
+        }
+        const float keep = b2 ? y[1] : y[0];
+        const float send = b2 ? y[0] : y[1];
+        z = keep + xor4_f(send, b2);
+    } else {
+        static_assert(V2 == 2, "8 or 16 values a lane");
+        const float keep = b3 ? x[1] : x[0];
+        const float send = b3 ? x[0] : x[1];
+        const float y = keep + dpp_f(send, 1);
+        z = y + xor4_f(y, b2);
+    }
+    z += dpp_f(z, 0);
+    if constexpr (!HALVES)
+        z += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, z), 0xB1, 0xF, 0xF, false));
+    return z;
+}
+
 // Waves per SIMD the main pass is compiled for: 3 with 8 states a lane (two
 // lanes per channel at N = 16; a few spills, measured faster than 2 without),
 // 2 otherwise.
@@ -440,18 +507,15 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
     constexpr int NL = N / G;              // states per lane
     constexpr int CPB = kBlk / G;          // channels per block
     constexpr int V = 2 * NL;              // dB_t and dC_t terms of one lane
-    constexpr int kTS = V + 4;             // transposition row stride (16-byte aligned rows)
     constexpr int NOUT = 2 * N;            // sums per token: dB_t, then dC_t
-    constexpr int R = 64 / NOUT;           // lanes per sum
-    constexpr int ROWS = 64 / G / R;       // rows each of them adds
+    constexpr int kSumShift = V == 16 ? 2 : 3;              // lane l holds value (l >> kSumShift) of the lane sums
+    constexpr int kWriter = ((1 << kSumShift) - 1) & (G == 2 ? ~1 : ~0);   // lanes with (l & kWriter) == 0 store it
     constexpr int kWinFloats = kWin * N;
     constexpr bool kKeepDecay = NL <= MAMBA_BWD_KEEP_NL;
-    static_assert(N % G == 0 && NL % 4 == 0 && 64 % NOUT == 0, "state split");
+    static_assert(N % G == 0 && NL % 4 == 0 && G <= 2 && (V == 8 || V == 16), "state split");
     __shared__ float4 sBC4[2 * kWinFloats / 4];          // B then C of the window
-    __shared__ float4 sT4[kWaves * 64 * kTS / 4];        // per-wave transposition
     __shared__ float sP[2][kWaves * kCk * NOUT];         // per-wave sums of a 16-token block (2 buffers)
     float* sBC = reinterpret_cast<float*>(sBC4);
-    float* sT = reinterpret_cast<float*>(sT4);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -589,7 +653,6 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
             for (int i = 0; i < NL; ++i) hs[k][i] = k == 0 ? st[i] : hs[k - 1][i];
             fstep(hs[k], dtv[k], dtv[k] * uv[k], o4 + k);
         }
-        float* row = sT + (wave * 64 + lane) * kTS;
 #pragma unroll
         for (int k = kPiece - 1; k >= 0; --k) {
             const int64_t t = s4 + k;
@@ -610,6 +673,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
             const float4* Bq = reinterpret_cast<const float4*>(sBC + o * N + n0);
             const float4* Cq = reinterpret_cast<const float4*>(sBC + kWinFloats + o * N + n0);
             float sB = 0.0f, sq = 0.0f, y = 0.0f;
+            float wsum[NL];        // dB_t and dC_t terms of state i, summed over lane bit 5
 #pragma unroll
             for (int q = 0; q < NL / 4; ++q) {
                 const float4 bv = Bq[q];
@@ -632,9 +696,8 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
                     vc[j] = dy * hs[k][i];
                     if constexpr (HAS_Z) y = __builtin_fmaf(cc[j], hs[k][i], y);
                 }
-                // this lane's dB_t, dC_t terms go to its transposition row
-                reinterpret_cast<float4*>(row)[q] = make_float4(vb[0], vb[1], vb[2], vb[3]);
-                reinterpret_cast<float4*>(row + NL)[q] = make_float4(vc[0], vc[1], vc[2], vc[3]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wsum[4 * q + j] = swap_add32(vb[j], vc[j]);
             }
             sB = sum_group<G>(sB);
             sq = sum_group<G>(sq);
@@ -654,28 +717,15 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
                     buf_store_s<T>(dz_rs, lane_off, so, dov[k] * yf * sgz * __builtin_fmaf(zv[k], 1.0f - sgz, 1.0f));
                 }
             }
-            // dB_t, dC_t: sum the wave's rows column by column.  Sum o covers
-            // value j of the lanes with sub-lane index h; R lanes share it.
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int os = lane % NOUT;
-            const int part = lane / NOUT;
-            const int h = os / V;
-            const int j = os % V;
-            const float* col = sT + (wave * 64 + h + G * part * ROWS) * kTS + j;
-            float sum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < ROWS; ++i) sum += col[i * G * kTS];
-#pragma unroll
-            for (int m = NOUT; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
-            if (lane < NOUT) {
-                const int n = j < NL ? h * NL + j : N + h * NL + (j - NL);
-                sp[(wave * kCk + k4 + k) * NOUT + n] = sum;
+            // dB_t, dC_t: the wave's sums over its channels (lane sums, no LDS);
+            // the 4 waves' sums meet in sp.
+            const float tot = lane_sum_finish<V, G == 2>(wsum, lane);
+            if ((lane & kWriter) == 0) {
+                const int vi = (lane >> kSumShift) & (V - 1);
+                const int h = G == 2 ? (lane & 1) : 0;
+                const int n = vi < NL ? h * NL + vi : N + h * NL + (vi - NL);
+                sp[(wave * kCk + k4 + k) * NOUT + n] = tot;
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #if MAMBA_BWD_TOKEN_BARRIER
             __builtin_amdgcn_sched_barrier(0);
 #endif
