@@ -234,8 +234,10 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
  *   ddelta_bias (D,) float32 or NULL (not computed).
  *   workspace  at least mamba_selective_scan_bwd_workspace_bytes bytes, 256-byte
  *              aligned, scratch (contents on entry ignored).
- * Supported: nheads == 0, N in {4, 8, 16}, and what the forward requires; others
- * return MAMBA_ERR_UNSUPPORTED.  Outputs must not overlap each other, the inputs
+ * Supported: nheads == 0, N in {4, 8, 16}, and what the forward requires; with
+ * bf16 also an even D; others return MAMBA_ERR_UNSUPPORTED.  With bf16, u,
+ * delta, z and dout must be 4-byte aligned (they are read as pairs of channels),
+ * else MAMBA_ERR_MISALIGNED.  Outputs must not overlap each other, the inputs
  * or the workspace.  The sums over channels, tokens and rows run in a fixed
  * order: repeated calls give bitwise identical results. */
 int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,

@@ -334,7 +334,13 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
     if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
         return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
-    const void* acts[] = {u, delta, z, dout, du, ddelta, dz};
+    // The main pass stages u, delta, z and dout through 4-byte loads (pairs of
+    // bf16 channels): even D, 4-byte aligned rows.
+    if (esz == 2 && Dm % 2 != 0) return MAMBA_ERR_UNSUPPORTED;
+    const void* staged[] = {u, delta, z, dout};
+    for (const void* t : staged)
+        if (t && !aligned(t, 4)) return MAMBA_ERR_MISALIGNED;
+    const void* acts[] = {du, ddelta, dz};
     for (const void* t : acts)
         if (t && !aligned(t, esz)) return MAMBA_ERR_MISALIGNED;
     if (!aligned(B, 4) || !aligned(C, 4) || !aligned(dB, esz) || !aligned(dC, esz) || (N * esz) % 4 != 0)

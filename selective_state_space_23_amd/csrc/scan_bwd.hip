@@ -44,9 +44,12 @@
 // Mapping: as in the forward, lanes are channels and keep their N states and
 // adjoints in VGPRs, B_t and C_t are staged in LDS per 64-token window, so du,
 // ddt and dA are per-lane sums.  dB_t and dC_t are sums over channels: each
-// wave transposes its 2N per-lane values of a token through LDS and sums
-// columns, the 4 waves' sums meet in LDS, and each block writes one partial per
-// token.
+// wave adds its 2N per-lane values of a token across its lanes with permlane
+// swaps and DPP (no LDS), the 4 waves' sums meet in LDS, and each block writes
+// one partial per token.  The main pass reads a 16-token block's per-channel
+// inputs (dt, u, dout, z, delta) from LDS, where buffer loads that write LDS
+// directly put them while the block after it (in time) is finishing, so the
+// memory latency is hidden without holding registers.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -516,6 +519,14 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
     __shared__ float4 sBC4[2 * kWinFloats / 4];          // B then C of the window
     __shared__ float sP[2][kWaves * kCk * NOUT];         // per-wave sums of a 16-token block (2 buffers)
     float* sBC = reinterpret_cast<float*>(sBC4);
+    // Per-wave staging of one 16-token block's per-channel inputs, token-major:
+    // dt (fp32), then u, dout, [z], [delta] (T) of the wave's CPW channels.
+    constexpr int CPW = 64 / G;                                          // channels per wave
+    constexpr int kTsz = static_cast<int>(sizeof(T));
+    constexpr int kNArr = 2 + (HAS_Z ? 1 : 0) + (SOFTPLUS ? 1 : 0);
+    constexpr int kStgBytes = kCk * CPW * (4 + kNArr * kTsz);
+    static_assert(kStgBytes % 16 == 0, "staging rows");
+    __shared__ float4 sStg4[kWaves * kStgBytes / 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -553,8 +564,8 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
     const float Dd = p.D ? p.D[dc] : 0.0f;
     const int64_t count = static_cast<int64_t>(p.nbatch) * p.dim * N;
     const int64_t my_slot = (b * p.dim + dc) * N + n0;
-    // Checkpoint k of this channel, row r: ck_lane[(k * (N + 2) + r) * dim].
-    const float* ck_lane = p.ckpt + b * p.nk * (N + 2) * p.dim + dc;
+    // Checkpoint k of this row: (N + 2) rows of dim floats at ck_row + k (N + 2) dim.
+    const float* ck_row = p.ckpt + b * p.nk * (N + 2) * p.dim;
 
     // Element offsets: a lane-constant byte offset plus a wave-uniform one per
     // token (the buffer instruction's scalar offset), so per-token addresses cost
@@ -584,16 +595,87 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
         // exponentials: each token already offers NL independent chains.
         __builtin_amdgcn_sched_barrier(0);
     };
-    // dt and u of token t: dt = 0 past the chunk end (an identity step), u = 0 on
-    // an inactive lane (its dB terms vanish).  The values pass through opaque()
-    // so that each recompute level evaluates its own exponentials.
-    auto load_dtu = [&](int64_t t, float& dt, float& uu) {
-        const int so = tok_soff(t);
-        dt = buf_load_s<float>(dt_rs, dc * 4, so * (4 / kEsz));
-        uu = buf_load_s<T>(u_rs, lane_off, so);
-        dt = opaque(t < t_end ? dt : 0.0f);
-        uu = active ? uu : 0.0f;
+    // Staging: the wave's inputs of the block at s_cur arrive in LDS through
+    // buffer loads that write LDS directly (no registers held while in flight),
+    // issued one block ahead.  Lane l of such a load writes the dword at
+    // lds + 4 l, so a load covers 64 / CPW (dt) or 64 / (CPW T / 4) (T arrays)
+    // token rows: a lane-constant byte offset (row within the load, channel)
+    // plus a wave-uniform one for the token.  Channels past the last are clamped
+    // to it (their lanes are inactive); tokens past the chunk end read the next
+    // chunk's values or, past the row end, zeros (the buffer range check), and
+    // are masked where they are used.
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    char* stg = reinterpret_cast<char*>(sStg4) + wave_s * kStgBytes;
+    const int cw0 = blockIdx.x * CPB + wave_s * CPW;                     // first channel of the wave
+    const int chw = lane / G;                                            // this lane's channel in the wave
+    auto lds_ptr = [](char* q) { return (__attribute__((address_space(3))) void*)(q); };
+    auto stage_voff = [&](int esz) {             // lane-constant part of a staging load's offset
+        const int lpr = CPW * esz / 4;          // dwords per token row
+        const int ce = (lane % lpr) * (4 / esz);
+        const int ch = cw0 + ce < p.dim ? cw0 + ce : p.dim - 4 / esz;
+        return ((lane / lpr) * p.dim + ch) * esz;
     };
+    const int voff_f = stage_voff(4);
+    const int voff_t = stage_voff(kTsz);
+    auto stage_arr = [&](__amdgpu_buffer_rsrc_t rs, int esz, int voff, char* dst, int64_t s0) {
+        const int tpi = 64 / (CPW * esz / 4);   // token rows per load
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i * tpi >= kCk) break;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst + i * tpi * CPW * esz), 4, voff,
+                                                     static_cast<int>((s0 + i * tpi) * p.dim * esz), 0, 0);
+        }
+    };
+    auto stage_block = [&](int64_t s0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's reads of the buffer are done
+        char* q = stg;
+        stage_arr(dt_rs, 4, voff_f, q, s0);
+        q += kCk * CPW * 4;
+        stage_arr(u_rs, kTsz, voff_t, q, s0);
+        q += kCk * CPW * kTsz;
+        stage_arr(do_rs, kTsz, voff_t, q, s0);
+        q += kCk * CPW * kTsz;
+        if constexpr (HAS_Z) {
+            stage_arr(z_rs, kTsz, voff_t, q, s0);
+            q += kCk * CPW * kTsz;
+        }
+        if constexpr (SOFTPLUS) stage_arr(dl_rs, kTsz, voff_t, q, s0);
+    };
+    auto stg_val = [&](int arr, int k) -> float {          // arr 0: dt, 1: u, 2: dout, 3: z, 4: delta
+        if (arr == 0) return reinterpret_cast<const float*>(stg)[k * CPW + chw];
+        int slot = arr - 1;
+        if (!HAS_Z && arr == 4) slot = 2;
+        const char* base = stg + kCk * CPW * 4 + slot * kCk * CPW * kTsz;
+        if constexpr (kTsz == 2)
+            return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[k * CPW + chw]);
+        else
+            return reinterpret_cast<const float*>(base)[k * CPW + chw];
+    };
+    int64_t s_cur = 0;                          // first token of the staged block
+    // dt and u of token t of the staged block: dt = 0 past the chunk end (an
+    // identity step), u = 0 on an inactive lane (its dB terms vanish).  The
+    // values pass through opaque() so that each recompute level evaluates its
+    // own exponentials.
+    const float active_f = active ? 1.0f : 0.0f;
+    auto load_dtu = [&](int64_t t, float& dt, float& uu) {
+        const int k = static_cast<int>(t - s_cur);
+        dt = opaque(stg_val(0, k) * (t < t_end ? 1.0f : 0.0f));
+        uu = stg_val(1, k) * active_f;
+    };
+    // The next block's checkpoint rows (local state, step-size sum, document
+    // flag), fetched into registers with the block's staging.
+    float ckv[NL], ck_cdt = 0.0f, ck_flag = 0.0f;
+    auto fetch_ck = [&](int64_t s0) {
+        const __amdgpu_buffer_rsrc_t ck_rs =
+            make_rsrc(ck_row + (s0 >> kCkShift) * (N + 2) * p.dim, (N + 2) * p.dim * 4);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) ckv[i] = buf_load_s<float>(ck_rs, (n0 * p.dim + dc) * 4, i * p.dim * 4);
+        ck_cdt = buf_load_s<float>(ck_rs, dc * 4, N * p.dim * 4);
+        ck_flag = buf_load_s<float>(ck_rs, dc * 4, (N + 1) * p.dim * 4);
+    };
+    // The state entering the chunk (row b of carry slot c - 1).
+    const __amdgpu_buffer_rsrc_t hin_rs =
+        make_rsrc(p.h_carry + (c > 0 ? c - 1 : 0) * count + b * p.dim * N, p.dim * N * 4);
     // h <- the state after tokens t0 .. t0 + 3 (window offsets o0 ..).
     auto advance4 = [&](float (&h)[NL], int64_t t0, int o0) {
         float dtv[kPiece], uv[kPiece];
@@ -641,10 +723,16 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
 #pragma unroll
         for (int k = 0; k < kPiece; ++k) {
             load_dtu(s4 + k, dtv[k], uv[k]);
-            const int so = tok_soff(s4 + k);
-            dov[k] = buf_load_s<T>(do_rs, lane_off, so);
-            zv[k] = HAS_Z ? buf_load_s<T>(z_rs, lane_off, so) : 0.0f;
-            dlv[k] = SOFTPLUS ? buf_load_s<T>(dl_rs, lane_off, so) : 0.0f;
+            const int kk = static_cast<int>(s4 + k - s_cur);
+            dov[k] = stg_val(2, kk);
+            zv[k] = HAS_Z ? stg_val(3, kk) : 0.0f;
+            dlv[k] = SOFTPLUS ? stg_val(4, kk) : 0.0f;
+        }
+        // The last piece of a block has read its inputs: the staging buffer is
+        // free for the block before it.
+        if (s4 == s_cur && s_cur > t_begin) {
+            stage_block(s_cur - kCk);
+            fetch_ck(s_cur - kCk);
         }
         float hs[kPiece][NL];
 #pragma unroll
@@ -732,6 +820,11 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
         }
     };
 
+    {
+        const int64_t s_last = t_begin + ((t_end - t_begin - 1) / kCk) * kCk;
+        stage_block(s_last);
+        fetch_ck(s_last);
+    }
     const int64_t nwin = (t_end - t_begin + kWin - 1) / kWin;
     for (int64_t wi = nwin - 1; wi >= 0; --wi) {
         const int64_t w0 = t_begin + wi * kWin;
@@ -749,22 +842,18 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
             const int os = kb * kCk;
             float* sp = sP[buf];
             float ck0[NL], ck8[NL];
+            // The block's staged inputs and checkpoint have landed.
+            s_cur = s;
+            __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
             // local checkpoint + exp(A * sum dt) * (state entering the chunk)
-            auto load_ck = [&](int64_t t, float (&h)[NL]) {
-                const float* src = ck_lane + (t >> kCkShift) * (N + 2) * p.dim;
-                const float cdt = src[static_cast<int64_t>(N) * p.dim];
-                const bool fresh = c == 0 || src[static_cast<int64_t>(N + 1) * p.dim] != 0.0f;
-                const float* hin = p.h_carry + (c > 0 ? c - 1 : 0) * count + my_slot;
-                if (fresh) {
+            {
+                const bool fresh = c == 0 || ck_flag != 0.0f;
 #pragma unroll
-                    for (int i = 0; i < NL; ++i) h[i] = src[static_cast<int64_t>(n0 + i) * p.dim];
-                } else {
-#pragma unroll
-                    for (int i = 0; i < NL; ++i)
-                        h[i] = __builtin_fmaf(exp2_fast(Al2[i] * cdt), hin[i], src[static_cast<int64_t>(n0 + i) * p.dim]);
-                }
-            };
-            load_ck(s, ck0);
+                for (int i = 0; i < NL; ++i)
+                    ck0[i] = fresh ? ckv[i]
+                                   : __builtin_fmaf(exp2_fast(Al2[i] * ck_cdt),
+                                                    buf_load_s<float>(hin_rs, (dc * N + n0) * 4, i * 4), ckv[i]);
+            }
 #pragma unroll
             for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];
             advance4(ck8, s, os);

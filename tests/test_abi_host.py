@@ -246,6 +246,10 @@ def test_bwd_validation(lib):
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=32)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=0), u=None, dout=None) == _lib.MAMBA_OK   # empty: no-op
+    # bf16 inputs are staged as channel pairs: even D, 4-byte aligned u, delta, z, dout
+    assert bwd(lib, d=dims(batch=1, seqlen=64, dim=63, dtype=1)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dtype=1), u=FAKE + 2) == _lib.MAMBA_ERR_MISALIGNED
+    assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dtype=1), dout=FAKE * 6 + 2) == _lib.MAMBA_ERR_MISALIGNED
 
 
 def test_conv_bwd_validation(lib):
