@@ -128,7 +128,7 @@ def copy_probe(torch, dev, mib=1024, reps=5):
 # The kernel sources each timed path is compiled from: a recorded FETCH/WRITE
 # profile counts only while these files are unchanged.
 FWD_SOURCES = ["device_common.hpp", "launch.hpp", "conv1d.hip", "scan.hip", "ssd.hip"]
-BWD_SOURCES = ["device_common.hpp", "launch.hpp", "scan.hip", "scan_bwd.hip", "conv1d_bwd.hip"]
+BWD_SOURCES = ["device_common.hpp", "launch.hpp", "scan_bwd.hip", "conv1d_bwd.hip"]
 
 
 def recorded_traffic(path, source_files):

@@ -662,9 +662,12 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
         dt = opaque(stg_val(0, k) * (t < t_end ? 1.0f : 0.0f));
         uu = stg_val(1, k) * active_f;
     };
+    // The state entering the chunk (row b of carry slot c - 1).
+    const __amdgpu_buffer_rsrc_t hin_rs =
+        make_rsrc(p.h_carry + (c > 0 ? c - 1 : 0) * count + b * p.dim * N, p.dim * N * 4);
     // The next block's checkpoint rows (local state, step-size sum, document
     // flag), fetched into registers with the block's staging.
-    float ckv[NL], ck_cdt = 0.0f, ck_flag = 0.0f;
+    float ckv[NL], hinv[NL], ck_cdt = 0.0f, ck_flag = 0.0f;
     auto fetch_ck = [&](int64_t s0) {
         const __amdgpu_buffer_rsrc_t ck_rs =
             make_rsrc(ck_row + (s0 >> kCkShift) * (N + 2) * p.dim, (N + 2) * p.dim * 4);
@@ -672,10 +675,9 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
         for (int i = 0; i < NL; ++i) ckv[i] = buf_load_s<float>(ck_rs, (n0 * p.dim + dc) * 4, i * p.dim * 4);
         ck_cdt = buf_load_s<float>(ck_rs, dc * 4, N * p.dim * 4);
         ck_flag = buf_load_s<float>(ck_rs, dc * 4, (N + 1) * p.dim * 4);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) hinv[i] = buf_load_s<float>(hin_rs, (dc * N + n0) * 4, i * 4);
     };
-    // The state entering the chunk (row b of carry slot c - 1).
-    const __amdgpu_buffer_rsrc_t hin_rs =
-        make_rsrc(p.h_carry + (c > 0 ? c - 1 : 0) * count + b * p.dim * N, p.dim * N * 4);
     // h <- the state after tokens t0 .. t0 + 3 (window offsets o0 ..).
     auto advance4 = [&](float (&h)[NL], int64_t t0, int o0) {
         float dtv[kPiece], uv[kPiece];
@@ -850,9 +852,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_
                 const bool fresh = c == 0 || ck_flag != 0.0f;
 #pragma unroll
                 for (int i = 0; i < NL; ++i)
-                    ck0[i] = fresh ? ckv[i]
-                                   : __builtin_fmaf(exp2_fast(Al2[i] * ck_cdt),
-                                                    buf_load_s<float>(hin_rs, (dc * N + n0) * 4, i * 4), ckv[i]);
+                    ck0[i] = fresh ? ckv[i] : __builtin_fmaf(exp2_fast(Al2[i] * ck_cdt), hinv[i], ckv[i]);
             }
 #pragma unroll
             for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];
