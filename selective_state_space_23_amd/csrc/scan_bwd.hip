@@ -64,7 +64,7 @@ constexpr int kCk = 16;                // tokens per block of the main pass
 constexpr int kCkShift = 4;            // a checkpoint before every block: log2(kCk)
 constexpr int kPiece = 4;              // tokens per innermost recompute piece
 #ifndef MAMBA_BWD_WAVES_PER_EU
-#define MAMBA_BWD_WAVES_PER_EU 0        // 0: chosen per state count (bwd_waves_per_eu)
+#define MAMBA_BWD_WAVES_PER_EU 0        // 0: the default, 2 waves per SIMD for the main pass
 #endif
 #ifndef MAMBA_BWD_TOKEN_BARRIER
 #define MAMBA_BWD_TOKEN_BARRIER 1
@@ -420,7 +420,8 @@ __global__ __launch_bounds__(256) void bwd_rev_carry_kernel(float* __restrict__ 
 // 4. Main pass over chunk blockIdx.y of row blockIdx.z.
 //
 // G lanes share one channel, each holding NL = N / G of its states (G = 2 at
-// N = 16 halves the per-lane arrays, which is what lets 3 waves share a SIMD);
+// N = 16 halves the per-lane arrays, which is what lets the pass run without
+// spills);
 // their partial sums over states (g.B, the A term, C.h) meet through one DPP
 // exchange per sum, and every lane of the group computes the per-token scalars.
 template <int G>
@@ -499,13 +500,14 @@ __device__ __forceinline__ float lane_sum_finish(const float (&w)[V / 2], int la
     return z;
 }
 
-// Waves per SIMD the main pass is compiled for: 3 with 8 states a lane (two
-// lanes per channel at N = 16; a few spills, measured faster than 2 without),
-// 2 otherwise.
-constexpr int bwd_waves_per_eu(int nl) { return MAMBA_BWD_WAVES_PER_EU > 0 ? MAMBA_BWD_WAVES_PER_EU : (nl == 8 ? 3 : 2); }
+// Waves per SIMD the main pass is compiled for: 2, which leaves it the
+// registers to run without spills (at 3 the spill traffic missed in L2 and cost
+// more than the extra wave hid; its inputs arrive through LDS, so it needs
+// little occupancy for latency).
+constexpr int kBwdWavesPerEu = MAMBA_BWD_WAVES_PER_EU > 0 ? MAMBA_BWD_WAVES_PER_EU : 2;
 
 template <typename T, int N, int G, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(N / G)))) void bwd_chunk_kernel(
+__global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesPerEu))) void bwd_chunk_kernel(
     const BwdKParams p) {
     constexpr int NL = N / G;              // states per lane
     constexpr int CPB = kBlk / G;          // channels per block
