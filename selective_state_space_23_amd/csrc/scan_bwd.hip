@@ -69,9 +69,6 @@ constexpr int kPiece = 4;              // tokens per innermost recompute piece
 #ifndef MAMBA_BWD_TOKEN_BARRIER
 #define MAMBA_BWD_TOKEN_BARRIER 1
 #endif
-#ifndef MAMBA_BWD_KEEP_NL
-#define MAMBA_BWD_KEEP_NL 4      // keep the recompute's decays in registers up to this many states a lane
-#endif
 #ifndef MAMBA_BWD_G16
 #define MAMBA_BWD_G16 2          // lanes per channel at N = 16
 #endif
@@ -516,7 +513,6 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
     constexpr int kSumShift = V == 16 ? 2 : 3;              // lane l holds value (l >> kSumShift) of the lane sums
     constexpr int kWriter = ((1 << kSumShift) - 1) & (G == 2 ? ~1 : ~0);   // lanes with (l & kWriter) == 0 store it
     constexpr int kWinFloats = kWin * N;
-    constexpr bool kKeepDecay = NL <= MAMBA_BWD_KEEP_NL;
     static_assert(N % G == 0 && NL % 4 == 0 && G <= 2 && (V == 8 || V == 16), "state split");
     __shared__ float4 sBC4[2 * kWinFloats / 4];          // B then C of the window
     __shared__ float sP[2][kWaves * kCk * NOUT];         // per-wave sums of a 16-token block (2 buffers)
@@ -751,9 +747,9 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
             const bool live = t < t_end && active;
             const int o = o4 + k;
             const float r = ((starts >> o) & 1ull) ? -__builtin_inff() : 0.0f;
-            // With few states per lane the decays of the recompute above stay in
-            // registers; otherwise they are evaluated again (registers are the limit).
-            const float dt = kKeepDecay ? dtv[k] : opaque(dtv[k]);
+            // The same dt as the recompute above, so the compiler keeps that
+            // recompute's decays in registers for the adjoint (4 x NL values).
+            const float dt = dtv[k];
             const float uu = uv[k];
             const float w = dt * uu;
             float sgz = 0.0f, dy = dov[k];
