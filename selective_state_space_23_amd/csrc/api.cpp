@@ -302,8 +302,8 @@ int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bia
     a.dweight = dweight; a.dbias = dbias; a.ws = static_cast<float*>(workspace);
     a.batch = batch; a.seqlen = seqlen; a.dim = dim;
     a.bf16 = dtype == MAMBA_DTYPE_BF16;
-    const size_t vbytes = 4 * esz;           // 4-channel vectors
-    a.vectorized = (dim % 4) == 0 && aligned(x, vbytes) && aligned(du, vbytes) && aligned(dx, vbytes);
+    const size_t vbytes = 2 * esz;           // channel pairs
+    a.vectorized = (dim % 2) == 0 && aligned(x, vbytes) && aligned(du, vbytes) && aligned(dx, vbytes);
     a.apply_silu = apply_silu != 0;
     a.stream = static_cast<hipStream_t>(stream);
     return mamba::launch_causal_conv1d_bwd(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;

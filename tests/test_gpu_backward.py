@@ -159,9 +159,10 @@ def test_bwd_workload(ssm, name):
 # ----------------------------------------------------------------------------
 CONV_BWD_CASES = [
     # (batch, seqlen, dim, dtype, docs)
-    (2, 200, 64, "bf16", 20.0),       # 16-byte vectors, several 48-token tiles
-    (2, 131, 37, "bf16", 9.0),        # ragged D: one channel a thread
-    (1, 100, 36, "f32", 7.0),         # ragged D for f32 vectors
+    (2, 200, 64, "bf16", 20.0),       # channel pairs, several 48-token tiles
+    (2, 131, 37, "bf16", 9.0),        # odd D: one channel a thread
+    (1, 100, 38, "f32", 7.0),         # D = 2 mod 4: f32 channel pairs
+    (2, 150, 38, "bf16", 12.0),       # D = 2 mod 4: bf16 channel pairs
     (3, 1, 24, "bf16", None),         # one token
     (2, 3, 24, "bf16", 2.0),          # fewer tokens than the conv width
     (1, 1000, 1536, "bf16", 64.0),
