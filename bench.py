@@ -525,8 +525,8 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
         "timings": {"scan_bwd_ms": call_ms, "conv_bwd_ms": conv_ms,
                     "conv_bwd_hbm_GBs": cbytes / (conv_ms * 1e-3) / 1e9,
                     "conv_bwd_hbm_frac": cbytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"kernel": "mamba_selective_scan_bwd, one call: forward aggregate and carry, reverse aggregate "
-                               "and carry, main pass, reductions",
+        "roofline": {"kernel": "mamba_selective_scan_bwd, one call: aggregate pass, forward and reverse carries, "
+                               "main pass, reductions",
                      "bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic, "algorithmic_flop_eq": flops,
                      "algorithmic_bytes": nbytes, "hbm_achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,

@@ -217,8 +217,8 @@ int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bia
  *   dD = sum_t dy_t u_t,  dz_t = dout_t y_t silu'(z_t),  ddelta_bias = sum_t ddelta_t. */
 
 /* Bytes of device workspace mamba_selective_scan_bwd needs for `dims` (about
- * B L D N * 4 / 16 + B L D * (elem size) + B L * ceil(D / 256) * 8 N bytes; 780 MB
- * at B = 2, L = 32768, D = 1536, N = 16, bf16). */
+ * B L D (N + 2) * 4 / 16 + B L D * 4 + B L ceil(D / 128) * 8 N bytes plus the
+ * per-chunk carries; 1.08 GB at B = 2, L = 32768, D = 1536, N = 16). */
 int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes);
 
 /* Selective scan backward.
