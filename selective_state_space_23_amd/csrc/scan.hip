@@ -28,6 +28,8 @@
 //          writes out and, for the last chunk, final_state.
 // The carries are the only intermediate data; the (B, L, D, N) state trajectory
 // is never stored.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -103,6 +105,25 @@ template <typename T>
 __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, int byte_off, float v) {
     if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rs, byte_off, 0, 0);
     else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, byte_off, 0, 0);
+}
+
+// The same with the offset split into a lane part (channel) and a wave-uniform
+// part (token) that rides in the instruction's scalar offset: no per-token VALU
+// address arithmetic.
+template <typename T>
+__device__ __forceinline__ float buf_load_s(__amdgpu_buffer_rsrc_t rs, int lane_off, int tok_off) {
+    if constexpr (sizeof(T) == 2) {
+        const uint16_t v = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, lane_off, tok_off, 0));
+        return bf16_to_f32(v);
+    } else {
+        return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, lane_off, tok_off, 0)));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void buf_store_s(__amdgpu_buffer_rsrc_t rs, int lane_off, int tok_off, float v) {
+    if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rs, lane_off, tok_off, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, lane_off, tok_off, 0);
 }
 
 // OUTPUT = false: pass 1 (aggregate of one chunk from a zero state).
@@ -224,9 +245,9 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             const int t = static_cast<int>((g0 + k < t_end) ? g0 + k : t_end - 1);  // clamp the tail
-            uu[k] = buf_load<T>(u_rs, (t * p.dim + dc) * kEsz);
-            dl[k] = buf_load<T>(dl_rs, (t * nd + dsel) * kEsz);
-            if constexpr (OUTPUT && HAS_Z) zz[k] = buf_load<T>(z_rs, (t * p.dim + dc) * kEsz);
+            uu[k] = buf_load_s<T>(u_rs, dc * kEsz, t * p.dim * kEsz);
+            dl[k] = buf_load_s<T>(dl_rs, dsel * kEsz, t * nd * kEsz);
+            if constexpr (OUTPUT && HAS_Z) zz[k] = buf_load_s<T>(z_rs, dc * kEsz, t * p.dim * kEsz);
             else zz[k] = 0.0f;
         }
     };
@@ -274,17 +295,24 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     };
 
     uint64_t starts = 0;
-    auto compute_group = [&](int64_t g0, const float (&cu)[G], const float (&cd)[G], const float (&cz)[G]) {
+    // FAST: every token of the group is inside the chunk and none starts a
+    // document (wave-uniform; all but a few groups), so the masks below fold
+    // away and stores go to the clamped channel (an inactive lane writes the
+    // value its clamped channel's own lane writes) with the token in the scalar
+    // offset.
+    auto compute_group = [&](auto fast_tag, int64_t g0, const float (&cu)[G], const float (&cd)[G],
+                             const float (&cz)[G]) {
+        constexpr bool FAST = decltype(fast_tag)::value;
         const int off = static_cast<int>((g0 - t_begin) & (kWin - 1));
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             // Tokens past the chunk end run as identity steps (dt = 0: decay 1, no
             // input) so the group stays straight-line code.
-            const bool valid = g0 + k < t_end;
+            const bool valid = FAST || g0 + k < t_end;
             const int64_t t = g0 + k;
             // A document start multiplies the carried state by exp2(-inf) = 0: the
             // reset rides in the exponent's addend, with no branch and no extra op.
-            const bool reset = (starts >> (off + k)) & 1ull;
+            const bool reset = !FAST && ((starts >> (off + k)) & 1ull);
             const float r = reset ? -__builtin_inff() : 0.0f;
             if (!OUTPUT) {
                 any_reset = any_reset || reset;
@@ -298,7 +326,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 if constexpr (SOFTPLUS) dt = softplus_f(dt);
                 if constexpr (kDtWs) {
                     if constexpr (sizeof(T) == 2) dt = bf16_to_f32(f32_to_bf16(dt));
-                    buf_store<T>(dto_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, dt);
+                    if constexpr (FAST) buf_store_s<T>(dto_rs, dc * kEsz, static_cast<int>(t) * p.dim * kEsz, dt);
+                    else buf_store<T>(dto_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, dt);
                 }
             }
             dt = valid ? dt : 0.0f;
@@ -316,7 +345,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 if constexpr (sizeof(T) == 2) uk = bf16_to_f32(f32_to_bf16(uk));   // the u pass 3 reads back
                 // Branchless: a store past the resource's end is dropped by the
                 // hardware, and a branch here would double the register footprint.
-                buf_store<T>(uo_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, uk);
+                if constexpr (FAST) buf_store_s<T>(uo_rs, dc * kEsz, static_cast<int>(t) * p.dim * kEsz, uk);
+                else buf_store<T>(uo_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, uk);
                 xh3 = xh2;
                 xh2 = xh1;
                 xh1 = xt;
@@ -350,7 +380,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             if constexpr (OUTPUT) {
                 float y = (y0 + y1) + Dd * cu[k];
                 if constexpr (HAS_Z) y *= silu_f(cz[k]);
-                if (active && valid) buf_store<T>(uo_rs, (static_cast<int>(t) * p.dim + d) * kEsz, y);
+                if constexpr (FAST) buf_store_s<T>(uo_rs, dc * kEsz, static_cast<int>(t) * p.dim * kEsz, y);
+                else if (active && valid) buf_store<T>(uo_rs, (static_cast<int>(t) * p.dim + d) * kEsz, y);
             } else {
                 sum_dt += dt;
             }
@@ -378,11 +409,18 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
         stage_window(w0);
         __syncthreads();
         const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
+        auto run_group = [&](int64_t g0, const float (&cu)[G], const float (&cd)[G], const float (&cz)[G]) {
+            const int off = static_cast<int>((g0 - t_begin) & (kWin - 1));
+            if (g0 + G <= t_end && ((starts >> off) & ((1ull << G) - 1)) == 0)
+                compute_group(std::true_type{}, g0, cu, cd, cz);
+            else
+                compute_group(std::false_type{}, g0, cu, cd, cz);
+        };
         for (int64_t g0 = w0; g0 < wend; g0 += 2 * G) {
             load_group(g0 + G, bu, bd, bz);
-            compute_group(g0, au, ad, az);
+            run_group(g0, au, ad, az);
             load_group(g0 + 2 * G, au, ad, az);
-            compute_group(g0 + G, bu, bd, bz);
+            run_group(g0 + G, bu, bd, bz);
         }
     }
 
