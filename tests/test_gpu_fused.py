@@ -73,6 +73,27 @@ def test_conv_scan_parity(ssm, case):
     assert_close(to_host(fin), fin_ref, dt, f"fused final_state {case}")
 
 
+@pytest.mark.parametrize("tail", [1, 2, 3])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_conv_scan_group_edges(ssm, tail, dt):
+    """Document starts at every offset inside a 4-token group (and two in one
+    group), and a row end inside a group: such groups take the scan's general
+    path, the others its fast path; both must agree with the oracle."""
+    torch = torch_mod()
+    L = 320 + tail
+    inp = make_custom(2, L, 96, 16, dtype=dt, docs=None, seed=760 + tail)
+    for t in (5, 66, 131, 196, 201, 262, 263, L - 1):     # offsets 1, 2, 3, 0, 1, 2, 3 and the last token
+        inp.doc_start[0, t] = 1
+    inp.doc_start[1, 7::61] = 1
+    dev = upload(inp)
+    u, out, fin = fused(ssm, dev)
+    u_conv = ssm.causal_conv1d_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["doc_start"])
+    assert torch.equal(u, u_conv), "fused conv differs from the conv kernel"
+    _, out_ref, fin_ref = oracle_pipeline(inp, np.arange(96))
+    assert_close(to_host(out), out_ref, dt, f"group edges out tail={tail}")
+    assert_close(to_host(fin), fin_ref, dt, f"group edges final_state tail={tail}")
+
+
 @pytest.mark.parametrize("H,N", [(0, 16), (2, 64)])
 def test_conv_scan_continuation(ssm, H, N):
     """[0, L1) and then [L1, L) with the first part's final state and conv window
