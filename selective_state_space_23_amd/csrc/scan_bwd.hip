@@ -442,12 +442,23 @@ __device__ __forceinline__ float sum_group(float v) {
 // afterwards holds value a summed over lane pairs (l, l + 32) in the low half
 // and value b in the high half; v_permlane16_swap does the same for odd and even
 // 16-lane rows.  Written as asm because the compiler's builtins for them lose
-// the second result (both results come back in one register); the s_nop before
-// gives the VALU-write-to-permlane-read distance the compiler cannot see through
-// asm, the one after covers the read of the results.
-__device__ __forceinline__ float swap_add32(float a, float b) {
-    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 0" : "+v"(a), "+v"(b));
-    return a + b;
+// the second result (both results come back in one register).  Four swaps share
+// one asm block: its leading s_nop gives the VALU-write-to-permlane-read
+// distance the compiler cannot see through asm (the swaps inside touch
+// different registers), the trailing one separates the last swap from a read
+// of its results.
+#define MAMBA_SWAP4(op, a, b)                                                                            \
+    asm("s_nop 1\n\t" op " %0, %4\n\t" op " %1, %5\n\t" op " %2, %6\n\t" op " %3, %7\n\ts_nop 0"   \
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]))
+__device__ __forceinline__ void swap_add32x4(float (&a)[4], float (&b)[4], float* out) {
+    MAMBA_SWAP4("v_permlane32_swap_b32", a, b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = a[j] + b[j];
+}
+__device__ __forceinline__ void swap_add16x4(float (&a)[4], float (&b)[4], float* out) {
+    MAMBA_SWAP4("v_permlane16_swap_b32", a, b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = a[j] + b[j];
 }
 __device__ __forceinline__ float swap_add16(float a, float b) {
     asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 0" : "+v"(a), "+v"(b));
@@ -469,8 +480,13 @@ template <int V, bool HALVES>
 __device__ __forceinline__ float lane_sum_finish(const float (&w)[V / 2], int lane) {
     constexpr int V2 = V / 4;
     float x[V2];
+    if constexpr (V2 == 4) {
+        float lo[4] = {w[0], w[1], w[2], w[3]}, hi[4] = {w[4], w[5], w[6], w[7]};
+        swap_add16x4(lo, hi, x);
+    } else {
 #pragma unroll
-    for (int i = 0; i < V2; ++i) x[i] = swap_add16(w[i], w[i + V2]);
+        for (int i = 0; i < V2; ++i) x[i] = swap_add16(w[i], w[i + V2]);
+    }
     const bool b3 = lane & 8, b2 = lane & 4;
     float z;
     if constexpr (V2 == 4) {
@@ -784,8 +800,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
                     vc[j] = dy * hs[k][i];
                     if constexpr (HAS_Z) y = __builtin_fmaf(cc[j], hs[k][i], y);
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) wsum[4 * q + j] = swap_add32(vb[j], vc[j]);
+                swap_add32x4(vb, vc, wsum + 4 * q);
             }
             sB = sum_group<G>(sB);
             sq = sum_group<G>(sq);
