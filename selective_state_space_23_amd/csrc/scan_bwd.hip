@@ -203,10 +203,10 @@ __device__ __forceinline__ float step_size(float delta, float bias) {
 //     from zero over the chunk.  Unrolled, X_c = sum_t R_t C_t dy_t with
 //     R_t = prod_{s = t0 .. t} a_s: a forward running sum over the same decays
 //     (three multiply-adds per element, no exponential).
-template <typename T, int N, bool HAS_Z, bool SOFTPLUS>
 #ifndef MAMBA_BWD_AGG_WAVES_PER_EU
-#define MAMBA_BWD_AGG_WAVES_PER_EU 3
+#define MAMBA_BWD_AGG_WAVES_PER_EU 3     // 155 VGPRs at N = 16, no spills
 #endif
+template <typename T, int N, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_AGG_WAVES_PER_EU))) void bwd_aggregate_kernel(
     const BwdKParams p) {
     constexpr int kWinFloats = kWin * N;
