@@ -36,7 +36,7 @@ struct ConvBwdArgs {
     float* ws;                // conv_bwd_workspace_bytes
     int64_t batch, seqlen, dim;
     bool bf16;
-    bool vectorized;          // 16-byte accesses: dim and pointers aligned
+    bool vectorized;          // channel pairs: even dim, pointers aligned to two elements
     bool apply_silu;
     hipStream_t stream;
 };
