@@ -10,7 +10,7 @@ Per channel d and state n, with a_t = exp(dt_t A[n]) (0 at a document start),
 h_t = a_t h_{t-1} + dt_t u_t B_t[n], y_t = C_t . h_t + D u_t, out_t = y_t silu(z_t):
 
     dy_t    = dout_t silu(z_t),        dz_t = dout_t y_t silu'(z_t)
-    g_t     = dL/dh_t = C_t dy_t + a_{t+1} g_{t+1}          (g_L = 0)
+    g_t     = dL/dh_t = C_t dy_t + a_{t+1} g_{t+1}          (a_L g_L = dL/d(final state), 0 if not given)
     dC_t   += dy_t h_t                (summed over channels)
     dB_t   += g_t dt_t u_t            (summed over channels)
     du_t    = dy_t D + sum_n g_t[n] dt_t B_t[n]
@@ -19,6 +19,7 @@ h_t = a_t h_{t-1} + dt_t u_t B_t[n], y_t = C_t . h_t + D u_t, out_t = y_t silu(z
     dD     += dy_t u_t
     ddelta_t = ddt_t softplus'(delta_t + bias) = ddt_t sigmoid(delta_t + bias)
     dbias  += ddelta_t
+    dh_{-1} = a_0 g_0                  (the carried-in state, when one is given)
 
 Pinned by central finite differences of `selective_scan` (tests/test_oracle_pins.py).
 """
@@ -31,10 +32,14 @@ from .mamba_oracle import _f64, doc_segment_start, sigmoid, silu
 
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
-                       doc_start=None):
-    """Gradients of sum(dout * out) for the per-channel-A selective scan (A of shape
-    (D, N), no initial state).  Returns a dict with du, ddelta, dA, dB, dC and,
-    when the input is given, dD, dz, ddelta_bias (all float64)."""
+                       doc_start=None, initial_state=None, d_final_state=None):
+    """Gradients of sum(dout * out) + sum(d_final_state * final_state) for the
+    per-channel-A selective scan (A of shape (D, N)).  ``initial_state`` (B, D, N),
+    if given, is the state before token 0 (token 0 then starts a document only
+    where doc_start flags it, as in the forward); ``d_final_state`` (B, D, N) is
+    the gradient arriving at the state after the last token (zero if None).
+    Returns a dict with du, ddelta, dA, dB, dC and, when the input is given, dD,
+    dz, ddelta_bias, d_initial_state (all float64)."""
     u = _f64(u)
     dl = _f64(delta)
     Am = _f64(A)
@@ -48,12 +53,14 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     dt = np.log1p(np.exp(-np.abs(pre))) + np.maximum(pre, 0.0) if delta_softplus else pre
     Dv = np.zeros(Dm) if D is None else _f64(D)
     zz = None if z is None else _f64(z)
-    starts = doc_segment_start(doc_start, Bt, L, first_is_start=True) == np.arange(L)[None, :]
+    first_is_start = initial_state is None
+    starts = doc_segment_start(doc_start, Bt, L, first_is_start=first_is_start) == np.arange(L)[None, :]
+    h_init = np.zeros((Bt, Dm, N)) if initial_state is None else _f64(initial_state)
 
     # Forward, keeping every state and decay (the oracle can afford it).
     a = np.empty((Bt, L, Dm, N))
     h = np.empty((Bt, L, Dm, N))
-    hprev = np.zeros((Bt, Dm, N))
+    hprev = h_init.copy()
     for t in range(L):
         at = np.exp(dt[:, t, :, None] * Am[None, :, :])
         at[starts[:, t]] = 0.0
@@ -80,9 +87,9 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         if t + 1 < L:
             g = a[:, t + 1] * g
         else:
-            g = np.zeros((Bt, Dm, N))
+            g = np.zeros((Bt, Dm, N)) if d_final_state is None else _f64(d_final_state).copy()
         g = g + Cm[:, t, None, :] * dy[:, t, :, None]
-        h_before = h[:, t - 1] if t > 0 else np.zeros((Bt, Dm, N))
+        h_before = h[:, t - 1] if t > 0 else h_init
         q = a[:, t] * h_before                                     # 0 at a start
         dB[:, t] = np.einsum("bdn,bd->bn", g, dt[:, t] * u[:, t])
         du[:, t] += np.einsum("bdn,bn->bd", g, Bm[:, t]) * dt[:, t]
@@ -97,10 +104,13 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         grads["dz"] = dz
     if delta_bias is not None:
         grads["ddelta_bias"] = ddelta.sum(axis=(0, 1))
+    if initial_state is not None:
+        grads["d_initial_state"] = (a[:, 0] * g) if L > 0 else (
+            np.zeros((Bt, Dm, N)) if d_final_state is None else _f64(d_final_state).copy())
     return grads
 
 
-def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu=True):
+def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu=True, conv_state=None):
     """Gradients of sum(du * u) for u = causal_conv1d(x, weight, bias, doc_start,
     apply_silu) ([S] S6 code: Conv1d with left padding W-1, first L outputs, SiLU;
     [A] packing: taps before the token's document start are zero).  With
@@ -109,7 +119,24 @@ def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu=True)
         dx_s      = sum_j dacc_{s+j} w[W-1-j]   over the j with s inside (s+j)'s document
         dw[W-1-j] = sum_t dacc_t x_{t-j}        over the same taps
         dbias     = sum_t dacc_t
-    Returns dx (B, L, D), dweight (D, W) and dbias (D,), float64."""
+    Returns dx (B, L, D), dweight (D, W) and dbias (D,), float64.
+
+    ``conv_state`` (B, D, W-1), if given, holds the inputs of the W-1 tokens
+    before token 0 (oldest first), and token 0 then starts a document only where
+    doc_start flags it.  Those tokens are differentiated as a prefix of the row
+    whose own outputs are not part of the loss, and the result gains a fourth
+    entry, their gradient d_conv_state (B, D, W-1)."""
+    if conv_state is not None:
+        hist = np.transpose(_f64(conv_state), (0, 2, 1))            # (B, W-1, D)
+        Bt, L, Dm = np.shape(x)
+        k = hist.shape[1]
+        flags = np.zeros((Bt, L), dtype=np.uint8) if doc_start is None else (np.asarray(doc_start) != 0)
+        ds_ext = np.concatenate([np.zeros((Bt, k), dtype=np.uint8), flags.astype(np.uint8)], axis=1)
+        ds_ext[:, 0] = 1                                            # the prefix's own start
+        dx_ext, dw, db = causal_conv1d_bwd(np.concatenate([hist, _f64(x)], axis=1), weight,
+                                           np.concatenate([np.zeros((Bt, k, Dm)), _f64(du)], axis=1),
+                                           bias, ds_ext, apply_silu)
+        return dx_ext[:, k:], dw, db, np.transpose(dx_ext[:, :k], (0, 2, 1))
     x = _f64(x)
     w = _f64(weight)
     g = _f64(du)

@@ -451,6 +451,144 @@ def test_conv_gradients_match_finite_differences(silu_on, docs):
             assert abs(fd - grad.flat[flat]) <= 1e-6 * max(1.0, abs(fd)), (flat, fd, grad.flat[flat])
 
 
+def test_gradients_with_carried_state_match_finite_differences():
+    """With an initial state and a gradient arriving at the final state, the loss is
+    sum(dout * out) + sum(d_final * final_state); every input, the initial state
+    included, against central differences.  Row 0 continues the carried state at
+    token 0, row 1 starts a document there (its d_initial_state is then 0)."""
+    args, dout = _grad_case(21)
+    rng = np.random.default_rng(22)
+    Bt, L, Dm = args["u"].shape
+    N = args["B"].shape[-1]
+    args["doc_start"][1, 0] = 1
+    init = rng.normal(size=(Bt, Dm, N))
+    dfin = rng.normal(size=(Bt, Dm, N))
+    g = oracle.selective_scan_bwd(args["u"], args["delta"], args["A"], args["B"], args["C"], dout, args["D"],
+                                  args["z"], args["delta_bias"], args["delta_softplus"], args["doc_start"],
+                                  initial_state=init, d_final_state=dfin)
+
+    def loss():
+        out, fin = oracle.selective_scan(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"],
+                                         args["z"], args["delta_bias"], args["delta_softplus"], args["doc_start"],
+                                         initial_state=init)
+        return float(np.sum(out * dout) + np.sum(fin * dfin))
+
+    assert np.all(g["d_initial_state"][1] == 0.0)
+    eps = 1e-6
+    pairs = [(args[k], g[v]) for k, v in (("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"),
+                                           ("C", "dC"), ("D", "dD"), ("z", "dz"), ("delta_bias", "ddelta_bias"))]
+    pairs.append((init, g["d_initial_state"]))
+    for x, gx in pairs:
+        for flat in range(x.size):
+            orig = x.flat[flat]
+            x.flat[flat] = orig + eps
+            lp = loss()
+            x.flat[flat] = orig - eps
+            lm = loss()
+            x.flat[flat] = orig
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - gx.flat[flat]) <= 1e-6 * max(1.0, abs(fd)), (flat, fd, gx.flat[flat])
+
+
+def _conv_with_history(x, hist, w, bias, ds, silu_on):
+    """The conv with W-1 tokens of history before token 0, written as its own loop:
+    tap j of token t reads x[t - j] (or the history for t - j < 0) unless a
+    document starts in (t - j, t]; token 0 starts one only where ds flags it."""
+    Bt, L, Dm = x.shape
+    W = w.shape[1]
+    u = np.zeros((Bt, L, Dm))
+    for b in range(Bt):
+        for t in range(L):
+            acc = bias.copy()
+            for j in range(W):
+                src = t - j
+                if any(ds[b, s] for s in range(max(src + 1, 0), t + 1)):
+                    break
+                val = x[b, src] if src >= 0 else hist[b, :, W - 1 + src]
+                acc = acc + w[:, W - 1 - j] * val
+            u[b, t] = acc / (1.0 + np.exp(-acc)) if silu_on else acc
+    return u
+
+
+@pytest.mark.parametrize("silu_on", [True, False])
+def test_conv_gradients_with_history_match_finite_differences(silu_on):
+    """oracle.causal_conv1d_bwd with conv_state against central differences of a
+    direct loop over the taps (history, weights, bias and x); row 1 flags a start
+    at token 2, so its taps into the history stop there."""
+    rng = np.random.default_rng(23)
+    Bt, L, Dm, W = 2, 7, 3, 4
+    x = rng.standard_normal((Bt, L, Dm))
+    hist = rng.standard_normal((Bt, Dm, W - 1))
+    w = rng.uniform(-0.7, 0.7, (Dm, W))
+    bias = rng.uniform(-0.3, 0.3, Dm)
+    ds = np.zeros((Bt, L), dtype=np.uint8)
+    ds[1, 2] = 1
+    du = rng.standard_normal((Bt, L, Dm))
+    dx, dw, db, dhist = oracle.causal_conv1d_bwd(x, w, du, bias, ds, apply_silu=silu_on, conv_state=hist)
+    assert np.allclose(_conv_with_history(x, np.zeros_like(hist), w, bias, np.where(np.arange(L) == 0, 1, ds), silu_on),
+                       oracle.causal_conv1d(x, w, bias, ds, apply_silu=silu_on))
+
+    def loss():
+        return float(np.sum(_conv_with_history(x, hist, w, bias, ds, silu_on) * du))
+
+    eps = 1e-6
+    for arr, grad in ((x, dx), (hist, dhist), (w, dw), (bias, db)):
+        for flat in range(arr.size):
+            orig = arr.flat[flat]
+            arr.flat[flat] = orig + eps
+            lp = loss()
+            arr.flat[flat] = orig - eps
+            lm = loss()
+            arr.flat[flat] = orig
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad.flat[flat]) <= 1e-6 * max(1.0, abs(fd)), (flat, fd, grad.flat[flat])
+
+
+def test_backward_of_a_split_row_equals_the_whole_row():
+    """A row cut at token 6: the second half's backward with the first half's final
+    state carried in gives d_initial_state, which the first half's backward takes
+    as d_final_state; the conv's d_conv_state adds to the first half's dx of its
+    last 3 tokens.  Every gradient then equals the whole row's."""
+    args, dout = _grad_case(24)
+    cut = 6
+    sl1, sl2 = slice(0, cut), slice(cut, None)
+    whole = oracle.selective_scan_bwd(args["u"], args["delta"], args["A"], args["B"], args["C"], dout, args["D"],
+                                      args["z"], args["delta_bias"], args["delta_softplus"], args["doc_start"])
+    part = {k: (args[k][:, sl1], args[k][:, sl2]) for k in ("u", "delta", "B", "C", "z", "doc_start")}
+    _, fin1 = oracle.selective_scan(part["u"][0], part["delta"][0], args["A"], part["B"][0], part["C"][0], args["D"],
+                                    part["z"][0], args["delta_bias"], args["delta_softplus"], part["doc_start"][0])
+    g2 = oracle.selective_scan_bwd(part["u"][1], part["delta"][1], args["A"], part["B"][1], part["C"][1],
+                                   dout[:, sl2], args["D"], part["z"][1], args["delta_bias"], args["delta_softplus"],
+                                   part["doc_start"][1], initial_state=fin1)
+    g1 = oracle.selective_scan_bwd(part["u"][0], part["delta"][0], args["A"], part["B"][0], part["C"][0],
+                                   dout[:, sl1], args["D"], part["z"][0], args["delta_bias"], args["delta_softplus"],
+                                   part["doc_start"][0], d_final_state=g2["d_initial_state"])
+    for k in ("du", "ddelta", "dB", "dC", "dz"):
+        assert np.allclose(np.concatenate([g1[k], g2[k]], axis=1), whole[k], rtol=1e-12, atol=1e-12), k
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert np.allclose(g1[k] + g2[k], whole[k], rtol=1e-11, atol=1e-12), k
+
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal(args["u"].shape)
+    w = rng.uniform(-0.7, 0.7, (x.shape[2], 4))
+    bias = rng.uniform(-0.3, 0.3, x.shape[2])
+    du = rng.standard_normal(x.shape)
+    ds = args["doc_start"]
+    dx, dw, db = oracle.causal_conv1d_bwd(x, w, du, bias, ds)
+    # The history the second half sees: the inputs of tokens cut-3 .. cut-1, with
+    # zeros for those before a document start at or before token cut-1 (the
+    # whole row's taps do not cross that start).  Row 0 starts one at token 4.
+    hist = np.transpose(x[:, cut - 3:cut], (0, 2, 1)).copy()
+    live = np.array([[not ds[b, cut - 3 + k + 1:cut].any() for k in range(3)] for b in range(x.shape[0])])
+    assert not live.all()
+    hist *= live[:, None, :]
+    dx1, dw1, db1 = oracle.causal_conv1d_bwd(x[:, sl1], w, du[:, sl1], bias, ds[:, sl1])
+    dx2, dw2, db2, dh2 = oracle.causal_conv1d_bwd(x[:, sl2], w, du[:, sl2], bias, ds[:, sl2], conv_state=hist)
+    dx1[:, cut - 3:cut] += np.transpose(dh2 * live[:, None, :], (0, 2, 1))
+    assert np.allclose(np.concatenate([dx1, dx2], axis=1), dx, rtol=1e-12, atol=1e-12)
+    assert np.allclose(dw1 + dw2, dw, rtol=1e-11) and np.allclose(db1 + db2, db, rtol=1e-11)
+
+
 def test_conv_gradient_of_one_hot_weights():
     """With w = e_3 (the current token only) and no SiLU the conv is the identity:
     dx = du and dw[:, 3] = sum_t du x (closed form), in every document."""
