@@ -189,20 +189,26 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
 int mamba_causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, size_t* bytes);
 
 /* Conv backward.
- *   x, weight, bias, doc_start, apply_silu, width, dtype: as the forward call
- *              (no history before token 0: conv_state is not supported here).
+ *   x, weight, bias, doc_start, conv_state, apply_silu, width, dtype: as the
+ *              forward call (conv_state NULL: token 0 starts a document).
  *   du         (B, L, D)  gradient of the loss with respect to the conv output.
  *   dx         (B, L, D)  written.
  *   dweight    (D, 4) float32, written.
  *   dbias      (D,) float32 or NULL (not computed).
+ *   d_conv_state (B, D, 3) float32 or NULL: the gradient with respect to
+ *              conv_state (zero where token 0 starts a document); requires
+ *              conv_state, else MAMBA_ERR_INVALID_ARGUMENT.  For a row split in
+ *              two pieces, the second piece's d_conv_state adds to dx of the
+ *              first piece's last three tokens.
  *   workspace  at least mamba_causal_conv1d_bwd_workspace_bytes bytes, 256-byte
  *              aligned, scratch.
  * Outputs must not overlap each other, the inputs or the workspace.  Sums run
- * in a fixed order (repeated calls give identical results). */
+ * in a fixed order (repeated calls give identical results).  With B L D == 0
+ * nothing is written. */
 int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
-                            const void* du, void* dx, float* dweight, float* dbias, int64_t batch, int64_t seqlen,
-                            int64_t dim, int32_t width, int32_t dtype, int32_t apply_silu, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            const void* conv_state, const void* du, void* dx, float* dweight, float* dbias,
+                            float* d_conv_state, int64_t batch, int64_t seqlen, int64_t dim, int32_t width,
+                            int32_t dtype, int32_t apply_silu, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- Backward pass (training) of the per-channel scan: the gradients of
  * sum(dout * out) through mamba_selective_scan_fwd, i.e. the adjoint of the
@@ -218,13 +224,17 @@ int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bia
 
 /* Bytes of device workspace mamba_selective_scan_bwd needs for `dims` (about
  * B L D (N + 2) * 4 / 16 + B L D * 4 + B L ceil(D / 128) * 8 N bytes plus the
- * per-chunk carries; 1.08 GB at B = 2, L = 32768, D = 1536, N = 16). */
+ * per-chunk carries and two (B, D, N) float32 arrays; 1.08 GB at B = 2, L = 32768, D = 1536, N = 16). */
 int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes);
 
 /* Selective scan backward.
- *   dims, u, delta, A, B, C, D, z, delta_bias, doc_start: as the forward call
- *              whose gradients are wanted (no initial state).
+ *   dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state: as the
+ *              forward call whose gradients are wanted (initial_state NULL:
+ *              token 0 starts a document).
  *   dout       (B, L, D)  gradient of the loss with respect to out.
+ *   d_final_state (B, D, N) float32 or NULL (= 0): gradient of the loss with
+ *              respect to the forward's final_state (the adjoint entering the
+ *              row from the right, e.g. from the next piece of a split row).
  *   du, ddelta (B, L, D)  written, dtype `dtype`.
  *   dA         (D, N) float32, written.
  *   dB, dC     (B, L, N)  written, dtype `dtype`.
@@ -232,6 +242,10 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
  *              (the gradient at D = 0).
  *   dz         (B, L, D); must be non-NULL exactly when z is.
  *   ddelta_bias (D,) float32 or NULL (not computed).
+ *   d_initial_state (B, D, N) float32 or NULL (not computed): the gradient with
+ *              respect to initial_state, i.e. the adjoint leaving the row at its
+ *              start (zero where token 0 starts a document); requires
+ *              initial_state, else MAMBA_ERR_INVALID_ARGUMENT.
  *   workspace  at least mamba_selective_scan_bwd_workspace_bytes bytes, 256-byte
  *              aligned, scratch (contents on entry ignored).
  * Supported: nheads == 0, N in {4, 8, 16}, and what the forward requires; with
@@ -239,12 +253,14 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
  * delta, z and dout must be 4-byte aligned (they are read as pairs of channels),
  * else MAMBA_ERR_MISALIGNED.  Outputs must not overlap each other, the inputs
  * or the workspace.  The sums over channels, tokens and rows run in a fixed
- * order: repeated calls give bitwise identical results. */
+ * order: repeated calls give bitwise identical results.  With B L D == 0
+ * nothing is written. */
 int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
                              const void* B, const void* C, const float* D, const void* z,
-                             const float* delta_bias, const uint8_t* doc_start, const void* dout,
-                             void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
-                             float* ddelta_bias, void* workspace, size_t workspace_bytes, void* stream);
+                             const float* delta_bias, const uint8_t* doc_start, const float* initial_state,
+                             const void* dout, const float* d_final_state, void* du, void* ddelta, float* dA,
+                             void* dB, void* dC, float* dD, void* dz, float* ddelta_bias, float* d_initial_state,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- One-token decode (Mamba skill page, "Dual Computation Modes": the
  * recurrent mode used for generation).  A prefill with mamba_causal_conv1d_fwd

@@ -360,12 +360,15 @@ def conv_state_update(x, conv_state, conv_weight, conv_bias, state, delta, A, B,
 
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, doc_start=None,
-                       delta_softplus: bool = True, workspace=None, grads=None):
-    """Gradients of sum(dout * out) for the per-channel-A scan (A of shape (D, N));
-    see mamba_selective_scan_bwd.  Arguments as selective_scan_fwd plus ``dout``
-    (B, L, D).  Returns a dict with du, ddelta, dB, dC (u's dtype), dA (D, N)
-    float32 and, for each optional input given, dD, dz, ddelta_bias.  ``grads``:
-    optional dict of preallocated outputs with the same keys."""
+                       delta_softplus: bool = True, workspace=None, grads=None, initial_state=None,
+                       d_final_state=None):
+    """Gradients of sum(dout * out) + sum(d_final_state * final_state) for the
+    per-channel-A scan (A of shape (D, N)); see mamba_selective_scan_bwd.
+    Arguments as selective_scan_fwd plus ``dout`` (B, L, D) and ``d_final_state``
+    (B, D, N) float32 or None.  Returns a dict with du, ddelta, dB, dC (u's
+    dtype), dA (D, N) float32 and, for each optional input given, dD, dz,
+    ddelta_bias, d_initial_state (B, D, N) float32.  ``grads``: optional dict of
+    preallocated outputs with the same keys."""
     torch = _torch()
     dev = _check_device(u)
     if u.dim() != 3 or A.dim() != 2:
@@ -385,6 +388,8 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         shapes["dz"] = ((Bt, L, Dm), u.dtype)
     if delta_bias is not None:
         shapes["ddelta_bias"] = ((Dm,), f32)
+    if initial_state is not None:
+        shapes["d_initial_state"] = ((Bt, Dm, N), f32)
     for k, (shape, dt) in shapes.items():
         if k not in g:
             g[k] = torch.empty(shape, dtype=dt, device=dev)
@@ -407,8 +412,11 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         _ptr(z, "z", dev, u.dtype, (Bt, L, Dm)),
         _ptr(delta_bias, "delta_bias", dev, f32, (Dm,)),
         _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(initial_state, "initial_state", dev, f32, (Bt, Dm, N)),
         _ptr(dout, "dout", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(d_final_state, "d_final_state", dev, f32, (Bt, Dm, N)),
         out("du"), out("ddelta"), out("dA"), out("dB"), out("dC"), out("dD"), out("dz"), out("ddelta_bias"),
+        out("d_initial_state"),
         _ptr(workspace, "workspace", dev, torch.uint8), workspace.numel(), _stream(dev))
     _lib.check(st, "mamba_selective_scan_bwd")
     return {k: g[k] for k in shapes}
@@ -422,10 +430,11 @@ def conv_bwd_workspace_bytes(batch, seqlen, dim) -> int:
 
 
 def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu: bool = True, workspace=None,
-                      dx=None, dweight=None, dbias=None):
+                      dx=None, dweight=None, dbias=None, conv_state=None, d_conv_state=None):
     """Gradients of sum(du * u) for u = causal_conv1d_fwd(x, weight, bias, doc_start,
-    apply_silu); see mamba_causal_conv1d_bwd.  Returns (dx, dweight (D, 4) float32,
-    dbias (D,) float32 or None when bias is None)."""
+    conv_state, apply_silu); see mamba_causal_conv1d_bwd.  Returns (dx, dweight
+    (D, 4) float32, dbias (D,) float32 or None when bias is None), and with a
+    conv_state (B, D, 3) also d_conv_state (B, D, 3) float32 as a fourth item."""
     torch = _torch()
     dev = _check_device(x)
     if x.dim() != 3:
@@ -442,6 +451,8 @@ def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu: bool
         dweight = torch.empty((Dm, W), dtype=torch.float32, device=dev)
     if dbias is None and bias is not None:
         dbias = torch.empty((Dm,), dtype=torch.float32, device=dev)
+    if d_conv_state is None and conv_state is not None:
+        d_conv_state = torch.empty((Bt, Dm, 3), dtype=torch.float32, device=dev)
     lib = _lib.load()
     need = ctypes.c_size_t(0)
     _lib.check(lib.mamba_causal_conv1d_bwd_workspace_bytes(Bt, L, Dm, ctypes.byref(need)),
@@ -452,9 +463,13 @@ def causal_conv1d_bwd(x, weight, du, bias=None, doc_start=None, apply_silu: bool
         _ptr(x, "x", dev), _ptr(weight, "weight", dev, torch.float32, (Dm, W)),
         _ptr(bias, "bias", dev, torch.float32, (Dm,)),
         _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(conv_state, "conv_state", dev, x.dtype, (Bt, Dm, 3)),
         _ptr(du, "du", dev, x.dtype, (Bt, L, Dm)), _ptr(dx, "dx", dev, x.dtype, (Bt, L, Dm)),
         _ptr(dweight, "dweight", dev, torch.float32, (Dm, W)), _ptr(dbias, "dbias", dev, torch.float32, (Dm,)),
+        _ptr(d_conv_state, "d_conv_state", dev, torch.float32, (Bt, Dm, 3)),
         Bt, L, Dm, W, _dtype_code(x), int(bool(apply_silu)),
         _ptr(workspace, "workspace", dev, torch.uint8), workspace.numel(), _stream(dev))
     _lib.check(st, "mamba_causal_conv1d_bwd")
+    if conv_state is not None:
+        return dx, dweight, dbias, d_conv_state
     return dx, dweight, dbias

@@ -96,11 +96,11 @@ def load() -> ctypes.CDLL:
     lib.mamba_selective_state_update.restype = ctypes.c_int
     lib.mamba_selective_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(sz)]
     lib.mamba_selective_scan_bwd_workspace_bytes.restype = ctypes.c_int
-    lib.mamba_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanDims)] + [vp] * 19 + [sz, vp]
+    lib.mamba_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanDims)] + [vp] * 22 + [sz, vp]
     lib.mamba_selective_scan_bwd.restype = ctypes.c_int
     lib.mamba_causal_conv1d_bwd_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
     lib.mamba_causal_conv1d_bwd_workspace_bytes.restype = ctypes.c_int
-    lib.mamba_causal_conv1d_bwd.argtypes = [vp] * 8 + [i64, i64, i64, i32, i32, i32, vp, sz, vp]
+    lib.mamba_causal_conv1d_bwd.argtypes = [vp] * 10 + [i64, i64, i64, i32, i32, i32, vp, sz, vp]
     lib.mamba_causal_conv1d_bwd.restype = ctypes.c_int
     lib.mamba_conv_state_update.argtypes = [ctypes.POINTER(ScanDims)] + [vp] * 16
     lib.mamba_conv_state_update.restype = ctypes.c_int

@@ -267,39 +267,43 @@ int mamba_causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64
 }
 
 int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
-                            const void* du, void* dx, float* dweight, float* dbias, int64_t batch, int64_t seqlen,
-                            int64_t dim, int32_t width, int32_t dtype, int32_t apply_silu, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const void* conv_state, const void* du, void* dx, float* dweight, float* dbias,
+                            float* d_conv_state, int64_t batch, int64_t seqlen, int64_t dim, int32_t width,
+                            int32_t dtype, int32_t apply_silu, void* workspace, size_t workspace_bytes, void* stream) {
     if (batch < 0 || seqlen < 0 || dim < 0) return MAMBA_ERR_INVALID_ARGUMENT;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARGUMENT;
     if (width != 4) return MAMBA_ERR_UNSUPPORTED;
     int64_t n;
     if (!mul_ok(batch, seqlen, dim, &n) || dim > kMaxDim || batch > 65535) return MAMBA_ERR_INVALID_ARGUMENT;
     if (seqlen > kMaxSeqlen) return MAMBA_ERR_UNSUPPORTED;
+    if (d_conv_state && !conv_state) return MAMBA_ERR_INVALID_ARGUMENT;
     if (n == 0) return MAMBA_OK;
     if (!x || !weight || !du || !dx || !dweight) return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
     if (!aligned(x, esz) || !aligned(du, esz) || !aligned(dx, esz) || !aligned(weight, 4) || !aligned(dweight, 4) ||
-        (bias && !aligned(bias, 4)) || (dbias && !aligned(dbias, 4)))
+        (bias && !aligned(bias, 4)) || (dbias && !aligned(dbias, 4)) || (conv_state && !aligned(conv_state, esz)) ||
+        (d_conv_state && !aligned(d_conv_state, 4)))
         return MAMBA_ERR_MISALIGNED;
     const size_t act = static_cast<size_t>(n) * esz;
+    const size_t hist = static_cast<size_t>(batch * dim * 3);
     const size_t need = mamba::conv_bwd_workspace_bytes(batch, seqlen, dim);
     if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;
-    const void* ins[] = {x, weight, bias, doc_start, du};
+    const void* ins[] = {x, weight, bias, doc_start, du, conv_state};
     const size_t insz[] = {act, static_cast<size_t>(dim) * 16, static_cast<size_t>(dim) * 4,
-                           static_cast<size_t>(batch * seqlen), act};
-    const void* outs[] = {dx, dweight, dbias, workspace};
-    const size_t outsz[] = {act, static_cast<size_t>(dim) * 16, static_cast<size_t>(dim) * 4, need};
-    for (int o = 0; o < 4; ++o) {
-        for (int i = 0; i < 5; ++i)
+                           static_cast<size_t>(batch * seqlen), act, hist * esz};
+    const void* outs[] = {dx, dweight, dbias, d_conv_state, workspace};
+    const size_t outsz[] = {act, static_cast<size_t>(dim) * 16, static_cast<size_t>(dim) * 4, hist * 4, need};
+    for (int o = 0; o < 5; ++o) {
+        for (int i = 0; i < 6; ++i)
             if (overlap(outs[o], outsz[o], ins[i], insz[i])) return MAMBA_ERR_INVALID_ARGUMENT;
-        for (int k = o + 1; k < 4; ++k)
+        for (int k = o + 1; k < 5; ++k)
             if (overlap(outs[o], outsz[o], outs[k], outsz[k])) return MAMBA_ERR_INVALID_ARGUMENT;
     }
     mamba::ConvBwdArgs a;
     a.x = x; a.weight = weight; a.bias = bias; a.doc_start = doc_start; a.du = du; a.dx = dx;
     a.dweight = dweight; a.dbias = dbias; a.ws = static_cast<float*>(workspace);
+    a.conv_state = conv_state; a.d_conv_state = d_conv_state;
     a.batch = batch; a.seqlen = seqlen; a.dim = dim;
     a.bf16 = dtype == MAMBA_DTYPE_BF16;
     const size_t vbytes = 2 * esz;           // channel pairs
@@ -322,14 +326,16 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
 
 int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
                              const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
-                             const uint8_t* doc_start, const void* dout, void* du, void* ddelta, float* dA, void* dB,
-                             void* dC, float* dD, void* dz, float* ddelta_bias, void* workspace,
+                             const uint8_t* doc_start, const float* initial_state, const void* dout,
+                             const float* d_final_state, void* du, void* ddelta, float* dA, void* dB, void* dC,
+                             float* dD, void* dz, float* ddelta_bias, float* d_initial_state, void* workspace,
                              size_t workspace_bytes, void* stream) {
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
     if (!mamba::scan_bwd_supported(dims->dstate, dims->nheads)) return MAMBA_ERR_UNSUPPORTED;
     const int64_t Bt = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     if ((z == nullptr) != (dz == nullptr)) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (d_initial_state && !initial_state) return MAMBA_ERR_INVALID_ARGUMENT;
     if (Bt * L * Dm == 0) return MAMBA_OK;
     if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
         return MAMBA_ERR_INVALID_ARGUMENT;
@@ -345,33 +351,37 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
         if (t && !aligned(t, esz)) return MAMBA_ERR_MISALIGNED;
     if (!aligned(B, 4) || !aligned(C, 4) || !aligned(dB, esz) || !aligned(dC, esz) || (N * esz) % 4 != 0)
         return MAMBA_ERR_MISALIGNED;
-    const float* f32s[] = {A, D, delta_bias, dA, dD, ddelta_bias};
+    const float* f32s[] = {A, D, delta_bias, dA, dD, ddelta_bias, initial_state, d_final_state, d_initial_state};
     for (const float* t : f32s)
         if (t && !aligned(t, 4)) return MAMBA_ERR_MISALIGNED;
 
     const size_t act = static_cast<size_t>(Bt * L * Dm) * esz;
     const size_t bc = static_cast<size_t>(Bt * L * N) * esz;
     const size_t dn = static_cast<size_t>(Dm * N) * 4, d1 = static_cast<size_t>(Dm) * 4;
-    const void* ins[] = {u, delta, A, B, C, D, z, delta_bias, doc_start, dout};
-    const size_t insz[] = {act, act, dn, bc, bc, d1, act, d1, static_cast<size_t>(Bt * L), act};
-    const void* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias};
-    const size_t outsz[] = {act, act, dn, bc, bc, d1, act, d1};
+    const size_t sb = static_cast<size_t>(Bt * Dm * N) * 4;
+    const void* ins[] = {u, delta, A, B, C, D, z, delta_bias, doc_start, dout, initial_state, d_final_state};
+    const size_t insz[] = {act, act, dn, bc, bc, d1, act, d1, static_cast<size_t>(Bt * L), act, sb, sb};
+    constexpr int kIns = 12;
+    const void* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, d_initial_state};
+    const size_t outsz[] = {act, act, dn, bc, bc, d1, act, d1, sb};
+    constexpr int kOuts = 9;
     const size_t need = mamba::scan_bwd_workspace_bytes(Bt, L, Dm, N, dims->dtype == MAMBA_DTYPE_BF16);
     if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;
-    for (int o = 0; o < 8; ++o) {
-        for (int i = 0; i < 10; ++i)
+    for (int o = 0; o < kOuts; ++o) {
+        for (int i = 0; i < kIns; ++i)
             if (overlap(outs[o], outsz[o], ins[i], insz[i])) return MAMBA_ERR_INVALID_ARGUMENT;
-        for (int k = o + 1; k < 8; ++k)
+        for (int k = o + 1; k < kOuts; ++k)
             if (overlap(outs[o], outsz[o], outs[k], outsz[k])) return MAMBA_ERR_INVALID_ARGUMENT;
         if (overlap(outs[o], outsz[o], workspace, need)) return MAMBA_ERR_INVALID_ARGUMENT;
     }
-    for (int i = 0; i < 10; ++i)
+    for (int i = 0; i < kIns; ++i)
         if (overlap(ins[i], insz[i], workspace, need)) return MAMBA_ERR_INVALID_ARGUMENT;
 
     mamba::ScanBwdArgs a;
     a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.delta_bias = delta_bias;
     a.doc_start = doc_start; a.dout = dout;
+    a.initial_state = initial_state; a.d_final_state = d_final_state; a.d_initial_state = d_initial_state;
     a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dz = dz; a.ddelta_bias = ddelta_bias;
     a.ws = workspace;
     a.batch = Bt; a.seqlen = L; a.dim = Dm; a.dstate = N;

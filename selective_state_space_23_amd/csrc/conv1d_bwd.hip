@@ -17,6 +17,12 @@
 // the taps that stay inside its document, and dx_{t-3} is then final.  dw and
 // dbias are summed over the tile's own tokens into per-tile partials, which a
 // second kernel adds in a fixed order.
+//
+// A row that continues a given history (conv_state: the inputs of tokens -3..-1)
+// treats those three as tokens of token 0's document (unless token 0 starts
+// one): they feed acc of tokens 0..2, and their own dx (the gradient of the
+// history, d_conv_state) comes out of the shift register of the first tile as
+// tokens 0..2 complete it.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -53,8 +59,8 @@ constexpr int kBlock = 256;
 template <typename T, int VEC, bool SILU>
 __global__ __launch_bounds__(kBlock) void conv1d_bwd_kernel(
     const void* __restrict__ x, const float* __restrict__ weight, const float* __restrict__ bias,
-    const uint8_t* __restrict__ doc_start, const void* __restrict__ du, void* __restrict__ dx,
-    float* __restrict__ part, int64_t seqlen, int dim) {
+    const uint8_t* __restrict__ doc_start, const void* __restrict__ conv_state, const void* __restrict__ du,
+    void* __restrict__ dx, float* __restrict__ d_conv_state, float* __restrict__ part, int64_t seqlen, int dim) {
     const int ngroups = (dim + VEC - 1) / VEC;
     const int grp = blockIdx.x * kBlock + threadIdx.x;
     const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kTile;
@@ -66,7 +72,7 @@ __global__ __launch_bounds__(kBlock) void conv1d_bwd_kernel(
     const int64_t tl = t0 - 3 + lane;
     bool is_start = false;
     if (lane < kTile + 6 && tl >= 0 && tl < seqlen)
-        is_start = tl == 0 || (doc_start != nullptr && doc_start[row + tl] != 0);
+        is_start = (tl == 0 && conv_state == nullptr) || (doc_start != nullptr && doc_start[row + tl] != 0);
     const uint64_t starts = __ballot(is_start);
     if (grp >= ngroups) return;
 
@@ -86,9 +92,15 @@ __global__ __launch_bounds__(kBlock) void conv1d_bwd_kernel(
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const int64_t t = t0 - 3 + k;
-        if (t < 0) continue;
         float xv[VEC];
-        VecIO<T, VEC>::load(x, (row + t) * dim + d0, xv);
+        if (t >= 0) {
+            VecIO<T, VEC>::load(x, (row + t) * dim + d0, xv);
+        } else if (conv_state != nullptr) {  // (B, D, 3): x_{-3}, x_{-2}, x_{-1} of each channel
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) xv[i] = Elem<T>::load(conv_state, (b * dim + d0 + i) * 3 + (3 + t));
+        } else {
+            continue;
+        }
         const bool reset = (starts >> k) & 1ull;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
@@ -106,8 +118,9 @@ __global__ __launch_bounds__(kBlock) void conv1d_bwd_kernel(
         p1[i] = p2[i] = p3[i] = 0.0f;
         gw0[i] = gw1[i] = gw2[i] = gw3[i] = gb[i] = 0.0f;
     }
-    // Tokens since the latest document start before t0, capped at 3 (the row's
-    // token 0 is a start, so tiles at the row start need no special case).
+    // Tokens since the latest document start before t0, capped at 3 (token 0 of
+    // a row without history is a start, and the history of one that has it
+    // belongs to token 0's document: tiles at the row start need no special case).
     int since = 3;
 #pragma unroll
     for (int k = 0; k < 3; ++k)
@@ -173,7 +186,12 @@ __global__ __launch_bounds__(kBlock) void conv1d_bwd_kernel(
         }
         since = since < 3 ? since + 1 : 3;
         const int64_t s = t - 3;
-        if (s >= t0 && s < own_end) VecIO<T, VEC>::store(dx, (row + s) * dim + d0, out);
+        if (s >= t0 && s < own_end) {
+            VecIO<T, VEC>::store(dx, (row + s) * dim + d0, out);
+        } else if (s < 0 && d_conv_state != nullptr) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) d_conv_state[(b * dim + d0 + i) * 3 + (3 + s)] = out[i];
+        }
     }
     // Per-tile partials: [b][tile][5][D] (dw columns 0..3, then dbias).
     const int64_t ntiles = gridDim.y;
@@ -229,10 +247,12 @@ hipError_t launch_conv_bwd_vec(const ConvBwdArgs& a) {
     dim3 grid((ngroups + kBlock - 1) / kBlock, static_cast<unsigned>(ntiles), static_cast<unsigned>(a.batch));
     if (a.apply_silu)
         hipLaunchKernelGGL((conv1d_bwd_kernel<T, VEC, true>), grid, dim3(kBlock), 0, a.stream, a.x, a.weight,
-                           a.bias, a.doc_start, a.du, a.dx, a.ws, a.seqlen, static_cast<int>(a.dim));
+                           a.bias, a.doc_start, a.conv_state, a.du, a.dx, a.d_conv_state, a.ws, a.seqlen,
+                           static_cast<int>(a.dim));
     else
         hipLaunchKernelGGL((conv1d_bwd_kernel<T, VEC, false>), grid, dim3(kBlock), 0, a.stream, a.x, a.weight,
-                           a.bias, a.doc_start, a.du, a.dx, a.ws, a.seqlen, static_cast<int>(a.dim));
+                           a.bias, a.doc_start, a.conv_state, a.du, a.dx, a.d_conv_state, a.ws, a.seqlen,
+                           static_cast<int>(a.dim));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(conv1d_bwd_reduce_kernel, dim3(static_cast<unsigned>((5 * a.dim + 63) / 64)), dim3(1024), 0,

@@ -33,6 +33,8 @@ struct ConvBwdArgs {
     void* dx;
     float* dweight;           // (D, 4)
     float* dbias;             // (D,) or null
+    const void* conv_state = nullptr;   // (B, D, 3) inputs before token 0, or null
+    float* d_conv_state = nullptr;      // (B, D, 3), written; needs conv_state
     float* ws;                // conv_bwd_workspace_bytes
     int64_t batch, seqlen, dim;
     bool bf16;
@@ -102,6 +104,9 @@ struct ScanBwdArgs {
     float* dD;            // or null
     void* dz;             // null iff z is null
     float* ddelta_bias;   // or null
+    const float* initial_state = nullptr;   // (B, D, N) state before token 0, or null
+    const float* d_final_state = nullptr;   // (B, D, N) gradient at the final state, or null
+    float* d_initial_state = nullptr;       // (B, D, N), written; needs initial_state
     void* ws;
     int64_t batch, seqlen, dim, dstate;
     bool bf16;

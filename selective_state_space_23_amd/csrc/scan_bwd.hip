@@ -98,6 +98,10 @@ struct BwdKParams {
     const float* ckpt;       // [B][nk][N + 2][D]: local checkpoints of the aggregate pass
     float* part_bc;          // [B][L][nblk][2N]: per-block sums of dB_t, dC_t
     float* part_w;           // [B][nchunks][N + 2][D]: per-chunk sums of dA, dD, ddelta_bias
+    const float* init;       // (B, D, N) state before token 0, or null (token 0 then starts a document)
+    const float* d_final;    // (B, D, N) gradient arriving at the final state, or null
+    float* x0;               // [B][D][N]: X_0 and R_0 of chunk 0 (for d_initial_state), or null
+    float* r0;
     void* du;
     void* ddelta;
     void* dz;
@@ -175,10 +179,12 @@ __device__ __forceinline__ void stage_rows(float* smem, const T* B_row, const T*
 }
 
 // Wave-uniform bit mask of the document starts among tokens w0 .. w0 + 63.
-__device__ __forceinline__ uint64_t window_starts(const uint8_t* ds_row, int64_t w0, int64_t t_end, int lane) {
+// Token 0 starts one unless a state is carried into the row.
+__device__ __forceinline__ uint64_t window_starts(const uint8_t* ds_row, int64_t w0, int64_t t_end, int lane,
+                                                  bool carried) {
     const int64_t tl = w0 + lane;
     bool st = false;
-    if (tl < t_end) st = tl == 0 || (ds_row != nullptr && ds_row[tl] != 0);
+    if (tl < t_end) st = (tl == 0 && !carried) || (ds_row != nullptr && ds_row[tl] != 0);
     return __ballot(st);
 }
 
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
     float au[kPiece], ad[kPiece], ao[kPiece], az[kPiece], bu[kPiece], bd[kPiece], bo[kPiece], bz[kPiece];
     fetch(t_begin, au, ad, ao, az);
     for (int64_t w0 = t_begin; w0 < t_end; w0 += kWin) {
-        starts = window_starts(ds_row, w0, t_end, lane);
+        starts = window_starts(ds_row, w0, t_end, lane, p.init != nullptr);
         __syncthreads();
         stage_rows<T, N, 2>(sBC, B_row, C_row, w0, t_end, tid);
         __syncthreads();
@@ -355,16 +361,23 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
             p.g_carry[(c - 1) * count + my_slot + n] = X[n];
             p.p_rev[(c - 1) * count + my_slot + n] = R[n];
         }
+    } else if (p.x0 != nullptr) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            p.x0[my_slot + n] = X[n];
+            p.r0[my_slot + n] = R[n];
+        }
     }
 }
 
 // 2. Forward carry: slot s turns from R_s into the state entering chunk s + 1,
-// carry_{s+1} = R_s carry_s + H_s (carry_0 = 0: no initial state).
+// carry_{s+1} = R_s carry_s + H_s (carry_0: the initial state, or 0).
 __global__ __launch_bounds__(256) void bwd_fwd_carry_kernel(float* __restrict__ ws_P, const float* __restrict__ ws_H,
-                                                            int64_t count, int64_t nslots) {
+                                                            const float* __restrict__ init, int64_t count,
+                                                            int64_t nslots) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= count) return;
-    float carry = 0.0f;
+    float carry = init != nullptr ? init[i] : 0.0f;
     int64_t s = 0;
     for (; s + 4 <= nslots; s += 4) {
         float P[4], H[4];
@@ -385,14 +398,18 @@ __global__ __launch_bounds__(256) void bwd_fwd_carry_kernel(float* __restrict__ 
     }
 }
 
-// 3. Reverse carry: slot s turns from X_{s+1} into G_s = X_{s+1} + P_{s+1} G_{s+1}
-// (G_{nchunks-1} = 0: no gradient flows in from past the row end).
+// 3. Reverse carry: slot s turns from X_{s+1} into G_s = X_{s+1} + P_{s+1} G_{s+1},
+// starting from the gradient arriving at the final state (or 0) as G of the
+// last chunk.  With d_init, the adjoint leaving the row to the left follows:
+// d_init = X_0 + R_0 G_0 (the same operator once more, over chunk 0).
 __global__ __launch_bounds__(256) void bwd_rev_carry_kernel(float* __restrict__ g_carry,
-                                                            const float* __restrict__ p_rev, int64_t count,
-                                                            int64_t nslots) {
+                                                            const float* __restrict__ p_rev,
+                                                            const float* __restrict__ d_final,
+                                                            const float* __restrict__ x0, const float* __restrict__ r0,
+                                                            float* __restrict__ d_init, int64_t count, int64_t nslots) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= count) return;
-    float G = 0.0f;
+    float G = d_final != nullptr ? d_final[i] : 0.0f;
     int64_t s = nslots - 1;
     for (; s >= 3; s -= 4) {
         float X[4], P[4];
@@ -411,6 +428,7 @@ __global__ __launch_bounds__(256) void bwd_rev_carry_kernel(float* __restrict__ 
         G = __builtin_fmaf(p_rev[s * count + i], G, g_carry[s * count + i]);
         g_carry[s * count + i] = G;
     }
+    if (d_init != nullptr) d_init[i] = __builtin_fmaf(r0[i], G, x0[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -676,9 +694,12 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
         dt = opaque(stg_val(0, k) * (t < t_end ? 1.0f : 0.0f));
         uu = stg_val(1, k) * active_f;
     };
-    // The state entering the chunk (row b of carry slot c - 1).
+    // The state entering the chunk (row b of carry slot c - 1, or of the initial
+    // state for chunk 0).
+    const bool carried_in = c > 0 || p.init != nullptr;
     const __amdgpu_buffer_rsrc_t hin_rs =
-        make_rsrc(p.h_carry + (c > 0 ? c - 1 : 0) * count + b * p.dim * N, p.dim * N * 4);
+        make_rsrc((c > 0 ? p.h_carry + (c - 1) * count : (p.init != nullptr ? p.init : p.h_carry)) + b * p.dim * N,
+                  p.dim * N * 4);
     // The next block's checkpoint rows (local state, step-size sum, document
     // flag), fetched into registers with the block's staging.
     float ckv[NL], hinv[NL], ck_cdt = 0.0f, ck_flag = 0.0f;
@@ -702,8 +723,9 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
     };
 
     float gn[NL];         // a_{t+1} g_{t+1}: the adjoint reaching token t from the right
-    if (c + 1 < p.nchunks) {
-        const float* gc = p.g_carry + c * count + my_slot;
+    if (c + 1 < p.nchunks || p.d_final != nullptr) {
+        // (the last chunk: the gradient arriving at the final state)
+        const float* gc = (c + 1 < p.nchunks ? p.g_carry + c * count : p.d_final) + my_slot;
 #pragma unroll
         for (int i = 0; i < NL; ++i) gn[i] = gc[i];
     } else {
@@ -843,7 +865,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
     const int64_t nwin = (t_end - t_begin + kWin - 1) / kWin;
     for (int64_t wi = nwin - 1; wi >= 0; --wi) {
         const int64_t w0 = t_begin + wi * kWin;
-        starts = window_starts(ds_row, w0, t_end, lane);
+        starts = window_starts(ds_row, w0, t_end, lane, p.init != nullptr);
         __syncthreads();
         stage_rows<T, N, 2>(sBC, B_row, C_row, w0, t_end, tid);
         __syncthreads();
@@ -862,7 +884,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
             __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
             // local checkpoint + exp(A * sum dt) * (state entering the chunk)
             {
-                const bool fresh = c == 0 || ck_flag != 0.0f;
+                const bool fresh = !carried_in || ck_flag != 0.0f;
 #pragma unroll
                 for (int i = 0; i < NL; ++i)
                     ck0[i] = fresh ? ckv[i] : __builtin_fmaf(exp2_fast(Al2[i] * ck_cdt), hinv[i], ckv[i]);
@@ -958,7 +980,7 @@ constexpr int lanes_per_channel(int64_t n) { return n == 16 ? MAMBA_BWD_G16 : (n
 
 // Workspace layout (byte offsets, each region 256-byte aligned).
 struct BwdLayout {
-    size_t h_carry, h_agg, g_carry, p_rev, dt, ckpt, part_bc, part_w, total;
+    size_t h_carry, h_agg, g_carry, p_rev, dt, ckpt, part_bc, part_w, x0, r0, total;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -979,7 +1001,9 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     l.ckpt = l.dt + align256(static_cast<size_t>(batch * seqlen * dim) * sizeof(float));
     l.part_bc = l.ckpt + align256(static_cast<size_t>(batch * nk * (dstate + 2) * dim) * sizeof(float));
     l.part_w = l.part_bc + align256(static_cast<size_t>(batch * seqlen * nblk * 2 * dstate) * sizeof(float));
-    l.total = l.part_w + align256(static_cast<size_t>(batch * plan.nchunks * (dstate + 2) * dim) * sizeof(float));
+    l.x0 = l.part_w + align256(static_cast<size_t>(batch * plan.nchunks * (dstate + 2) * dim) * sizeof(float));
+    l.r0 = l.x0 + align256(count * sizeof(float));
+    l.total = l.r0 + align256(count * sizeof(float));
     return l;
 }
 
@@ -1001,6 +1025,12 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     p.part_bc = reinterpret_cast<float*>(ws + l.part_bc);
     p.part_w = reinterpret_cast<float*>(ws + l.part_w);
     p.du = a.du; p.ddelta = a.ddelta; p.dz = a.dz;
+    p.init = a.initial_state;
+    p.d_final = a.d_final_state;
+    if (a.d_initial_state != nullptr) {
+        p.x0 = reinterpret_cast<float*>(ws + l.x0);
+        p.r0 = reinterpret_cast<float*>(ws + l.r0);
+    }
     p.seqlen = a.seqlen;
     p.chunk_len = plan.chunk_len;
     p.nchunks = plan.nchunks;
@@ -1024,14 +1054,17 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const dim3 gc(static_cast<unsigned>((count + 255) / 256));
     if (p.nslots > 0) {
-        const dim3 gc(static_cast<unsigned>((count + 255) / 256));
         hipLaunchKernelGGL(bwd_fwd_carry_kernel, gc, dim3(256), 0, a.stream, p.h_agg_P,
-                           static_cast<const float*>(p.h_agg_H), count, p.nslots);
+                           static_cast<const float*>(p.h_agg_H), a.initial_state, count, p.nslots);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if (p.nslots > 0 || a.d_initial_state != nullptr) {
         hipLaunchKernelGGL(bwd_rev_carry_kernel, gc, dim3(256), 0, a.stream, p.g_carry, static_cast<const float*>(p.p_rev),
-                           count, p.nslots);
+                           a.d_final_state, static_cast<const float*>(p.x0), static_cast<const float*>(p.r0),
+                           a.d_initial_state, count, p.nslots);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

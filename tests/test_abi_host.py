@@ -210,10 +210,10 @@ def test_conv_scan_validation(lib):
 
 def bwd(lib, d=None, u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None, bias=None,
         ds=None, dout=FAKE * 6, du=FAKE * 7, ddelta=FAKE * 8, dA=FAKE * 9, dB=FAKE * 10, dC=FAKE * 11, dD=None,
-        dz=None, dbias=None, ws=FAKE * 64, wsb=1 << 40):
+        dz=None, dbias=None, ws=FAKE * 64, wsb=1 << 40, h0=None, dhT=None, dh0=None):
     d = d or dims(batch=1, seqlen=64, dim=64)
-    return lib.mamba_selective_scan_bwd(ctypes.byref(d), u, delta, A, B, C, D, z, bias, ds, dout, du, ddelta, dA,
-                                        dB, dC, dD, dz, dbias, ws, wsb, None)
+    return lib.mamba_selective_scan_bwd(ctypes.byref(d), u, delta, A, B, C, D, z, bias, ds, h0, dout, dhT, du,
+                                        ddelta, dA, dB, dC, dD, dz, dbias, dh0, ws, wsb, None)
 
 
 def test_bwd_workspace_query(lib):
@@ -250,6 +250,14 @@ def test_bwd_validation(lib):
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=63, dtype=1)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dtype=1), u=FAKE + 2) == _lib.MAMBA_ERR_MISALIGNED
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dtype=1), dout=FAKE * 6 + 2) == _lib.MAMBA_ERR_MISALIGNED
+    # carried state: d_initial_state needs initial_state; both states are float32 (B, D, N)
+    assert bwd(lib, dh0=FAKE * 13) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert bwd(lib, d=dims(batch=0), u=None, dout=None, dh0=FAKE * 13) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert bwd(lib, h0=FAKE * 12 + 2, dh0=FAKE * 13) == _lib.MAMBA_ERR_MISALIGNED
+    assert bwd(lib, dhT=FAKE * 14 + 2) == _lib.MAMBA_ERR_MISALIGNED
+    assert bwd(lib, h0=FAKE * 12, dh0=FAKE * 12) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # d_initial_state aliases it
+    assert bwd(lib, dhT=FAKE * 14, dh0=FAKE * 14, h0=FAKE * 12) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert bwd(lib, h0=FAKE * 12, dh0=FAKE * 7) == _lib.MAMBA_ERR_INVALID_ARGUMENT    # ... or du
 
 
 def test_conv_bwd_validation(lib):
@@ -259,8 +267,9 @@ def test_conv_bwd_validation(lib):
     assert lib.mamba_causal_conv1d_bwd_workspace_bytes(-1, 8, 8, ctypes.byref(n)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
 
     def cb(x=FAKE, w=FAKE * 2, b=None, ds=None, du=FAKE * 3, dx=FAKE * 4, dw=FAKE * 5, db=None, B=1, L=64, D=16,
-           W=4, dtype=1, silu=1, ws=FAKE * 8, wsb=1 << 30):
-        return lib.mamba_causal_conv1d_bwd(x, w, b, ds, du, dx, dw, db, B, L, D, W, dtype, silu, ws, wsb, None)
+           W=4, dtype=1, silu=1, ws=FAKE * 8, wsb=1 << 30, hist=None, dhist=None):
+        return lib.mamba_causal_conv1d_bwd(x, w, b, ds, hist, du, dx, dw, db, dhist, B, L, D, W, dtype, silu, ws,
+                                           wsb, None)
 
     assert cb(W=3) == _lib.MAMBA_ERR_UNSUPPORTED
     assert cb(dtype=5) == _lib.MAMBA_ERR_INVALID_ARGUMENT
@@ -273,6 +282,11 @@ def test_conv_bwd_validation(lib):
     assert cb(dw=FAKE * 4) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # dweight inside dx
     assert cb(ws=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT              # workspace over x
     assert cb(B=0, x=None, du=None) == _lib.MAMBA_OK                  # empty: no-op
+    assert cb(dhist=FAKE * 9) == _lib.MAMBA_ERR_INVALID_ARGUMENT       # d_conv_state without conv_state
+    assert cb(hist=FAKE * 9 + 1, dhist=FAKE * 10) == _lib.MAMBA_ERR_MISALIGNED
+    assert cb(hist=FAKE * 9, dhist=FAKE * 10 + 2) == _lib.MAMBA_ERR_MISALIGNED
+    assert cb(hist=FAKE * 9, dhist=FAKE * 9) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # d_conv_state aliases it
+    assert cb(hist=FAKE * 9, dhist=FAKE * 4) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # ... or dx
 
 
 def test_conv_state_update_validation(lib):

@@ -244,3 +244,188 @@ def test_mixer_core_backward_chain(ssm):
     assert_close(to_host(db), db_r, "bf16", "chain dbias")
     for k in ("dA", "dB", "dC", "dD", "dz", "ddelta", "ddelta_bias"):
         assert_close(to_host(g[k]), gr[k], "bf16", f"chain {k}")
+
+
+# ----------------------------------------------------------------------------
+# Carried state: a given state before token 0 (initial_state / conv_state) and
+# a gradient arriving at the final state (d_final_state)
+# ----------------------------------------------------------------------------
+CARRY_CASES = [
+    # (batch, seqlen, dim, dstate, dtype, docs)
+    (2, 64, 16, 4, "f32", None),            # one chunk: no carries between chunks
+    (2, 600, 96, 16, "bf16", 100.0),        # several chunks
+    (2, 1000, 100, 8, "f32", 300.0),        # ragged D, a 104-token tail
+    (2, 3, 16, 16, "bf16", None),           # fewer tokens than a piece
+]
+
+
+def carry_inputs(case, seed):
+    Bt, L, Dm, N, dt, docs = case
+    inp = make_custom(Bt, L, Dm, N, dtype=dt, docs=docs, seed=seed)
+    inp.doc_start[0, 0] = 0       # row 0 continues the given state
+    inp.doc_start[1, 0] = 1       # row 1 starts a document at token 0 (its d_initial_state is 0)
+    rng = np.random.default_rng(seed + 1)
+    init = rng.normal(0.0, 0.5, size=(Bt, Dm, N)).astype(np.float32)
+    dfin = rng.normal(0.0, 1.0, size=(Bt, Dm, N)).astype(np.float32)
+    return inp, init, dfin
+
+
+@pytest.mark.parametrize("case", CARRY_CASES, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("with_init,with_dfin", [(True, True), (True, False), (False, True)])
+def test_bwd_carried_state(ssm, case, with_init, with_dfin):
+    torch = torch_mod()
+    inp, init, dfin = carry_inputs(case, seed=840 + case[1] + case[2])
+    if not with_init:
+        inp.doc_start[:, 0] = 1
+    Bt, L, Dm = inp.x.shape
+    dout = make_cotangent(Bt, L, Dm, dtype=inp.dtype, seed=940 + L)
+    dev = upload(inp)
+    got = ssm.selective_scan_bwd(to_dev(inp.x, inp.dtype), dev["delta"], dev["A"], dev["B"], dev["C"],
+                                 to_dev(dout, inp.dtype), D=dev["D"], z=dev["z"], delta_bias=dev["delta_bias"],
+                                 doc_start=dev["doc_start"],
+                                 initial_state=torch.from_numpy(init).cuda() if with_init else None,
+                                 d_final_state=torch.from_numpy(dfin).cuda() if with_dfin else None)
+    ref = oracle.selective_scan_bwd(inp.x, inp.delta, inp.A, inp.B, inp.C, dout, D=inp.D, z=inp.z,
+                                    delta_bias=inp.delta_bias, doc_start=inp.doc_start,
+                                    initial_state=init if with_init else None,
+                                    d_final_state=dfin if with_dfin else None)
+    compare(got, ref, inp.dtype, f"carried bwd {case} init={with_init} dfin={with_dfin}")
+    if with_init:
+        assert torch.count_nonzero(got["d_initial_state"][1]) == 0      # row 1 starts a document
+
+
+def test_bwd_split_row_equals_whole(ssm):
+    """The scan backward of a row cut in two pieces, run back to front (the second
+    piece's d_initial_state is the first piece's d_final_state; its initial_state
+    is the first piece's final_state from the GPU forward), gives the whole row's
+    gradients; the parameter gradients are the sums of the pieces'."""
+    torch = torch_mod()
+    inp = make_custom(2, 900, 96, 16, dtype="f32", docs=200.0, seed=850)
+    Bt, L, Dm = inp.x.shape
+    dout = make_cotangent(Bt, L, Dm, dtype="f32", seed=950)
+    ref = oracle.selective_scan_bwd(inp.x, inp.delta, inp.A, inp.B, inp.C, dout, D=inp.D, z=inp.z,
+                                    delta_bias=inp.delta_bias, doc_start=inp.doc_start)
+    dev = upload(inp)
+    u = to_dev(inp.x, "f32")
+    dy = to_dev(dout, "f32")
+    cut = 389            # inside a chunk, not on a window or piece edge
+    s1, s2 = slice(0, cut), slice(cut, L)
+    piece = lambda sl: {k: (v[:, sl].contiguous() if k in ("delta", "B", "C", "z", "doc_start") else v)  # noqa: E731
+                        for k, v in dev.items()}
+    p1, p2 = piece(s1), piece(s2)
+    _, h_cut = ssm.selective_scan_fwd(u[:, s1].contiguous(), p1["delta"], p1["A"], p1["B"], p1["C"], p1["D"],
+                                      p1["z"], p1["delta_bias"], p1["doc_start"], final_state=True)
+    g2 = ssm.selective_scan_bwd(u[:, s2].contiguous(), p2["delta"], p2["A"], p2["B"], p2["C"], dy[:, s2].contiguous(),
+                                D=p2["D"], z=p2["z"], delta_bias=p2["delta_bias"], doc_start=p2["doc_start"],
+                                initial_state=h_cut)
+    g1 = ssm.selective_scan_bwd(u[:, s1].contiguous(), p1["delta"], p1["A"], p1["B"], p1["C"], dy[:, s1].contiguous(),
+                                D=p1["D"], z=p1["z"], delta_bias=p1["delta_bias"], doc_start=p1["doc_start"],
+                                d_final_state=g2["d_initial_state"])
+    for k in ("du", "ddelta", "dB", "dC", "dz"):
+        assert_close(np.concatenate([to_host(g1[k]), to_host(g2[k])], axis=1), ref[k], "f32", f"split {k}")
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert_close(to_host(g1[k]) + to_host(g2[k]), ref[k], "f32", f"split {k}")
+
+
+def test_bwd_workload_carried(ssm):
+    """The packed 32K workload shape with a given initial state and a gradient at
+    the final state, both supported on the sampled channels' adjoints."""
+    torch = torch_mod()
+    inp = make_inputs("packed_32k")
+    Bt, L, Dm = inp.x.shape
+    N = inp.A.shape[1]
+    inp.doc_start[0, 0] = 0
+    ch = np.array(SAMPLES["packed_32k"])
+    print(f"[bwd carried] packed_32k shape={inp.x.shape}", flush=True)
+    rng = np.random.default_rng(921)
+    init = rng.normal(0.0, 0.5, size=(Bt, Dm, N)).astype(np.float32)
+    dfin = np.zeros((Bt, Dm, N), dtype=np.float32)
+    dfin[:, ch] = rng.normal(0.0, 1.0, size=(Bt, len(ch), N))
+    dout = make_cotangent(Bt, L, Dm, dtype=inp.dtype, seed=922, channels=ch)
+    dev = upload(inp)
+    got = ssm.selective_scan_bwd(to_dev(inp.x, inp.dtype), dev["delta"], dev["A"], dev["B"], dev["C"],
+                                 to_dev(dout, inp.dtype), D=dev["D"], z=dev["z"], delta_bias=dev["delta_bias"],
+                                 doc_start=dev["doc_start"], initial_state=torch.from_numpy(init).cuda(),
+                                 d_final_state=torch.from_numpy(dfin).cuda())
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(ch).to(got["du"].device)
+    others = torch.from_numpy(np.setdiff1d(np.arange(Dm), ch)).to(got["du"].device)
+    assert torch.count_nonzero(got["d_initial_state"].index_select(1, others)) == 0
+    sub = {k: to_host(got[k].index_select(2, idx)) for k in ("du", "ddelta", "dz")}
+    sub.update({k: to_host(got[k].index_select(0, idx)) for k in ("dA", "dD", "ddelta_bias")})
+    sub.update({k: to_host(got[k]) for k in ("dB", "dC")})
+    sub["d_initial_state"] = to_host(got["d_initial_state"].index_select(1, idx))
+    del dev, got
+    ref = oracle.selective_scan_bwd(inp.x[:, :, ch], inp.delta[:, :, ch], inp.A[ch], inp.B, inp.C, dout[:, :, ch],
+                                    D=inp.D[ch], z=inp.z[:, :, ch], delta_bias=inp.delta_bias[ch],
+                                    doc_start=inp.doc_start, initial_state=init[:, ch], d_final_state=dfin[:, ch])
+    for k in sorted(ref):
+        assert_close(sub[k], ref[k], inp.dtype, f"carried packed_32k {k}")
+
+
+CONV_HIST_CASES = [
+    # (batch, seqlen, dim, dtype, docs)
+    (2, 200, 64, "bf16", 20.0),       # channel pairs
+    (2, 131, 37, "f32", 9.0),         # odd D: one channel a thread
+    (2, 1, 24, "bf16", None),         # one token: the history gets w of taps 1..3 only
+    (2, 2, 38, "f32", None),
+]
+
+
+@pytest.mark.parametrize("case", CONV_HIST_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_conv_bwd_with_history(ssm, case):
+    torch = torch_mod()
+    Bt, L, Dm, dt, docs = case
+    inp = make_custom(Bt, L, Dm, 4, dtype=dt, docs=docs, seed=860 + L + Dm)
+    inp.conv_b[:] = np.linspace(-0.3, 0.3, Dm).astype(np.float32)
+    inp.doc_start[0, 0] = 0       # row 0 continues the history
+    inp.doc_start[1, 0] = 1       # row 1 starts a document: zero history gradient
+    if L > 2:
+        inp.doc_start[0, 2] = 1   # and in row 0 a start cuts the history off token 2
+    rng = np.random.default_rng(861)
+    hist = rng.normal(0.0, 1.0, size=(Bt, Dm, 3)).astype(np.float32)
+    if dt == "bf16":
+        hist = bf16_round(hist)
+    du = make_cotangent(Bt, L, Dm, dtype=dt, seed=960 + L)
+    dev = upload(inp)
+    got = ssm.causal_conv1d_bwd(dev["x"], dev["conv_w"], to_dev(du, dt), dev["conv_b"], dev["doc_start"],
+                                conv_state=to_dev(hist, dt))
+    ref = oracle.causal_conv1d_bwd(inp.x, inp.conv_w, du, inp.conv_b, inp.doc_start, conv_state=hist)
+    for i, what in enumerate(("dx", "dweight", "dbias", "d_conv_state")):
+        assert_close(to_host(got[i]), ref[i], dt, f"conv history {what}")
+    assert torch.count_nonzero(got[3][1]) == 0
+
+
+def test_conv_bwd_split_row_equals_whole(ssm):
+    """Conv backward of a row cut in two: the second piece takes the first piece's
+    last three inputs as history (zeroed before a document start inside them), and
+    its d_conv_state adds to the first piece's dx there."""
+    inp = make_custom(2, 400, 64, 4, dtype="f32", docs=30.0, seed=870)
+    inp.conv_b[:] = 0.1
+    cut = 150
+    inp.doc_start[0, cut - 1] = 1   # row 0: a document starts inside the history window
+    inp.doc_start[1, cut - 3:cut + 1] = 0
+    Bt, L, Dm = inp.x.shape
+    du = make_cotangent(Bt, L, Dm, dtype="f32", seed=970)
+    ref = oracle.causal_conv1d_bwd(inp.x, inp.conv_w, du, inp.conv_b, inp.doc_start)
+    hist = np.ascontiguousarray(inp.x[:, cut - 3:cut].transpose(0, 2, 1))
+    for b in range(Bt):
+        starts = np.nonzero(inp.doc_start[b, cut - 3:cut])[0]
+        if starts.size:
+            hist[b, :, :starts[-1]] = 0.0
+    dev = upload(inp)
+    s1, s2 = slice(0, cut), slice(cut, L)
+    dx1, dw1, db1 = ssm.causal_conv1d_bwd(dev["x"][:, s1].contiguous(), dev["conv_w"], to_dev(du[:, s1], "f32"),
+                                          dev["conv_b"], dev["doc_start"][:, s1].contiguous())
+    dx2, dw2, db2, dh2 = ssm.causal_conv1d_bwd(dev["x"][:, s2].contiguous(), dev["conv_w"], to_dev(du[:, s2], "f32"),
+                                               dev["conv_b"], dev["doc_start"][:, s2].contiguous(),
+                                               conv_state=to_dev(hist, "f32"))
+    dx = np.concatenate([to_host(dx1), to_host(dx2)], axis=1)
+    dh = to_host(dh2).transpose(0, 2, 1)                         # (B, 3, D)
+    for b in range(Bt):
+        starts = np.nonzero(inp.doc_start[b, cut - 3:cut])[0]
+        lo = starts[-1] if starts.size else 0
+        dx[b, cut - 3 + lo:cut] += dh[b, lo:]
+    assert_close(dx, ref[0], "f32", "split conv dx")
+    assert_close(to_host(dw1) + to_host(dw2), ref[1], "f32", "split conv dweight")
+    assert_close(to_host(db1) + to_host(db2), ref[2], "f32", "split conv dbias")
