@@ -97,6 +97,13 @@ def test_workspace_query(lib):
     assert ws_bytes(lib, dims(dtype=3))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
     assert ws_bytes(lib, dims(seqlen=400000))[0] == _lib.MAMBA_ERR_UNSUPPORTED      # a row above 2 GiB at 4 B
     assert ws_bytes(lib, dims(batch=1, seqlen=65536, dim=5120))[0] == _lib.MAMBA_OK
+    # the boundary: (L + 64) * D * 4 <= 2^31 - 1 (the longest row test_gpu_limits.py runs)
+    assert ws_bytes(lib, dims(seqlen=262079, dim=2048, dtype=0))[0] == _lib.MAMBA_OK
+    assert ws_bytes(lib, dims(seqlen=262080, dim=2048, dtype=0))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    for L, st in ((262079, _lib.MAMBA_OK), (262080, _lib.MAMBA_ERR_UNSUPPORTED)):
+        d = dims(seqlen=L, dim=2048, dtype=0)
+        assert lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == st
     assert ws_bytes(lib, dims(dstate=0))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
     # scalar-A heads with bf16 I/O: headdim 32 or 64, a multiple of 8 states up to 128
     assert ws_bytes(lib, dims(nheads=32, dstate=128))[0] == _lib.MAMBA_ERR_UNSUPPORTED      # headdim 48

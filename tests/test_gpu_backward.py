@@ -429,3 +429,60 @@ def test_conv_bwd_split_row_equals_whole(ssm):
     assert_close(dx, ref[0], "f32", "split conv dx")
     assert_close(to_host(dw1) + to_host(dw2), ref[1], "f32", "split conv dweight")
     assert_close(to_host(db1) + to_host(db2), ref[2], "f32", "split conv dbias")
+
+
+def test_train_step_graph_replays_match_eager(ssm):
+    """The fused forward, the scan backward and the conv backward captured in one
+    HIP graph (caller-owned outputs and workspaces, nothing allocated by the
+    library): every replay, with eager work between replays, reproduces the
+    eager results bit for bit."""
+    torch = torch_mod()
+    inp = make_custom(2, 1000, 128, 16, dtype="bf16", docs=150.0, seed=880)
+    Bt, L, Dm = inp.x.shape
+    N = inp.A.shape[1]
+    dev = upload(inp)
+    dout = to_dev(make_cotangent(Bt, L, Dm, dtype="bf16", seed=980), "bf16")
+    ws_f = torch.empty(max(ssm.scan_workspace_bytes(Bt, L, Dm, N), 1), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(ssm.scan_bwd_workspace_bytes(Bt, L, Dm, N), dtype=torch.uint8, device="cuda")
+    ws_c = torch.empty(ssm.conv_bwd_workspace_bytes(Bt, L, Dm), dtype=torch.uint8, device="cuda")
+    u = torch.empty_like(dev["x"])
+    out = torch.empty_like(dev["x"])
+    fin = torch.empty((Bt, Dm, N), dtype=torch.float32, device="cuda")
+    grads = ssm.selective_scan_bwd(u, dev["delta"], dev["A"], dev["B"], dev["C"], dout, dev["D"], dev["z"],
+                                   dev["delta_bias"], dev["doc_start"], workspace=ws_b)
+    dx = torch.empty_like(dev["x"])
+    dw = torch.empty((Dm, 4), dtype=torch.float32, device="cuda")
+    db = torch.empty((Dm,), dtype=torch.float32, device="cuda")
+
+    def step():
+        ssm.conv_scan_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["delta"], dev["A"], dev["B"], dev["C"],
+                          dev["D"], dev["z"], dev["delta_bias"], dev["doc_start"], u=u, out=out, final_state=fin,
+                          workspace=ws_f)
+        ssm.selective_scan_bwd(u, dev["delta"], dev["A"], dev["B"], dev["C"], dout, dev["D"], dev["z"],
+                               dev["delta_bias"], dev["doc_start"], workspace=ws_b, grads=grads)
+        ssm.causal_conv1d_bwd(dev["x"], dev["conv_w"], grads["du"], dev["conv_b"], dev["doc_start"],
+                              workspace=ws_c, dx=dx, dweight=dw, dbias=db)
+
+    results = lambda: [t.clone() for t in (u, out, fin, dx, dw, db)] + [grads[k].clone() for k in sorted(grads)]  # noqa: E731
+    step()
+    torch.cuda.synchronize()
+    ref = results()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (u, out, fin, dx, dw, db, *grads.values()):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(results(), ref)):
+            assert torch.equal(a, b), f"replay {rep}: result {i}"
+        _ = (out.float() * 2).sum().item()      # eager work between replays
