@@ -122,13 +122,29 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t rs, int byte_of
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// LDS layout of one workgroup.  Row strides carry 8 bf16 (16 bytes) of padding so
-// that the 16 rows read by one fragment load start on different banks.
+// Row padding of the LDS tiles, in elements (tunable; fragment loads need the
+// bf16 row strides to stay multiples of 8 elements, the fp32 one of 4).
+#ifndef MAMBA_SSD_PAD_N
+#define MAMBA_SSD_PAD_N 8
+#endif
+#ifndef MAMBA_SSD_PAD_Q
+#define MAMBA_SSD_PAD_Q 16
+#endif
+#ifndef MAMBA_SSD_PAD_Y
+#define MAMBA_SSD_PAD_Y 4
+#endif
+
+// LDS layout of one workgroup.  Row strides carry padding so that the 16 rows
+// read by one fragment load start on different banks: 8 bf16 for the [*][N]
+// tiles; 16 bf16 for the [*][Q] tiles, whose transposing 2-byte stores (x^T, M,
+// dt-weighted B^T) conflict least at that stride (measured on the 32K heads
+// shape: 518 us per call against 535 with 8, 553-569 with 24-56).
 template <int NP, int P, bool OUTPUT>
 struct SsdLds {
-    static constexpr int SN = NP + 8;              // [*][NP] bf16 tiles
-    static constexpr int SQ = kQ + 8;              // [*][Q] bf16 tiles
-    static constexpr int SY = P / kRowW + 4;       // per-wave fp32 output tile [16][SY]
+    static constexpr int SN = NP + MAMBA_SSD_PAD_N;        // [*][NP] bf16 tiles
+    static constexpr int SQ = kQ + MAMBA_SSD_PAD_Q;        // [*][Q] bf16 tiles
+    static constexpr int SY = P / kRowW + MAMBA_SSD_PAD_Y; // per-wave fp32 output tile [16][SY]
+    static_assert(SN % 8 == 0 && SQ % 8 == 0 && SY % 4 == 0, "row strides of the fragment and vector accesses");
     static constexpr int kBBytes = kQ * SN * 2;
     static constexpr int kYBytes = OUTPUT ? kWaves * 16 * SY * 4 : 0;
     // B rows, x^T and the per-token scalars are double-buffered by chunk parity:
