@@ -191,8 +191,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the scan shards trivially over batch rows and channels; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the scan shards over batch rows and channels with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -289,7 +289,7 @@ def main():
     pair_gbs = (sb + cb) / (call_ms * 1e-3) / 1e9
     if H > 0 and inp.dtype == "bf16":
         # Scalar-A heads run as bf16 matrix products: the chunked form's flops go to
-        # the matrix cores and the call is judged against HBM (its MFMA share beside).
+        # the matrix cores and the call is measured against HBM (its MFMA share beside).
         mf = ssd_mfma_flops(B, L, D, N, H)
         roof = {"kernel": kernel, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": dom_bytes,

@@ -12,7 +12,7 @@ from workloads import bf16_bits, bf16_round
 
 # Tolerances stated for the path: fp32 I/O to 1e-4 relative; bf16 I/O with fp32
 # state to 2e-2 relative / absolute.  fp32 uses an absolute floor of 1e-4 x the
-# reference's rms so that entries near zero are judged on the output's scale.
+# reference's rms so that entries near zero are measured on the output's scale.
 TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 2e-2)}
 
 
