@@ -35,8 +35,10 @@
  *     delta_bias) and the final state are always float32.  All arithmetic and
  *     the recurrent state are float32; bf16 outputs are rounded to nearest even.
  *   - doc_start is (B, L) uint8; nonzero marks the first token of a document.
- *     Token 0 of every row always starts a document.  NULL = one document per row.
- *     A document start zeroes the conv history and the recurrent state.
+ *     Token 0 of every row starts a document, unless the call continues a given
+ *     history (conv_state, initial_state: then only where doc_start marks it).
+ *     NULL = no starts besides that one.  A document start zeroes the conv
+ *     history and the recurrent state.
  *   - `stream` is a hipStream_t (NULL = the null stream).
  *   - Every call validates its arguments before any launch and returns a status
  *     code; no exception crosses the ABI.  Errors raised by a kernel while it
