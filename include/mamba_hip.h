@@ -45,6 +45,11 @@
  *     runs surface at the caller's next synchronisation, as for any HIP call.
  *   - Calls are reentrant.  Concurrent calls must not share output or workspace
  *     buffers.  Inputs and outputs must not overlap.
+ *   - A call with no tokens (B L D == 0) reads no input and writes only what
+ *     has a value without tokens: a final state equal to the initial state (or
+ *     0), the adjoint passed through (d_initial_state = d_final_state, or 0),
+ *     and zero for the sums over tokens (dA, dD, ddelta_bias, dweight, dbias,
+ *     d_conv_state).
  */
 #ifndef MAMBA_HIP_H
 #define MAMBA_HIP_H
@@ -205,8 +210,7 @@ int mamba_causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64
  *   workspace  at least mamba_causal_conv1d_bwd_workspace_bytes bytes, 256-byte
  *              aligned, scratch.
  * Outputs must not overlap each other, the inputs or the workspace.  Sums run
- * in a fixed order (repeated calls give identical results).  With B L D == 0
- * nothing is written. */
+ * in a fixed order (repeated calls give identical results). */
 int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
                             const void* conv_state, const void* du, void* dx, float* dweight, float* dbias,
                             float* d_conv_state, int64_t batch, int64_t seqlen, int64_t dim, int32_t width,
@@ -255,8 +259,7 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
  * delta, z and dout must be 4-byte aligned (they are read as pairs of channels),
  * else MAMBA_ERR_MISALIGNED.  Outputs must not overlap each other, the inputs
  * or the workspace.  The sums over channels, tokens and rows run in a fixed
- * order: repeated calls give bitwise identical results.  With B L D == 0
- * nothing is written. */
+ * order: repeated calls give bitwise identical results. */
 int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A,
                              const void* B, const void* C, const float* D, const void* z,
                              const float* delta_bias, const uint8_t* doc_start, const float* initial_state,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 LIB_NAME = "libmamba_hip.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.cpp", "conv1d.hip", "conv1d_bwd.hip", "scan.hip", "scan_bwd.hip", "ssd.hip", "decode.hip"]
+SOURCES = ["api.cpp", "conv1d.hip", "conv1d_bwd.hip", "scan.hip", "scan_bwd.hip", "ssd.hip", "decode.hip", "fill.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for all device code: hipcc would otherwise

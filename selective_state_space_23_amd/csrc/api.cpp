@@ -8,6 +8,7 @@
 #include <climits>
 #include <cstdint>
 
+#include "fill.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -170,6 +171,29 @@ int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, 
     return MAMBA_OK;
 }
 
+// Outputs of a call with no tokens (B L D == 0, dims already checked): the
+// state passes through unchanged, final_state = initial_state (or 0).
+int empty_scan_outputs(const mamba_scan_dims_t* dims, const float* initial_state, float* final_state,
+                       void* stream) {
+    const int64_t n = dims->batch * dims->dim * dims->dstate;
+    if (dims->seqlen != 0 || n == 0 || final_state == nullptr) return MAMBA_OK;
+    if (!aligned(final_state, 4) || (initial_state && !aligned(initial_state, 4))) return MAMBA_ERR_MISALIGNED;
+    if (overlap(final_state, n * 4, initial_state, n * 4)) return MAMBA_ERR_INVALID_ARGUMENT;
+    return mamba::launch_fill(final_state, initial_state, n, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MAMBA_OK
+               : MAMBA_ERR_HIP;
+}
+
+// Zero-fills the float32 arrays (dst[i], n[i] elements) that are not null.
+int zero_outputs(float* const* dst, const int64_t* n, int count, void* stream) {
+    for (int i = 0; i < count; ++i)
+        if (dst[i] && n[i] > 0 && !aligned(dst[i], 4)) return MAMBA_ERR_MISALIGNED;
+    for (int i = 0; i < count; ++i)
+        if (dst[i] && n[i] > 0 && mamba::launch_fill(dst[i], nullptr, n[i], static_cast<hipStream_t>(stream)) != hipSuccess)
+            return MAMBA_ERR_HIP;
+    return MAMBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,7 +243,8 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
     bool empty;
     const int st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out,
                               final_state, workspace, workspace_bytes, stream, nullptr, nullptr, 0, &a, &empty);
-    if (st != MAMBA_OK || empty) return st;
+    if (st != MAMBA_OK) return st;
+    if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
     return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
@@ -237,7 +262,8 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
     bool empty;
     int st = check_conv(x, conv_weight, conv_bias, doc_start, conv_state, u, dims->batch, dims->seqlen, dims->dim, 4,
                         dims->dtype, 1, stream, &ca, &empty);
-    if (st != MAMBA_OK || empty) return st;
+    if (st != MAMBA_OK) return st;
+    if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
     // u is written by the conv and read by the scan: it may overlap nothing else.
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
     const size_t act = static_cast<size_t>(dims->batch * dims->seqlen * dims->dim) * esz;
@@ -247,7 +273,8 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
     mamba::ScanArgs a;
     st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out, final_state, workspace,
                     workspace_bytes, stream, conv_in, conv_sz, 4, &a, &empty);
-    if (st != MAMBA_OK || empty) return st;
+    if (st != MAMBA_OK) return st;
+    if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
     if (dims->nheads == 0) {
         a.conv_x = x; a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state;
         return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
@@ -277,7 +304,14 @@ int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bia
     if (!mul_ok(batch, seqlen, dim, &n) || dim > kMaxDim || batch > 65535) return MAMBA_ERR_INVALID_ARGUMENT;
     if (seqlen > kMaxSeqlen) return MAMBA_ERR_UNSUPPORTED;
     if (d_conv_state && !conv_state) return MAMBA_ERR_INVALID_ARGUMENT;
-    if (n == 0) return MAMBA_OK;
+    if (n == 0) {
+        // No tokens: the weight and bias gradients are sums over none, and the
+        // history influenced nothing.
+        float* zs[] = {batch * seqlen == 0 ? dweight : nullptr, batch * seqlen == 0 ? dbias : nullptr,
+                       seqlen == 0 ? d_conv_state : nullptr};
+        const int64_t zn[] = {dim * 4, dim, batch * dim * 3};
+        return zero_outputs(zs, zn, 3, stream);
+    }
     if (!x || !weight || !du || !dx || !dweight) return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
     if (!aligned(x, esz) || !aligned(du, esz) || !aligned(dx, esz) || !aligned(weight, 4) || !aligned(dweight, 4) ||
@@ -336,7 +370,20 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
     const int64_t Bt = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     if ((z == nullptr) != (dz == nullptr)) return MAMBA_ERR_INVALID_ARGUMENT;
     if (d_initial_state && !initial_state) return MAMBA_ERR_INVALID_ARGUMENT;
-    if (Bt * L * Dm == 0) return MAMBA_OK;
+    if (Bt * L * Dm == 0) {
+        // No tokens: dA, dD and ddelta_bias are sums over none, and the adjoint
+        // passes through the empty row (d_initial_state = d_final_state, or 0).
+        float* zs[] = {Bt * L == 0 ? dA : nullptr, Bt * L == 0 ? dD : nullptr, Bt * L == 0 ? ddelta_bias : nullptr};
+        const int64_t zn[] = {Dm * N, Dm, Dm};
+        int zst = zero_outputs(zs, zn, 3, stream);
+        if (zst != MAMBA_OK || L != 0 || Bt * Dm == 0 || !d_initial_state) return zst;
+        const int64_t ns = Bt * Dm * N;
+        if (!aligned(d_initial_state, 4) || (d_final_state && !aligned(d_final_state, 4))) return MAMBA_ERR_MISALIGNED;
+        if (overlap(d_initial_state, ns * 4, d_final_state, ns * 4)) return MAMBA_ERR_INVALID_ARGUMENT;
+        return mamba::launch_fill(d_initial_state, d_final_state, ns, static_cast<hipStream_t>(stream)) == hipSuccess
+                   ? MAMBA_OK
+                   : MAMBA_ERR_HIP;
+    }
     if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
         return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;

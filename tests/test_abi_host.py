@@ -154,6 +154,10 @@ def test_scan_validation(lib):
     # empty shapes are a no-op
     assert scan(lib, d=dims(batch=0), u=None, out=None) == _lib.MAMBA_OK
     assert scan(lib, d=dims(seqlen=0), u=None, out=None) == _lib.MAMBA_OK
+    # no tokens: final_state = initial_state, so both are still checked
+    assert scan(lib, d=dims(seqlen=0), u=None, out=None, fs=FAKE * 9 + 2) == _lib.MAMBA_ERR_MISALIGNED
+    assert scan(lib, d=dims(seqlen=0), u=None, out=None, init=FAKE * 9, fs=FAKE * 9) == \
+        _lib.MAMBA_ERR_INVALID_ARGUMENT
 
 
 def test_python_binding_rejects_cpu_tensors():
@@ -252,7 +256,13 @@ def test_bwd_validation(lib):
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, nheads=2)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=32)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
-    assert bwd(lib, d=dims(batch=0), u=None, dout=None) == _lib.MAMBA_OK   # empty: no-op
+    assert bwd(lib, d=dims(batch=0), u=None, dout=None, dA=None) == _lib.MAMBA_OK   # empty: nothing to write
+    # empty calls still check what they would write (dA = 0 over no tokens)
+    assert bwd(lib, d=dims(batch=0), u=None, dout=None, dA=FAKE * 9 + 2) == _lib.MAMBA_ERR_MISALIGNED
+    assert bwd(lib, d=dims(seqlen=0), u=None, dout=None, dA=None, h0=FAKE * 12, dh0=FAKE * 13 + 2) == \
+        _lib.MAMBA_ERR_MISALIGNED
+    assert bwd(lib, d=dims(seqlen=0), u=None, dout=None, dA=None, h0=FAKE * 12, dhT=FAKE * 13, dh0=FAKE * 13) == \
+        _lib.MAMBA_ERR_INVALID_ARGUMENT
     # bf16 inputs are staged as channel pairs: even D, 4-byte aligned u, delta, z, dout
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=63, dtype=1)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dtype=1), u=FAKE + 2) == _lib.MAMBA_ERR_MISALIGNED
@@ -288,7 +298,8 @@ def test_conv_bwd_validation(lib):
     assert cb(dx=FAKE * 3) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # dx aliases du
     assert cb(dw=FAKE * 4) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # dweight inside dx
     assert cb(ws=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT              # workspace over x
-    assert cb(B=0, x=None, du=None) == _lib.MAMBA_OK                  # empty: no-op
+    assert cb(B=0, x=None, du=None, dw=None) == _lib.MAMBA_OK          # empty: nothing to write
+    assert cb(B=0, x=None, du=None, dw=FAKE * 5 + 2) == _lib.MAMBA_ERR_MISALIGNED
     assert cb(dhist=FAKE * 9) == _lib.MAMBA_ERR_INVALID_ARGUMENT       # d_conv_state without conv_state
     assert cb(hist=FAKE * 9 + 1, dhist=FAKE * 10) == _lib.MAMBA_ERR_MISALIGNED
     assert cb(hist=FAKE * 9, dhist=FAKE * 10 + 2) == _lib.MAMBA_ERR_MISALIGNED
