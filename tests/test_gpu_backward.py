@@ -486,3 +486,20 @@ def test_train_step_graph_replays_match_eager(ssm):
         for i, (a, b) in enumerate(zip(results(), ref)):
             assert torch.equal(a, b), f"replay {rep}: result {i}"
         _ = (out.float() * 2).sum().item()      # eager work between replays
+
+
+@pytest.mark.parametrize("case", ["A_zero", "step_to_zero", "large_step"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_degenerate_parameters(ssm, case, dtype):
+    """The method's degenerate cases, backward: A = 0 (the state is a running
+    sum), a vanishing step (delta_bias = -60: softplus ~ 1e-26, only the skip
+    and gate terms carry gradient) and a large step (delta_bias = +5: decays
+    down to e^-5 and below, each token nearly forgets the last)."""
+    inp = make_custom(2, 700, 96, 16, dtype=dtype, docs=150.0, seed=890)
+    if case == "A_zero":
+        inp.A[:] = 0.0
+    elif case == "step_to_zero":
+        inp.delta_bias[:] = -60.0
+    else:
+        inp.delta_bias[:] = 5.0
+    bwd_case(ssm, inp, seed=990)
