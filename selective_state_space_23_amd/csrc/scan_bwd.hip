@@ -35,9 +35,9 @@
 //      plus exp(A sum) * (chunk's carry), or the checkpoint alone if a document
 //      started since the chunk start.
 //      The blocks are walked last to first: from that checkpoint recompute the
-//      state before token 8, and for each 4-token piece (last first) its start
-//      state (4 more steps for the odd pieces) and its four states, then run
-//      the adjoint over them;
+//      state before token 8 (keeping the one before token 4 in LDS), and for
+//      each 4-token piece (last first) its start state (4 more steps for the
+//      last piece) and its four states, then run the adjoint over them;
 //   5. fixed-order reduction of the per-block partial sums (dB, dC) and of the
 //      per-chunk partial sums (dA, dD, ddelta_bias): results are deterministic.
 //
@@ -74,6 +74,9 @@ constexpr int kPiece = 4;              // tokens per innermost recompute piece
 #endif
 #ifndef MAMBA_BWD_G8
 #define MAMBA_BWD_G8 1           // lanes per channel at N = 8
+#endif
+#ifndef MAMBA_BWD_ST4_LDS
+#define MAMBA_BWD_ST4_LDS 1      // the state before token 4 of a block kept in LDS
 #endif
 
 struct BwdKParams {
@@ -559,6 +562,13 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
     constexpr int kStgBytes = kCk * CPW * (4 + kNArr * kTsz);
     static_assert(kStgBytes % 16 == 0, "staging rows");
     __shared__ float4 sStg4[kWaves * kStgBytes / 16];
+#if MAMBA_BWD_ST4_LDS
+    // The state before token 4 of the current block, saved while the state
+    // before token 8 is recomputed: piece 1 starts from it instead of
+    // re-advancing tokens 0..3 a third time.  [q][thread] float4s.
+    static_assert(NL % 4 == 0, "states in float4s");
+    __shared__ float4 sH4[(NL / 4) * kBlk];
+#endif
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -892,6 +902,11 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
 #pragma unroll
             for (int i = 0; i < NL; ++i) ck8[i] = ck0[i];
             advance4(ck8, s, os);
+#if MAMBA_BWD_ST4_LDS
+#pragma unroll
+            for (int q = 0; q < NL / 4; ++q)
+                sH4[q * kBlk + tid] = make_float4(ck8[4 * q], ck8[4 * q + 1], ck8[4 * q + 2], ck8[4 * q + 3]);
+#endif
             advance4(ck8, s + 4, os + 4);
 #pragma unroll
             for (int i = 0; i < NL; ++i) ck8[i] = opaque(ck8[i]);
@@ -904,7 +919,17 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
                 float st[NL];
 #pragma unroll
                 for (int i = 0; i < NL; ++i) st[i] = j >= 2 ? ck8[i] : ck0[i];
+#if MAMBA_BWD_ST4_LDS
+                if (j == 1) {
+#pragma unroll
+                    for (int q = 0; q < NL / 4; ++q) {
+                        const float4 v = sH4[q * kBlk + tid];
+                        st[4 * q] = v.x; st[4 * q + 1] = v.y; st[4 * q + 2] = v.z; st[4 * q + 3] = v.w;
+                    }
+                } else if (j == 3) {
+#else
                 if (j & 1) {
+#endif
                     advance4(st, s4 - kPiece, os + j * kPiece - kPiece);
 #pragma unroll
                     for (int i = 0; i < NL; ++i) st[i] = opaque(st[i]);
