@@ -6,8 +6,9 @@
  *
  *   mamba_causal_conv1d_fwd   depthwise causal conv1d (width 4) + optional SiLU.
  *       Defined by the "Mamba: Selective State Spaces (S6)" section of the Mamba
- *       skill page (Conv1d(d_inner, d_inner, d_conv, padding=d_conv-1,
- *       groups=d_inner), the first L outputs kept, then SiLU) and by the packing
+ *       skill page (a per-channel causal convolution of width 4: each channel
+ *       filtered on its own, three zero taps of left padding, only the first L
+ *       outputs kept, then SiLU) and by the packing
  *       paragraph of the axolotl "FLA Mamba and Mamba2" page (the convolution
  *       state starts fresh at every document start).
  *
@@ -174,7 +175,9 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims,
  * mamba_selective_scan_workspace_bytes) on its output; the conv output is also
  * written to `u` (B, L, D).  With per-channel A the convolution runs inside the
  * scan's first pass, which saves the conv's separate pass over x and u.
- * conv_state and initial_state are normally given together (a continuation). */
+ * conv_state and initial_state act on their own stage each, as in the two
+ * separate calls: a continuation passes both; a conv_state alone continues
+ * the conv's history while the scan's state starts at zero. */
 int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const float* conv_weight,
                         const float* conv_bias, const void* conv_state, const void* delta,
                         const float* A, const void* B, const void* C, const float* D,

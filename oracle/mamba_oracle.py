@@ -92,8 +92,8 @@ def silu(v):
 
 
 # ----------------------------------------------------------------------------
-# Depthwise causal conv1d (S6 section: Conv1d(groups=d_inner, padding=d_conv-1),
-# first L outputs kept, then SiLU)
+# Depthwise causal conv1d (S6 section: each channel filtered on its own, three
+# zero taps of left padding, first L outputs kept, then SiLU)
 # ----------------------------------------------------------------------------
 def causal_conv1d(x, weight, bias=None, doc_start=None, apply_silu=True):
     """u[b,t,d] = act(bias[d] + sum_j weight[d, W-1-j] * x[b, t-j, d]).

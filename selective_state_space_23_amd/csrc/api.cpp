@@ -255,9 +255,6 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
                         void* workspace, size_t workspace_bytes, void* stream) {
     const int sd = check_dims(dims);
     if (sd != MAMBA_OK) return sd;
-    // The conv history is a continuation of the state: without an initial state
-    // token 0 starts a document for both, and the history is not used.
-    if (!initial_state) conv_state = nullptr;
     mamba::ConvArgs ca;
     bool empty;
     int st = check_conv(x, conv_weight, conv_bias, doc_start, conv_state, u, dims->batch, dims->seqlen, dims->dim, 4,

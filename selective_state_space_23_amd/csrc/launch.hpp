@@ -71,6 +71,10 @@ struct ScanArgs {
     bool bf16;
     bool softplus;
     hipStream_t stream;
+    // Per-channel A: pass 1 hands its step sizes (rounded to the I/O dtype) to
+    // pass 3 through the workspace; false: pass 3 recomputes them from delta and
+    // the workspace holds the chunk carries only.
+    bool dt_handoff = true;
 };
 
 // Chunking of the sequence used by the scan for a given shape.
@@ -80,7 +84,8 @@ struct ScanPlan {
 };
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim);
-size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16);
+size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16,
+                            bool dt_handoff = true);
 bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16);
 hipError_t launch_selective_scan(const ScanArgs& a);
 

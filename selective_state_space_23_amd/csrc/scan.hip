@@ -146,10 +146,15 @@ __device__ __forceinline__ void buf_store_s(__amdgpu_buffer_rsrc_t rs, int lane_
 // before the chunk), stores u (rounded to T) for pass 3 and scans with it.  The
 // arithmetic and its order are those of the standalone conv kernel, so u is
 // bitwise the same.
-template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS, bool CONV = false>
+//
+// DTWS (per-channel A): pass 1 stores dt (rounded to T) in the workspace and
+// pass 3 reads it back instead of recomputing the softplus; without it pass 3
+// recomputes dt from delta and the workspace holds the carries only.
+template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS, bool CONV, bool DTWS>
 __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMBA_SCAN_WAVES_PER_EU))) void scan_chunk_kernel(
     const ScanKParams p) {
     static_assert(!CONV || (!OUTPUT && !HEADS), "the conv runs in the aggregate pass of the per-channel scan");
+    static_assert(!(HEADS && DTWS), "step sizes are handed over for per-channel A only");
     constexpr int G = kGroup;
     constexpr int kWin = 64;                                   // tokens per staged window
     constexpr int kRows = OUTPUT ? 2 : 1;                      // B and C, or B only
@@ -179,9 +184,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
         make_rsrc(static_cast<const T*>(CONV ? p.conv_x : p.u) + b * act_row, act_row * kEsz);
     const __amdgpu_buffer_rsrc_t uo_rs =
         make_rsrc(static_cast<T*>(CONV ? p.u_out : p.out) + b * act_row, act_row * kEsz);
-    // Per-channel A: pass 1 stores dt (rounded to T) and pass 3 reads it back
-    // instead of recomputing the softplus; both passes use the same rounded dt.
-    constexpr bool kDtWs = !HEADS;
+    // With the hand-off both passes use the same rounded dt.
+    constexpr bool kDtWs = DTWS;
     const __amdgpu_buffer_rsrc_t dl_rs =
         make_rsrc(static_cast<const T*>((kDtWs && OUTPUT) ? p.dt_ws : p.delta) + b * L * nd, L * nd * kEsz);
     const __amdgpu_buffer_rsrc_t dto_rs =
@@ -221,7 +225,11 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     // Fused conv: weights and the input history x[t-1], x[t-2], x[t-3] as seen by
     // the chunk's first token (taps before its document start read zero).
     float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f, xh1 = 0.0f, xh2 = 0.0f, xh3 = 0.0f;
+    // Token 0 continues the conv history although the scan restarts there: a
+    // conv_state without an initial_state.
+    bool conv_keep0 = false;
     if constexpr (CONV) {
+        conv_keep0 = p.conv_state != nullptr && !(ds_row != nullptr && ds_row[0] != 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) cw[j] = p.conv_w[static_cast<int64_t>(dc) * 4 + j];
         cb = p.conv_b ? p.conv_b[dc] : 0.0f;
@@ -231,9 +239,11 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             if (p.conv_state == nullptr) return 0.0f;
             return Elem<T>::load(p.conv_state, (b * p.dim + dc) * 3 + (3 - k));
         };
-        auto starts_at = [&](int64_t t) -> bool {      // same rule as the window mask
+        // The conv's own rule for token 0: it starts a document unless a
+        // history is given (the scan's rule looks at initial_state instead).
+        auto starts_at = [&](int64_t t) -> bool {
             if (t < 0) return false;
-            return (t == 0 && p.initial_state == nullptr) || (ds_row != nullptr && ds_row[t] != 0);
+            return (t == 0 && p.conv_state == nullptr) || (ds_row != nullptr && ds_row[t] != 0);
         };
         const bool s1 = starts_at(t_begin - 1), s2 = starts_at(t_begin - 2);
         xh1 = hist(1);
@@ -334,9 +344,10 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             float uk = cu[k];
             if constexpr (CONV) {
                 const float xt = cu[k];
-                xh1 = reset ? 0.0f : xh1;
-                xh2 = reset ? 0.0f : xh2;
-                xh3 = reset ? 0.0f : xh3;
+                const bool creset = reset && !(t == 0 && conv_keep0);
+                xh1 = creset ? 0.0f : xh1;
+                xh2 = creset ? 0.0f : xh2;
+                xh3 = creset ? 0.0f : xh3;
                 float acc = __builtin_fmaf(cw[3], xt, cb);
                 acc = __builtin_fmaf(cw[2], xh1, acc);
                 acc = __builtin_fmaf(cw[1], xh2, acc);
@@ -485,7 +496,7 @@ size_t dt_ws_offset(int64_t batch, int64_t dim, int64_t dstate, const ScanPlan& 
     return (carries + 255) / 256 * 256;
 }
 
-template <typename T, int N, bool HEADS>
+template <typename T, int N, bool HEADS, bool DTWS>
 hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     ScanKParams p;
     p.u = a.u; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
@@ -495,7 +506,7 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     const int64_t nslots = plan.nchunks - 1;
     p.ws_P = a.ws;
     p.ws_H = a.ws ? a.ws + nslots * count : nullptr;
-    p.dt_ws = (!HEADS && a.ws) ? reinterpret_cast<char*>(a.ws) + dt_ws_offset(a.batch, a.dim, N, plan) : nullptr;
+    p.dt_ws = (DTWS && a.ws) ? reinterpret_cast<char*>(a.ws) + dt_ws_offset(a.batch, a.dim, N, plan) : nullptr;
     p.seqlen = a.seqlen;
     p.chunk_len = plan.chunk_len;
     p.dim = static_cast<int>(a.dim);
@@ -508,75 +519,75 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     p.nslots = nslots;
 
     const unsigned gx = static_cast<unsigned>((a.dim + kScanBlock - 1) / kScanBlock);
-    if constexpr (!HEADS) {
-        if (a.conv_x != nullptr) {
-            // Fused conv: pass 1 runs on every chunk (the last one only to produce u).
-            dim3 g1(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
-            if (a.softplus)
-                hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, true, true>), g1, dim3(kScanBlock),
-                                   0, a.stream, p);
-            else
-                hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, false, true>), g1,
+    const dim3 gall(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
+    // Pass 1 runs on every chunk when it also produces something the last chunk
+    // needs (u of the fused conv, the handed-over step sizes); otherwise on every
+    // chunk but the last.
+    const bool pass1_all = a.conv_x != nullptr || DTWS;
+    if (pass1_all || nslots > 0) {
+        const dim3 g1 = pass1_all ? gall : dim3(gx, static_cast<unsigned>(nslots), static_cast<unsigned>(a.batch));
+        if constexpr (!HEADS) {
+            if (a.conv_x != nullptr) {
+                if (a.softplus)
+                    hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, true, true, DTWS>), g1,
+                                       dim3(kScanBlock), 0, a.stream, p);
+                else
+                    hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, false, true, DTWS>), g1,
+                                       dim3(kScanBlock), 0, a.stream, p);
+            } else if (a.softplus) {
+                hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, true, false, DTWS>), g1,
                                    dim3(kScanBlock), 0, a.stream, p);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
+            } else {
+                hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, false, false, DTWS>), g1,
+                                   dim3(kScanBlock), 0, a.stream, p);
+            }
+        } else {
+            if (a.softplus)
+                hipLaunchKernelGGL((scan_chunk_kernel<T, N, true, false, false, true, false, false>), g1,
+                                   dim3(kScanBlock), 0, a.stream, p);
+            else
+                hipLaunchKernelGGL((scan_chunk_kernel<T, N, true, false, false, false, false, false>), g1,
+                                   dim3(kScanBlock), 0, a.stream, p);
         }
-    }
-    if (!HEADS && a.conv_x == nullptr) {
-        // Pass 1 runs on every chunk: the last one only to store its step sizes.
-        dim3 g1(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
-        if (a.softplus)
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, true>), g1, dim3(kScanBlock), 0,
-                               a.stream, p);
-        else
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, false>), g1, dim3(kScanBlock), 0,
-                               a.stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (nslots > 0) {
-        if (HEADS && a.conv_x == nullptr) {
-            dim3 g1(gx, static_cast<unsigned>(nslots), static_cast<unsigned>(a.batch));
-            if (a.softplus)
-                hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, true>), g1, dim3(kScanBlock), 0,
-                                   a.stream, p);
-            else
-                hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, false, false, false>), g1, dim3(kScanBlock), 0,
-                                   a.stream, p);
-        }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         dim3 g2(static_cast<unsigned>((count + 255) / 256));
         hipLaunchKernelGGL(scan_carry_kernel, g2, dim3(256), 0, a.stream, p.ws_P, p.ws_H, a.initial_state, count,
                            nslots);
-        e = hipGetLastError();
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dim3 g3(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
     if (a.z) {
         if (a.softplus)
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, true, true>), g3, dim3(kScanBlock), 0,
-                               a.stream, p);
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, true, true, false, DTWS>), gall, dim3(kScanBlock),
+                               0, a.stream, p);
         else
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, true, false>), g3, dim3(kScanBlock), 0,
-                               a.stream, p);
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, true, false, false, DTWS>), gall,
+                               dim3(kScanBlock), 0, a.stream, p);
     } else {
         if (a.softplus)
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, false, true>), g3, dim3(kScanBlock), 0,
-                               a.stream, p);
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, false, true, false, DTWS>), gall,
+                               dim3(kScanBlock), 0, a.stream, p);
         else
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, false, false>), g3, dim3(kScanBlock), 0,
-                               a.stream, p);
+            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, false, false, false, DTWS>), gall,
+                               dim3(kScanBlock), 0, a.stream, p);
     }
     return hipGetLastError();
+}
+
+template <typename T, int N>
+hipError_t launch_scan_channels(const ScanArgs& a, const ScanPlan& plan) {
+    return a.dt_handoff ? launch_scan_typed<T, N, false, true>(a, plan) : launch_scan_typed<T, N, false, false>(a, plan);
 }
 
 template <typename T>
 hipError_t launch_scan_dtype(const ScanArgs& a, const ScanPlan& plan) {
     switch (a.dstate) {
-        case 4: return launch_scan_typed<T, 4, false>(a, plan);
-        case 8: return launch_scan_typed<T, 8, false>(a, plan);
-        case 16: return launch_scan_typed<T, 16, false>(a, plan);
+        case 4: return launch_scan_channels<T, 4>(a, plan);
+        case 8: return launch_scan_channels<T, 8>(a, plan);
+        case 16: return launch_scan_channels<T, 16>(a, plan);
         default: return hipErrorInvalidValue;
     }
 }
@@ -585,10 +596,10 @@ hipError_t launch_scan_dtype(const ScanArgs& a, const ScanPlan& plan) {
 // matrix-core form rounds its operands to bf16, below what fp32 I/O promises.
 hipError_t launch_heads_f32(const ScanArgs& a, const ScanPlan& plan) {
     switch (a.dstate) {
-        case 16: return launch_scan_typed<float, 16, true>(a, plan);
-        case 32: return launch_scan_typed<float, 32, true>(a, plan);
-        case 64: return launch_scan_typed<float, 64, true>(a, plan);
-        case 128: return launch_scan_typed<float, 128, true>(a, plan);
+        case 16: return launch_scan_typed<float, 16, true, false>(a, plan);
+        case 32: return launch_scan_typed<float, 32, true, false>(a, plan);
+        case 64: return launch_scan_typed<float, 64, true, false>(a, plan);
+        case 128: return launch_scan_typed<float, 128, true, false>(a, plan);
         default: return hipErrorInvalidValue;
     }
 }
@@ -620,14 +631,15 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim) {
     return p;
 }
 
-size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16) {
+size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16,
+                            bool dt_handoff) {
     if (nheads > 0 && bf16) return ssd_workspace_bytes(batch, seqlen, dim, dstate, nheads);
     const ScanPlan plan = plan_scan(batch, seqlen, dim);
     const size_t carries =
         plan.nchunks > 1
             ? static_cast<size_t>(2 * (plan.nchunks - 1)) * static_cast<size_t>(batch * dim * dstate) * sizeof(float)
             : 0;
-    if (nheads > 0) return carries;
+    if (nheads > 0 || !dt_handoff) return carries;
     // Per-channel A: the step sizes pass 1 hands to pass 3 follow the carries.
     return dt_ws_offset(batch, dim, dstate, plan) +
            static_cast<size_t>(batch * seqlen * dim) * (bf16 ? 2 : 4);

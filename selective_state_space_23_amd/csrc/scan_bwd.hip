@@ -664,8 +664,11 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if (i * tpi >= kCk) break;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst + i * tpi * CPW * esz), 4, voff,
-                                                     static_cast<int>((s0 + i * tpi) * p.dim * esz), 0, 0);
+            // The token part goes into the lane (VGPR) offset, not the scalar one:
+            // the buffer's range check covers only the former, and the last block
+            // of a row reaches up to 15 token rows past the row's end.
+            const int v = voff + static_cast<int>((s0 + i * tpi) * p.dim * esz);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst + i * tpi * CPW * esz), 4, v, 0, 0, 0);
         }
     };
     auto stage_block = [&](int64_t s0) {

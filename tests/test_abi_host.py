@@ -324,3 +324,4 @@ def test_conv_state_update_validation(lib):
     assert csu(cs=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT              # window over x
     assert csu(uo=FAKE * 9) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # u_out over out
     assert csu(d=dims(batch=0, seqlen=1), x=None) == _lib.MAMBA_OK      # empty: no-op
+

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make_custom, make_inputs
+from workloads import bf16_round, make_custom, make_inputs
 
 from gpu_helpers import assert_close, oracle_pipeline, to_dev, to_host, torch_mod, upload
 
@@ -119,6 +119,37 @@ def test_conv_scan_continuation(ssm, H, N):
     u2 = ssm.causal_conv1d_fwd(second["x"], dev["conv_w"], dev["conv_b"], second["doc_start"], conv_state=window)
     u_exact = oracle.causal_conv1d(inp.x, inp.conv_w, inp.conv_b, inp.doc_start)[:, L1:]
     assert_close(to_host(u2), u_exact, "bf16", "conv with history")
+
+
+@pytest.mark.parametrize("H,N,dt", [(0, 16, "bf16"), (0, 8, "f32"), (2, 64, "bf16")])
+def test_conv_state_without_initial_state(ssm, H, N, dt):
+    """A conv history alone: the conv continues it at token 0 (unless doc_start[b, 0]
+    is set) while the scan's state starts at zero, exactly as the conv call with
+    that history followed by the scan call without an initial state."""
+    torch = torch_mod()
+    L, Dm = 600, 128
+    inp = make_custom(2, L, Dm, N, nheads=H, dtype=dt, docs=120.0, seed=730 + N)
+    inp.doc_start[:, 0] = 0
+    inp.doc_start[1, 0] = 1                   # row 1 starts a document at token 0 anyway
+    dev = upload(inp)
+    rng = np.random.default_rng(731)
+    win = rng.standard_normal((2, Dm, 3)).astype(np.float32)
+    window = to_dev(win if dt == "f32" else bf16_round(win), dt)
+    u, out, fin = fused(ssm, dev, conv_state=window)
+    u_split = ssm.causal_conv1d_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["doc_start"], conv_state=window)
+    out_split, fin_split = ssm.selective_scan_fwd(u_split, dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"],
+                                                  dev["z"], dev["delta_bias"], dev["doc_start"])
+    assert torch.equal(u, u_split), "fused u differs from the conv call with the same history"
+    if H:   # the heads path runs the conv kernel, then the same scan
+        assert torch.equal(out, out_split), "fused out differs from the split calls"
+    assert_close(to_host(out), to_host(out_split), dt, "fused vs split out")
+    assert_close(to_host(fin), to_host(fin_split), dt, "fused vs split final_state")
+    # and against the oracle: the conv of the history followed by the rows
+    xs = np.concatenate([np.transpose(to_host(window), (0, 2, 1)), inp.x.astype(np.float64)], axis=1)
+    ds = np.concatenate([np.zeros((2, 3), np.uint8), inp.doc_start], axis=1)
+    ds[:, 0] = 1
+    u_exact = oracle.causal_conv1d(xs, inp.conv_w, inp.conv_b, ds)[:, 3:]
+    assert_close(to_host(u), u_exact, dt, "conv with history, no initial state")
 
 
 SAMPLES = {"packed_32k": [0, 5, 63, 64, 700, 1535], "heads_32k": [0, 64, 700, 1535], "m130_2k": [0, 777, 1535]}
