@@ -9,9 +9,13 @@ of `workloads`, uploaded once, and are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is tokens/s of the step (conv + scan; by default
 one fused mamba_conv_scan_fwd call).  Extra objects: `roofline` for the timed
-call (live HIP-event timing), the HBM roofline of the conv + scan pair, a device
-copy probe, and `cpu_baseline` (the fp64 oracle timed on this host on a bounded
-sample).
+call (live HIP-event timing; the metric's own quantity, the HBM roofline of the
+conv + scan pair), its ALU fraction beside it (fp32 VALU slots priced with the
+measured gfx950 issue rates), a device copy probe, call times with the MALL
+flushed before every call (median and min), and `cpu_baseline` (the fp64 oracle
+timed on this host: one core, and all cores of the GPU's CPU share).
+
+`--path rates` runs the ALU issue-rate probe instead (libmamba_probe.so).
 """
 
 from __future__ import annotations
@@ -27,8 +31,26 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selective-scan fwd tokens/s + % HBM roofline, B=2 L=32K D=1536 N=16 bf16"
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3
+# MI355X fp32 vector peak without packed fp32 (which every device file here is
+# built without): 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz.
+FP32_VECTOR_PEAK_TFLOPS = 78.6
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+CPU_SHARE = 16          # host cores that go with one GPU on the GPU machines
+RATES_FILE = os.path.join(ROOT, "profiles", "alu_rates_gfx950.md")
+
+
+def trans_slots():
+    """Cost of v_exp_f32, v_log_f32, v_rcp_f32 in full-rate fp32 VALU issue slots
+    (a v_fma_f32 is 1 slot), from the committed rate table of the probe; 4 (the
+    quarter rate of earlier CDNA parts) for any kind the table does not hold."""
+    out = {"exp": 4.0, "log": 4.0, "rcp": 4.0, "source": "assumed quarter rate"}
+    if os.path.exists(RATES_FILE):
+        for line in open(RATES_FILE):
+            if line.startswith("slots_") and ":" in line:
+                k, v = line.split(":", 1)
+                out[k[len("slots_"):].strip()] = float(v)
+                out["source"] = "profiles/alu_rates_gfx950.md"
+    return out
 
 
 def scan_bytes(B, L, D, N, nheads, esz):
@@ -45,22 +67,26 @@ def conv_bytes(B, L, D, esz):
     return B * L * (2 * esz * D + 1) + D * 5 * 4
 
 
-def scan_alu_flop_eq(B, L, D, N, nheads):
-    """Algorithmic fp32 VALU work of one scan call in flop-equivalents.
+def scan_alu_slots(B, L, D, N, nheads, w):
+    """Algorithmic fp32 VALU work of one scan call, in full-rate issue slots
+    (an FMA, multiply or add is 1 slot; a transcendental costs w[kind] slots).
 
-    Counted in full-rate VALU issue slots (an FMA is one slot = 2 flops; a
-    transcendental v_exp/v_log/v_rcp runs at quarter rate = 4 slots = 8 flops),
-    so that the chip's 157.3 TFLOP/s fp32 vector peak is the matching ceiling.
-    Per (t, d, n) element, per-channel A: dt*A (1) + exp (4) + dt*u*B (1) + state
-    FMA (1) + C*h FMA (1) = 8 slots.  Scalar-A heads: dt*u*B + two FMAs = 3 slots,
-    plus one exp per (t, head).  Per (t, d): softplus (exp + log + 5) = 13, SiLU
-    (exp + rcp + 2) = 10, dt*u, D*u, gate = 3 slots (softplus per head for heads)."""
+    Per (t, d, n) element, per-channel A: dt*A, dt*u*B, the state FMA, the C*h
+    FMA (4 slots) and one exp.  Scalar-A heads: dt*u*B and the two FMAs (3
+    slots), one exp per (t, head).  Per (t, d): softplus (5 ops, exp, log),
+    SiLU(z) (3 ops, exp, rcp), dt*u, D*u and the gate (3 ops); softplus per head
+    for heads."""
     el = B * L * D * N
+    sp = 5 + w["exp"] + w["log"]
+    silu = 3 + w["exp"] + w["rcp"]
     if nheads == 0:
-        slots = el * 8 + B * L * D * 26
-    else:
-        slots = el * 3 + B * L * D * 13 + B * L * nheads * (13 + 4 + 1)
-    return 2.0 * slots
+        return el * (4 + w["exp"]) + B * L * D * (sp + silu + 3)
+    return el * 3 + B * L * nheads * (sp + w["exp"] + 1) + B * L * D * (silu + 3)
+
+
+def conv_alu_slots(B, L, D, w):
+    """4 FMAs + SiLU (3 ops, exp, rcp) per (t, d)."""
+    return B * L * D * (4 + 3 + w["exp"] + w["rcp"])
 
 
 def ssd_mfma_flops(B, L, D, N, H, q=64):
@@ -90,19 +116,15 @@ def conv_bwd_bytes(B, L, D, esz):
     return B * L * (3 * esz * D + 1) + D * 10 * 4
 
 
-def bwd_alu_flop_eq(B, L, D, N):
-    """Algorithmic fp32 VALU work of the backward in flop-equivalents (slots as in
-    scan_alu_flop_eq).  Per (t, d, n): the decay (dt*A + exp = 5), the state
-    (dt*u*B, FMA = 2), the adjoint (C*dy FMA, times the decay = 2), a*h_{t-1} and
-    g*(a*h) (2), the A and dA terms (2), g.B (1), the dB and dC terms (2) and their
-    sums over channels (2) = 18 slots.  Per (t, d): softplus, its sigmoid, SiLU(z)
-    with its derivative, du, ddt, dz and the dD / ddelta_bias sums, about 48 slots."""
-    return 2.0 * (B * L * D * N * 18 + B * L * D * 48)
-
-
-def conv_alu_flop_eq(B, L, D):
-    """4 FMAs + SiLU (exp, rcp, 2 ops) per (t, d) = 14 slots."""
-    return 2.0 * 14 * B * L * D
+def bwd_alu_slots(B, L, D, N, w):
+    """Algorithmic fp32 VALU work of one backward call, in slots as in
+    scan_alu_slots.  Per (t, d, n): the decay (dt*A + exp), the state (dt*u*B,
+    FMA = 2), the adjoint (C*dy FMA, times the decay = 2), a*h_{t-1} and
+    g*(a*h) (2), the A and dA terms (2), g.B (1), the dB and dC terms (2) and
+    their sums over channels (2) = 14 slots + exp.  Per (t, d): softplus, its
+    sigmoid, SiLU(z) with its derivative, du, ddt, dz and the dD / ddelta_bias
+    sums: about 30 ops and 5 transcendentals."""
+    return B * L * D * N * (14 + w["exp"]) + B * L * D * (30 + 3 * w["exp"] + w["log"] + w["rcp"])
 
 
 def copy_probe(torch, dev, mib=1024, reps=5):
@@ -154,24 +176,161 @@ def recorded_traffic(path, source_files):
         return None
 
 
-def cpu_baseline(inp, tokens_per_row):
-    """Time the fp64 oracle (conv + scan, as it stands) on the first tokens of every row."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores():
+    """Cores of this process's CPU share: the affinity set, capped at the share a
+    GPU has on the GPU machines."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, CPU_SHARE))
+
+
+_SHARD_INP = None     # the workload, inherited by the forked oracle workers
+
+
+def _oracle_fwd_shard(job):
+    """The oracle's conv + scan on one (row, channel range) of the shared workload's
+    first T tokens; every (row, channel) chain is independent, so the shards
+    together are the whole computation.  Returns the shard's seconds."""
     from threadpoolctl import threadpool_limits
 
     import oracle
 
-    T = min(tokens_per_row, inp.x.shape[1])
-    sl = slice(0, T)
+    b, c0, c1, T = job
+    inp = _SHARD_INP
+    ch, rows, ts = slice(c0, c1), slice(b, b + 1), slice(0, T)
+    if inp.nheads:
+        P = inp.x.shape[2] // inp.nheads
+        hs = slice(c0 // P, c1 // P)
+        A, delta, bias = inp.A[hs], inp.delta[rows, ts, hs], inp.delta_bias[hs]
+    else:
+        A, delta, bias = inp.A[ch], inp.delta[rows, ts, ch], inp.delta_bias[ch]
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        u = oracle.causal_conv1d(inp.x[:, sl], inp.conv_w, inp.conv_b, inp.doc_start[:, sl])
-        oracle.selective_scan(u, inp.delta[:, sl], inp.A, inp.B[:, sl], inp.C[:, sl], inp.D, inp.z[:, sl],
-                              inp.delta_bias, True, inp.doc_start[:, sl])
-        dt = time.perf_counter() - t0
-    ntok = inp.x.shape[0] * T
-    return dict(value=ntok / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"first {T} tokens of each of the {inp.x.shape[0]} rows, all {inp.x.shape[2]} channels "
-                       f"({ntok} tokens, {dt:.1f} s, fp64 numpy, one thread)")
+        u = oracle.causal_conv1d(inp.x[rows, ts, ch], inp.conv_w[ch], inp.conv_b[ch], inp.doc_start[rows, ts])
+        oracle.selective_scan(u, delta, A, inp.B[rows, ts], inp.C[rows, ts], inp.D[ch], inp.z[rows, ts, ch], bias,
+                              True, inp.doc_start[rows, ts])
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(inp, tokens_one_core, tokens_all_cores):
+    """Time the fp64 oracle (conv + scan, as it stands) on this host.
+
+    Two legs: one core on the first `tokens_one_core` tokens of every row, and
+    all cores of the CPU share on the first `tokens_all_cores` tokens, sharded
+    over independent (row, channel range) pieces in forked worker processes.
+    Runs before the GPU is initialised (the workers are forked)."""
+    import multiprocessing
+
+    global _SHARD_INP
+    _SHARD_INP = inp
+    Bt, L, Dm = inp.x.shape
+    P = Dm // inp.nheads if inp.nheads else 1
+    T1 = min(tokens_one_core, L)
+    t1 = sum(_oracle_fwd_shard((b, 0, Dm, T1)) for b in range(Bt))
+    one = dict(value=Bt * T1 / t1, unit="tokens/s", cores=1, seconds=t1,
+               sample=f"first {T1} tokens of each of the {Bt} rows, all {Dm} channels, one process, one thread")
+    ncores = host_cores()
+    T = min(tokens_all_cores, L)
+    per_row = max(1, ncores // Bt)
+    step = -(-Dm // per_row)
+    step = -(-step // P) * P                       # whole heads per shard
+    jobs = [(b, c0, min(c0 + step, Dm), T) for b in range(Bt) for c0 in range(0, Dm, step)]
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(min(ncores, len(jobs))) as pool:
+        pool.map(_oracle_fwd_shard, jobs, chunksize=1)
+    wall = time.perf_counter() - t0
+    _SHARD_INP = None
+    return dict(value=Bt * T / wall, unit="tokens/s", cores=min(ncores, len(jobs)), kind="oracle",
+                cpu_model=cpu_model(),
+                sample=f"first {T} tokens of each of the {Bt} rows, all {Dm} channels, fp64 numpy, "
+                       f"{len(jobs)} (row, channel range) shards over {min(ncores, len(jobs))} worker processes of "
+                       f"one thread each, {wall:.1f} s wall",
+                one_core=one)
+
+
+def mall_flusher(torch, dev, mib=768):
+    """A fill of `mib` MiB: run between timed calls (outside their events) it
+    evicts the previous call's data from the 256 MB MALL and the L2."""
+    buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    return lambda: buf.fill_(1)
+
+
+def bench_rates(args):
+    """ALU issue rates of gfx950 from the probe library: wave64 instructions
+    retired per SIMD per shader clock, for independent chains (throughput) and one
+    dependent chain (latency, cycles per instruction)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib = ctypes.CDLL(os.path.join(ROOT, "selective_state_space_23_amd", "libmamba_probe.so"))
+    lib.probe_alu_rate.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_alu_rate.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    names = ["v_fma_f32", "v_mul_f32", "v_add_f32", "v_exp_f32", "v_log_f32", "v_rcp_f32",
+             "1 exp : 1 fma", "1 exp : 3 fma", "1 exp : 5 fma"]
+    per_step = {6: (4, 4), 7: (2, 6), 8: (1, 5)}   # (exp, fma) chains of the mixes
+    results = []
+    for kind, name in enumerate(names):
+        for chains in ((8,) if kind < 6 else (sum(per_step[kind]),)) + ((1,) if kind < 6 else ()):
+            # throughput: 8 waves on every SIMD; latency: one wave per CU
+            blocks, threads = (cus * 8, 256) if chains > 1 else (cus, 64)
+            iters = 4096 if chains > 1 else 8192
+            out = torch.empty(blocks * threads, dtype=torch.float32, device=dev)
+            clk = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+            stream = torch.cuda.current_stream(dev).cuda_stream
+            for _ in range(2):
+                st = lib.probe_alu_rate(kind, chains, blocks, threads, iters, out.data_ptr(), clk.data_ptr(), stream)
+                if st != 0:
+                    raise RuntimeError(f"probe_alu_rate({kind}, {chains}) failed: hip error {st}")
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lib.probe_alu_rate(kind, chains, blocks, threads, iters, out.data_ptr(), clk.data_ptr(), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            c = clk.view(-1, 2).cpu().numpy().astype(np.float64)
+            ghz = float(np.median(c[:, 0] / c[:, 1]) * 0.1)            # s_memrealtime ticks at 100 MHz
+            wave_cycles = float(np.median(c[:, 0]))
+            instr_per_wave = iters * 8 * chains
+            waves = blocks * threads // 64
+            rec = dict(kind=name, chains=chains, ms=ms, clock_GHz=ghz)
+            if chains > 1:
+                simd = cus * 4
+                # wave instructions per SIMD per clock over the kernel's span
+                rec["wave_instr_per_simd_clock"] = waves * instr_per_wave / (simd * ms * 1e-3 * ghz * 1e9)
+                rec["lane_ops_per_s"] = waves * 64 * instr_per_wave / (ms * 1e-3)
+            else:
+                rec["latency_cycles"] = wave_cycles / instr_per_wave
+            results.append(rec)
+            print(json.dumps(rec), flush=True)
+    fma = next(r for r in results if r["kind"] == "v_fma_f32" and r["chains"] > 1)["wave_instr_per_simd_clock"]
+    slots = {}
+    for key, name in (("exp", "v_exp_f32"), ("log", "v_log_f32"), ("rcp", "v_rcp_f32")):
+        r = next(r for r in results if r["kind"] == name and r["chains"] > 1)
+        slots[key] = fma / r["wave_instr_per_simd_clock"]
+    print(json.dumps({"metric": "gfx950 fp32 VALU issue rates", "device": props.name, "cus": cus,
+                      "fma_wave_instr_per_simd_clock": fma, "trans_slots": slots, "results": results}), flush=True)
 
 
 def main():
@@ -182,12 +341,16 @@ def main():
     ap.add_argument("--config", default="packed_32k",
                     help="workload name from workloads.CONFIGS (default: the 32K packed bf16 shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32768, help="oracle sample: tokens per row")
+    ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle, one core: tokens per row")
+    ap.add_argument("--cpu-tokens-all", type=int, default=32768, help="oracle, all cores: tokens per row")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the device copy probe (0: skip)")
-    ap.add_argument("--path", choices=("fused", "split", "bwd", "decode"), default="fused",
+    ap.add_argument("--flush-reps", type=int, default=20,
+                    help="calls timed one by one with the MALL flushed before each (0: skip)")
+    ap.add_argument("--path", choices=("fused", "split", "bwd", "decode", "rates"), default="fused",
                     help="fused: one mamba_conv_scan_fwd call per step; split: conv call, then scan call; "
                          "bwd: scan backward then conv backward (per-channel A workloads); "
-                         "decode: one token per row (conv window update + recurrence step)")
+                         "decode: one token per row (conv window update + recurrence step); "
+                         "rates: the ALU issue-rate probe")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -195,15 +358,26 @@ def main():
               "(the scan shards over batch rows and channels with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
+    if args.path == "rates":
+        return bench_rates(args)
 
     import numpy as np
+
+    from workloads import CONFIGS, make_inputs
+
+    spec = CONFIGS[args.config]
+    inp = make_inputs(args.config)
+    # The oracle legs run first: their workers are forked before the GPU is touched.
+    cpu = None
+    if not args.no_cpu_baseline and args.path in ("fused", "split"):
+        cpu = cpu_baseline(inp, args.cpu_tokens, args.cpu_tokens_all)
+    if not args.no_cpu_baseline and args.path == "bwd":
+        cpu = cpu_baseline_bwd(inp, dout_seed=7, tokens_per_row=min(args.cpu_tokens, 4096))
+
     import torch
 
     import selective_state_space_23_amd as ssm
-    from workloads import CONFIGS, make_inputs
-
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import upload
+    from workloads.device import upload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -212,22 +386,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    spec = CONFIGS[args.config]
-    inp = make_inputs(args.config)
     B, L, D = inp.x.shape
     N = inp.B.shape[-1]
     H = inp.nheads
     esz = 2 if inp.dtype == "bf16" else 4
     t = upload(inp, dev)
+    if args.path == "bwd":
+        return bench_bwd(args, torch, np, ssm, inp, t, spec, dev, cpu)
+    if args.path == "decode":
+        return bench_decode(args, torch, np, ssm, inp, t, spec, dev)
     u = torch.empty_like(t["x"])
     out = torch.empty_like(t["x"])
     fin = torch.empty((B, D, N), dtype=torch.float32, device=dev)
     ws = torch.empty(max(ssm.scan_workspace_bytes(B, L, D, N, H, inp.dtype), 1), dtype=torch.uint8, device=dev)
-
-    if args.path == "bwd":
-        return bench_bwd(args, torch, np, ssm, inp, t, spec, dev)
-    if args.path == "decode":
-        return bench_decode(args, torch, np, ssm, inp, t, spec, dev)
     fused = args.path == "fused"
 
     def step(ev=None):
@@ -261,8 +432,25 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     # HIP events on torch's current stream, which is the stream the binding
     # passes to every launch of the library.
-    call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
-    first_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    call_all = np.array([e[0].elapsed_time(e[2]) for e in events])
+    first_all = np.array([e[0].elapsed_time(e[1]) for e in events])
+    call_ms, first_ms = float(call_all.mean()), float(first_all.mean())
+
+    # The same call timed one by one with the MALL and L2 flushed before each.
+    flushed = None
+    if args.flush_reps > 0:
+        flush = mall_flusher(torch, dev)
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.flush_reps)]
+        for e in fev:
+            flush()
+            e[0].record()
+            step()
+            e[1].record()
+        torch.cuda.synchronize()
+        f = np.array([e[0].elapsed_time(e[1]) for e in fev])
+        flushed = {"reps": args.flush_reps, "flush_MiB": 768, "call_ms_median": float(np.median(f)),
+                   "call_ms_min": float(f.min())}
+        del flush
 
     probe = copy_probe(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
     csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
@@ -270,36 +458,39 @@ def main():
         os.path.join(ROOT, "profiles", f"{args.path}_{args.config}_hbm_traffic.txt"),
         [os.path.join(csrc, f) for f in FWD_SOURCES])
 
+    w = trans_slots()
     tokens = B * L
     sb = scan_bytes(B, L, D, N, H, esz)
     cb = conv_bytes(B, L, D, esz)
-    scan_flops = scan_alu_flop_eq(B, L, D, N, H)
-    conv_flops = conv_alu_flop_eq(B, L, D)
     if fused:
         kernel = ("mamba_conv_scan_fwd, one call: conv + aggregate pass, carry pass, output pass"
                   if H == 0 else "mamba_conv_scan_fwd, one call: conv, aggregate pass, carry pass, output pass")
-        dom_ms, dom_flops, dom_bytes = call_ms, scan_flops + conv_flops, sb + cb
-        timings = {"call_ms": call_ms}
+        dom_ms, dom_bytes = call_ms, sb + cb
+        dom_slots = scan_alu_slots(B, L, D, N, H, w) + conv_alu_slots(B, L, D, w)
+        timings = {"call_ms": call_ms, "call_ms_median": float(np.median(call_all)), "call_ms_min": float(call_all.min())}
     else:
         kernel = "mamba_selective_scan_fwd, one call: aggregate pass, carry pass, output pass"
-        dom_ms, dom_flops, dom_bytes = call_ms - first_ms, scan_flops, sb
+        dom_ms, dom_bytes = call_ms - first_ms, sb
+        dom_slots = scan_alu_slots(B, L, D, N, H, w)
         timings = {"conv_ms": first_ms, "scan_ms": call_ms - first_ms}
-    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     pair_gbs = (sb + cb) / (call_ms * 1e-3) / 1e9
+    # flop-equivalents: a slot is one lane FMA = 2 flops
+    alu_tflops = 2.0 * dom_slots / (dom_ms * 1e-3) / 1e12
+    roof = {"kernel": kernel, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": dom_bytes, "avg_ms": dom_ms}
     if H > 0 and inp.dtype == "bf16":
-        # Scalar-A heads run as bf16 matrix products: the chunked form's flops go to
-        # the matrix cores and the call is measured against HBM (its MFMA share beside).
+        # Scalar-A heads run as bf16 matrix products: their share of the matrix cores beside.
         mf = ssd_mfma_flops(B, L, D, N, H)
-        roof = {"kernel": kernel, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": dom_bytes,
-                "mfma_flops": mf, "mfma_TFLOPs": mf / (dom_ms * 1e-3) / 1e12,
-                "mfma_frac": mf / (dom_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, "avg_ms": dom_ms}
+        roof.update(mfma_flops=mf, mfma_TFLOPs=mf / (dom_ms * 1e-3) / 1e12,
+                    mfma_frac=mf / (dom_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS)
     else:
-        roof = {"kernel": kernel, "bound": "alu", "achieved": dom_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": dom_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic,
-                "algorithmic_flop_eq": dom_flops, "algorithmic_bytes": dom_bytes, "hbm_achieved_GBs": dom_gbs,
-                "hbm_frac": dom_gbs / HBM_PEAK_GBS, "avg_ms": dom_ms}
+        roof["alu"] = {"algorithmic_slots": dom_slots, "achieved_TFLOPs": alu_tflops,
+                       "peak_TFLOPs": FP32_VECTOR_PEAK_TFLOPS, "frac": alu_tflops / FP32_VECTOR_PEAK_TFLOPS,
+                       "trans_slots": w,
+                       "note": "fp32 VALU issue slots of the method's own work (one exp and four fp32 ops per "
+                               "(t,d,n), the per-token softplus, SiLU and conv) at the non-packed fp32 peak; "
+                               "transcendentals priced at the measured gfx950 rates"}
     result = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -315,16 +506,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "batch": B, "seqlen": L, "dim": D, "dstate": N, "nheads": H,
                    "d_conv": 4, "doc_mean_len": spec["docs"], "io_dtype": inp.dtype, "state_dtype": "f32",
-                   "path": args.path},
+                   "path": args.path, "u_written": True},
         "roofline": roof,
         "hbm_roofline_pair": dict(
             {"achieved": pair_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pair_gbs / HBM_PEAK_GBS,
              "algorithmic_bytes": sb + cb, "conv_bytes": cb, "scan_bytes": sb}, **timings),
+        "mall_flushed": flushed,
         "copy_probe": None if probe is None else dict(
             probe, pair_frac_of_copy=pair_gbs / probe["GBs"], kernel="hipMemcpyAsync device-to-device"),
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
@@ -448,12 +640,12 @@ def bench_decode(args, torch, np, ssm, inp, t, spec, dev, tokens=64, graphs_per_
     print(json.dumps(result), flush=True)
 
 
-def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
+def bench_bwd(args, torch, np, ssm, inp, t, spec, dev, cpu=None):
     """One step = the mixer core's backward: mamba_selective_scan_bwd (gradients of
     sum(dout * out) with respect to u, delta, A, B, C, D, z and delta_bias, u being
     the conv output the forward stores) then mamba_causal_conv1d_bwd (dx and the
     conv's weight and bias gradients from du)."""
-    from gpu_helpers import to_dev
+    from workloads.device import to_dev
     from workloads import make_cotangent
 
     B, L, D = inp.x.shape
@@ -502,7 +694,8 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
     csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
     traffic = recorded_traffic(os.path.join(ROOT, "profiles", f"bwd_{args.config}_hbm_traffic.txt"),
                                [os.path.join(csrc, f) for f in BWD_SOURCES])
-    flops = bwd_alu_flop_eq(B, L, D, N)
+    w = trans_slots()
+    flops = 2.0 * bwd_alu_slots(B, L, D, N, w)
     nbytes = bwd_bytes(B, L, D, N, esz)
     cbytes = conv_bwd_bytes(B, L, D, esz)
     tflops = flops / (call_ms * 1e-3) / 1e12
@@ -533,8 +726,8 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev):
                      "avg_ms": call_ms},
         "copy_probe": probe,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_bwd(inp, dout_seed=7, tokens_per_row=min(args.cpu_tokens, 4096))
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

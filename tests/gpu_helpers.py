@@ -8,7 +8,8 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
-from workloads import bf16_bits, bf16_round
+from workloads import bf16_round
+from workloads.device import to_dev, to_host, upload  # noqa: F401
 
 # Tolerances stated for the path: fp32 I/O to 1e-4 relative; bf16 I/O with fp32
 # state to 2e-2 relative / absolute.  fp32 uses an absolute floor of 1e-4 x the
@@ -19,32 +20,6 @@ TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 2e-2)}
 def torch_mod():
     import torch
     return torch
-
-
-def to_dev(a: np.ndarray, dtype: str, device="cuda"):
-    """Upload a float32 numpy array as float32 or bf16 (values already bf16-exact)."""
-    torch = torch_mod()
-    if dtype == "bf16":
-        bits = bf16_bits(a)
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
-
-
-def to_host(t) -> np.ndarray:
-    torch = torch_mod()
-    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
-
-
-def upload(inp, device="cuda"):
-    torch = torch_mod()
-    dt = inp.dtype
-    return dict(
-        x=to_dev(inp.x, dt, device), z=to_dev(inp.z, dt, device), delta=to_dev(inp.delta, dt, device),
-        B=to_dev(inp.B, dt, device), C=to_dev(inp.C, dt, device),
-        conv_w=torch.from_numpy(inp.conv_w).to(device), conv_b=torch.from_numpy(inp.conv_b).to(device),
-        A=torch.from_numpy(inp.A).to(device), D=torch.from_numpy(inp.D).to(device),
-        delta_bias=torch.from_numpy(inp.delta_bias).to(device),
-        doc_start=torch.from_numpy(inp.doc_start).to(device))
 
 
 def assert_close(got, ref, dtype, what, rms_floor=True):
