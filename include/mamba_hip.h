@@ -168,6 +168,33 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims,
                              void* out, float* final_state,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Selective scan forward that allocates nothing and takes no workspace: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *   Arguments and results as mamba_selective_scan_fwd without workspace.  The
+ *   chunk carries live in a 64 MiB array of the library's own, one per GPU,
+ *   held from the library's first use on that GPU until the process ends.  The
+ *   step sizes are recomputed in the output pass instead of being handed over
+ *   (with bf16 I/O, results may therefore differ from mamba_selective_scan_fwd
+ *   by the rounding of dt to bf16, well inside the bf16 tolerance; with fp32 I/O
+ *   they are the same).
+ *   Carries take 8 (ceil(L / chunk) - 1) B D N bytes (per-channel A, fp32
+ *   scalar-A heads; the chunk is 128 to 4096 tokens, chosen so that about 4096
+ *   waves run: 50 MB at B = 2, L = 32768, D = 1536, N = 16) or, for bf16
+ *   scalar-A heads, the matrix form's segment states (25 MB at B = 2, L = 32768,
+ *   24 heads of 64 channels, N = 128).  A call that needs more than 64 MiB
+ *   returns MAMBA_ERR_WORKSPACE before any launch.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time on
+ *   one GPU (different streams or host threads) race and must be serialised by
+ *   the caller.  Nothing needs clearing between calls.
+ *   MAMBA_ERR_HIP also reports a failed lookup of the array's address. */
+int mamba_selective_scan_fwd_noalloc(const mamba_scan_dims_t* dims,
+                                     const void* u, const void* delta, const float* A,
+                                     const void* B, const void* C, const float* D,
+                                     const void* z, const float* delta_bias,
+                                     const uint8_t* doc_start, const float* initial_state,
+                                     void* out, float* final_state, void* stream);
+
 /* Conv1d (width 4, SiLU) and selective scan in one call: the whole forward path
  * of the mixer core.  Same arguments and results as mamba_causal_conv1d_fwd
  * (x, conv_weight, conv_bias, doc_start, conv_state; apply_silu = 1) followed by

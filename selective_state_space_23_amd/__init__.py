@@ -30,6 +30,7 @@ from ._lib import MambaArgumentError, MambaError, ScanDims  # noqa: F401
 __all__ = [
     "causal_conv1d_fwd",
     "selective_scan_fwd",
+    "selective_scan_fwd_noalloc",
     "scan_workspace_bytes",
     "conv_scan_fwd",
     "causal_conv1d_update",
@@ -194,6 +195,43 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, doc_s
         _ptr(final_state, "final_state", dev, torch.float32, (Bt, Dm, N)),
         ws_ptr, ws_bytes, _stream(dev))
     _lib.check(st, "mamba_selective_scan_fwd")
+    return out, final_state
+
+
+def selective_scan_fwd_noalloc(u, delta, A, B, C, out, D=None, z=None, delta_bias=None, doc_start=None,
+                               delta_softplus: bool = True, final_state=None, initial_state=None):
+    """Selective scan forward with no workspace; see mamba_selective_scan_fwd_noalloc.
+
+    Arguments as selective_scan_fwd; ``out`` (B, L, D) and the optional
+    ``final_state`` (B, D, N) float32 are caller-owned tensors the call fills
+    (nothing is allocated here or in the library).  Returns (out, final_state)."""
+    torch = _torch()
+    dev = _check_device(u)
+    if u.dim() != 3:
+        raise ValueError("u must be (B, L, D)")
+    Bt, L, Dm = u.shape
+    N = B.shape[-1]
+    nheads = A.shape[0] if A.dim() == 1 else 0
+    nd = nheads if nheads else Dm
+    if doc_start is not None and doc_start.dtype == torch.bool:
+        raise ValueError("doc_start must be uint8 (a bool mask would need a converted copy)")
+    dims = _scan_dims(Bt, L, Dm, N, nheads, _dtype_code(u), delta_softplus)
+    st = _lib.load().mamba_selective_scan_fwd_noalloc(
+        ctypes.byref(dims),
+        _ptr(u, "u", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(delta, "delta", dev, u.dtype, (Bt, L, nd)),
+        _ptr(A, "A", dev, torch.float32, (nheads,) if nheads else (Dm, N)),
+        _ptr(B, "B", dev, u.dtype, (Bt, L, N)),
+        _ptr(C, "C", dev, u.dtype, (Bt, L, N)),
+        _ptr(D, "D", dev, torch.float32, (Dm,)),
+        _ptr(z, "z", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)),
+        _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
+        _ptr(initial_state, "initial_state", dev, torch.float32, (Bt, Dm, N)),
+        _ptr(out, "out", dev, u.dtype, (Bt, L, Dm)),
+        _ptr(final_state, "final_state", dev, torch.float32, (Bt, Dm, N)),
+        _stream(dev))
+    _lib.check(st, "mamba_selective_scan_fwd_noalloc")
     return out, final_state
 
 

@@ -32,6 +32,7 @@ EXPORTED = (
     "mamba_causal_conv1d_bwd_workspace_bytes",
     "mamba_causal_conv1d_bwd",
     "mamba_conv_state_update",
+    "mamba_selective_scan_fwd_noalloc",
 )
 
 
@@ -104,6 +105,8 @@ def load() -> ctypes.CDLL:
     lib.mamba_causal_conv1d_bwd.restype = ctypes.c_int
     lib.mamba_conv_state_update.argtypes = [ctypes.POINTER(ScanDims)] + [vp] * 16
     lib.mamba_conv_state_update.restype = ctypes.c_int
+    lib.mamba_selective_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanDims)] + [vp] * 13
+    lib.mamba_selective_scan_fwd_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -101,7 +101,7 @@ int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, 
                const void* C, const float* D, const void* z, const float* delta_bias, const uint8_t* doc_start,
                const float* initial_state, void* out, float* final_state, void* workspace, size_t workspace_bytes,
                void* stream, const void* const* extra, const size_t* extra_sz, int nextra, mamba::ScanArgs* a,
-               bool* empty) {
+               bool* empty, bool own_scratch = false) {
     *empty = false;
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
@@ -147,8 +147,12 @@ int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, 
                 return MAMBA_ERR_INVALID_ARGUMENT;
     }
 
-    const size_t need = mamba::scan_workspace_bytes(Bt, L, Dm, N, dims->nheads, dims->dtype == MAMBA_DTYPE_BF16);
-    if (need > 0) {
+    const size_t need = mamba::scan_workspace_bytes(Bt, L, Dm, N, dims->nheads, dims->dtype == MAMBA_DTYPE_BF16,
+                                                    !own_scratch);
+    if (own_scratch) {
+        // The library's own scratch: a distinct device allocation of fixed size.
+        if (need > mamba::noalloc_scratch_bytes()) return MAMBA_ERR_WORKSPACE;
+    } else if (need > 0) {
         if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;
         for (int i = 0; i < kIns; ++i)
@@ -168,6 +172,7 @@ int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, 
     a->bf16 = dims->dtype == MAMBA_DTYPE_BF16;
     a->softplus = dims->delta_softplus != 0;
     a->stream = static_cast<hipStream_t>(stream);
+    a->dt_handoff = !own_scratch;
     return MAMBA_OK;
 }
 
@@ -245,6 +250,22 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
                               final_state, workspace, workspace_bytes, stream, nullptr, nullptr, 0, &a, &empty);
     if (st != MAMBA_OK) return st;
     if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
+    return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+int mamba_selective_scan_fwd_noalloc(const mamba_scan_dims_t* dims, const void* u, const void* delta,
+                                     const float* A, const void* B, const void* C, const float* D, const void* z,
+                                     const float* delta_bias, const uint8_t* doc_start, const float* initial_state,
+                                     void* out, float* final_state, void* stream) {
+    mamba::ScanArgs a;
+    bool empty;
+    const int st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out,
+                              final_state, nullptr, 0, stream, nullptr, nullptr, 0, &a, &empty, true);
+    if (st != MAMBA_OK) return st;
+    if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
+    void* ws = nullptr;
+    if (mamba::noalloc_scratch(a.stream, &ws) != hipSuccess) return MAMBA_ERR_HIP;
+    a.ws = static_cast<float*>(ws);
     return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 

@@ -172,4 +172,9 @@ bool ssd_supported(int64_t dim, int64_t dstate, int nheads);
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads);
 hipError_t launch_ssd(const ScanArgs& a);
 
+// The library's own device scratch for callers that cannot allocate
+// (noalloc.hip): its size, and its address on the device of `stream`.
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 }  // namespace mamba

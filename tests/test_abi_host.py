@@ -325,3 +325,28 @@ def test_conv_state_update_validation(lib):
     assert csu(uo=FAKE * 9) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # u_out over out
     assert csu(d=dims(batch=0, seqlen=1), x=None) == _lib.MAMBA_OK      # empty: no-op
 
+
+def scan_noalloc(lib, d=None, u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None, bias=None,
+                 ds=None, init=None, out=FAKE * 6, fs=None):
+    d = d or dims(batch=1, seqlen=64, dim=64)
+    return lib.mamba_selective_scan_fwd_noalloc(ctypes.byref(d), u, delta, A, B, C, D, z, bias, ds, init, out, fs,
+                                                None)
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free scan checks its arguments like mamba_selective_scan_fwd and
+    refuses, before any HIP call, a shape whose carries exceed its 64 MiB array."""
+    assert scan_noalloc(lib, u=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    assert scan_noalloc(lib, u=FAKE + 1) == _lib.MAMBA_ERR_MISALIGNED
+    assert scan_noalloc(lib, out=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT          # out overlaps u
+    assert scan_noalloc(lib, d=dims(batch=1, seqlen=64, dim=64, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert scan_noalloc(lib, d=dims(batch=0), u=None, out=None) == _lib.MAMBA_OK
+    base = 1 << 40
+    kw = dict(u=base, delta=base * 2, A=base * 3, B=base * 4, C=base * 5, out=base * 6)
+    # carries of 8 (nchunks - 1) B D N bytes: 2 x 127 chunks x 1536 x 16 = 50 MB fit; a
+    # wide 64K row (1 x 5120 channels, 64 chunks of 1024) needs 8 x 63 x 5120 x 16 = 41 MB;
+    # 8 rows of 256K tokens x 1536 channels need 8 x 511 x 8 x 1536 x 16 = 804 MB
+    assert scan_noalloc(lib, d=dims(batch=8, seqlen=262144, dim=1536), **kw) == _lib.MAMBA_ERR_WORKSPACE
+    # fp32 scalar-A heads keep per-channel carries of all 128 states
+    assert scan_noalloc(lib, d=dims(batch=2, seqlen=32768, dim=1536, nheads=24, dstate=128, dtype=0),
+                        **kw) == _lib.MAMBA_ERR_WORKSPACE
