@@ -150,14 +150,20 @@ int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* 
  * Supported (others return MAMBA_ERR_UNSUPPORTED):
  *   ngroups == 1, and (L + 64) * max(D, N) * 4 < 2^31 (a batch row of any
  *   tensor is addressed with 32-bit offsets);
- *   nheads == 0: N in {4, 8, 16};
- *   nheads > 0, float32: N in {16, 32, 64, 128} (recurrent form, fp32 throughout);
- *   nheads > 0, bf16: head size D / H in {32, 64} and N a multiple of 8 up to
- *   128 (chunked matrix-product form: bf16 operands, fp32 accumulation and
- *   state; Mamba skill page, "Mamba-2: Structured State Space Duality (SSD)").
+ *   nheads == 0: 1 <= N <= 16;
+ *   nheads > 0, float32: 1 <= N <= 128 (recurrent form, fp32 throughout);
+ *   nheads > 0, bf16: head size D / H in {32, 64} and 1 <= N <= 128 (chunked
+ *   matrix-product form: bf16 operands, fp32 accumulation and state; Mamba
+ *   skill page, "Mamba-2: Structured State Space Duality (SSD)").
+ *   The kernels are compiled for N = 4, 8, 16 (per channel), 16, 32, 64, 128
+ *   (fp32 heads) and multiples of 8 (bf16 heads); any other N runs on copies of
+ *   B, C, A and the states padded with zeros to the next such size inside the
+ *   workspace (a padded state stays zero and adds nothing: the results are
+ *   those of N states).
  * Alignment: activations aligned to their element size; B and C rows must be
- * 4-byte aligned (N even for bf16); with nheads > 0 and bf16, u, z, out, B and
- * C must be 16-byte aligned.  Otherwise MAMBA_ERR_MISALIGNED.
+ * 4-byte aligned when N is a compiled size (N even for bf16); with nheads > 0
+ * and bf16, u, z, out, B and C must be 16-byte aligned (B and C only when N is
+ * a multiple of 8).  Otherwise MAMBA_ERR_MISALIGNED.
  * B, L or D of 0 is a no-op.
  * Repeated calls with the same arguments give bitwise identical results. */
 int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims,
@@ -284,7 +290,8 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
  *              initial_state, else MAMBA_ERR_INVALID_ARGUMENT.
  *   workspace  at least mamba_selective_scan_bwd_workspace_bytes bytes, 256-byte
  *              aligned, scratch (contents on entry ignored).
- * Supported: nheads == 0, N in {4, 8, 16}, and what the forward requires; with
+ * Supported: nheads == 0, 1 <= N <= 16 (N other than 4, 8, 16 on zero-padded
+ * copies in the workspace, as the forward), and what the forward requires; with
  * bf16 also an even D; others return MAMBA_ERR_UNSUPPORTED.  With bf16, u,
  * delta, z and dout must be 4-byte aligned (they are read as pairs of channels),
  * else MAMBA_ERR_MISALIGNED.  Outputs must not overlap each other, the inputs
@@ -319,14 +326,15 @@ int mamba_causal_conv1d_update(const void* x, void* conv_state, const float* wei
 
 /* Selective-scan recurrence for one token per row.
  *   dims       as mamba_selective_scan_fwd with seqlen == 1.
- *   state      (B, D, N) float32, 16-byte aligned, updated in place:
+ *   state      (B, D, N) float32, updated in place (16-byte aligned when N is a
+ *              power of two from 4 up, else 4-byte):
  *              h <- exp(dt A) h + dt u B.
  *   u, z, out  (B, D); delta (B, D|H); B, C (B, N); A, D, delta_bias as
  *              mamba_selective_scan_fwd.
  *   reset      (B,) uint8 or NULL: nonzero where the token starts a new document
  *              (the state is zeroed first).
  *   out        = (C . h + D u) silu(z).
- * Supported: N in {4, 8, 16, 32, 64, 128}, either A layout, ngroups == 1. */
+ * Supported: 1 <= N <= 128, either A layout, ngroups == 1. */
 int mamba_selective_state_update(const mamba_scan_dims_t* dims, float* state, const void* u,
                                  const void* delta, const float* A, const void* B, const void* C,
                                  const float* D, const void* z, const float* delta_bias,

@@ -53,6 +53,142 @@ int check_dims(const mamba_scan_dims_t* d) {
     return MAMBA_OK;
 }
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of one forward scan: the kernels' own workspace at the state size nt
+// they run with, then, when nt > N, the zero-padded copies (pad.hip) of B, C, A
+// and the initial and final states.
+struct FwdLayout {
+    int64_t n = 0, nt = 0;
+    size_t off_B = 0, off_C = 0, off_A = 0, off_h0 = 0, off_hT = 0, total = 0;
+    bool padded() const { return nt != n; }
+};
+
+FwdLayout fwd_layout(const mamba_scan_dims_t* d, bool dt_handoff) {
+    FwdLayout w;
+    const bool bf16 = d->dtype == MAMBA_DTYPE_BF16;
+    w.n = d->dstate;
+    w.nt = mamba::scan_kernel_dstate(d->dim, d->dstate, d->nheads, bf16);
+    size_t off = mamba::scan_workspace_bytes(d->batch, d->seqlen, d->dim, w.nt, d->nheads, bf16, dt_handoff);
+    if (!w.padded()) {
+        w.total = off;
+        return w;
+    }
+    const size_t esz = bf16 ? 2 : 4;
+    const size_t bc = static_cast<size_t>(d->batch * d->seqlen * w.nt) * esz;
+    const size_t st = static_cast<size_t>(d->batch * d->dim * w.nt) * 4;
+    off = align256(off);
+    w.off_B = off; off += align256(bc);
+    w.off_C = off; off += align256(bc);
+    w.off_A = off; off += d->nheads ? 0 : align256(static_cast<size_t>(d->dim * w.nt) * 4);
+    w.off_h0 = off; off += align256(st);
+    w.off_hT = off; off += align256(st);
+    w.total = off;
+    return w;
+}
+
+// Runs the scan of `a` (whose dstate is the requested N), on zero-padded copies
+// in the workspace when the kernels run a larger state size.
+hipError_t launch_scan_layout(mamba::ScanArgs a, const FwdLayout& w) {
+    if (!w.padded()) return mamba::launch_selective_scan(a);
+    char* ws = reinterpret_cast<char*>(a.ws);
+    const int esz = a.bf16 ? 2 : 4;
+    const int n = static_cast<int>(w.n), nt = static_cast<int>(w.nt);
+    const int64_t bl = a.batch * a.seqlen, bd = a.batch * a.dim;
+    hipError_t e;
+    if ((e = mamba::launch_pad_rows(a.B, ws + w.off_B, bl, n, nt, esz, a.stream)) != hipSuccess) return e;
+    if ((e = mamba::launch_pad_rows(a.C, ws + w.off_C, bl, n, nt, esz, a.stream)) != hipSuccess) return e;
+    if (a.nheads == 0 && (e = mamba::launch_pad_rows(a.A, ws + w.off_A, a.dim, n, nt, 4, a.stream)) != hipSuccess)
+        return e;
+    if (a.initial_state &&
+        (e = mamba::launch_pad_rows(a.initial_state, ws + w.off_h0, bd, n, nt, 4, a.stream)) != hipSuccess)
+        return e;
+    float* fin = a.final_state;
+    a.B = ws + w.off_B;
+    a.C = ws + w.off_C;
+    if (a.nheads == 0) a.A = reinterpret_cast<const float*>(ws + w.off_A);
+    if (a.initial_state) a.initial_state = reinterpret_cast<const float*>(ws + w.off_h0);
+    a.final_state = fin ? reinterpret_cast<float*>(ws + w.off_hT) : nullptr;
+    a.dstate = nt;
+    if ((e = mamba::launch_selective_scan(a)) != hipSuccess) return e;
+    return fin ? mamba::launch_unpad_rows(ws + w.off_hT, fin, bd, n, nt, 4, a.stream) : hipSuccess;
+}
+
+// Workspace of one scan backward: the kernels' own workspace at their state size
+// nt, then, when nt > N, zero-padded copies of B, C, A, the initial state and the
+// final state's gradient, and the padded gradients dA, dB, dC, d_initial_state
+// whose first N states per row are copied out.
+struct BwdLayout {
+    int64_t n = 0, nt = 0;
+    size_t off_B = 0, off_C = 0, off_A = 0, off_h0 = 0, off_dhT = 0;
+    size_t off_dA = 0, off_dB = 0, off_dC = 0, off_dh0 = 0, total = 0;
+    bool padded() const { return nt != n; }
+};
+
+BwdLayout bwd_layout_of(const mamba_scan_dims_t* d) {
+    BwdLayout w;
+    const bool bf16 = d->dtype == MAMBA_DTYPE_BF16;
+    w.n = d->dstate;
+    w.nt = mamba::scan_bwd_kernel_dstate(d->dstate, d->nheads);
+    size_t off = mamba::scan_bwd_workspace_bytes(d->batch, d->seqlen, d->dim, w.nt, bf16);
+    if (!w.padded()) {
+        w.total = off;
+        return w;
+    }
+    const size_t esz = bf16 ? 2 : 4;
+    const size_t bc = align256(static_cast<size_t>(d->batch * d->seqlen * w.nt) * esz);
+    const size_t st = align256(static_cast<size_t>(d->batch * d->dim * w.nt) * 4);
+    const size_t dn = align256(static_cast<size_t>(d->dim * w.nt) * 4);
+    off = align256(off);
+    w.off_B = off; off += bc;
+    w.off_C = off; off += bc;
+    w.off_A = off; off += dn;
+    w.off_h0 = off; off += st;
+    w.off_dhT = off; off += st;
+    w.off_dA = off; off += dn;
+    w.off_dB = off; off += bc;
+    w.off_dC = off; off += bc;
+    w.off_dh0 = off; off += st;
+    w.total = off;
+    return w;
+}
+
+hipError_t launch_bwd_layout(mamba::ScanBwdArgs a, const BwdLayout& w) {
+    if (!w.padded()) return mamba::launch_selective_scan_bwd(a);
+    char* ws = static_cast<char*>(a.ws);
+    const int esz = a.bf16 ? 2 : 4;
+    const int n = static_cast<int>(w.n), nt = static_cast<int>(w.nt);
+    const int64_t bl = a.batch * a.seqlen, bd = a.batch * a.dim;
+    const hipStream_t s = a.stream;
+    hipError_t e;
+    if ((e = mamba::launch_pad_rows(a.B, ws + w.off_B, bl, n, nt, esz, s)) != hipSuccess) return e;
+    if ((e = mamba::launch_pad_rows(a.C, ws + w.off_C, bl, n, nt, esz, s)) != hipSuccess) return e;
+    if ((e = mamba::launch_pad_rows(a.A, ws + w.off_A, a.dim, n, nt, 4, s)) != hipSuccess) return e;
+    if (a.initial_state && (e = mamba::launch_pad_rows(a.initial_state, ws + w.off_h0, bd, n, nt, 4, s)) != hipSuccess)
+        return e;
+    if (a.d_final_state && (e = mamba::launch_pad_rows(a.d_final_state, ws + w.off_dhT, bd, n, nt, 4, s)) != hipSuccess)
+        return e;
+    float* dA = a.dA;
+    void* dB = a.dB;
+    void* dC = a.dC;
+    float* dh0 = a.d_initial_state;
+    a.B = ws + w.off_B;
+    a.C = ws + w.off_C;
+    a.A = reinterpret_cast<const float*>(ws + w.off_A);
+    if (a.initial_state) a.initial_state = reinterpret_cast<const float*>(ws + w.off_h0);
+    if (a.d_final_state) a.d_final_state = reinterpret_cast<const float*>(ws + w.off_dhT);
+    a.dA = reinterpret_cast<float*>(ws + w.off_dA);
+    a.dB = ws + w.off_dB;
+    a.dC = ws + w.off_dC;
+    if (dh0) a.d_initial_state = reinterpret_cast<float*>(ws + w.off_dh0);
+    a.dstate = nt;
+    if ((e = mamba::launch_selective_scan_bwd(a)) != hipSuccess) return e;
+    if ((e = mamba::launch_unpad_rows(ws + w.off_dA, dA, a.dim, n, nt, 4, s)) != hipSuccess) return e;
+    if ((e = mamba::launch_unpad_rows(ws + w.off_dB, dB, bl, n, nt, esz, s)) != hipSuccess) return e;
+    if ((e = mamba::launch_unpad_rows(ws + w.off_dC, dC, bl, n, nt, esz, s)) != hipSuccess) return e;
+    return dh0 ? mamba::launch_unpad_rows(ws + w.off_dh0, dh0, bd, n, nt, 4, s) : hipSuccess;
+}
+
 // Checks of one conv1d call (shared by the conv and the fused conv + scan entry
 // points); fills `a` on success.
 int check_conv(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
@@ -101,10 +237,11 @@ int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, 
                const void* C, const float* D, const void* z, const float* delta_bias, const uint8_t* doc_start,
                const float* initial_state, void* out, float* final_state, void* workspace, size_t workspace_bytes,
                void* stream, const void* const* extra, const size_t* extra_sz, int nextra, mamba::ScanArgs* a,
-               bool* empty, bool own_scratch = false) {
+               FwdLayout* lay, bool* empty, bool own_scratch = false) {
     *empty = false;
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
+    *lay = fwd_layout(dims, !own_scratch);
     const int64_t Bt = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     if (Bt * L * Dm == 0) {
         *empty = true;
@@ -115,11 +252,13 @@ int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, 
     const int64_t nd = dims->nheads ? dims->nheads : Dm;
     if (!aligned(u, esz) || !aligned(delta, esz) || !aligned(out, esz) || (z && !aligned(z, esz)))
         return MAMBA_ERR_MISALIGNED;
-    // B and C rows are read as 32-bit words.
-    if (!aligned(B, 4) || !aligned(C, 4) || (N * esz) % 4 != 0) return MAMBA_ERR_MISALIGNED;
+    // B and C rows are read as 32-bit words (element by element when padded).
+    if (!aligned(B, esz) || !aligned(C, esz)) return MAMBA_ERR_MISALIGNED;
+    if (!lay->padded() && (!aligned(B, 4) || !aligned(C, 4) || (N * esz) % 4 != 0)) return MAMBA_ERR_MISALIGNED;
     // Scalar-A heads with bf16 I/O move u, z, out, B and C in 16-byte vectors.
     if (dims->nheads > 0 && dims->dtype == MAMBA_DTYPE_BF16 &&
-        (!aligned(u, 16) || !aligned(out, 16) || (z && !aligned(z, 16)) || !aligned(B, 16) || !aligned(C, 16)))
+        (!aligned(u, 16) || !aligned(out, 16) || (z && !aligned(z, 16)) ||
+         (!lay->padded() && (!aligned(B, 16) || !aligned(C, 16)))))
         return MAMBA_ERR_MISALIGNED;
     if (!aligned(A, 4) || (D && !aligned(D, 4)) || (delta_bias && !aligned(delta_bias, 4)) ||
         (final_state && !aligned(final_state, 4)) || (initial_state && !aligned(initial_state, 4)))
@@ -147,8 +286,7 @@ int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, 
                 return MAMBA_ERR_INVALID_ARGUMENT;
     }
 
-    const size_t need = mamba::scan_workspace_bytes(Bt, L, Dm, N, dims->nheads, dims->dtype == MAMBA_DTYPE_BF16,
-                                                    !own_scratch);
+    const size_t need = lay->total;
     if (own_scratch) {
         // The library's own scratch: a distinct device allocation of fixed size.
         if (need > mamba::noalloc_scratch_bytes()) return MAMBA_ERR_WORKSPACE;
@@ -234,8 +372,7 @@ int mamba_selective_scan_workspace_bytes(const mamba_scan_dims_t* dims, size_t* 
     *bytes = 0;
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
-    *bytes = mamba::scan_workspace_bytes(dims->batch, dims->seqlen, dims->dim, dims->dstate, dims->nheads,
-                                         dims->dtype == MAMBA_DTYPE_BF16);
+    *bytes = fwd_layout(dims, true).total;
     return MAMBA_OK;
 }
 
@@ -245,12 +382,13 @@ int mamba_selective_scan_fwd(const mamba_scan_dims_t* dims, const void* u, const
                              void* out, float* final_state, void* workspace, size_t workspace_bytes,
                              void* stream) {
     mamba::ScanArgs a;
+    FwdLayout lay;
     bool empty;
     const int st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out,
-                              final_state, workspace, workspace_bytes, stream, nullptr, nullptr, 0, &a, &empty);
+                              final_state, workspace, workspace_bytes, stream, nullptr, nullptr, 0, &a, &lay, &empty);
     if (st != MAMBA_OK) return st;
     if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
-    return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+    return launch_scan_layout(a, lay) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
 int mamba_selective_scan_fwd_noalloc(const mamba_scan_dims_t* dims, const void* u, const void* delta,
@@ -258,15 +396,16 @@ int mamba_selective_scan_fwd_noalloc(const mamba_scan_dims_t* dims, const void* 
                                      const float* delta_bias, const uint8_t* doc_start, const float* initial_state,
                                      void* out, float* final_state, void* stream) {
     mamba::ScanArgs a;
+    FwdLayout lay;
     bool empty;
     const int st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out,
-                              final_state, nullptr, 0, stream, nullptr, nullptr, 0, &a, &empty, true);
+                              final_state, nullptr, 0, stream, nullptr, nullptr, 0, &a, &lay, &empty, true);
     if (st != MAMBA_OK) return st;
     if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
     void* ws = nullptr;
     if (mamba::noalloc_scratch(a.stream, &ws) != hipSuccess) return MAMBA_ERR_HIP;
     a.ws = static_cast<float*>(ws);
-    return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+    return launch_scan_layout(a, lay) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
 int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const float* conv_weight,
@@ -289,16 +428,17 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
     const size_t conv_sz[] = {act, static_cast<size_t>(dims->dim) * 16, static_cast<size_t>(dims->dim) * 4,
                               static_cast<size_t>(dims->batch * dims->dim * 3) * esz};
     mamba::ScanArgs a;
+    FwdLayout lay;
     st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out, final_state, workspace,
-                    workspace_bytes, stream, conv_in, conv_sz, 4, &a, &empty);
+                    workspace_bytes, stream, conv_in, conv_sz, 4, &a, &lay, &empty);
     if (st != MAMBA_OK) return st;
     if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
     if (dims->nheads == 0) {
         a.conv_x = x; a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state;
-        return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+        return launch_scan_layout(a, lay) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
     }
     if (mamba::launch_causal_conv1d(ca) != hipSuccess) return MAMBA_ERR_HIP;
-    return mamba::launch_selective_scan(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+    return launch_scan_layout(a, lay) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
 int mamba_causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, size_t* bytes) {
@@ -371,8 +511,7 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
     if (!mamba::scan_bwd_supported(dims->dstate, dims->nheads)) return MAMBA_ERR_UNSUPPORTED;
-    *bytes = mamba::scan_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->dim, dims->dstate,
-                                             dims->dtype == MAMBA_DTYPE_BF16);
+    *bytes = bwd_layout_of(dims).total;
     return MAMBA_OK;
 }
 
@@ -414,8 +553,9 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
     const void* acts[] = {du, ddelta, dz};
     for (const void* t : acts)
         if (t && !aligned(t, esz)) return MAMBA_ERR_MISALIGNED;
-    if (!aligned(B, 4) || !aligned(C, 4) || !aligned(dB, esz) || !aligned(dC, esz) || (N * esz) % 4 != 0)
-        return MAMBA_ERR_MISALIGNED;
+    const BwdLayout lay = bwd_layout_of(dims);
+    if (!aligned(B, esz) || !aligned(C, esz) || !aligned(dB, esz) || !aligned(dC, esz)) return MAMBA_ERR_MISALIGNED;
+    if (!lay.padded() && (!aligned(B, 4) || !aligned(C, 4) || (N * esz) % 4 != 0)) return MAMBA_ERR_MISALIGNED;
     const float* f32s[] = {A, D, delta_bias, dA, dD, ddelta_bias, initial_state, d_final_state, d_initial_state};
     for (const float* t : f32s)
         if (t && !aligned(t, 4)) return MAMBA_ERR_MISALIGNED;
@@ -430,7 +570,7 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
     const void* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, d_initial_state};
     const size_t outsz[] = {act, act, dn, bc, bc, d1, act, d1, sb};
     constexpr int kOuts = 9;
-    const size_t need = mamba::scan_bwd_workspace_bytes(Bt, L, Dm, N, dims->dtype == MAMBA_DTYPE_BF16);
+    const size_t need = lay.total;
     if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MAMBA_ERR_MISALIGNED;
     for (int o = 0; o < kOuts; ++o) {
@@ -453,7 +593,7 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
     a.bf16 = dims->dtype == MAMBA_DTYPE_BF16;
     a.softplus = dims->delta_softplus != 0;
     a.stream = static_cast<hipStream_t>(stream);
-    return mamba::launch_selective_scan_bwd(a) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+    return launch_bwd_layout(a, lay) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
 int mamba_causal_conv1d_update(const void* x, void* conv_state, const float* weight, const float* bias,
@@ -506,7 +646,10 @@ int check_state_update(const mamba_scan_dims_t* dims, float* state, const void* 
     }
     if (!state || !u || !delta || !A || !B || !C || !out) return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
-    if (!aligned(state, 16) || !aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) ||
+    // A state row whose length is a power of two from 4 up is moved in 16-byte pieces.
+    const bool pow2 = N >= 4 && (N & (N - 1)) == 0;
+    if (!aligned(state, pow2 ? 16 : 4) || !aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) ||
+        !aligned(C, esz) ||
         !aligned(out, esz) || (z && !aligned(z, esz)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
         (delta_bias && !aligned(delta_bias, 4)))
         return MAMBA_ERR_MISALIGNED;

@@ -42,15 +42,18 @@ __global__ __launch_bounds__(256) void conv1d_update_kernel(const void* __restri
     Elem<T>::store(conv_state, i * 3 + 2, xt);
 }
 
-// G = N / 4 consecutive lanes own one (row, channel): four states each, so the
+// G = NT / 4 consecutive lanes own one (row, channel): four states each, so the
 // state row of a channel is read and written as contiguous 16-byte pieces and
-// C . h is a sum over the G lanes (xor shuffles inside the group).
+// C . h is a sum over the G lanes (xor shuffles inside the group).  NT is the
+// power of two at or above N; for N < NT the state rows are N long and each
+// lane touches only its states below N, element by element.
 // CONV: the conv step runs first in the same launch; every lane of the group
 // forms u from the window (rounded to T, as the separate conv step stores it)
 // and the group's first lane writes the window back.
 template <typename T, int G, bool HEADS, bool CONV>
 __global__ __launch_bounds__(256) void state_update_kernel(const StateUpdateArgs a) {
-    constexpr int N = 4 * G;
+    const int N = static_cast<int>(a.dstate);
+    const bool exact = N == 4 * G;
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t chan = gid / G;                   // b * dim + d
     const int q = static_cast<int>(gid % G);        // which four states
@@ -89,12 +92,22 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StateUpdateArgs
     }
     const float w = dt * u;
 
-    float4 h = clear ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : reinterpret_cast<const float4*>(a.state)[cc * G + q];
-    float hv[4] = {h.x, h.y, h.z, h.w};
+    float hv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (!clear) {
+        if (exact) {
+            const float4 h = reinterpret_cast<const float4*>(a.state)[cc * G + q];
+            hv[0] = h.x; hv[1] = h.y; hv[2] = h.z; hv[3] = h.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (4 * q + j < N) hv[j] = a.state[cc * N + 4 * q + j];
+        }
+    }
     float y = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = 4 * q + j;
+        if (!exact && n >= N) continue;           // a padded state: stays zero, adds nothing
         const float Al = HEADS ? a.A[head] : a.A[d * N + n];
         const float decay = exp2_fast(dt * Al * kLog2e);
         hv[j] = __builtin_fmaf(decay, hv[j], w * Elem<T>::load(a.B, b * N + n));
@@ -103,7 +116,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StateUpdateArgs
 #pragma unroll
     for (int m = G / 2; m > 0; m >>= 1) y += __shfl_xor(y, m);
     if (!live) return;
-    reinterpret_cast<float4*>(a.state)[cc * G + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    if (exact) {
+        reinterpret_cast<float4*>(a.state)[cc * G + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (4 * q + j < N) a.state[cc * N + 4 * q + j] = hv[j];
+    }
     if (q == 0) {
         y = __builtin_fmaf(a.D != nullptr ? a.D[d] : 0.0f, u, y);
         if (a.z != nullptr) y *= silu_f(Elem<T>::load(a.z, cc));
@@ -113,7 +132,8 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StateUpdateArgs
 
 template <typename T, bool HEADS, bool CONV>
 hipError_t launch_state_update_typed(const StateUpdateArgs& a) {
-    const int G = static_cast<int>(a.dstate / 4);
+    int G = 1;
+    while (4 * G < a.dstate) G *= 2;
     const int64_t threads = a.batch * a.dim * G;
     const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
     switch (G) {
@@ -135,9 +155,7 @@ hipError_t launch_state_update_conv(const StateUpdateArgs& a) {
 
 }  // namespace
 
-bool state_update_supported(int64_t dstate) {
-    return dstate == 4 || dstate == 8 || dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128;
-}
+bool state_update_supported(int64_t dstate) { return dstate >= 1 && dstate <= 128; }
 
 hipError_t launch_state_update(const StateUpdateArgs& a) {
     if (a.bf16) return a.nheads ? launch_state_update_conv<bf16_t, true>(a) : launch_state_update_conv<bf16_t, false>(a);

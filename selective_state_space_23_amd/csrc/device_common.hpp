@@ -124,19 +124,17 @@ __device__ __forceinline__ float silu_f(float v) {
 }
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).
-// With y = e^-|v| in (0, 1]: for |v| > 4 (y < 0.0184) log1p(y) uses its series
-// to the y^5 term (truncation below 7e-12 relative); otherwise log2(1 + y) ln 2,
-// where 1 + y >= 1.018 keeps the rounding of 1 + y harmless.  This keeps small
-// step sizes (dt near 1e-3, the low end of the usual dt range) accurate to a
-// few ulp, where log(1 + e^v) evaluated directly would lose ~3 digits.
+// With y = e^-|v| in (0, 1] and u = 1 + y rounded to float, c = (u - 1) - y is
+// exactly the rounding error of 1 + y, and log1p(y) = log(u) - c/u + O(c^2);
+// taking -c for -c/u errs by c y / u <= 2^-24 y, i.e. below one ulp of
+// log1p(y) ~ y.  So small step sizes (dt near 1e-3, y near 1e-3) keep full
+// relative accuracy without a separate series, for 9 VALU slots of arithmetic
+// after the exponential.
 __device__ __forceinline__ float softplus_f(float v) {
-    const float av = __builtin_fabsf(v);
-    const float y = exp2_fast(-av * kLog2e);
-    const float series =
-        y * __builtin_fmaf(-y, __builtin_fmaf(-y, __builtin_fmaf(-y, __builtin_fmaf(-y, 0.2f, 0.25f),
-                                                                  0.33333334f), 0.5f), 1.0f);
-    const float direct = log2_fast(1.0f + y) * kLn2;
-    return __builtin_fmaxf(v, 0.0f) + (av > 4.0f ? series : direct);
+    const float y = exp2_fast(-__builtin_fabsf(v) * kLog2e);
+    const float u = 1.0f + y;
+    const float c = (u - 1.0f) - y;
+    return __builtin_fmaxf(v, 0.0f) + __builtin_fmaf(log2_fast(u), kLn2, -c);
 }
 
 }  // namespace mamba

@@ -84,6 +84,10 @@ struct ScanPlan {
 };
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim);
+// The state size the scan's kernels run a requested N with (N itself, or the
+// next compiled size, the states above N padded with zeros; pad.hip), or 0 when
+// no kernel can run it.
+int64_t scan_kernel_dstate(int64_t dim, int64_t dstate, int nheads, bool bf16);
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16,
                             bool dt_handoff = true);
 bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16);
@@ -120,6 +124,7 @@ struct ScanBwdArgs {
 };
 
 bool scan_bwd_supported(int64_t dstate, int nheads);
+int64_t scan_bwd_kernel_dstate(int64_t dstate, int nheads);   // as scan_kernel_dstate, or 0
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool bf16);
 hipError_t launch_selective_scan_bwd(const ScanBwdArgs& a);
 
@@ -171,6 +176,11 @@ hipError_t launch_state_update(const StateUpdateArgs& a);
 bool ssd_supported(int64_t dim, int64_t dstate, int nheads);
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads);
 hipError_t launch_ssd(const ScanArgs& a);
+
+// Row padding of the state dimension (pad.hip): dst rows of nt elements from
+// src rows of n (zeros above n), and back; esz is 2 or 4 bytes.
+hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int n, int nt, int esz, hipStream_t stream);
+hipError_t launch_unpad_rows(const void* src, void* dst, int64_t rows, int n, int nt, int esz, hipStream_t stream);
 
 // The library's own device scratch for callers that cannot allocate
 // (noalloc.hip): its size, and its address on the device of `stream`.

@@ -305,29 +305,48 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     };
 
     uint64_t starts = 0;
+    // Pass 1: the first token whose recurrence reaches the chunk's aggregate.  The
+    // state restarts from zero at the chunk's last document start, so the
+    // tokens before it only need their u and dt (stored for pass 3); the last
+    // chunk's aggregate is never used at all.  Uniform over the block.
+    int64_t rec_from = t_begin;
+    if constexpr (!OUTPUT) {
+        if (c >= p.nslots) {
+            rec_from = t_end;
+        } else {
+            for (int64_t w0 = t_begin; w0 < t_end; w0 += kWin) {
+                const int64_t tl = w0 + lane;
+                const bool st = tl < t_end && ((tl == 0 && p.initial_state == nullptr) ||
+                                               (ds_row != nullptr && ds_row[tl] != 0));
+                const uint64_t m = __ballot(st);
+                if (m != 0) rec_from = w0 + 63 - __builtin_clzll(m);
+            }
+        }
+    }
     // FAST: every token of the group is inside the chunk and none starts a
     // document (wave-uniform; all but a few groups), so the masks below fold
     // away and stores go to the clamped channel (an inactive lane writes the
     // value its clamped channel's own lane writes) with the token in the scalar
-    // offset.
-    auto compute_group = [&](auto fast_tag, int64_t g0, const float (&cu)[G], const float (&cd)[G],
+    // offset.  REC (always, in pass 3): the group runs the recurrence; pass 1's
+    // groups before rec_from only form u and dt.
+    auto compute_group = [&](auto fast_tag, auto rec_tag, int64_t g0, const float (&cu)[G], const float (&cd)[G],
                              const float (&cz)[G]) {
         constexpr bool FAST = decltype(fast_tag)::value;
+        constexpr bool REC = OUTPUT || decltype(rec_tag)::value;
         const int off = static_cast<int>((g0 - t_begin) & (kWin - 1));
+        // Phase 1: the per-token inputs of the recurrence for the whole group
+        // (dt, and w = dt u; the conv, softplus and their stores in pass 1).
+        // These are long dependent chains (exp, log, rcp); the
+        // group's tokens are independent here, so their chains overlap instead
+        // of stalling each token's state updates.
+        float dtk[G], wk[G];
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             // Tokens past the chunk end run as identity steps (dt = 0: decay 1, no
             // input) so the group stays straight-line code.
             const bool valid = FAST || g0 + k < t_end;
             const int64_t t = g0 + k;
-            // A document start multiplies the carried state by exp2(-inf) = 0: the
-            // reset rides in the exponent's addend, with no branch and no extra op.
             const bool reset = !FAST && ((starts >> (off + k)) & 1ull);
-            const float r = reset ? -__builtin_inff() : 0.0f;
-            if (!OUTPUT) {
-                any_reset = any_reset || reset;
-                sum_dt = reset ? 0.0f : sum_dt;
-            }
             float dt;
             if constexpr (kDtWs && OUTPUT) {
                 dt = cd[k];                                   // stored by pass 1
@@ -341,6 +360,10 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 }
             }
             dt = valid ? dt : 0.0f;
+            if constexpr (!OUTPUT && REC) {
+                any_reset = any_reset || reset;
+                sum_dt = (reset ? 0.0f : sum_dt) + dt;
+            }
             float uk = cu[k];
             if constexpr (CONV) {
                 const float xt = cu[k];
@@ -362,7 +385,21 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 xh2 = xh1;
                 xh1 = xt;
             }
-            const float w = dt * uk;
+            dtk[k] = dt;
+            wk[k] = dt * uk;
+        }
+        if constexpr (!REC) return;
+        // Phase 2: the recurrence, token by token.
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const bool valid = FAST || g0 + k < t_end;
+            const int64_t t = g0 + k;
+            // A document start multiplies the carried state by exp2(-inf) = 0: the
+            // reset rides in the exponent's addend, with no branch and no extra op.
+            const bool reset = !FAST && ((starts >> (off + k)) & 1ull);
+            const float r = reset ? -__builtin_inff() : 0.0f;
+            const float dt = dtk[k];
+            const float w = wk[k];
             float y0 = 0.0f, y1 = 0.0f;          // two partial sums of C . h
             float a_head = 0.0f;
             if constexpr (HEADS) a_head = exp2_fast(__builtin_fmaf(dt, Al2[0], r));
@@ -393,8 +430,6 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 if constexpr (HAS_Z) y *= silu_f(cz[k]);
                 if constexpr (FAST) buf_store_s<T>(uo_rs, dc * kEsz, static_cast<int>(t) * p.dim * kEsz, y);
                 else if (active && valid) buf_store<T>(uo_rs, (static_cast<int>(t) * p.dim + d) * kEsz, y);
-            } else {
-                sum_dt += dt;
             }
             // Keep the scheduler from hoisting later tokens' exponentials: one
             // token already offers N independent chains, and hoisting only
@@ -416,16 +451,25 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             if (tl < t_end) st = (tl == 0 && p.initial_state == nullptr) || (ds_row != nullptr && ds_row[tl] != 0);
             starts = __ballot(st);
         }
-        __syncthreads();                 // every wave is done with the previous window
-        stage_window(w0);
-        __syncthreads();
+        if (OUTPUT || w0 + kWin > rec_from) {    // B is read by some group of the window
+            __syncthreads();             // every wave is done with the previous window
+            stage_window(w0);
+            __syncthreads();
+        }
         const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
         auto run_group = [&](int64_t g0, const float (&cu)[G], const float (&cd)[G], const float (&cz)[G]) {
             const int off = static_cast<int>((g0 - t_begin) & (kWin - 1));
-            if (g0 + G <= t_end && ((starts >> off) & ((1ull << G) - 1)) == 0)
-                compute_group(std::true_type{}, g0, cu, cd, cz);
-            else
-                compute_group(std::false_type{}, g0, cu, cd, cz);
+            const bool fast = g0 + G <= t_end && ((starts >> off) & ((1ull << G) - 1)) == 0;
+            if (!OUTPUT && g0 + G <= rec_from) {
+                if constexpr (!OUTPUT) {
+                    if (fast) compute_group(std::true_type{}, std::false_type{}, g0, cu, cd, cz);
+                    else compute_group(std::false_type{}, std::false_type{}, g0, cu, cd, cz);
+                }
+            } else if (fast) {
+                compute_group(std::true_type{}, std::true_type{}, g0, cu, cd, cz);
+            } else {
+                compute_group(std::false_type{}, std::true_type{}, g0, cu, cd, cz);
+            }
         };
         for (int64_t g0 = w0; g0 < wend; g0 += 2 * G) {
             load_group(g0 + G, bu, bd, bz);
@@ -466,16 +510,19 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(float* __restrict__ ws_
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= count) return;
     float carry = init != nullptr ? init[i] : 0.0f;
+    // The chain over chunks is sequential; its loads are issued 16 chunks at a
+    // time so that their latency overlaps.
+    constexpr int kBatch = 16;
     int64_t c = 0;
-    for (; c + 4 <= nslots; c += 4) {
-        float P[4], H[4];
+    for (; c + kBatch <= nslots; c += kBatch) {
+        float P[kBatch], H[kBatch];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kBatch; ++k) {
             P[k] = ws_P[(c + k) * count + i];
             H[k] = ws_H[(c + k) * count + i];
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kBatch; ++k) {
             carry = __builtin_fmaf(P[k], carry, H[k]);
             ws_P[(c + k) * count + i] = carry;
         }
@@ -606,25 +653,42 @@ hipError_t launch_heads_f32(const ScanArgs& a, const ScanPlan& plan) {
 
 }  // namespace
 
-bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16) {
-    if (nheads == 0) return dstate == 4 || dstate == 8 || dstate == 16;
-    if (bf16) return ssd_supported(dim, dstate, nheads);
-    return dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128;
+int64_t scan_kernel_dstate(int64_t dim, int64_t dstate, int nheads, bool bf16) {
+    if (dstate < 1) return 0;
+    if (nheads == 0) return dstate <= 4 ? 4 : dstate <= 8 ? 8 : dstate <= 16 ? 16 : 0;
+    if (bf16) {
+        const int64_t nt = (dstate + 7) / 8 * 8;
+        return ssd_supported(dim, nt, nheads) ? nt : 0;
+    }
+    for (int64_t nt = 16; nt <= 128; nt *= 2)
+        if (dstate <= nt) return nt;
+    return 0;
 }
 
-// Chunks are sized so that each pass launches roughly 4096 or more waves (four
-// or more per SIMD on 256 CUs) while keeping the carry workspace small.
+bool scan_supported(int64_t dim, int64_t dstate, int nheads, bool bf16) {
+    return scan_kernel_dstate(dim, dstate, nheads, bf16) != 0;
+}
+
+// Chunks are sized for enough waves per pass: about 8192 (two rounds of four
+// waves per SIMD on 256 CUs) while a chunk keeps at least 512 tokens, else about
+// 4096.  The chunk is the largest power of two not above the length that gives
+// that count: rounding up instead left wide rows (one row of 5120 channels) at
+// 2.5 waves per SIMD and 20% slower; 8192 waves with 512-token chunks run a
+// 64K-token row of 5120 channels 3.5% faster than 5120 waves with 1024, while
+// two 32K rows of 1536 channels are fastest at 6144 waves with 256 (128 and 512
+// are 2.5% slower).  Below 128 tokens per chunk the per-chunk overhead wins.
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim) {
     const int64_t chains = batch * ((dim + 63) / 64);
-    int64_t want_chunks = chains > 0 ? (MAMBA_SCAN_TARGET_WAVES + chains - 1) / chains : 1;
-    if (want_chunks < 1) want_chunks = 1;
-    int64_t len = (seqlen + want_chunks - 1) / want_chunks;
-    // The largest power of two not above that length: rounding up instead left
-    // wide rows (one row of 5120 channels) at 2.5 waves per SIMD and 20% slower.
-    // Below 128 tokens per chunk the per-chunk overhead wins (2K-token rows).
-    int64_t chunk = 128;
-    while (chunk * 2 <= len) chunk *= 2;
-    if (chunk > 4096) chunk = 4096;
+    auto chunk_for = [&](int64_t target_waves) {
+        int64_t want_chunks = chains > 0 ? (target_waves + chains - 1) / chains : 1;
+        if (want_chunks < 1) want_chunks = 1;
+        const int64_t len = (seqlen + want_chunks - 1) / want_chunks;
+        int64_t chunk = 128;
+        while (chunk * 2 <= len) chunk *= 2;
+        return chunk > 4096 ? int64_t(4096) : chunk;
+    };
+    int64_t chunk = chunk_for(2 * MAMBA_SCAN_TARGET_WAVES);
+    if (chunk < 512) chunk = chunk_for(MAMBA_SCAN_TARGET_WAVES);
     ScanPlan p;
     p.chunk_len = chunk;
     p.nchunks = seqlen > 0 ? (seqlen + chunk - 1) / chunk : 0;

@@ -1119,9 +1119,12 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
 
 }  // namespace
 
-bool scan_bwd_supported(int64_t dstate, int nheads) {
-    return nheads == 0 && (dstate == 4 || dstate == 8 || dstate == 16);
+int64_t scan_bwd_kernel_dstate(int64_t dstate, int nheads) {
+    if (nheads != 0 || dstate < 1) return 0;
+    return dstate <= 4 ? 4 : dstate <= 8 ? 8 : dstate <= 16 ? 16 : 0;
 }
+
+bool scan_bwd_supported(int64_t dstate, int nheads) { return scan_bwd_kernel_dstate(dstate, nheads) != 0; }
 
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool bf16) {
     (void)bf16;   // the step sizes are float32 for either I/O dtype

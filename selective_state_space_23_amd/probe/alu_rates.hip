@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.hpp"
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -93,9 +95,26 @@ hipError_t launch_kind(int chains, int blocks, int threads, int iters, float* ou
     }
 }
 
+// The library's own device softplus (device_common.hpp) on given inputs, so that
+// a test can check its accuracy against a float64 reference.
+__global__ void softplus_kernel(const float* v, float* out, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = mamba::softplus_f(v[i]);
+}
+
 }  // namespace
 
 extern "C" {
+
+// out[i] = softplus of v[i] as the library's kernels evaluate it.  Returns a
+// hipError_t value.
+int probe_softplus(const float* v, float* out, int n, void* stream) {
+    if (n < 0 || (n > 0 && (!v || !out))) return hipErrorInvalidValue;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(softplus_kernel, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), v,
+                       out, n);
+    return hipGetLastError();
+}
 
 // One timed launch.  kind: 0..8 as above; chains: 1 (dependent latency) or 8
 // (throughput; the mixes 6..8 take E + F chains: 8, 8, 6).  out holds

@@ -91,7 +91,12 @@ def test_workspace_query(lib):
     # one chunk: no carries, only the step sizes handed from the first pass to the last
     assert st == _lib.MAMBA_OK and n == 2 * 64 * 1536 * 2
     assert ws_bytes(lib, dims(ngroups=2))[0] == _lib.MAMBA_ERR_UNSUPPORTED
-    assert ws_bytes(lib, dims(dstate=5))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    # any N in 1..16 per channel: N other than 4, 8, 16 adds zero-padded copies to the workspace
+    assert ws_bytes(lib, dims(dstate=17))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    for n in (1, 2, 3, 5, 12):
+        st, nb = ws_bytes(lib, dims(dstate=n))
+        nt = 4 if n <= 4 else 8 if n <= 8 else 16
+        assert st == _lib.MAMBA_OK and nb > ws_bytes(lib, dims(dstate=nt))[1], n
     assert ws_bytes(lib, dims(nheads=7))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT     # 1536 % 7
     assert ws_bytes(lib, dims(nheads=24, dstate=128))[0] == _lib.MAMBA_OK
     assert ws_bytes(lib, dims(dtype=3))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
@@ -107,11 +112,12 @@ def test_workspace_query(lib):
     assert ws_bytes(lib, dims(dstate=0))[0] == _lib.MAMBA_ERR_INVALID_ARGUMENT
     # scalar-A heads with bf16 I/O: headdim 32 or 64, a multiple of 8 states up to 128
     assert ws_bytes(lib, dims(nheads=32, dstate=128))[0] == _lib.MAMBA_ERR_UNSUPPORTED      # headdim 48
-    assert ws_bytes(lib, dims(nheads=24, dstate=12))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    assert ws_bytes(lib, dims(nheads=24, dstate=12))[0] == _lib.MAMBA_OK       # padded to 16
     assert ws_bytes(lib, dims(nheads=24, dstate=136))[0] == _lib.MAMBA_ERR_UNSUPPORTED
     assert ws_bytes(lib, dims(nheads=24, dstate=24))[0] == _lib.MAMBA_OK
     assert ws_bytes(lib, dims(nheads=32, dstate=128, dtype=0))[0] == _lib.MAMBA_OK           # f32: recurrent form
-    assert ws_bytes(lib, dims(nheads=24, dstate=24, dtype=0))[0] == _lib.MAMBA_ERR_UNSUPPORTED
+    assert ws_bytes(lib, dims(nheads=24, dstate=24, dtype=0))[0] == _lib.MAMBA_OK             # f32, padded to 32
+    assert ws_bytes(lib, dims(nheads=24, dstate=129, dtype=0))[0] == _lib.MAMBA_ERR_UNSUPPORTED
     st, n = ws_bytes(lib, dims(nheads=24, dstate=128, seqlen=64))
     assert st == _lib.MAMBA_OK and n == 0                 # one chunk: no carries
     st, n = ws_bytes(lib, dims(nheads=24, dstate=128, seqlen=32768))
@@ -133,7 +139,11 @@ def test_scan_validation(lib):
     assert scan(lib, u=FAKE + 1) == _lib.MAMBA_ERR_MISALIGNED
     assert scan(lib, B=FAKE * 4 + 2) == _lib.MAMBA_ERR_MISALIGNED
     assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
-    assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=3)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=17)) == _lib.MAMBA_ERR_UNSUPPORTED
+    # a padded N needs its copies in the workspace, and B, C only element-aligned
+    assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=3)) == _lib.MAMBA_ERR_WORKSPACE
+    assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=3), B=FAKE * 4 + 2) == _lib.MAMBA_ERR_WORKSPACE
+    assert scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=3), B=FAKE * 4 + 1) == _lib.MAMBA_ERR_MISALIGNED
     assert scan(lib, out=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT           # out overlaps u
     assert scan(lib, fs=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT        # final_state overlaps out
     assert scan(lib, fs=FAKE * 8, init=FAKE * 8) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # initial = final state
@@ -192,7 +202,11 @@ def state_update(lib, d=None, state=FAKE * 16, u=FAKE, delta=FAKE * 2, A=FAKE * 
 
 def test_state_update_validation(lib):
     assert state_update(lib, d=dims(batch=2, seqlen=2, dim=64, dstate=16)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
-    assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=12)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=129)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=0)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
+    # N not a power of two: 4-byte state rows are enough, misaligned ones still refused
+    assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=12), state=FAKE * 16 + 2) == \
+        _lib.MAMBA_ERR_MISALIGNED
     assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=16, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert state_update(lib, d=dims(batch=2, seqlen=1, dim=64, dstate=16, nheads=3)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
     assert state_update(lib, state=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
@@ -215,7 +229,7 @@ def test_conv_scan_validation(lib):
     assert conv_scan(lib, u=FAKE * 7) == _lib.MAMBA_ERR_INVALID_ARGUMENT        # u aliases x
     assert conv_scan(lib, u=FAKE * 2) == _lib.MAMBA_ERR_INVALID_ARGUMENT        # u aliases delta
     assert conv_scan(lib, cw=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT       # weights inside out
-    assert conv_scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=5)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert conv_scan(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=17)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert conv_scan(lib, d=dims(batch=0), x=None, u=None, out=None) == _lib.MAMBA_OK
 
 
@@ -318,7 +332,7 @@ def test_conv_state_update_validation(lib):
     assert csu(cw=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
     assert csu(x=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
     assert csu(d=dims(batch=2, seqlen=2, dim=64)) == _lib.MAMBA_ERR_INVALID_ARGUMENT
-    assert csu(d=dims(batch=2, seqlen=1, dim=64, dstate=5)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert csu(d=dims(batch=2, seqlen=1, dim=64, dstate=200)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert csu(st=FAKE * 4 + 8) == _lib.MAMBA_ERR_MISALIGNED
     assert csu(cs=FAKE * 2 + 1) == _lib.MAMBA_ERR_MISALIGNED
     assert csu(cs=FAKE) == _lib.MAMBA_ERR_INVALID_ARGUMENT              # window over x

@@ -1,0 +1,155 @@
+"""GPU parity at state sizes N without a kernel of their own: per-channel
+1 <= N <= 16 other than 4, 8, 16; scalar-A heads N up to 128 that are not a
+compiled size (fp32: 16, 32, 64, 128; bf16: multiples of 8).  The chunked scan
+and its backward run them on zero-padded copies in the workspace; the decode
+step handles any N itself.  Each path is compared with the fp64 oracle run at the
+same N (d_state is a constructor parameter of the S6 layer on the Mamba skill
+page), over several chunks with packed documents and a carried state."""
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_cotangent, make_custom
+
+from gpu_helpers import assert_close, oracle_pipeline, oracle_scan, to_dev, to_host, torch_mod, upload
+
+pytestmark = pytest.mark.gpu
+
+CHANNEL_N = [1, 2, 3, 5, 12]
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (they fail instead of skipping)")
+    import selective_state_space_23_amd as mod
+    mod._lib.load()
+    return mod
+
+
+def carried_state(Bt, Dm, N, seed):
+    rng = np.random.default_rng(seed)
+    return (0.3 * rng.standard_normal((Bt, Dm, N))).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", CHANNEL_N)
+def test_fused_forward_channels(ssm, N, dtype):
+    """Conv + scan in one call, several chunks (ragged tail and channel count)."""
+    inp = make_custom(2, 700, 100, N, dtype=dtype, docs=150.0, seed=1000 + N)
+    print(f"[N] fused channels N={N} {dtype}", flush=True)
+    dev = upload(inp)
+    u, out, fin = ssm.conv_scan_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["delta"], dev["A"], dev["B"],
+                                    dev["C"], dev["D"], dev["z"], dev["delta_bias"], dev["doc_start"])
+    _, out_ref, fin_ref = oracle_pipeline(inp, np.arange(100))
+    assert_close(to_host(out), out_ref, dtype, f"fused out N={N}")
+    assert_close(to_host(fin), fin_ref, dtype, f"fused final_state N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", [1, 5, 12])
+def test_scan_with_initial_state_channels(ssm, N, dtype):
+    """The split scan with a carried state in and the final state out (both padded)."""
+    torch = torch_mod()
+    inp = make_custom(2, 900, 72, N, dtype=dtype, docs=300.0, seed=1100 + N)
+    inp.doc_start[:, 0] = 0
+    inp.doc_start[1, 0] = 1
+    init = carried_state(2, 72, N, 1150 + N)
+    print(f"[N] scan+init channels N={N} {dtype}", flush=True)
+    dev = upload(inp)
+    u = to_dev(inp.x, dtype)
+    out, fin = ssm.selective_scan_fwd(u, dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                                      dev["delta_bias"], dev["doc_start"], initial_state=torch.from_numpy(init).cuda())
+    out_ref, fin_ref = oracle_scan(inp, inp.x.astype(np.float64), np.arange(72), initial_state=init)
+    assert_close(to_host(out), out_ref, dtype, f"scan out N={N}")
+    assert_close(to_host(fin), fin_ref, dtype, f"scan final_state N={N}")
+
+
+@pytest.mark.parametrize("case", [(24, "f32"), (100, "f32"), (20, "bf16"), (100, "bf16"), (3, "bf16")],
+                         ids=lambda c: f"N{c[0]}-{c[1]}")
+def test_heads_forward(ssm, case):
+    """Scalar-A heads (2 heads of 64 channels): fp32 recurrent form padded to 32 or
+    128 states, bf16 matrix form padded to a multiple of 8."""
+    N, dtype = case
+    inp = make_custom(2, 600, 128, N, nheads=2, dtype=dtype, docs=120.0, seed=1200 + N)
+    print(f"[N] heads N={N} {dtype}", flush=True)
+    dev = upload(inp)
+    u, out, fin = ssm.conv_scan_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["delta"], dev["A"], dev["B"],
+                                    dev["C"], dev["D"], dev["z"], dev["delta_bias"], dev["doc_start"])
+    _, out_ref, fin_ref = oracle_pipeline(inp, np.arange(128))
+    assert_close(to_host(out), out_ref, dtype, f"heads out N={N}")
+    assert_close(to_host(fin), fin_ref, dtype, f"heads final_state N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", [1, 3, 5, 12])
+def test_backward_channels(ssm, N, dtype):
+    """Scan gradients with a carried state and a gradient at the final state: the
+    padded dA, dB, dC and d_initial_state are copied back at N."""
+    torch = torch_mod()
+    inp = make_custom(2, 600, 96, N, dtype=dtype, docs=130.0, seed=1300 + N)
+    inp.doc_start[:, 0] = 0
+    inp.doc_start[1, 0] = 1
+    init = carried_state(2, 96, N, 1350 + N)
+    dfin = carried_state(2, 96, N, 1360 + N)
+    dout = make_cotangent(2, 600, 96, dtype=dtype, seed=1370 + N)
+    print(f"[N] backward N={N} {dtype}", flush=True)
+    dev = upload(inp)
+    got = ssm.selective_scan_bwd(to_dev(inp.x, dtype), dev["delta"], dev["A"], dev["B"], dev["C"],
+                                 to_dev(dout, dtype), D=dev["D"], z=dev["z"], delta_bias=dev["delta_bias"],
+                                 doc_start=dev["doc_start"], initial_state=torch.from_numpy(init).cuda(),
+                                 d_final_state=torch.from_numpy(dfin).cuda())
+    ref = oracle.selective_scan_bwd(inp.x, inp.delta, inp.A, inp.B, inp.C, dout, D=inp.D, z=inp.z,
+                                    delta_bias=inp.delta_bias, doc_start=inp.doc_start, initial_state=init,
+                                    d_final_state=dfin)
+    assert set(got) == set(ref)
+    for k in sorted(ref):
+        assert_close(to_host(got[k]), ref[k], dtype, f"bwd N={N} {k}")
+
+
+@pytest.mark.parametrize("case", [(1, 0, "bf16"), (5, 0, "f32"), (12, 0, "bf16"), (24, 2, "bf16"),
+                                  (100, 2, "f32")], ids=lambda c: f"N{c[0]}-H{c[1]}-{c[2]}")
+def test_decode_steps(ssm, case):
+    """The one-token step from a zero state over 30 tokens (document starts as
+    resets), against the oracle's whole sequence."""
+    torch = torch_mod()
+    N, H, dtype = case
+    Dm = 128
+    inp = make_custom(2, 30, Dm, N, nheads=H, dtype=dtype, docs=9.0, seed=1400 + N)
+    print(f"[N] decode N={N} H={H} {dtype}", flush=True)
+    dev = upload(inp)
+    conv_state = torch.zeros((2, Dm, 3), dtype=dev["x"].dtype, device="cuda")
+    state = torch.zeros((2, Dm, N), dtype=torch.float32, device="cuda")
+    outs = []
+    for t in range(30):
+        reset = dev["doc_start"][:, t].contiguous()
+        if t == 0:
+            reset = torch.ones_like(reset)
+        o = ssm.conv_state_update(dev["x"][:, t].contiguous(), conv_state, dev["conv_w"], dev["conv_b"], state,
+                                  dev["delta"][:, t].contiguous(), dev["A"], dev["B"][:, t].contiguous(),
+                                  dev["C"][:, t].contiguous(), dev["D"], dev["z"][:, t].contiguous(),
+                                  dev["delta_bias"], reset=reset)
+        outs.append(to_host(o))
+    _, ref_out, ref_fin = oracle_pipeline(inp, np.arange(Dm))
+    assert_close(np.stack(outs, axis=1), ref_out, dtype, f"decode out N={N}")
+    assert_close(to_host(state), ref_fin, dtype, f"decode state N={N}")
+
+
+@pytest.mark.parametrize("N", [5, 12])
+def test_noalloc_padded(ssm, N):
+    """The allocation-free entry point pads inside its own array the same way."""
+    torch = torch_mod()
+    inp = make_custom(2, 1500, 128, N, dtype="f32", docs=400.0, seed=1500 + N)
+    print(f"[N] noalloc N={N}", flush=True)
+    dev = upload(inp)
+    u = to_dev(inp.x, "f32")
+    ref_out, ref_fin = ssm.selective_scan_fwd(u, dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                                              dev["delta_bias"], dev["doc_start"])
+    out = torch.empty_like(u)
+    fin = torch.empty((2, 128, N), dtype=torch.float32, device="cuda")
+    ssm.selective_scan_fwd_noalloc(u, dev["delta"], dev["A"], dev["B"], dev["C"], out, dev["D"], dev["z"],
+                                   dev["delta_bias"], dev["doc_start"], final_state=fin)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin)
