@@ -34,12 +34,46 @@ from .mamba_oracle import _f64, doc_segment_start, sigmoid, silu
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
                        doc_start=None, initial_state=None, d_final_state=None):
     """Gradients of sum(dout * out) + sum(d_final_state * final_state) for the
-    per-channel-A selective scan (A of shape (D, N)).  ``initial_state`` (B, D, N),
-    if given, is the state before token 0 (token 0 then starts a document only
-    where doc_start flags it, as in the forward); ``d_final_state`` (B, D, N) is
-    the gradient arriving at the state after the last token (zero if None).
-    Returns a dict with du, ddelta, dA, dB, dC and, when the input is given, dD,
-    dz, ddelta_bias, d_initial_state (all float64)."""
+    selective scan.  ``initial_state`` (B, D, N), if given, is the state before
+    token 0 (token 0 then starts a document only where doc_start flags it, as in
+    the forward); ``d_final_state`` (B, D, N) is the gradient arriving at the
+    state after the last token (zero if None).  Returns a dict with du, ddelta,
+    dA, dB, dC and, when the input is given, dD, dz, ddelta_bias,
+    d_initial_state (all float64).
+
+    A of shape (D, N): per-channel A, delta (B, L, D), delta_bias (D,).
+    A of shape (H,): scalar-A heads ("Mamba-2 (SSD)" section of the skill page),
+    delta (B, L, H), delta_bias (H,), channel d in head d // (D / H).  The heads
+    form is the per-channel scan whose A (on every state), step size and bias
+    are shared by the channels of a head; the gradient of a shared parameter is
+    the sum of the gradients of its copies, so dA (H,), ddelta (B, L, H) and
+    ddelta_bias (H,) sum the per-channel ones over the head's channels (and dA
+    over the states)."""
+    Am = _f64(A)
+    if Am.ndim == 2:
+        return _channels_bwd(u, delta, Am, B, C, dout, D, z, delta_bias, delta_softplus, doc_start, initial_state,
+                             d_final_state)
+    H = Am.shape[0]
+    Dm = np.shape(u)[2]
+    N = np.shape(B)[-1]
+    head = np.arange(Dm) // (Dm // H)                 # head of each channel
+    A_ch = np.repeat(Am[head][:, None], N, axis=1)
+    delta_ch = _f64(delta)[:, :, head]
+    bias_ch = None if delta_bias is None else _f64(delta_bias)[head]
+    g = _channels_bwd(u, delta_ch, A_ch, B, C, dout, D, z, bias_ch, delta_softplus, doc_start, initial_state,
+                      d_final_state)
+    fold = np.zeros((Dm, H))
+    fold[np.arange(Dm), head] = 1.0                   # sums a channel's gradient into its head
+    g["dA"] = g["dA"].sum(axis=1) @ fold
+    g["ddelta"] = g["ddelta"] @ fold
+    if "ddelta_bias" in g:
+        g["ddelta_bias"] = g["ddelta_bias"] @ fold
+    return g
+
+
+def _channels_bwd(u, delta, A, B, C, dout, D, z, delta_bias, delta_softplus, doc_start, initial_state,
+                  d_final_state):
+    """selective_scan_bwd for per-channel A (D, N)."""
     u = _f64(u)
     dl = _f64(delta)
     Am = _f64(A)

@@ -182,3 +182,28 @@ def test_fused_decode_step_matches_two_steps(ssm, case):
         assert torch.equal(o1, o2), f"out at token {t}"
         assert torch.equal(st1, st2), f"state at token {t}"
         assert torch.equal(cs1, cs2), f"conv window at token {t}"
+
+
+@pytest.mark.parametrize("Dm", [1536, 5120])
+def test_decode_model_widths(ssm, Dm):
+    """The fused one-token step at the model widths of the workloads (mamba-130m's
+    1536 channels, mamba-2.8b's 5120), N = 16, from a zero state over 24 tokens
+    with document starts, against the oracle on every channel."""
+    torch = torch_mod()
+    inp = make_custom(2, 24, Dm, 16, dtype="bf16", docs=8.0, seed=450 + Dm)
+    dev = upload(inp)
+    conv_state = torch.zeros((2, Dm, 3), dtype=dev["x"].dtype, device="cuda")
+    state = torch.zeros((2, Dm, 16), dtype=torch.float32, device="cuda")
+    outs = []
+    for t in range(24):
+        reset = dev["doc_start"][:, t].contiguous()
+        if t == 0:
+            reset = torch.ones_like(reset)
+        o = ssm.conv_state_update(dev["x"][:, t].contiguous(), conv_state, dev["conv_w"], dev["conv_b"], state,
+                                  dev["delta"][:, t].contiguous(), dev["A"], dev["B"][:, t].contiguous(),
+                                  dev["C"][:, t].contiguous(), dev["D"], dev["z"][:, t].contiguous(),
+                                  dev["delta_bias"], reset=reset)
+        outs.append(to_host(o))
+    _, ref_out, ref_fin = oracle_pipeline(inp, np.arange(Dm))
+    assert_close(np.stack(outs, axis=1), ref_out, "bf16", f"decode out D={Dm}")
+    assert_close(to_host(state), ref_fin, "bf16", f"decode state D={Dm}")

@@ -152,7 +152,8 @@ def test_conv_state_without_initial_state(ssm, H, N, dt):
     assert_close(to_host(u), u_exact, dt, "conv with history, no initial state")
 
 
-SAMPLES = {"packed_32k": [0, 5, 63, 64, 700, 1535], "heads_32k": [0, 64, 700, 1535], "m130_2k": [0, 777, 1535]}
+SAMPLES = {"packed_32k": [0, 5, 63, 64, 700, 1535], "heads_32k": [0, 64, 700, 1535], "m130_2k": [0, 777, 1535],
+           "wide_64k": [0, 1, 2047, 4000, 5119], "tiny_f32": list(range(16))}
 
 
 @pytest.mark.parametrize("name", list(SAMPLES))

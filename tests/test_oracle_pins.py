@@ -418,6 +418,55 @@ def test_gradients_match_finite_differences(flags):
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (arg, flat, fd, an)
 
 
+@pytest.mark.parametrize("softplus", [True, False], ids=["softplus", "no_softplus"])
+def test_heads_gradients_match_finite_differences(softplus):
+    """Scalar-A heads (A (H,), delta (B, L, H), delta_bias (H,)): every input,
+    a carried state and a gradient at the final state included, against central
+    differences of the heads-mode forward; row 0 continues the carried state,
+    row 1 starts a document at token 0 (its d_initial_state is then 0)."""
+    rng = np.random.default_rng(31)
+    Bt, L, H, P, N = 2, 10, 2, 2, 3
+    Dm = H * P
+    args = dict(u=rng.normal(size=(Bt, L, Dm)),
+                delta=rng.normal(0.0, 0.5, size=(Bt, L, H)) + (0.0 if softplus else 1.0),
+                A=-np.exp(rng.normal(size=H)), B=rng.normal(size=(Bt, L, N)), C=rng.normal(size=(Bt, L, N)),
+                D=rng.normal(size=Dm), z=rng.normal(size=(Bt, L, Dm)), delta_bias=rng.normal(0.0, 0.3, size=H),
+                initial_state=rng.normal(size=(Bt, Dm, N)))
+    ds = np.zeros((Bt, L), dtype=np.uint8)
+    ds[0, 6] = 1
+    ds[1, 0] = 1
+    ds[1, 3] = 1
+    dout = rng.normal(size=(Bt, L, Dm))
+    dfin = rng.normal(size=(Bt, Dm, N))
+    g = oracle.selective_scan_bwd(args["u"], args["delta"], args["A"], args["B"], args["C"], dout, args["D"],
+                                  args["z"], args["delta_bias"], softplus, ds, initial_state=args["initial_state"],
+                                  d_final_state=dfin)
+    assert g["dA"].shape == (H,) and g["ddelta"].shape == (Bt, L, H) and g["ddelta_bias"].shape == (H,)
+
+    def loss():
+        out, fin = oracle.selective_scan(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"],
+                                         args["z"], args["delta_bias"], softplus, ds,
+                                         initial_state=args["initial_state"])
+        return float(np.sum(out * dout) + np.sum(fin * dfin))
+
+    names = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+             "delta_bias": "ddelta_bias", "initial_state": "d_initial_state"}
+    eps = 1e-6
+    for arg, gname in names.items():
+        x = args[arg]
+        for flat in range(x.size):
+            orig = x.flat[flat]
+            x.flat[flat] = orig + eps
+            lp = loss()
+            x.flat[flat] = orig - eps
+            lm = loss()
+            x.flat[flat] = orig
+            fd = (lp - lm) / (2 * eps)
+            an = g[gname].flat[flat]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (arg, flat, fd, an)
+    assert np.all(g["d_initial_state"][1] == 0.0)
+
+
 @pytest.mark.parametrize("silu_on,docs", [(True, True), (False, True), (True, False)], ids=str)
 def test_conv_gradients_match_finite_differences(silu_on, docs):
     """oracle.causal_conv1d_bwd against central differences of oracle.causal_conv1d:
