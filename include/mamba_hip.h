@@ -21,7 +21,7 @@
  *       packing paragraph (recurrent state restarts at every document start).
  *
  * Further entry points: the two in one call (mamba_conv_scan_fwd), one-token
- * decode steps, and the backward passes of the conv and of the per-channel scan
+ * decode steps, and the backward passes of the conv and of the scan
  * (mamba_causal_conv1d_bwd, mamba_selective_scan_bwd), each described at its
  * declaration below.
  *
@@ -252,7 +252,7 @@ int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bia
                             float* d_conv_state, int64_t batch, int64_t seqlen, int64_t dim, int32_t width,
                             int32_t dtype, int32_t apply_silu, void* workspace, size_t workspace_bytes, void* stream);
 
-/* ---- Backward pass (training) of the per-channel scan: the gradients of
+/* ---- Backward pass (training) of the scan: the gradients of
  * sum(dout * out) through mamba_selective_scan_fwd, i.e. the adjoint of the
  * recurrence run from the row end back to token 0.  Defined by the same pages
  * as the forward; the states are recomputed rather than stored (Mamba skill
@@ -262,11 +262,20 @@ int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bia
  *   du_t = D dy_t + dt_t (g_t . B_t)
  *   ddelta_t = [u_t (g_t . B_t) + sum_n A g_t a_t h_{t-1}] * sigmoid(delta_t + delta_bias)
  *   dB_t = sum_d g_t dt_t u_t,  dC_t = sum_d dy_t h_t,  dA = sum_t dt_t g_t a_t h_{t-1}
- *   dD = sum_t dy_t u_t,  dz_t = dout_t y_t silu'(z_t),  ddelta_bias = sum_t ddelta_t. */
+ *   dD = sum_t dy_t u_t,  dz_t = dout_t y_t silu'(z_t),  ddelta_bias = sum_t ddelta_t.
+ * With scalar-A heads (nheads > 0; "Mamba-2 (SSD)" section of the Mamba skill
+ * page) A, delta and delta_bias are shared by the D / H channels and N states
+ * of a head, so their gradients are the sums of the per-channel ones above over
+ * those channels and states (dA over all of them, ddelta and ddelta_bias over
+ * the head's channels). */
 
-/* Bytes of device workspace mamba_selective_scan_bwd needs for `dims` (about
- * B L D (N + 2) * 4 / 16 + B L D * 4 + B L ceil(D / 128) * 8 N bytes plus the
- * per-chunk carries and two (B, D, N) float32 arrays; 1.08 GB at B = 2, L = 32768, D = 1536, N = 16). */
+/* Bytes of device workspace mamba_selective_scan_bwd needs for `dims`.
+ * Per channel: about B L D (N + 2) * 4 / 16 + B L D * 4 + B L ceil(D / 128) * 8 N
+ * bytes plus the per-chunk carries and two (B, D, N) float32 arrays; 1.08 GB at
+ * B = 2, L = 32768, D = 1536, N = 16.  Scalar-A heads: about B D N ceil(L / 16)
+ * * 4 (the state entering every 16-token chunk) + 2 B H L N * 4 (per-head dB,
+ * dC) bytes; 4.88 GB at B = 2, L = 32768, D = 1536, H = 24, N = 128.  States
+ * padded to a compiled size (below) add their zero-padded copies. */
 int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size_t* bytes);
 
 /* Selective scan backward.
@@ -290,9 +299,13 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
  *              initial_state, else MAMBA_ERR_INVALID_ARGUMENT.
  *   workspace  at least mamba_selective_scan_bwd_workspace_bytes bytes, 256-byte
  *              aligned, scratch (contents on entry ignored).
- * Supported: nheads == 0, 1 <= N <= 16 (N other than 4, 8, 16 on zero-padded
- * copies in the workspace, as the forward), and what the forward requires; with
- * bf16 also an even D; others return MAMBA_ERR_UNSUPPORTED.  With bf16, u,
+ *   With nheads > 0: A, dA (H,); delta, ddelta (B, L, H); delta_bias,
+ *              ddelta_bias (H,).
+ * Supported: nheads == 0 with 1 <= N <= 16 and, with bf16, an even D; nheads > 0
+ * with head size D / H of 32 or 64 and 1 <= N <= 128 (both dtypes; the arithmetic
+ * is fp32).  N other than a compiled size (4, 8, 16 per channel; 16, 32, 64, 128
+ * for heads) runs on zero-padded copies in the workspace, as the forward.  Also
+ * what the forward requires; others return MAMBA_ERR_UNSUPPORTED.  With bf16, u,
  * delta, z and dout must be 4-byte aligned (they are read as pairs of channels),
  * else MAMBA_ERR_MISALIGNED.  Outputs must not overlap each other, the inputs
  * or the workspace.  The sums over channels, tokens and rows run in a fixed

@@ -354,9 +354,9 @@ def selective_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=
     return out
 
 
-def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16") -> int:
+def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16", nheads=0) -> int:
     code = _lib.MAMBA_DTYPE_BF16 if dtype == "bf16" else _lib.MAMBA_DTYPE_F32
-    dims = _scan_dims(batch, seqlen, dim, dstate, 0, code, True)
+    dims = _scan_dims(batch, seqlen, dim, dstate, nheads, code, True)
     n = ctypes.c_size_t(0)
     _lib.check(_lib.load().mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)),
                "mamba_selective_scan_bwd_workspace_bytes")
@@ -401,37 +401,40 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
                        delta_softplus: bool = True, workspace=None, grads=None, initial_state=None,
                        d_final_state=None):
     """Gradients of sum(dout * out) + sum(d_final_state * final_state) for the
-    per-channel-A scan (A of shape (D, N)); see mamba_selective_scan_bwd.
-    Arguments as selective_scan_fwd plus ``dout`` (B, L, D) and ``d_final_state``
-    (B, D, N) float32 or None.  Returns a dict with du, ddelta, dB, dC (u's
-    dtype), dA (D, N) float32 and, for each optional input given, dD, dz,
-    ddelta_bias, d_initial_state (B, D, N) float32.  ``grads``: optional dict of
-    preallocated outputs with the same keys."""
+    scan; see mamba_selective_scan_bwd.  Arguments as selective_scan_fwd (A
+    (D, N) per channel, or (H,) for scalar-A heads with delta (B, L, H)) plus
+    ``dout`` (B, L, D) and ``d_final_state`` (B, D, N) float32 or None.  Returns
+    a dict with du, ddelta, dB, dC (u's dtype), dA (A's shape) float32 and, for
+    each optional input given, dD, dz, ddelta_bias, d_initial_state (B, D, N)
+    float32.  ``grads``: optional dict of preallocated outputs with the same
+    keys."""
     torch = _torch()
     dev = _check_device(u)
-    if u.dim() != 3 or A.dim() != 2:
-        raise ValueError("u must be (B, L, D) and A (D, N)")
+    if u.dim() != 3 or A.dim() not in (1, 2):
+        raise ValueError("u must be (B, L, D) and A (D, N) or (H,)")
     Bt, L, Dm = u.shape
-    N = A.shape[1]
+    N = B.shape[-1]
+    nheads = A.shape[0] if A.dim() == 1 else 0
+    nd = nheads if nheads else Dm
     code = _dtype_code(u)
     if doc_start is not None and doc_start.dtype == torch.bool:
         doc_start = doc_start.to(torch.uint8)
     g = dict(grads) if grads else {}
     f32 = torch.float32
-    shapes = {"du": ((Bt, L, Dm), u.dtype), "ddelta": ((Bt, L, Dm), u.dtype), "dA": ((Dm, N), f32),
+    shapes = {"du": ((Bt, L, Dm), u.dtype), "ddelta": ((Bt, L, nd), u.dtype), "dA": (tuple(A.shape), f32),
               "dB": ((Bt, L, N), u.dtype), "dC": ((Bt, L, N), u.dtype)}
     if D is not None:
         shapes["dD"] = ((Dm,), f32)
     if z is not None:
         shapes["dz"] = ((Bt, L, Dm), u.dtype)
     if delta_bias is not None:
-        shapes["ddelta_bias"] = ((Dm,), f32)
+        shapes["ddelta_bias"] = ((nd,), f32)
     if initial_state is not None:
         shapes["d_initial_state"] = ((Bt, Dm, N), f32)
     for k, (shape, dt) in shapes.items():
         if k not in g:
             g[k] = torch.empty(shape, dtype=dt, device=dev)
-    dims = _scan_dims(Bt, L, Dm, N, 0, code, delta_softplus)
+    dims = _scan_dims(Bt, L, Dm, N, nheads, code, delta_softplus)
     lib = _lib.load()
     need = ctypes.c_size_t(0)
     _lib.check(lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(need)),
@@ -442,13 +445,13 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     st = lib.mamba_selective_scan_bwd(
         ctypes.byref(dims),
         _ptr(u, "u", dev, u.dtype, (Bt, L, Dm)),
-        _ptr(delta, "delta", dev, u.dtype, (Bt, L, Dm)),
-        _ptr(A, "A", dev, f32, (Dm, N)),
+        _ptr(delta, "delta", dev, u.dtype, (Bt, L, nd)),
+        _ptr(A, "A", dev, f32, tuple(A.shape)),
         _ptr(B, "B", dev, u.dtype, (Bt, L, N)),
         _ptr(C, "C", dev, u.dtype, (Bt, L, N)),
         _ptr(D, "D", dev, f32, (Dm,)),
         _ptr(z, "z", dev, u.dtype, (Bt, L, Dm)),
-        _ptr(delta_bias, "delta_bias", dev, f32, (Dm,)),
+        _ptr(delta_bias, "delta_bias", dev, f32, (nd,)),
         _ptr(doc_start, "doc_start", dev, torch.uint8, (Bt, L)),
         _ptr(initial_state, "initial_state", dev, f32, (Bt, Dm, N)),
         _ptr(dout, "dout", dev, u.dtype, (Bt, L, Dm)),

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 LIB_NAME = "libmamba_hip.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["api.cpp", "noalloc.hip", "conv1d.hip", "conv1d_bwd.hip", "scan.hip", "scan_bwd.hip", "ssd.hip",
-           "decode.hip", "fill.hip", "pad.hip"]
+           "decode.hip", "fill.hip", "pad.hip", "heads_bwd.hip"]
 # The ALU issue-rate probe bench.py runs (measurement only, not part of the C ABI).
 PROBE_SRC = os.path.join(PKG_DIR, "probe", "alu_rates.hip")
 PROBE_PATH = os.path.join(PKG_DIR, "libmamba_probe.so")

@@ -125,12 +125,20 @@ struct BwdLayout {
     bool padded() const { return nt != n; }
 };
 
+// The backward's kernels: per-channel A (scan_bwd.hip) or scalar-A heads
+// (heads_bwd.hip); the state size they run N with (0: unsupported).
+int64_t bwd_kernel_dstate(const mamba_scan_dims_t* d) {
+    return d->nheads > 0 ? mamba::heads_bwd_kernel_dstate(d->dim, d->dstate, d->nheads)
+                         : mamba::scan_bwd_kernel_dstate(d->dstate, 0);
+}
+
 BwdLayout bwd_layout_of(const mamba_scan_dims_t* d) {
     BwdLayout w;
     const bool bf16 = d->dtype == MAMBA_DTYPE_BF16;
     w.n = d->dstate;
-    w.nt = mamba::scan_bwd_kernel_dstate(d->dstate, d->nheads);
-    size_t off = mamba::scan_bwd_workspace_bytes(d->batch, d->seqlen, d->dim, w.nt, bf16);
+    w.nt = bwd_kernel_dstate(d);
+    size_t off = d->nheads > 0 ? mamba::heads_bwd_workspace_bytes(d->batch, d->seqlen, d->dim, w.nt, d->nheads)
+                               : mamba::scan_bwd_workspace_bytes(d->batch, d->seqlen, d->dim, w.nt, bf16);
     if (!w.padded()) {
         w.total = off;
         return w;
@@ -138,7 +146,8 @@ BwdLayout bwd_layout_of(const mamba_scan_dims_t* d) {
     const size_t esz = bf16 ? 2 : 4;
     const size_t bc = align256(static_cast<size_t>(d->batch * d->seqlen * w.nt) * esz);
     const size_t st = align256(static_cast<size_t>(d->batch * d->dim * w.nt) * 4);
-    const size_t dn = align256(static_cast<size_t>(d->dim * w.nt) * 4);
+    // A and dA are (H,) for heads: nothing to pad
+    const size_t dn = d->nheads > 0 ? 0 : align256(static_cast<size_t>(d->dim * w.nt) * 4);
     off = align256(off);
     w.off_B = off; off += bc;
     w.off_C = off; off += bc;
@@ -153,8 +162,13 @@ BwdLayout bwd_layout_of(const mamba_scan_dims_t* d) {
     return w;
 }
 
+hipError_t launch_bwd_kernels(const mamba::ScanBwdArgs& a) {
+    return a.nheads > 0 ? mamba::launch_heads_bwd(a) : mamba::launch_selective_scan_bwd(a);
+}
+
 hipError_t launch_bwd_layout(mamba::ScanBwdArgs a, const BwdLayout& w) {
-    if (!w.padded()) return mamba::launch_selective_scan_bwd(a);
+    if (!w.padded()) return launch_bwd_kernels(a);
+    const bool heads = a.nheads > 0;
     char* ws = static_cast<char*>(a.ws);
     const int esz = a.bf16 ? 2 : 4;
     const int n = static_cast<int>(w.n), nt = static_cast<int>(w.nt);
@@ -163,7 +177,7 @@ hipError_t launch_bwd_layout(mamba::ScanBwdArgs a, const BwdLayout& w) {
     hipError_t e;
     if ((e = mamba::launch_pad_rows(a.B, ws + w.off_B, bl, n, nt, esz, s)) != hipSuccess) return e;
     if ((e = mamba::launch_pad_rows(a.C, ws + w.off_C, bl, n, nt, esz, s)) != hipSuccess) return e;
-    if ((e = mamba::launch_pad_rows(a.A, ws + w.off_A, a.dim, n, nt, 4, s)) != hipSuccess) return e;
+    if (!heads && (e = mamba::launch_pad_rows(a.A, ws + w.off_A, a.dim, n, nt, 4, s)) != hipSuccess) return e;
     if (a.initial_state && (e = mamba::launch_pad_rows(a.initial_state, ws + w.off_h0, bd, n, nt, 4, s)) != hipSuccess)
         return e;
     if (a.d_final_state && (e = mamba::launch_pad_rows(a.d_final_state, ws + w.off_dhT, bd, n, nt, 4, s)) != hipSuccess)
@@ -174,16 +188,16 @@ hipError_t launch_bwd_layout(mamba::ScanBwdArgs a, const BwdLayout& w) {
     float* dh0 = a.d_initial_state;
     a.B = ws + w.off_B;
     a.C = ws + w.off_C;
-    a.A = reinterpret_cast<const float*>(ws + w.off_A);
+    if (!heads) a.A = reinterpret_cast<const float*>(ws + w.off_A);
     if (a.initial_state) a.initial_state = reinterpret_cast<const float*>(ws + w.off_h0);
     if (a.d_final_state) a.d_final_state = reinterpret_cast<const float*>(ws + w.off_dhT);
-    a.dA = reinterpret_cast<float*>(ws + w.off_dA);
+    if (!heads) a.dA = reinterpret_cast<float*>(ws + w.off_dA);
     a.dB = ws + w.off_dB;
     a.dC = ws + w.off_dC;
     if (dh0) a.d_initial_state = reinterpret_cast<float*>(ws + w.off_dh0);
     a.dstate = nt;
-    if ((e = mamba::launch_selective_scan_bwd(a)) != hipSuccess) return e;
-    if ((e = mamba::launch_unpad_rows(ws + w.off_dA, dA, a.dim, n, nt, 4, s)) != hipSuccess) return e;
+    if ((e = launch_bwd_kernels(a)) != hipSuccess) return e;
+    if (!heads && (e = mamba::launch_unpad_rows(ws + w.off_dA, dA, a.dim, n, nt, 4, s)) != hipSuccess) return e;
     if ((e = mamba::launch_unpad_rows(ws + w.off_dB, dB, bl, n, nt, esz, s)) != hipSuccess) return e;
     if ((e = mamba::launch_unpad_rows(ws + w.off_dC, dC, bl, n, nt, esz, s)) != hipSuccess) return e;
     return dh0 ? mamba::launch_unpad_rows(ws + w.off_dh0, dh0, bd, n, nt, 4, s) : hipSuccess;
@@ -510,7 +524,7 @@ int mamba_selective_scan_bwd_workspace_bytes(const mamba_scan_dims_t* dims, size
     *bytes = 0;
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
-    if (!mamba::scan_bwd_supported(dims->dstate, dims->nheads)) return MAMBA_ERR_UNSUPPORTED;
+    if (bwd_kernel_dstate(dims) == 0) return MAMBA_ERR_UNSUPPORTED;
     *bytes = bwd_layout_of(dims).total;
     return MAMBA_OK;
 }
@@ -523,15 +537,18 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
                              size_t workspace_bytes, void* stream) {
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
-    if (!mamba::scan_bwd_supported(dims->dstate, dims->nheads)) return MAMBA_ERR_UNSUPPORTED;
+    if (bwd_kernel_dstate(dims) == 0) return MAMBA_ERR_UNSUPPORTED;
     const int64_t Bt = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
+    const bool heads = dims->nheads > 0;
+    const int64_t nd = heads ? dims->nheads : Dm;          // width of delta, ddelta, delta_bias, ddelta_bias
+    const int64_t na = heads ? dims->nheads : Dm * N;      // elements of A and dA
     if ((z == nullptr) != (dz == nullptr)) return MAMBA_ERR_INVALID_ARGUMENT;
     if (d_initial_state && !initial_state) return MAMBA_ERR_INVALID_ARGUMENT;
     if (Bt * L * Dm == 0) {
         // No tokens: dA, dD and ddelta_bias are sums over none, and the adjoint
         // passes through the empty row (d_initial_state = d_final_state, or 0).
         float* zs[] = {Bt * L == 0 ? dA : nullptr, Bt * L == 0 ? dD : nullptr, Bt * L == 0 ? ddelta_bias : nullptr};
-        const int64_t zn[] = {Dm * N, Dm, Dm};
+        const int64_t zn[] = {na, Dm, nd};
         int zst = zero_outputs(zs, zn, 3, stream);
         if (zst != MAMBA_OK || L != 0 || Bt * Dm == 0 || !d_initial_state) return zst;
         const int64_t ns = Bt * Dm * N;
@@ -544,9 +561,9 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
     if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
         return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
-    // The main pass stages u, delta, z and dout through 4-byte loads (pairs of
-    // bf16 channels): even D, 4-byte aligned rows.
-    if (esz == 2 && Dm % 2 != 0) return MAMBA_ERR_UNSUPPORTED;
+    // The per-channel main pass stages u, delta, z and dout through 4-byte loads
+    // (pairs of bf16 channels): even D, 4-byte aligned rows.
+    if (!heads && esz == 2 && Dm % 2 != 0) return MAMBA_ERR_UNSUPPORTED;
     const void* staged[] = {u, delta, z, dout};
     for (const void* t : staged)
         if (t && !aligned(t, 4)) return MAMBA_ERR_MISALIGNED;
@@ -561,14 +578,16 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
         if (t && !aligned(t, 4)) return MAMBA_ERR_MISALIGNED;
 
     const size_t act = static_cast<size_t>(Bt * L * Dm) * esz;
+    const size_t dlt = static_cast<size_t>(Bt * L * nd) * esz;
     const size_t bc = static_cast<size_t>(Bt * L * N) * esz;
-    const size_t dn = static_cast<size_t>(Dm * N) * 4, d1 = static_cast<size_t>(Dm) * 4;
+    const size_t dn = static_cast<size_t>(na) * 4, d1 = static_cast<size_t>(Dm) * 4;
+    const size_t n1 = static_cast<size_t>(nd) * 4;
     const size_t sb = static_cast<size_t>(Bt * Dm * N) * 4;
     const void* ins[] = {u, delta, A, B, C, D, z, delta_bias, doc_start, dout, initial_state, d_final_state};
-    const size_t insz[] = {act, act, dn, bc, bc, d1, act, d1, static_cast<size_t>(Bt * L), act, sb, sb};
+    const size_t insz[] = {act, dlt, dn, bc, bc, d1, act, n1, static_cast<size_t>(Bt * L), act, sb, sb};
     constexpr int kIns = 12;
     const void* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, d_initial_state};
-    const size_t outsz[] = {act, act, dn, bc, bc, d1, act, d1, sb};
+    const size_t outsz[] = {act, dlt, dn, bc, bc, d1, act, n1, sb};
     constexpr int kOuts = 9;
     const size_t need = lay.total;
     if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
@@ -590,6 +609,7 @@ int mamba_selective_scan_bwd(const mamba_scan_dims_t* dims, const void* u, const
     a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dz = dz; a.ddelta_bias = ddelta_bias;
     a.ws = workspace;
     a.batch = Bt; a.seqlen = L; a.dim = Dm; a.dstate = N;
+    a.nheads = dims->nheads;
     a.bf16 = dims->dtype == MAMBA_DTYPE_BF16;
     a.softplus = dims->delta_softplus != 0;
     a.stream = static_cast<hipStream_t>(stream);

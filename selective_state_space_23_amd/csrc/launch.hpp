@@ -118,6 +118,7 @@ struct ScanBwdArgs {
     float* d_initial_state = nullptr;       // (B, D, N), written; needs initial_state
     void* ws;
     int64_t batch, seqlen, dim, dstate;
+    int nheads = 0;       // > 0: scalar A per head (heads_bwd.hip)
     bool bf16;
     bool softplus;
     hipStream_t stream;
@@ -125,6 +126,12 @@ struct ScanBwdArgs {
 
 bool scan_bwd_supported(int64_t dstate, int nheads);
 int64_t scan_bwd_kernel_dstate(int64_t dstate, int nheads);   // as scan_kernel_dstate, or 0
+
+// Backward of the scalar-A heads scan (heads_bwd.hip): the state size its
+// kernels run a requested N with (0: unsupported), their workspace, the launch.
+int64_t heads_bwd_kernel_dstate(int64_t dim, int64_t dstate, int nheads);
+size_t heads_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads);
+hipError_t launch_heads_bwd(const ScanBwdArgs& a);
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool bf16);
 hipError_t launch_selective_scan_bwd(const ScanBwdArgs& a);
 

@@ -247,7 +247,10 @@ def test_bwd_workspace_query(lib):
     assert lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == _lib.MAMBA_OK
     # at least the 16-token checkpoints and the step sizes
     assert n.value >= 2 * 2048 * 1536 * 16 * 4 + 2 * 32768 * 1536 * 2
-    for bad in (dims(nheads=24, dstate=128), dims(dstate=32)):
+    st = lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(dims(nheads=24, dstate=128, seqlen=32768)),
+                                                      ctypes.byref(n))
+    assert st == _lib.MAMBA_OK and n.value > 0            # scalar-A heads (heads_bwd.hip)
+    for bad in (dims(nheads=32, dstate=128), dims(nheads=24, dstate=129), dims(dstate=32)):
         assert lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == \
             _lib.MAMBA_ERR_UNSUPPORTED
     assert lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(d), None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
@@ -267,7 +270,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, ws=FAKE * 2) == _lib.MAMBA_ERR_INVALID_ARGUMENT            # workspace over delta
     assert bwd(lib, wsb=16) == _lib.MAMBA_ERR_WORKSPACE
     assert bwd(lib, ws=None) == _lib.MAMBA_ERR_WORKSPACE
-    assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, nheads=2)) == _lib.MAMBA_ERR_UNSUPPORTED
+    assert bwd(lib, d=dims(batch=1, seqlen=64, dim=96, nheads=2)) == _lib.MAMBA_ERR_UNSUPPORTED   # head size 48
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, dstate=32)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=1, seqlen=64, dim=64, ngroups=2)) == _lib.MAMBA_ERR_UNSUPPORTED
     assert bwd(lib, d=dims(batch=0), u=None, dout=None, dA=None) == _lib.MAMBA_OK   # empty: nothing to write
