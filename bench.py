@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0
 # built without): 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz.
 FP32_VECTOR_PEAK_TFLOPS = 78.6
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
 CPU_SHARE = 16          # host cores that go with one GPU on the GPU machines
 RATES_FILE = os.path.join(ROOT, "profiles", "alu_rates_gfx950.md")
 
@@ -102,12 +103,25 @@ def ssd_mfma_flops(B, L, D, N, H, q=64):
     return B * H * (-(-L // q)) * per_chunk
 
 
-def bwd_bytes(B, L, D, N, esz):
+def bwd_bytes(B, L, D, N, esz, nheads=0):
     """Algorithmic HBM bytes of one backward call: u, delta, z, dout, B, C and the
-    doc flags read once; du, ddelta, dz, dB, dC written once; parameters and their
-    gradients."""
-    per_token = esz * 7 * D + 4 * esz * N + 1
-    return B * L * per_token + 4 * 2 * (D * N + 3 * D)
+    doc flags read once; du, ddelta, dz, dB, dC written once; parameters (A, D,
+    delta_bias) and their gradients.  delta is (B, L, H) for scalar-A heads."""
+    nd = nheads if nheads else D
+    na = nheads if nheads else D * N
+    per_token = esz * (5 * D + 2 * nd + 4 * N) + 1
+    return B * L * per_token + 4 * 2 * (na + D + nd)
+
+
+def heads_bwd_mfma_flops(B, L, D, N, H, q=16):
+    """fp32 MFMA flops of the scalar-A heads backward per call, from its 16-token
+    chunked form (P = D / H channels per head).  Per chunk: the forward pass's
+    state update and reverse aggregate (2 products of Q x N x P); in the main pass
+    C H, B dH, dY H^T, x dH^T and C^T dY (5 more of Q x N x P), C B^T, dS B and
+    dS^T C (3 of Q x Q x N), and M x, M^T dY, dY x^T (3 of Q x Q x P)."""
+    P = D // H
+    per_chunk = 2 * (7 * q * N * P + 3 * q * q * N + 3 * q * q * P)
+    return B * H * (-(-L // q)) * per_chunk
 
 
 def conv_bwd_bytes(B, L, D, esz):
@@ -151,6 +165,7 @@ def copy_probe(torch, dev, mib=1024, reps=5):
 # profile counts only while these files are unchanged.
 FWD_SOURCES = ["device_common.hpp", "launch.hpp", "conv1d.hip", "scan.hip", "ssd.hip"]
 BWD_SOURCES = ["device_common.hpp", "launch.hpp", "scan_bwd.hip", "conv1d_bwd.hip"]
+HEADS_BWD_SOURCES = ["device_common.hpp", "launch.hpp", "heads_bwd.hip", "pad.hip"]
 
 
 def recorded_traffic(path, source_files):
@@ -344,11 +359,13 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle, one core: tokens per row")
     ap.add_argument("--cpu-tokens-all", type=int, default=32768, help="oracle, all cores: tokens per row")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the device copy probe (0: skip)")
+    ap.add_argument("--no-u", action="store_true",
+                    help="fused path: the conv output u is not written (u = NULL; the output pass forms it again)")
     ap.add_argument("--flush-reps", type=int, default=20,
                     help="calls timed one by one with the MALL flushed before each (0: skip)")
     ap.add_argument("--path", choices=("fused", "split", "bwd", "decode", "rates"), default="fused",
                     help="fused: one mamba_conv_scan_fwd call per step; split: conv call, then scan call; "
-                         "bwd: scan backward then conv backward (per-channel A workloads); "
+                         "bwd: scan backward then conv backward; "
                          "decode: one token per row (conv window update + recurrence step); "
                          "rates: the ALU issue-rate probe")
     args = ap.parse_args()
@@ -372,7 +389,8 @@ def main():
     if not args.no_cpu_baseline and args.path in ("fused", "split"):
         cpu = cpu_baseline(inp, args.cpu_tokens, args.cpu_tokens_all)
     if not args.no_cpu_baseline and args.path == "bwd":
-        cpu = cpu_baseline_bwd(inp, dout_seed=7, tokens_per_row=min(args.cpu_tokens, 4096))
+        # about 15 s of one core: the heads workload (N = 128) costs 8x per token
+        cpu = cpu_baseline_bwd(inp, dout_seed=7, tokens_per_row=min(args.cpu_tokens, 1024 if inp.nheads else 4096))
 
     import torch
 
@@ -398,6 +416,10 @@ def main():
     u = torch.empty_like(t["x"])
     out = torch.empty_like(t["x"])
     fin = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+    if args.no_u and args.path != "fused":
+        print("--no-u applies to the fused path", file=sys.stderr)
+        sys.exit(2)
+    u_arg = None if args.no_u else u
     ws = torch.empty(max(ssm.scan_workspace_bytes(B, L, D, N, H, inp.dtype), 1), dtype=torch.uint8, device=dev)
     fused = args.path == "fused"
 
@@ -406,7 +428,7 @@ def main():
             ev[0].record()
         if fused:
             ssm.conv_scan_fwd(t["x"], t["conv_w"], t["conv_b"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
-                              t["delta_bias"], t["doc_start"], u=u, out=out, final_state=fin, workspace=ws)
+                              t["delta_bias"], t["doc_start"], u=u_arg, out=out, final_state=fin, workspace=ws)
             if ev is not None:
                 ev[1].record()
         else:
@@ -455,7 +477,7 @@ def main():
     probe = copy_probe(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
     csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
     traffic = recorded_traffic(
-        os.path.join(ROOT, "profiles", f"{args.path}_{args.config}_hbm_traffic.txt"),
+        os.path.join(ROOT, "profiles", f"{args.path}{'_no_u' if args.no_u else ''}_{args.config}_hbm_traffic.txt"),
         [os.path.join(csrc, f) for f in FWD_SOURCES])
 
     w = trans_slots()
@@ -506,7 +528,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "batch": B, "seqlen": L, "dim": D, "dstate": N, "nheads": H,
                    "d_conv": 4, "doc_mean_len": spec["docs"], "io_dtype": inp.dtype, "state_dtype": "f32",
-                   "path": args.path, "u_written": True},
+                   "path": args.path, "u_written": not args.no_u},
         "roofline": roof,
         "hbm_roofline_pair": dict(
             {"achieved": pair_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pair_gbs / HBM_PEAK_GBS,
@@ -520,7 +542,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-METRIC_BWD = "conv + selective-scan bwd tokens/s, B=2 L=32K D=1536 N=16 bf16"
+METRIC_BWD = "conv + selective-scan bwd tokens/s"
 
 
 def bench_decode(args, torch, np, ssm, inp, t, spec, dev, tokens=64, graphs_per_run=None):
@@ -650,12 +672,11 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev, cpu=None):
 
     B, L, D = inp.x.shape
     N = inp.B.shape[-1]
-    if inp.nheads:
-        print("the backward pass covers per-channel A workloads only", file=sys.stderr)
-        sys.exit(2)
+    H = inp.nheads
     esz = 2 if inp.dtype == "bf16" else 4
     dout = to_dev(make_cotangent(B, L, D, dtype=inp.dtype, seed=7), inp.dtype, dev)
-    ws = torch.empty(ssm.scan_bwd_workspace_bytes(B, L, D, N, inp.dtype), dtype=torch.uint8, device=dev)
+    ws = torch.empty(ssm.scan_bwd_workspace_bytes(B, L, D, N, inp.dtype, nheads=H), dtype=torch.uint8,
+                     device=dev)
     grads = {}
 
     # u as the forward leaves it (the conv output, stored in the I/O dtype)
@@ -693,13 +714,27 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev, cpu=None):
     probe = copy_probe(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
     csrc = os.path.join(ROOT, "selective_state_space_23_amd", "csrc")
     traffic = recorded_traffic(os.path.join(ROOT, "profiles", f"bwd_{args.config}_hbm_traffic.txt"),
-                               [os.path.join(csrc, f) for f in BWD_SOURCES])
-    w = trans_slots()
-    flops = 2.0 * bwd_alu_slots(B, L, D, N, w)
-    nbytes = bwd_bytes(B, L, D, N, esz)
+                               [os.path.join(csrc, f) for f in (HEADS_BWD_SOURCES if H else BWD_SOURCES)])
+    nbytes = bwd_bytes(B, L, D, N, esz, H)
     cbytes = conv_bwd_bytes(B, L, D, esz)
-    tflops = flops / (call_ms * 1e-3) / 1e12
     gbs = nbytes / (call_ms * 1e-3) / 1e9
+    if H:
+        # products of the chunked form on v_mfma_f32_16x16x4f32: the fp32 matrix peak
+        flops = heads_bwd_mfma_flops(B, L, D, N, H)
+        tflops = flops / (call_ms * 1e-3) / 1e12
+        roofline = {"kernel": "mamba_selective_scan_bwd (scalar-A heads), one call: forward pass, carries, "
+                              "main pass, reductions",
+                    "bound": "mfma", "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tflops / FP32_MFMA_PEAK_TFLOPS, "traffic": traffic, "mfma_dtype": "f32",
+                    "algorithmic_flops": flops}
+    else:
+        flops = 2.0 * bwd_alu_slots(B, L, D, N, trans_slots())
+        tflops = flops / (call_ms * 1e-3) / 1e12
+        roofline = {"kernel": "mamba_selective_scan_bwd, one call: aggregate pass, forward and reverse carries, "
+                              "main pass, reductions",
+                    "bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic, "algorithmic_flop_eq": flops}
+    roofline.update(algorithmic_bytes=nbytes, hbm_achieved_GBs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, avg_ms=call_ms)
     result = {
         "metric": METRIC_BWD,
         "value": B * L / (ms_per_step * 1e-3),
@@ -713,17 +748,12 @@ def bench_bwd(args, torch, np, ssm, inp, t, spec, dev, cpu=None):
         "vs_baseline": None,
         "dtype": "bf16" if inp.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": args.config, "batch": B, "seqlen": L, "dim": D, "dstate": N, "nheads": 0,
+        "config": {"workload": args.config, "batch": B, "seqlen": L, "dim": D, "dstate": N, "nheads": H,
                    "doc_mean_len": spec["docs"], "io_dtype": inp.dtype, "state_dtype": "f32", "path": "bwd"},
         "timings": {"scan_bwd_ms": call_ms, "conv_bwd_ms": conv_ms,
                     "conv_bwd_hbm_GBs": cbytes / (conv_ms * 1e-3) / 1e9,
                     "conv_bwd_hbm_frac": cbytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"kernel": "mamba_selective_scan_bwd, one call: aggregate pass, forward and reverse carries, "
-                               "main pass, reductions",
-                     "bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic, "algorithmic_flop_eq": flops,
-                     "algorithmic_bytes": nbytes, "hbm_achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-                     "avg_ms": call_ms},
+        "roofline": roofline,
         "copy_probe": probe,
     }
     if cpu is not None:

@@ -206,8 +206,11 @@ int mamba_selective_scan_fwd_noalloc(const mamba_scan_dims_t* dims,
  * (x, conv_weight, conv_bias, doc_start, conv_state; apply_silu = 1) followed by
  * mamba_selective_scan_fwd (dims, delta ... final_state, workspace sized by
  * mamba_selective_scan_workspace_bytes) on its output; the conv output is also
- * written to `u` (B, L, D).  With per-channel A the convolution runs inside the
- * scan's first pass, which saves the conv's separate pass over x and u.
+ * written to `u` (B, L, D), or not at all when u is NULL (inference needs only
+ * out).  With per-channel A the convolution runs inside the scan's first pass,
+ * which saves the conv's separate pass over x and u; with u NULL the second pass
+ * forms the conv output again from x instead of reading it back.  Scalar-A
+ * heads require u (MAMBA_ERR_UNSUPPORTED for NULL).
  * conv_state and initial_state act on their own stage each, as in the two
  * separate calls: a continuation passes both; a conv_state alone continues
  * the conv's history while the scan's state starts at zero. */

@@ -236,13 +236,14 @@ def selective_scan_fwd_noalloc(u, delta, A, B, C, out, D=None, z=None, delta_bia
 
 
 def conv_scan_fwd(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, delta_bias=None, doc_start=None,
-                  delta_softplus: bool = True, initial_state=None, conv_state=None, u=None, out=None,
+                  delta_softplus: bool = True, initial_state=None, conv_state=None, u=True, out=None,
                   final_state=True, workspace=None):
     """Conv1d (width 4) + SiLU and the selective scan in one call; see mamba_conv_scan_fwd.
 
     Arguments as causal_conv1d_fwd (x, conv_weight, conv_bias, doc_start,
-    conv_state) and selective_scan_fwd (the rest).  ``u``: optional (B, L, D)
-    tensor that receives the conv output.  Returns (u, out, final_state or None)."""
+    conv_state) and selective_scan_fwd (the rest).  ``u``: a (B, L, D) tensor that
+    receives the conv output, True (allocate one) or None (the conv output is not
+    written).  Returns (u or None, out, final_state or None)."""
     torch = _torch()
     dev = _check_device(x)
     if x.dim() != 3:
@@ -255,8 +256,10 @@ def conv_scan_fwd(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, del
     nd = nheads if nheads else Dm
     if doc_start is not None and doc_start.dtype == torch.bool:
         doc_start = doc_start.to(torch.uint8)
-    if u is None:
+    if u is True:
         u = torch.empty_like(x)
+    elif u is False:
+        u = None
     if out is None:
         out = torch.empty_like(x)
     if final_state is True:

@@ -207,7 +207,8 @@ hipError_t launch_bwd_layout(mamba::ScanBwdArgs a, const BwdLayout& w) {
 // points); fills `a` on success.
 int check_conv(const void* x, const float* weight, const float* bias, const uint8_t* doc_start,
                const void* conv_state, void* out, int64_t batch, int64_t seqlen, int64_t dim, int32_t width,
-               int32_t dtype, int32_t apply_silu, void* stream, mamba::ConvArgs* a, bool* empty) {
+               int32_t dtype, int32_t apply_silu, void* stream, mamba::ConvArgs* a, bool* empty,
+               bool out_optional = false) {
     *empty = false;
     if (batch < 0 || seqlen < 0 || dim < 0) return MAMBA_ERR_INVALID_ARGUMENT;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARGUMENT;
@@ -219,9 +220,9 @@ int check_conv(const void* x, const float* weight, const float* bias, const uint
         *empty = true;
         return MAMBA_OK;
     }
-    if (!x || !weight || !out) return MAMBA_ERR_INVALID_ARGUMENT;
+    if (!x || !weight || (!out && !out_optional)) return MAMBA_ERR_INVALID_ARGUMENT;
     const size_t esz = dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
-    if (!aligned(x, esz) || !aligned(out, esz) || !aligned(weight, 4) || (bias && !aligned(bias, 4)) ||
+    if (!aligned(x, esz) || (out && !aligned(out, esz)) || !aligned(weight, 4) || (bias && !aligned(bias, 4)) ||
         (conv_state && !aligned(conv_state, esz)))
         return MAMBA_ERR_MISALIGNED;
     const size_t bytes = static_cast<size_t>(n) * esz;
@@ -236,7 +237,7 @@ int check_conv(const void* x, const float* weight, const float* bias, const uint
     a->batch = batch; a->seqlen = seqlen; a->dim = dim;
     a->bf16 = dtype == MAMBA_DTYPE_BF16;
     const int64_t vec = a->bf16 ? 8 : 4;
-    a->vectorized = (dim % vec) == 0 && aligned(x, 16) && aligned(out, 16);
+    a->vectorized = (dim % vec) == 0 && aligned(x, 16) && (!out || aligned(out, 16));
     a->apply_silu = apply_silu != 0;
     a->stream = static_cast<hipStream_t>(stream);
     return MAMBA_OK;
@@ -244,14 +245,15 @@ int check_conv(const void* x, const float* weight, const float* bias, const uint
 
 // Checks of one selective-scan call (shared by the scan and the fused conv + scan
 // entry points); fills `a` on success.  For the fused call (nextra > 0) u is
-// written too, and `extra` lists its further read-only inputs (conv input,
-// weights, history; byte sizes in extra_sz): neither may overlap what else the
-// call reads or writes.
+// written too unless u_written is false (then `u` is the conv input, read only),
+// and `extra` lists its further read-only inputs (conv input, weights, history;
+// byte sizes in extra_sz): neither may overlap what else the call reads or
+// writes.
 int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, const float* A, const void* B,
                const void* C, const float* D, const void* z, const float* delta_bias, const uint8_t* doc_start,
                const float* initial_state, void* out, float* final_state, void* workspace, size_t workspace_bytes,
                void* stream, const void* const* extra, const size_t* extra_sz, int nextra, mamba::ScanArgs* a,
-               FwdLayout* lay, bool* empty, bool own_scratch = false) {
+               FwdLayout* lay, bool* empty, bool own_scratch = false, bool u_written = true) {
     *empty = false;
     const int st = check_dims(dims);
     if (st != MAMBA_OK) return st;
@@ -293,7 +295,7 @@ int check_scan(const mamba_scan_dims_t* dims, const void* u, const void* delta, 
     }
     if (overlap(out, act, final_state, fsb)) return MAMBA_ERR_INVALID_ARGUMENT;
     if (nextra > 0) {
-        for (int i = 1; i < kIns; ++i)           // u is written: it may not overlap the scan's inputs
+        for (int i = 1; i < kIns && u_written; ++i)   // u is written: it may not overlap the scan's inputs
             if (overlap(ins[i], insz[i], u, act)) return MAMBA_ERR_INVALID_ARGUMENT;
         for (int i = 0; i < nextra; ++i)
             if (overlap(extra[i], extra_sz[i], out, act) || overlap(extra[i], extra_sz[i], final_state, fsb))
@@ -431,10 +433,12 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
     if (sd != MAMBA_OK) return sd;
     mamba::ConvArgs ca;
     bool empty;
+    const bool has_u = u != nullptr;        // NULL: the conv output is not written
     int st = check_conv(x, conv_weight, conv_bias, doc_start, conv_state, u, dims->batch, dims->seqlen, dims->dim, 4,
-                        dims->dtype, 1, stream, &ca, &empty);
+                        dims->dtype, 1, stream, &ca, &empty, true);
     if (st != MAMBA_OK) return st;
     if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
+    if (!has_u && dims->nheads > 0) return MAMBA_ERR_UNSUPPORTED;
     // u is written by the conv and read by the scan: it may overlap nothing else.
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
     const size_t act = static_cast<size_t>(dims->batch * dims->seqlen * dims->dim) * esz;
@@ -443,12 +447,13 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
                               static_cast<size_t>(dims->batch * dims->dim * 3) * esz};
     mamba::ScanArgs a;
     FwdLayout lay;
-    st = check_scan(dims, u, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out, final_state, workspace,
-                    workspace_bytes, stream, conv_in, conv_sz, 4, &a, &lay, &empty);
+    st = check_scan(dims, has_u ? u : x, delta, A, B, C, D, z, delta_bias, doc_start, initial_state, out, final_state,
+                    workspace, workspace_bytes, stream, conv_in, conv_sz, 4, &a, &lay, &empty, false, has_u);
     if (st != MAMBA_OK) return st;
     if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
     if (dims->nheads == 0) {
         a.conv_x = x; a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state;
+        a.u = u;                    // the conv output's destination, or NULL
         return launch_scan_layout(a, lay) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
     }
     if (mamba::launch_causal_conv1d(ca) != hipSuccess) return MAMBA_ERR_HIP;

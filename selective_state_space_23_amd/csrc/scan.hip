@@ -52,6 +52,10 @@ constexpr int kScanBlock = 256;    // 4 independent waves, 256 consecutive chann
 #endif
 constexpr int kGroup = MAMBA_SCAN_GROUP;   // tokens whose activations are fetched together
 constexpr int kNoStore = 0x7fffff00;       // buffer offset past any resource: the access is dropped
+// The fused conv of the per-channel scan (template argument CONV).
+constexpr int kConvNone = 0;               // the activations loaded are u
+constexpr int kConvStoreU = 1;             // loaded x, u formed and stored (pass 1)
+constexpr int kConvNoStore = 2;            // loaded x, u formed, not stored
 
 struct ScanKParams {
     const void* u;
@@ -140,20 +144,23 @@ __device__ __forceinline__ void buf_store_s(__amdgpu_buffer_rsrc_t rs, int lane_
 //     so no loaded register is ever copied (a copy would wait on the load);
 //   - addresses are a wave-uniform 64-bit row base plus a 32-bit element offset.
 //
-// CONV (pass 1 only): the activations loaded are the conv input x, and each lane
-// forms u = SiLU(bias + w . (x[t-3], x[t-2], x[t-1], x[t])) itself from a 3-token
-// history in registers (cleared at document starts, primed from the tokens
-// before the chunk), stores u (rounded to T) for pass 3 and scans with it.  The
+// CONV (per-channel A): the activations loaded are the conv input x, and each
+// lane forms u = SiLU(bias + w . (x[t-3], x[t-2], x[t-1], x[t])) itself from a
+// 3-token history in registers (cleared at document starts, primed from the
+// tokens before the chunk), rounded to T, and scans with it.  kConvStoreU (pass
+// 1): u is also stored, for pass 3 and the caller.  kConvNoStore: not stored
+// (the caller asked for no u); pass 3 then forms u again the same way.  The
 // arithmetic and its order are those of the standalone conv kernel, so u is
-// bitwise the same.
+// bitwise the same in every pass.
 //
 // DTWS (per-channel A): pass 1 stores dt (rounded to T) in the workspace and
 // pass 3 reads it back instead of recomputing the softplus; without it pass 3
 // recomputes dt from delta and the workspace holds the carries only.
-template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS, bool CONV, bool DTWS>
+template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, bool SOFTPLUS, int CONV, bool DTWS>
 __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMBA_SCAN_WAVES_PER_EU))) void scan_chunk_kernel(
     const ScanKParams p) {
-    static_assert(!CONV || (!OUTPUT && !HEADS), "the conv runs in the aggregate pass of the per-channel scan");
+    static_assert(CONV == kConvNone || !HEADS, "the conv is fused for per-channel A");
+    static_assert(!(OUTPUT && CONV == kConvStoreU), "u is stored by pass 1");
     static_assert(!(HEADS && DTWS), "step sizes are handed over for per-channel A only");
     constexpr int G = kGroup;
     constexpr int kWin = 64;                                   // tokens per staged window
@@ -181,9 +188,9 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     constexpr int kEsz = static_cast<int>(sizeof(T));
     const int64_t act_row = L * p.dim;
     const __amdgpu_buffer_rsrc_t u_rs =
-        make_rsrc(static_cast<const T*>(CONV ? p.conv_x : p.u) + b * act_row, act_row * kEsz);
+        make_rsrc(static_cast<const T*>(CONV != kConvNone ? p.conv_x : p.u) + b * act_row, act_row * kEsz);
     const __amdgpu_buffer_rsrc_t uo_rs =
-        make_rsrc(static_cast<T*>(CONV ? p.u_out : p.out) + b * act_row, act_row * kEsz);
+        make_rsrc(static_cast<T*>(CONV == kConvStoreU ? p.u_out : p.out) + b * act_row, act_row * kEsz);
     // With the hand-off both passes use the same rounded dt.
     constexpr bool kDtWs = DTWS;
     const __amdgpu_buffer_rsrc_t dl_rs =
@@ -191,7 +198,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     const __amdgpu_buffer_rsrc_t dto_rs =
         make_rsrc(static_cast<T*>(kDtWs ? p.dt_ws : p.out) + b * act_row, kDtWs ? act_row * kEsz : 0);
     const __amdgpu_buffer_rsrc_t z_rs =
-        make_rsrc(HAS_Z ? static_cast<const T*>(p.z) + b * act_row : static_cast<const T*>(p.u), act_row * kEsz);
+        make_rsrc(static_cast<const T*>(HAS_Z ? p.z : (CONV != kConvNone ? p.conv_x : p.u)) + b * act_row,
+                  HAS_Z ? act_row * kEsz : 0);
     const T* B_row = static_cast<const T*>(p.B) + b * L * N;
     const T* C_row = static_cast<const T*>(p.C) + b * L * N;
     const uint8_t* ds_row = p.doc_start ? p.doc_start + b * L : nullptr;
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     // Token 0 continues the conv history although the scan restarts there: a
     // conv_state without an initial_state.
     bool conv_keep0 = false;
-    if constexpr (CONV) {
+    if constexpr (CONV != kConvNone) {
         conv_keep0 = p.conv_state != nullptr && !(ds_row != nullptr && ds_row[0] != 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) cw[j] = p.conv_w[static_cast<int64_t>(dc) * 4 + j];
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     // value its clamped channel's own lane writes) with the token in the scalar
     // offset.  REC (always, in pass 3): the group runs the recurrence; pass 1's
     // groups before rec_from only form u and dt.
-    auto compute_group = [&](auto fast_tag, auto rec_tag, int64_t g0, const float (&cu)[G], const float (&cd)[G],
+    auto compute_group = [&](auto fast_tag, auto rec_tag, int64_t g0, float (&cu)[G], const float (&cd)[G],
                              const float (&cz)[G]) {
         constexpr bool FAST = decltype(fast_tag)::value;
         constexpr bool REC = OUTPUT || decltype(rec_tag)::value;
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 sum_dt = (reset ? 0.0f : sum_dt) + dt;
             }
             float uk = cu[k];
-            if constexpr (CONV) {
+            if constexpr (CONV != kConvNone) {
                 const float xt = cu[k];
                 const bool creset = reset && !(t == 0 && conv_keep0);
                 xh1 = creset ? 0.0f : xh1;
@@ -376,17 +384,20 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 acc = __builtin_fmaf(cw[1], xh2, acc);
                 acc = __builtin_fmaf(cw[0], xh3, acc);
                 uk = silu_f(acc);
-                if constexpr (sizeof(T) == 2) uk = bf16_to_f32(f32_to_bf16(uk));   // the u pass 3 reads back
+                if constexpr (sizeof(T) == 2) uk = bf16_to_f32(f32_to_bf16(uk));   // u as stored
                 // Branchless: a store past the resource's end is dropped by the
                 // hardware, and a branch here would double the register footprint.
-                if constexpr (FAST) buf_store_s<T>(uo_rs, dc * kEsz, static_cast<int>(t) * p.dim * kEsz, uk);
-                else buf_store<T>(uo_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, uk);
+                if constexpr (CONV == kConvStoreU) {
+                    if constexpr (FAST) buf_store_s<T>(uo_rs, dc * kEsz, static_cast<int>(t) * p.dim * kEsz, uk);
+                    else buf_store<T>(uo_rs, (active && valid) ? (static_cast<int>(t) * p.dim + d) * kEsz : kNoStore, uk);
+                }
                 xh3 = xh2;
                 xh2 = xh1;
                 xh1 = xt;
             }
             dtk[k] = dt;
             wk[k] = dt * uk;
+            if constexpr (CONV != kConvNone) cu[k] = uk;     // x is not needed past this point
         }
         if constexpr (!REC) return;
         // Phase 2: the recurrence, token by token.
@@ -457,7 +468,7 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             __syncthreads();
         }
         const int64_t wend = (w0 + kWin < t_end) ? w0 + kWin : t_end;
-        auto run_group = [&](int64_t g0, const float (&cu)[G], const float (&cd)[G], const float (&cz)[G]) {
+        auto run_group = [&](int64_t g0, float (&cu)[G], const float (&cd)[G], const float (&cz)[G]) {
             const int off = static_cast<int>((g0 - t_begin) & (kWin - 1));
             const bool fast = g0 + G <= t_end && ((starts >> off) & ((1ull << G) - 1)) == 0;
             if (!OUTPUT && g0 + G <= rec_from) {
@@ -543,6 +554,16 @@ size_t dt_ws_offset(int64_t batch, int64_t dim, int64_t dstate, const ScanPlan& 
     return (carries + 255) / 256 * 256;
 }
 
+template <typename T, int N, bool HEADS, bool OUTPUT, bool HAS_Z, int CONV, bool DTWS>
+void launch_pass(const ScanKParams& p, bool softplus, dim3 grid, hipStream_t stream) {
+    if (softplus)
+        hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, OUTPUT, HAS_Z, true, CONV, DTWS>), grid, dim3(kScanBlock), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, OUTPUT, HAS_Z, false, CONV, DTWS>), grid, dim3(kScanBlock), 0,
+                           stream, p);
+}
+
 template <typename T, int N, bool HEADS, bool DTWS>
 hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     ScanKParams p;
@@ -567,34 +588,23 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
 
     const unsigned gx = static_cast<unsigned>((a.dim + kScanBlock - 1) / kScanBlock);
     const dim3 gall(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
+    // Without a u output the conv is formed in both passes, else pass 3 reads u.
+    const bool store_u = p.u_out != nullptr;
     // Pass 1 runs on every chunk when it also produces something the last chunk
     // needs (u of the fused conv, the handed-over step sizes); otherwise on every
     // chunk but the last.
-    const bool pass1_all = a.conv_x != nullptr || DTWS;
+    const bool pass1_all = (a.conv_x != nullptr && store_u) || DTWS;
     if (pass1_all || nslots > 0) {
         const dim3 g1 = pass1_all ? gall : dim3(gx, static_cast<unsigned>(nslots), static_cast<unsigned>(a.batch));
         if constexpr (!HEADS) {
-            if (a.conv_x != nullptr) {
-                if (a.softplus)
-                    hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, true, true, DTWS>), g1,
-                                       dim3(kScanBlock), 0, a.stream, p);
-                else
-                    hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, false, true, DTWS>), g1,
-                                       dim3(kScanBlock), 0, a.stream, p);
-            } else if (a.softplus) {
-                hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, true, false, DTWS>), g1,
-                                   dim3(kScanBlock), 0, a.stream, p);
-            } else {
-                hipLaunchKernelGGL((scan_chunk_kernel<T, N, false, false, false, false, false, DTWS>), g1,
-                                   dim3(kScanBlock), 0, a.stream, p);
-            }
-        } else {
-            if (a.softplus)
-                hipLaunchKernelGGL((scan_chunk_kernel<T, N, true, false, false, true, false, false>), g1,
-                                   dim3(kScanBlock), 0, a.stream, p);
+            if (a.conv_x != nullptr && store_u)
+                launch_pass<T, N, false, false, false, kConvStoreU, DTWS>(p, a.softplus, g1, a.stream);
+            else if (a.conv_x != nullptr)
+                launch_pass<T, N, false, false, false, kConvNoStore, DTWS>(p, a.softplus, g1, a.stream);
             else
-                hipLaunchKernelGGL((scan_chunk_kernel<T, N, true, false, false, false, false, false>), g1,
-                                   dim3(kScanBlock), 0, a.stream, p);
+                launch_pass<T, N, false, false, false, kConvNone, DTWS>(p, a.softplus, g1, a.stream);
+        } else {
+            launch_pass<T, N, true, false, false, kConvNone, false>(p, a.softplus, g1, a.stream);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -606,20 +616,14 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    constexpr int kConv3 = HEADS ? kConvNone : kConvNoStore;
+    const bool conv3 = !HEADS && a.conv_x != nullptr && !store_u;
     if (a.z) {
-        if (a.softplus)
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, true, true, false, DTWS>), gall, dim3(kScanBlock),
-                               0, a.stream, p);
-        else
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, true, false, false, DTWS>), gall,
-                               dim3(kScanBlock), 0, a.stream, p);
+        if (conv3) launch_pass<T, N, HEADS, true, true, kConv3, DTWS>(p, a.softplus, gall, a.stream);
+        else launch_pass<T, N, HEADS, true, true, kConvNone, DTWS>(p, a.softplus, gall, a.stream);
     } else {
-        if (a.softplus)
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, false, true, false, DTWS>), gall,
-                               dim3(kScanBlock), 0, a.stream, p);
-        else
-            hipLaunchKernelGGL((scan_chunk_kernel<T, N, HEADS, true, false, false, false, DTWS>), gall,
-                               dim3(kScanBlock), 0, a.stream, p);
+        if (conv3) launch_pass<T, N, HEADS, true, false, kConv3, DTWS>(p, a.softplus, gall, a.stream);
+        else launch_pass<T, N, HEADS, true, false, kConvNone, DTWS>(p, a.softplus, gall, a.stream);
     }
     return hipGetLastError();
 }

@@ -1,0 +1,99 @@
+"""The fused conv + scan call without a u output (u = NULL): pass 1 forms the
+conv output without storing it and the output pass forms it again from x with
+the same arithmetic, so out and final_state must equal, bit for bit, those of
+the call that writes u (and match the fp64 oracle)."""
+
+import numpy as np
+import pytest
+
+from workloads import bf16_round, make_custom, make_inputs
+
+from gpu_helpers import assert_close, oracle_pipeline, to_dev, to_host, torch_mod, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (they fail instead of skipping)")
+    import selective_state_space_23_amd as mod
+    mod._lib.load()
+    return mod
+
+
+def fused(ssm, dev, **kw):
+    return ssm.conv_scan_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["delta"], dev["A"], dev["B"], dev["C"],
+                             dev["D"], dev["z"], dev["delta_bias"], dev["doc_start"], **kw)
+
+
+CASES = [
+    # (batch, seqlen, dim, dstate, dtype, docs)
+    (2, 1000, 100, 16, "bf16", 150.0),      # ragged D, several chunks
+    (1, 500, 72, 4, "f32", 60.0),
+    (2, 333, 64, 5, "bf16", 40.0),          # N padded to 8
+    (3, 50, 64, 16, "bf16", 9.0),           # one chunk: no carry pass
+    (2, 700, 96, 12, "f32", 3.0),           # a document start every few tokens
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_no_u_equals_u_written(ssm, case):
+    torch = torch_mod()
+    Bt, L, Dm, N, dt, docs = case
+    inp = make_custom(Bt, L, Dm, N, dtype=dt, docs=docs, seed=900 + L + N)
+    inp.conv_b[:] = np.linspace(-0.3, 0.3, Dm).astype(np.float32)
+    print(f"[no-u] {case}", flush=True)
+    dev = upload(inp)
+    u, out, fin = fused(ssm, dev)
+    none, out2, fin2 = fused(ssm, dev, u=None)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(out, out2), "out differs when u is not written"
+    assert torch.equal(fin, fin2), "final_state differs when u is not written"
+    _, out_ref, fin_ref = oracle_pipeline(inp, np.arange(Dm))
+    assert_close(to_host(out2), out_ref, dt, f"no-u out {case}")
+    assert_close(to_host(fin2), fin_ref, dt, f"no-u final_state {case}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_no_u_with_histories(ssm, dt):
+    """A conv history with and without a scan state: the output pass primes its
+    conv from conv_state exactly as pass 1 does."""
+    torch = torch_mod()
+    L, Dm, N = 900, 128, 16
+    inp = make_custom(2, L, Dm, N, dtype=dt, docs=200.0, seed=950)
+    inp.doc_start[:, 0] = 0
+    inp.doc_start[1, 0] = 1
+    dev = upload(inp)
+    rng = np.random.default_rng(951)
+    win = rng.standard_normal((2, Dm, 3)).astype(np.float32)
+    window = to_dev(win if dt == "f32" else bf16_round(win), dt)
+    init = torch.from_numpy((0.3 * rng.standard_normal((2, Dm, N))).astype(np.float32)).cuda()
+    print(f"[no-u] histories {dt}", flush=True)
+    for kw in ({"conv_state": window}, {"conv_state": window, "initial_state": init}):
+        _, out, fin = fused(ssm, dev, **kw)
+        _, out2, fin2 = fused(ssm, dev, u=None, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2) and torch.equal(fin, fin2), f"no-u differs with {sorted(kw)}"
+
+
+def test_no_u_workload(ssm):
+    """The 2 x 32768 x 1536, N = 16 bf16 workload in the launch configuration the
+    benchmark times."""
+    torch = torch_mod()
+    inp = make_inputs("packed_32k")
+    print("[no-u] packed_32k", flush=True)
+    dev = upload(inp)
+    _, out, fin = fused(ssm, dev)
+    _, out2, fin2 = fused(ssm, dev, u=None)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(fin, fin2)
+    ch = np.array([0, 63, 700, 1535])
+    idx = torch.from_numpy(ch).to(out2.device)
+    got_out, got_fin = to_host(out2.index_select(2, idx)), to_host(fin2.index_select(1, idx))
+    del dev, out, fin, out2, fin2
+    _, out_ref, fin_ref = oracle_pipeline(inp, ch)
+    assert_close(got_out, out_ref, "bf16", "packed_32k no-u out")
+    assert_close(got_fin, fin_ref, "bf16", "packed_32k no-u final_state")
