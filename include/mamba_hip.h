@@ -209,8 +209,11 @@ int mamba_selective_scan_fwd_noalloc(const mamba_scan_dims_t* dims,
  * written to `u` (B, L, D), or not at all when u is NULL (inference needs only
  * out).  With per-channel A the convolution runs inside the scan's first pass,
  * which saves the conv's separate pass over x and u; with u NULL the second pass
- * forms the conv output again from x instead of reading it back.  Scalar-A
- * heads require u (MAMBA_ERR_UNSUPPORTED for NULL).
+ * forms the conv output again from x instead of reading it back.  With bf16
+ * scalar-A heads the conv runs first and the scan reads u, or, with u NULL,
+ * both passes of the scan form it from x (x then 16-byte aligned, else
+ * MAMBA_ERR_MISALIGNED).  fp32 scalar-A heads require u (MAMBA_ERR_UNSUPPORTED
+ * for NULL).
  * conv_state and initial_state act on their own stage each, as in the two
  * separate calls: a continuation passes both; a conv_state alone continues
  * the conv's history while the scan's state starts at zero. */

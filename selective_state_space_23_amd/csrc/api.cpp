@@ -438,7 +438,15 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
                         dims->dtype, 1, stream, &ca, &empty, true);
     if (st != MAMBA_OK) return st;
     if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
-    if (!has_u && dims->nheads > 0) return MAMBA_ERR_UNSUPPORTED;
+    // Per-channel A: the conv runs inside the scan's first pass.  bf16 scalar-A
+    // heads: the conv kernel writes u first (faster than forming u in the
+    // matrix-form passes), unless there is no u; then both passes form it.  The
+    // fp32 recurrent form of heads always runs the conv kernel first: it needs u.
+    const bool heads_bf16 = dims->nheads > 0 && dims->dtype == MAMBA_DTYPE_BF16;
+    const bool fused_conv = dims->nheads == 0 || (heads_bf16 && !has_u);
+    if (!has_u && !fused_conv) return MAMBA_ERR_UNSUPPORTED;
+    // The bf16 heads scan reads its conv input in 16-byte vectors, as it reads u.
+    if (heads_bf16 && !has_u && !aligned(x, 16)) return MAMBA_ERR_MISALIGNED;
     // u is written by the conv and read by the scan: it may overlap nothing else.
     const size_t esz = dims->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
     const size_t act = static_cast<size_t>(dims->batch * dims->seqlen * dims->dim) * esz;
@@ -451,7 +459,7 @@ int mamba_conv_scan_fwd(const mamba_scan_dims_t* dims, const void* x, const floa
                     workspace, workspace_bytes, stream, conv_in, conv_sz, 4, &a, &lay, &empty, false, has_u);
     if (st != MAMBA_OK) return st;
     if (empty) return empty_scan_outputs(dims, initial_state, final_state, stream);
-    if (dims->nheads == 0) {
+    if (fused_conv) {
         a.conv_x = x; a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state;
         a.u = u;                    // the conv output's destination, or NULL
         return launch_scan_layout(a, lay) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;

@@ -56,6 +56,12 @@ constexpr int kThreads = 64 * kWaves;
 #endif
 constexpr int64_t kTargetBlocks = MAMBA_SSD_TARGET_BLOCKS;  // workgroups per pass
 constexpr int kXcds = 8;
+// The fused conv (template argument CONV): used when the caller wants no u.  With
+// u wanted, the conv kernel writes it first: forming u in the aggregate pass
+// costs that latency-bound pass more than the conv kernel's own pass over x and
+// u (549 against 520 us per call on 2 x 32768 tokens, 24 heads, N = 128).
+constexpr int kConvNone = 0;            // the activations loaded are u
+constexpr int kConvForm = 1;            // loaded x; u formed (not stored)
 #ifndef MAMBA_SSD_WAVES_PER_EU
 #define MAMBA_SSD_WAVES_PER_EU 2        // up to 256 VGPRs: one 8-wave workgroup per CU
 #endif
@@ -73,6 +79,10 @@ struct SsdParams {
     const float* initial_state;   // (B, D, N) or null: state before token 0
     uint16_t* out;
     float* final_state;
+    const uint16_t* conv_x;       // fused conv: its input x (B, L, D), or null (u is given)
+    const float* conv_w;          // (D, 4)
+    const float* conv_b;          // (D,) or null
+    const uint16_t* conv_state;   // (B, D, 3) or null: x of the three tokens before token 0
     float* ws_H;        // [B*H][nseg-1][P][N]: segment end states, then carries
     float* ws_G;        // [B*H][nseg-1]: segment decays
     int64_t seqlen;
@@ -157,10 +167,11 @@ struct SsdLds {
     static constexpr int oM = oXT + 2 * P * SQ * 2;                 // M [t][s]
     static constexpr int oHT = oM + (OUTPUT ? kQ * SQ * 2 : 0);     // chunk-entry state^T [p][n]
     static constexpr int oTok = oHT + (OUTPUT ? P * SN * 2 : 0);    // 2 x per-token scalars
-    static constexpr int kBytes = oTok + 2 * 5 * kQ * 4;
+    static constexpr int oCw = oTok + 2 * 5 * kQ * 4;               // fused conv: taps [P][4], bias [P]
+    static constexpr int kBytes = oCw + P * 5 * 4;
 };
 
-template <int NP, int P, bool OUTPUT, bool HAS_Z, bool SOFTPLUS>
+template <int NP, int P, bool OUTPUT, bool HAS_Z, bool SOFTPLUS, int CONV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_SSD_WAVES_PER_EU))) void ssd_chunk_kernel(
     const SsdParams p) {
     using Lay = SsdLds<NP, P, OUTPUT>;
@@ -244,6 +255,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
     float Dp[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) Dp[e] = (OUTPUT && p.D) ? p.D[h * P + x_p0 + e] : 0.0f;
+    // Fused conv: the taps and bias of the head's channels, in LDS (read per chunk:
+    // 40 registers per lane would halve the aggregate pass's occupancy).
+    float* sCw = reinterpret_cast<float*>(lds + Lay::oCw);
+    float* sCb = sCw + 4 * P;
+    if constexpr (CONV != kConvNone) {
+        if (tid < 4 * P) sCw[tid] = p.conv_w[static_cast<int64_t>(h) * P * 4 + tid];
+        if (tid < P) sCb[tid] = p.conv_b ? p.conv_b[h * P + tid] : 0.0f;
+        lds_barrier();
+    }
 
     // Global data of one chunk, held in registers one chunk ahead so that its
     // loads overlap the current chunk's work.  Every load is unconditional (token
@@ -251,14 +271,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
     // meet a zero step size, and padded states are zeroed when consumed.
     u32x4_t pb_[kBV], pc_[kKB], px_, pz_;
     uint32_t pdelta = 0, pflag = 0;
+    // Fused conv: x of the three tokens before this lane's token (row offsets 1..3)
+    // and doc_start of the token and the two before it.
+    constexpr int kCH = CONV != kConvNone ? 3 : 1;
+    u32x4_t ph_[kCH];
+    uint32_t pf_[kCH];
     // Buffer resources per row: wave-uniform base and size in SGPRs, 32-bit byte
     // offsets per lane (a row of any tensor is below 2 GiB, checked on the host).
     // A load past a resource's end returns zeros.
     const int64_t arow = L * p.dim;
     const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Brow, L * N * 2);
     const __amdgpu_buffer_rsrc_t rsC = make_rsrc(Crow, L * N * 2);
-    const __amdgpu_buffer_rsrc_t rsU = make_rsrc(p.u + b * arow, arow * 2);
-    const __amdgpu_buffer_rsrc_t rsZ = make_rsrc(HAS_Z ? p.z + b * arow : p.u, arow * 2);
+    const __amdgpu_buffer_rsrc_t rsU = make_rsrc((CONV != kConvNone ? p.conv_x : p.u) + b * arow, arow * 2);
+    const __amdgpu_buffer_rsrc_t rsZ = make_rsrc(HAS_Z ? p.z + b * arow : nullptr, HAS_Z ? arow * 2 : 0);
     const __amdgpu_buffer_rsrc_t rsDl = make_rsrc(p.delta + b * L * p.nheads, L * p.nheads * 2);
     const __amdgpu_buffer_rsrc_t rsDs = make_rsrc(p.doc_start ? p.doc_start + b * L : nullptr, p.doc_start ? L : 0);
     const int xcol = h * P + x_p0;
@@ -279,6 +304,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
         }
         const int xoff = ((c0i + x_row) * p.dim + xcol) * 2;
         px_ = load16(rsU, xoff);
+        if constexpr (CONV != kConvNone) {
+            // Rows before the row start give negative offsets: past the resource
+            // (as unsigned), so they load zeros, as do flags past the row.
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                ph_[k] = load16(rsU, xoff - (k + 1) * p.dim * 2);
+                pf_[k] = __builtin_amdgcn_raw_buffer_load_b8(rsDs, c0i + x_row - k, 0, 0);
+            }
+        }
         if (OUTPUT && HAS_Z) pz_ = load16(rsZ, xoff);
         if (wave == 0) {
             pdelta = __builtin_amdgcn_raw_buffer_load_b16(rsDl, ((c0i + lane) * p.nheads + h) * 2, 0, 0);
@@ -301,8 +335,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
         float* sScale = sW + kQ;
         int* sSeg = reinterpret_cast<int*>(sScale + kQ);
         float* sYw = reinterpret_cast<float*>(sB) + wave * 16 * SY;   // this wave's output tile (over B rows)
-        // ---- 1. take the prefetched chunk: B rows to LDS, x transposed to LDS,
-        //         per-token scalars, this wave's C fragments, the gate
+        // ---- 1. take the prefetched chunk: u (formed by the fused conv), B rows to
+        //         LDS, u transposed to LDS, per-token scalars, this wave's C
+        //         fragments, the gate
+        u32x4_t cx = px_, cz = kZero;
+        pin(cx);
+        if constexpr (CONV != kConvNone) {
+            u32x4_t hx[3];
+            uint32_t fl[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                hx[k] = ph_[k];
+                fl[k] = pf_[k];
+                pin(hx[k]);
+                pin(fl[k]);
+            }
+            if (p.conv_state != nullptr && t0 + x_row < 3) {
+                // the given history before token 0: (B, D, 3), oldest first
+                const uint16_t* cs = p.conv_state + (static_cast<int64_t>(b) * p.dim + h * P + x_p0) * 3;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    const int r = static_cast<int>(t0) + x_row - (k + 1);
+                    if (r < 0) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            hx[k][j] = static_cast<uint32_t>(cs[(2 * j) * 3 + 3 + r]) |
+                                       (static_cast<uint32_t>(cs[(2 * j + 1) * 3 + 3 + r]) << 16);
+                    }
+                }
+            }
+            // A document start at the token (or one or two before it) cuts the taps
+            // that reach past it: they read zero, as in the conv kernel.
+            const bool c1 = fl[0] == 0, c2 = c1 && fl[1] == 0, c3 = c2 && fl[2] == 0;
+            const float4 cb0 = *reinterpret_cast<const float4*>(sCb + x_p0);
+            const float4 cb1 = *reinterpret_cast<const float4*>(sCb + x_p0 + 4);
+            const float cbias[8] = {cb0.x, cb0.y, cb0.z, cb0.w, cb1.x, cb1.y, cb1.z, cb1.w};
+            uint32_t uo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float uv[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int e = 2 * j + q;
+                    const float4 w = *reinterpret_cast<const float4*>(sCw + (x_p0 + e) * 4);
+                    auto el = [&](uint32_t v) { return q == 0 ? lo_bf16(v) : hi_bf16(v); };
+                    const float h1 = c1 ? el(hx[0][j]) : 0.0f;
+                    const float h2 = c2 ? el(hx[1][j]) : 0.0f;
+                    const float h3 = c3 ? el(hx[2][j]) : 0.0f;
+                    float acc = __builtin_fmaf(w.w, el(cx[j]), cbias[e]);
+                    acc = __builtin_fmaf(w.z, h1, acc);
+                    acc = __builtin_fmaf(w.y, h2, acc);
+                    acc = __builtin_fmaf(w.x, h3, acc);
+                    uv[q] = silu_f(acc);
+                }
+                uo[j] = pack2(uv[0], uv[1]);
+            }
+            cx = u32x4_t{uo[0], uo[1], uo[2], uo[3]};
+        }
 #pragma unroll
         for (int k = 0; k < kBV; ++k) {
             const int i = tid + kThreads * k;
@@ -319,8 +408,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
                 pin(cf[kb]);
             }
         }
-        u32x4_t cx = px_, cz = kZero;
-        pin(cx);
         if constexpr (OUTPUT && HAS_Z) {
             cz = pz_;
             pin(cz);
@@ -553,12 +640,14 @@ SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int nheads) {
     return s;
 }
 
-template <int NP, int P, bool OUTPUT, bool HAS_Z>
+template <int NP, int P, bool OUTPUT, bool HAS_Z, int CONV>
 void launch_chunk(const SsdParams& p, bool softplus, unsigned blocks, hipStream_t stream) {
     if (softplus)
-        hipLaunchKernelGGL((ssd_chunk_kernel<NP, P, OUTPUT, HAS_Z, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((ssd_chunk_kernel<NP, P, OUTPUT, HAS_Z, true, CONV>), dim3(blocks), dim3(kThreads), 0, stream,
+                           p);
     else
-        hipLaunchKernelGGL((ssd_chunk_kernel<NP, P, OUTPUT, HAS_Z, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((ssd_chunk_kernel<NP, P, OUTPUT, HAS_Z, false, CONV>), dim3(blocks), dim3(kThreads), 0,
+                           stream, p);
 }
 
 template <int NP, int P>
@@ -588,10 +677,17 @@ hipError_t launch_ssd_typed(const ScanArgs& a, const SsdPlan& plan) {
     p.dstate = static_cast<int>(a.dstate);
     p.nseg = plan.nseg;
     p.nbatch = static_cast<int>(a.batch);
+    // Fused conv (no u output): both passes form u from x.
+    const bool conv = a.conv_x != nullptr;
+    p.conv_x = static_cast<const uint16_t*>(a.conv_x);
+    p.conv_w = a.conv_w;
+    p.conv_b = a.conv_b;
+    p.conv_state = static_cast<const uint16_t*>(a.conv_state);
 
     const unsigned blocks = static_cast<unsigned>(nbh * plan.nseg);
     if (nslot > 0) {
-        launch_chunk<NP, P, false, false>(p, a.softplus, blocks, a.stream);
+        if (conv) launch_chunk<NP, P, false, false, kConvForm>(p, a.softplus, blocks, a.stream);
+        else launch_chunk<NP, P, false, false, kConvNone>(p, a.softplus, blocks, a.stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t count = nbh * PN;
@@ -600,8 +696,13 @@ hipError_t launch_ssd_typed(const ScanArgs& a, const SsdPlan& plan) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.z) launch_chunk<NP, P, true, true>(p, a.softplus, blocks, a.stream);
-    else launch_chunk<NP, P, true, false>(p, a.softplus, blocks, a.stream);
+    if (a.z) {
+        if (conv) launch_chunk<NP, P, true, true, kConvForm>(p, a.softplus, blocks, a.stream);
+        else launch_chunk<NP, P, true, true, kConvNone>(p, a.softplus, blocks, a.stream);
+    } else {
+        if (conv) launch_chunk<NP, P, true, false, kConvForm>(p, a.softplus, blocks, a.stream);
+        else launch_chunk<NP, P, true, false, kConvNone>(p, a.softplus, blocks, a.stream);
+    }
     return hipGetLastError();
 }
 

@@ -224,9 +224,11 @@ def conv_scan(lib, d=None, x=FAKE * 7, cw=FAKE * 8, cb=None, cs=None, delta=FAKE
 
 def test_conv_scan_validation(lib):
     assert conv_scan(lib, x=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
-    # u = NULL: the conv output is not written (per-channel A); heads need it
-    assert conv_scan(lib, u=None, d=dims(batch=1, seqlen=64, dim=64, dstate=16, nheads=2)) == \
+    # u = NULL: the conv output is not written; fp32 scalar-A heads need it
+    assert conv_scan(lib, u=None, d=dims(batch=1, seqlen=64, dim=64, dstate=16, nheads=2, dtype=0)) == \
         _lib.MAMBA_ERR_UNSUPPORTED
+    assert conv_scan(lib, u=None, x=FAKE * 7 + 8, d=dims(batch=1, seqlen=64, dim=64, dstate=16, nheads=2)) == \
+        _lib.MAMBA_ERR_MISALIGNED                           # bf16 heads: x in 16-byte vectors
     assert conv_scan(lib, u=None, x=None) == _lib.MAMBA_ERR_INVALID_ARGUMENT
     assert conv_scan(lib, u=None, x=FAKE * 7 + 1) == _lib.MAMBA_ERR_MISALIGNED
     assert conv_scan(lib, u=None, x=FAKE * 6) == _lib.MAMBA_ERR_INVALID_ARGUMENT   # x aliases out

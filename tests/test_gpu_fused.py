@@ -50,7 +50,7 @@ CASES = [
     (1, 500, 72, 4, 0, "f32", 60.0),
     (2, 130, 64, 8, 0, "bf16", 20.0),         # a few chunks with a tail
     (3, 50, 64, 16, 0, "bf16", 9.0),          # one chunk: no carry pass
-    (1, 300, 128, 64, 2, "bf16", 70.0),       # heads: conv kernel, then the matrix-core scan
+    (1, 300, 128, 64, 2, "bf16", 70.0),       # heads: the conv inside the matrix-form passes
     (2, 200, 128, 32, 2, "f32", 50.0),
 ]
 
@@ -140,7 +140,7 @@ def test_conv_state_without_initial_state(ssm, H, N, dt):
     out_split, fin_split = ssm.selective_scan_fwd(u_split, dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"],
                                                   dev["z"], dev["delta_bias"], dev["doc_start"])
     assert torch.equal(u, u_split), "fused u differs from the conv call with the same history"
-    if H:   # the heads path runs the conv kernel, then the same scan
+    if H:   # the heads path forms u as the conv kernel does, then scans it the same way
         assert torch.equal(out, out_split), "fused out differs from the split calls"
     assert_close(to_host(out), to_host(out_split), dt, "fused vs split out")
     assert_close(to_host(fin), to_host(fin_split), dt, "fused vs split final_state")

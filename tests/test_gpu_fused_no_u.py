@@ -1,7 +1,8 @@
 """The fused conv + scan call without a u output (u = NULL): pass 1 forms the
 conv output without storing it and the output pass forms it again from x with
 the same arithmetic, so out and final_state must equal, bit for bit, those of
-the call that writes u (and match the fp64 oracle)."""
+the call that writes u (and match the fp64 oracle).  Per-channel A and bf16
+scalar-A heads (whose matrix-form passes fuse the conv the same way)."""
 
 import numpy as np
 import pytest
@@ -29,20 +30,24 @@ def fused(ssm, dev, **kw):
 
 
 CASES = [
-    # (batch, seqlen, dim, dstate, dtype, docs)
-    (2, 1000, 100, 16, "bf16", 150.0),      # ragged D, several chunks
-    (1, 500, 72, 4, "f32", 60.0),
-    (2, 333, 64, 5, "bf16", 40.0),          # N padded to 8
-    (3, 50, 64, 16, "bf16", 9.0),           # one chunk: no carry pass
-    (2, 700, 96, 12, "f32", 3.0),           # a document start every few tokens
+    # (batch, seqlen, dim, dstate, nheads, dtype, docs)
+    (2, 1000, 100, 16, 0, "bf16", 150.0),   # ragged D, several chunks
+    (1, 500, 72, 4, 0, "f32", 60.0),
+    (2, 333, 64, 5, 0, "bf16", 40.0),       # N padded to 8
+    (3, 50, 64, 16, 0, "bf16", 9.0),        # one chunk: no carry pass
+    (2, 700, 96, 12, 0, "f32", 3.0),        # a document start every few tokens
+    (1, 300, 128, 64, 2, "bf16", 70.0),     # heads of 64 channels
+    (2, 1000, 128, 32, 2, "bf16", 150.0),
+    (2, 333, 64, 16, 2, "bf16", 4.0),       # heads of 32 channels, short documents
+    (1, 64, 128, 20, 2, "bf16", 30.0),      # one 64-token chunk, N padded to 24
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
 def test_no_u_equals_u_written(ssm, case):
     torch = torch_mod()
-    Bt, L, Dm, N, dt, docs = case
-    inp = make_custom(Bt, L, Dm, N, dtype=dt, docs=docs, seed=900 + L + N)
+    Bt, L, Dm, N, H, dt, docs = case
+    inp = make_custom(Bt, L, Dm, N, nheads=H, dtype=dt, docs=docs, seed=900 + L + N)
     inp.conv_b[:] = np.linspace(-0.3, 0.3, Dm).astype(np.float32)
     print(f"[no-u] {case}", flush=True)
     dev = upload(inp)
@@ -57,13 +62,13 @@ def test_no_u_equals_u_written(ssm, case):
     assert_close(to_host(fin2), fin_ref, dt, f"no-u final_state {case}")
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_no_u_with_histories(ssm, dt):
+@pytest.mark.parametrize("H,N,dt", [(0, 16, "bf16"), (0, 16, "f32"), (2, 64, "bf16")])
+def test_no_u_with_histories(ssm, H, N, dt):
     """A conv history with and without a scan state: the output pass primes its
     conv from conv_state exactly as pass 1 does."""
     torch = torch_mod()
-    L, Dm, N = 900, 128, 16
-    inp = make_custom(2, L, Dm, N, dtype=dt, docs=200.0, seed=950)
+    L, Dm = 900, 128
+    inp = make_custom(2, L, Dm, N, nheads=H, dtype=dt, docs=200.0, seed=950)
     inp.doc_start[:, 0] = 0
     inp.doc_start[1, 0] = 1
     dev = upload(inp)
@@ -79,12 +84,13 @@ def test_no_u_with_histories(ssm, dt):
         assert torch.equal(out, out2) and torch.equal(fin, fin2), f"no-u differs with {sorted(kw)}"
 
 
-def test_no_u_workload(ssm):
-    """The 2 x 32768 x 1536, N = 16 bf16 workload in the launch configuration the
-    benchmark times."""
+@pytest.mark.parametrize("name", ["packed_32k", "heads_32k"])
+def test_no_u_workload(ssm, name):
+    """The 2 x 32768 x 1536 bf16 workloads (N = 16 per channel; 24 heads, N = 128)
+    in the launch configuration the benchmark times."""
     torch = torch_mod()
-    inp = make_inputs("packed_32k")
-    print("[no-u] packed_32k", flush=True)
+    inp = make_inputs(name)
+    print(f"[no-u] {name}", flush=True)
     dev = upload(inp)
     _, out, fin = fused(ssm, dev)
     _, out2, fin2 = fused(ssm, dev, u=None)
@@ -95,5 +101,5 @@ def test_no_u_workload(ssm):
     got_out, got_fin = to_host(out2.index_select(2, idx)), to_host(fin2.index_select(1, idx))
     del dev, out, fin, out2, fin2
     _, out_ref, fin_ref = oracle_pipeline(inp, ch)
-    assert_close(got_out, out_ref, "bf16", "packed_32k no-u out")
-    assert_close(got_fin, fin_ref, "bf16", "packed_32k no-u final_state")
+    assert_close(got_out, out_ref, "bf16", f"{name} no-u out")
+    assert_close(got_fin, fin_ref, "bf16", f"{name} no-u final_state")
