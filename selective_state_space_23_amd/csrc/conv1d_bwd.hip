@@ -37,7 +37,7 @@ template <> struct VecIO<bf16_t, 2> {
     }
     __device__ __forceinline__ static void store(void* base, int64_t off, const float (&v)[2]) {
         *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + off) =
-            static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+            pack_bf16x2(v[0], v[1]);
     }
 };
 template <> struct VecIO<float, 2> {

@@ -9,6 +9,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace mamba {
@@ -31,6 +32,73 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     __bf16 h = static_cast<__bf16>(f);
     return __builtin_bit_cast(uint16_t, h);
+}
+
+// Inclusive prefix sum over the lanes of a wave64 (lane i gets x_0 + ... + x_i),
+// in DPP moves that stay in the vector ALU (a __shfl_up ladder goes through
+// ds_bpermute and waits on LDS at each of its six steps).  Hillis-Steele inside
+// each row of 16 lanes (row_shr 1, 2, 4, 8; a lane without a source reads the
+// identity 0), then row_bcast:15 adds lane 15 of each row to the next row (rows
+// 1 and 3) and row_bcast:31 adds lane 31 to rows 2 and 3.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    auto shifted = [](float v, auto ctrl, auto row_mask) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctrl)::value,
+                                                                     decltype(row_mask)::value, 0xf, false));
+    };
+    using I = int;
+    x += shifted(x, std::integral_constant<I, 0x111>{}, std::integral_constant<I, 0xf>{});   // row_shr:1
+    x += shifted(x, std::integral_constant<I, 0x112>{}, std::integral_constant<I, 0xf>{});   // row_shr:2
+    x += shifted(x, std::integral_constant<I, 0x114>{}, std::integral_constant<I, 0xf>{});   // row_shr:4
+    x += shifted(x, std::integral_constant<I, 0x118>{}, std::integral_constant<I, 0xf>{});   // row_shr:8
+    x += shifted(x, std::integral_constant<I, 0x142>{}, std::integral_constant<I, 0xa>{});   // row_bcast:15
+    x += shifted(x, std::integral_constant<I, 0x143>{}, std::integral_constant<I, 0xc>{});   // row_bcast:31
+    return x;
+}
+
+// The same inside each row of 16 lanes only (lane i gets the sum over lanes
+// 16 (i / 16) .. i).
+__device__ __forceinline__ float row16_prefix_sum(float x) {
+    auto shifted = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    using I = int;
+    x += shifted(x, std::integral_constant<I, 0x111>{});
+    x += shifted(x, std::integral_constant<I, 0x112>{});
+    x += shifted(x, std::integral_constant<I, 0x114>{});
+    x += shifted(x, std::integral_constant<I, 0x118>{});
+    return x;
+}
+
+// Inclusive suffix sum inside each row of 16 lanes (lane i gets the sum over
+// lanes i .. 16 (i / 16) + 15): row_shl 1, 2, 4, 8.
+__device__ __forceinline__ float row16_suffix_sum(float x) {
+    auto shifted = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    using I = int;
+    x += shifted(x, std::integral_constant<I, 0x101>{});
+    x += shifted(x, std::integral_constant<I, 0x102>{});
+    x += shifted(x, std::integral_constant<I, 0x104>{});
+    x += shifted(x, std::integral_constant<I, 0x108>{});
+    return x;
+}
+
+// Lane `src`'s value of x in every lane (v_readlane: a scalar register).
+__device__ __forceinline__ float lane_value(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+}
+
+// Two floats to a packed pair of bf16 (lo in bits 0..15), rounded to nearest
+// even: one v_cvt_pk_bf16_f32 on gfx950 (two scalar conversions and a merge
+// otherwise).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Load / store one element of storage type T as float.
@@ -74,8 +142,7 @@ template <> struct VecIO<bf16_t, 8> {
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
-                   (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+            w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 };
@@ -90,8 +157,8 @@ template <> struct VecIO<bf16_t, 4> {
         v[3] = __uint_as_float(raw.y & 0xffff0000u);
     }
     __device__ __forceinline__ static void store(void* base, int64_t off, const float (&v)[4]) {
-        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        const uint32_t lo = pack_bf16x2(v[0], v[1]);
+        const uint32_t hi = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = make_uint2(lo, hi);
     }
 };

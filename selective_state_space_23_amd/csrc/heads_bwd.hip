@@ -139,18 +139,13 @@ __device__ ChunkScalars chunk_scalars(const HbParams& p, int b, int h, int64_t t
     const bool start = s.valid && ((t == 0 && p.init == nullptr) ||
                                    (p.doc_start != nullptr && p.doc_start[static_cast<int64_t>(b) * p.seqlen + t] != 0));
     // inclusive sum of dt over the 16 tokens (lanes 0..15 of the wave)
-    float S = s.dt;
-#pragma unroll
-    for (int off = 1; off < kQ; off <<= 1) {
-        const float o = __shfl_up(S, off, 64);
-        if ((lane & 15) >= off) S += o;
-    }
+    const float S = row16_prefix_sum(s.dt);
     s.S = S;
     s.cs2 = S * a_l2;
     const uint64_t m = __ballot(start) & 0xffffull;
     s.seg = __popcll(m & ((2ull << (lane & 15)) - 1ull));
     const int seg_end = __popcll(m);
-    const float cs_end = __shfl(s.cs2, 15, 64);
+    const float cs_end = lane_value(s.cs2, 15);
     s.scale = s.seg == 0 ? exp2_fast(s.cs2) : 0.0f;
     s.wexp = s.seg == seg_end ? exp2_fast(cs_end - s.cs2) : 0.0f;
     s.W = s.wexp * s.dt;
@@ -541,12 +536,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
             float dcs = rowE - colE + sSc[6 * kQ + t] * scale - W * dW;
             if (t == kQ - 1) dcs += dg * g + sumWdW;
             // A sum_{t' >= t} dcs_t'
-            float rev = dcs;
-#pragma unroll
-            for (int off = 1; off < kQ; off <<= 1) {
-                const float o = __shfl_down(rev, off, 64);
-                if (t + off < kQ) rev += o;
-            }
+            const float rev = row16_suffix_sum(dcs);
             float ddt = t1 + dW * sSc[3 * kQ + t] + A * rev;
             const bool valid = lane < kQ && t0 + t < t_seg1;
             if (p.softplus) ddt *= rcp_fast(1.0f + exp2_fast(-sPre[t] * kLog2e));

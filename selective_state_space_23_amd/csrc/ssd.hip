@@ -104,9 +104,7 @@ __device__ __forceinline__ f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
 // outstanding global load of the wave, which would stall the next chunk's
@@ -431,16 +429,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
             }
             // Token 0 starts a document unless the row continues an initial state.
             const bool reset = valid && ((tg == 0 && p.initial_state == nullptr) || pflag != 0);
-            float cs = dt * a_l2;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(cs, off);
-                if (lane >= off) cs += o;
-            }
+            const float cs = wave_prefix_sum(dt * a_l2);
             const uint64_t rmask = __ballot(reset);
             const int sg = __popcll(rmask & ((2ull << lane) - 1ull));
             const int sg_end = __popcll(rmask);
-            const float cs_end = __shfl(cs, 63);
+            const float cs_end = lane_value(cs, 63);
             sDt[lane] = dt;
             sCs[lane] = cs;
             sSeg[lane] = sg;
