@@ -51,8 +51,9 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 16;              // tokens per chunk: one MFMA tile along the tokens
-constexpr int kThreads = 256;       // 4 waves
+constexpr int kThreads = 512;       // 8 waves: two per SIMD (one 112 KB workgroup per CU)
 constexpr int kWaves = kThreads / 64;
+static_assert(kWaves == 8, "the wave roles of the main pass assume 8 waves");
 constexpr int64_t kTargetBlocks = 768;
 
 struct HbParams {
@@ -368,7 +369,10 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
     // per-lane sums carried over the chunks
     float dD_acc = 0.0f;                  // channel 16 wave + r of Y tiles (waves < kTP)
     float dA_acc = 0.0f, db_acc = 0.0f;   // wave 0, lanes < 16
-    const float Dp = (wave < kTP && p.D != nullptr) ? p.D[h * P + 16 * wave + r] : 0.0f;
+    // Waves 0 .. kTP-1 own the Y tiles of channel tile `wave`, waves kTP .. 2 kTP-1
+    // the dx tiles of channel tile wave - kTP: both need D of that tile.
+    const int ptile = wave % kTP;
+    const float Dp = (wave < 2 * kTP && p.D != nullptr) ? p.D[h * P + 16 * ptile + r] : 0.0f;
 
     const int64_t nck_seg = (t_seg1 - t_seg0 + kQ - 1) / kQ;
     for (int64_t cl = nck_seg - 1; cl >= 0; --cl) {
@@ -415,13 +419,15 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
         }
         __syncthreads();
 
-        // ---- products over the states and channels
-        if (wave == 0) {
+        // ---- products over the states and channels: C H on waves 0 .. 3, B dH on
+        //      waves 4 .. 7 (channel tiles kTP <= 4), C B^T and dY x^T on the two
+        //      waves with the least of the rest
+        if (wave == 3) {
             f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
             a = mm<NT>(sC, LN, 1, sB, 1, LN, a);                       // C B^T
 #pragma unroll
             for (int e = 0; e < 4; ++e) sCB[(4 * q + e) * LQ + r] = a[e];
-        } else if (wave == 1) {
+        } else if (wave == 7) {
             f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
             a = mm<P>(sDY, LP, 1, sX, 1, LP, a);                        // dY x^T
 #pragma unroll
@@ -432,15 +438,17 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
             a = mm<NT>(sC, LN, 1, sH + 16 * wave, LP, 1, a);            // C H
 #pragma unroll
             for (int e = 0; e < 4; ++e) sCH[(4 * q + e) * LP + 16 * wave + r] = a[e];
+        } else if (wave >= 4 && wave < 4 + kTP) {
+            const int pt = wave - 4;
             f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-            c = mm<NT>(sB, LN, 1, sdH + 16 * wave, LP, 1, c);           // B dH
+            c = mm<NT>(sB, LN, 1, sdH + 16 * pt, LP, 1, c);             // B dH
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sBdH[(4 * q + e) * LP + 16 * wave + r] = c[e];
+            for (int e = 0; e < 4; ++e) sBdH[(4 * q + e) * LP + 16 * pt + r] = c[e];
         }
         __syncthreads();
 
         // ---- the Q x Q terms (one element per thread), and the row sums of dY o (C H) and x o (B dH)
-        {
+        if (tid < kQ * kQ) {
             const int t = tid >> 4, s = tid & 15;
             const bool in = s <= t && sSeg[s] == sSeg[t];
             const float lm = in ? exp2_fast(sSc[4 * kQ + t] - sSc[4 * kQ + s]) : 0.0f;
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
             sE[t * LQ + s] = dm * m;
             sT1[t * LQ + s] = dm * cb * lm;
         }
-        if (wave >= 2) {
+        if (wave == 2 || wave == 3) {
             // wave 2: dscale_t = dY_t . (C H)_t; wave 3: dW_s = x_s . (B dH)_s
             const float* U = wave == 2 ? sDY : sX;
             const float* V = wave == 2 ? sCH : sBdH;
@@ -472,28 +480,39 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
         }
         __syncthreads();
 
-        // ---- outputs over the tokens: Y and dx tiles (channel tile = wave), dC and dB tiles (state tiles)
+        // ---- outputs over the tokens: Y tiles (waves 0 .. kTP-1: dz, dD) and dx
+        //      tiles (waves kTP .. 2 kTP-1: du) of channel tile `ptile`; dC and dB
+        //      tiles (state tiles)
         if (wave < kTP) {
-            const int pc = 16 * wave + r;
+            const int pc = 16 * ptile + r;
             f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
-            y = mm<kQ>(sM, LQ, 1, sX + 16 * wave, LP, 1, y);             // M x
-            f32x4_t dx = {0.0f, 0.0f, 0.0f, 0.0f};
-            dx = mm<kQ>(sM, 1, LQ, sDY + 16 * wave, LP, 1, dx);          // M^T dY
+            y = mm<kQ>(sM, LQ, 1, sX + 16 * ptile, LP, 1, y);            // M x
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * q + e;
                 const int64_t tg = t0 + t;
                 const float xv = sX[t * LP + pc], dyv = sDY[t * LP + pc];
                 dD_acc = __builtin_fmaf(dyv, xv, dD_acc);
+                if (p.has_z && tg < t_seg1) {
+                    const int64_t o = (static_cast<int64_t>(b) * L + tg) * p.dim + h * P + pc;
+                    const float yv = __builtin_fmaf(Dp, xv, __builtin_fmaf(sSc[1 * kQ + t], sCH[t * LP + pc], y[e]));
+                    const float zv = ld<T>(p.z, o);
+                    const float sg = rcp_fast(1.0f + exp2_fast(-zv * kLog2e));
+                    const float dsilu = sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f);
+                    Elem<T>::store(p.dz, o, ld<T>(p.dout, o) * yv * dsilu);
+                }
+            }
+        } else if (wave < 2 * kTP) {
+            const int pc = 16 * ptile + r;
+            f32x4_t dx = {0.0f, 0.0f, 0.0f, 0.0f};
+            dx = mm<kQ>(sM, 1, LQ, sDY + 16 * ptile, LP, 1, dx);         // M^T dY
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * q + e;
+                const int64_t tg = t0 + t;
                 if (tg < t_seg1) {
                     const int64_t o = (static_cast<int64_t>(b) * L + tg) * p.dim + h * P + pc;
-                    if (p.has_z) {
-                        const float yv = __builtin_fmaf(Dp, xv, __builtin_fmaf(sSc[1 * kQ + t], sCH[t * LP + pc], y[e]));
-                        const float zv = ld<T>(p.z, o);
-                        const float sg = rcp_fast(1.0f + exp2_fast(-zv * kLog2e));
-                        const float dsilu = sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f);
-                        Elem<T>::store(p.dz, o, ld<T>(p.dout, o) * yv * dsilu);
-                    }
+                    const float dyv = sDY[t * LP + pc];
                     const float du = __builtin_fmaf(Dp, dyv, __builtin_fmaf(sSc[2 * kQ + t], sBdH[t * LP + pc], dx[e]));
                     Elem<T>::store(p.du, o, du);
                 }
