@@ -34,6 +34,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load and store of the wave, which would expose the memory
+// latency at each barrier of a chunk loop (stores to drain, prefetches to land);
+// here the wave waits for its own LDS operations (lgkmcnt) and then meets the
+// others.  Global data a wave stores is never read back by another wave of the
+// same launch in these kernels.  The "memory" clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Inclusive prefix sum over the lanes of a wave64 (lane i gets x_0 + ... + x_i),
 // in DPP moves that stay in the vector ALU (a __shfl_up ladder goes through
 // ds_bpermute and waits on LDS at each of its six steps).  Hillis-Steele inside

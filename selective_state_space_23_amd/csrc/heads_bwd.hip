@@ -103,7 +103,9 @@ template <int K, int SX = 0>
 __device__ __forceinline__ f32x4_t mm(const float* X, int xi, int xk, const float* Y, int yk, int yj, f32x4_t acc,
                                       const float* sx = nullptr) {
     const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
-#pragma unroll
+    // 8 products per trip: enough loads in flight without hoisting all 2 K / 4
+    // operands into registers at once
+#pragma unroll 8
     for (int k0 = 0; k0 < K; k0 += 4) {
         float a = X[r * xi + (k0 + q) * xk];
         if constexpr (SX == 1) a *= sx[k0 + q];
@@ -176,6 +178,71 @@ struct HbLds {
     static constexpr int kFloats = oRed + kThreads;
 };
 
+// Stage one chunk's B, C rows (Q x NT) and x, dY = dout silu(z) (Q x P) into
+// LDS as fp32; tokens past the segment end read as zeros.  Every thread issues
+// all of its 16-byte loads before its first LDS store, so their latencies
+// overlap (element loads interleaved with LDS stores go one latency at a time:
+// a flat load may alias LDS, so none can move above the previous store).
+template <typename T, int NT, int P>
+__device__ __forceinline__ void stage_chunk(const HbParams& p, int b, int h, int64_t t0, int64_t t_end, float* sB,
+                                            float* sC, float* sX, float* sDY, int tid) {
+    using Lay = HbLds<NT, P>;
+    constexpr int LN = Lay::LN, LP = Lay::LP;
+    constexpr int VEC = 16 / Elem<T>::kBytes;            // elements per 16-byte load
+    constexpr int kBC = kQ * NT / VEC;                   // vectors per B or C chunk
+    constexpr int kBCit = (2 * kBC + kThreads - 1) / kThreads;
+    constexpr int kXv = kQ * P / VEC;                    // vectors per x or dout chunk
+    static_assert(kXv <= kThreads, "one x vector per thread");
+    const int64_t L = p.seqlen;
+    float bc[kBCit][VEC];
+#pragma unroll
+    for (int k = 0; k < kBCit; ++k) {
+        const int i = tid + kThreads * k;
+        if (i < 2 * kBC) {
+            const int e = (i % kBC) * VEC, t = e / NT, n = e % NT;
+            const int64_t tg = t0 + t < t_end ? t0 + t : t0;
+            VecIO<T, VEC>::load(i < kBC ? p.B : p.C, (static_cast<int64_t>(b) * L + tg) * NT + n, bc[k]);
+        }
+    }
+    float xv[VEC], dv[VEC], zv[VEC];
+    const bool xl = tid < kXv;
+    const int xe = (xl ? tid : 0) * VEC, xt = xe / P, xc = xe % P;
+    const int64_t xo = (static_cast<int64_t>(b) * L + (t0 + xt < t_end ? t0 + xt : t0)) * p.dim + h * P + xc;
+    if (xl) {
+        VecIO<T, VEC>::load(p.u, xo, xv);
+        VecIO<T, VEC>::load(p.dout, xo, dv);
+        if (p.has_z) VecIO<T, VEC>::load(p.z, xo, zv);
+    }
+#pragma unroll
+    for (int k = 0; k < kBCit; ++k) {
+        const int i = tid + kThreads * k;
+        if (i < 2 * kBC) {
+            const int e = (i % kBC) * VEC, t = e / NT, n = e % NT;
+            const bool v = t0 + t < t_end;
+            float* dst = (i < kBC ? sB : sC) + t * LN + n;
+#pragma unroll
+            for (int j = 0; j < VEC; j += 4)
+                *reinterpret_cast<float4*>(dst + j) = v ? make_float4(bc[k][j], bc[k][j + 1], bc[k][j + 2], bc[k][j + 3])
+                                                        : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+    if (xl) {
+        const bool v = t0 + xt < t_end;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            float dy = dv[j];
+            if (p.has_z) dy *= silu_f(zv[j]);
+            xv[j] = v ? xv[j] : 0.0f;
+            dv[j] = v ? dy : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; j += 4) {
+            *reinterpret_cast<float4*>(sX + xt * LP + xc + j) = make_float4(xv[j], xv[j + 1], xv[j + 2], xv[j + 3]);
+            *reinterpret_cast<float4*>(sDY + xt * LP + xc + j) = make_float4(dv[j], dv[j + 1], dv[j + 2], dv[j + 3]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 1. forward pass over one segment
 // ---------------------------------------------------------------------------
@@ -224,26 +291,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_fwd_kernel(const HbParams 
             }
         }
         if (tid == 0) p.gin[bh * p.nck + ci] = G;
-        // stage B, C, x, dY
-        for (int i = tid; i < kQ * NT; i += kThreads) {
-            const int t = i / NT, n = i % NT;
-            const int64_t tg = t0 + t;
-            const bool v = tg < t_seg1;
-            const int64_t o = (static_cast<int64_t>(b) * L + (v ? tg : t0)) * NT + n;
-            sB[t * LN + n] = v ? ld<T>(p.B, o) : 0.0f;
-            sC[t * LN + n] = v ? ld<T>(p.C, o) : 0.0f;
-        }
-        for (int i = tid; i < kQ * P; i += kThreads) {
-            const int t = i / P, c = i % P;
-            const int64_t tg = t0 + t;
-            const bool v = tg < t_seg1;
-            const int64_t o = (static_cast<int64_t>(b) * L + (v ? tg : t0)) * p.dim + h * P + c;
-            const float x = v ? ld<T>(p.u, o) : 0.0f;
-            float dy = v ? ld<T>(p.dout, o) : 0.0f;
-            if (p.has_z) dy *= silu_f(ld<T>(p.z, o));
-            sX[t * LP + c] = x;
-            sDY[t * LP + c] = dy;
-        }
+        stage_chunk<T, NT, P>(p, b, h, t0, t_seg1, sB, sC, sX, sDY, tid);
         if (wave == 0) {
             const ChunkScalars s = chunk_scalars<T>(p, b, h, t0, a_l2, dbias);
             if (lane < kQ) {
@@ -252,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_fwd_kernel(const HbParams 
                 sSc[2 * kQ + lane] = s.W;
             }
         }
-        __syncthreads();
+        lds_barrier();
         const float g = sSc[1 * kQ + kQ - 1];
         // H <- g H + (diag(W) B)^T x;  X += G C^T diag(scale) dY
 #pragma unroll
@@ -268,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_fwd_kernel(const HbParams 
             }
         }
         G *= g;
-        __syncthreads();
+        lds_barrier();
     }
     float* hs = p.hseg + (bh * p.nseg + seg) * PN;
     float* xs = p.xseg + (bh * p.nseg + seg) * PN;
@@ -363,8 +411,9 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
 
     // dH at the segment end, and D of this head's channels
     {
-        const float* src = p.xseg + (bh * p.nseg + seg) * PN;
-        for (int i = tid; i < NT * P; i += kThreads) sdH[(i / P) * LP + i % P] = src[i];
+        const float4* src = reinterpret_cast<const float4*>(p.xseg + (bh * p.nseg + seg) * PN);
+        for (int i = tid; i < NT * P / 4; i += kThreads)
+            *reinterpret_cast<float4*>(sdH + (4 * i / P) * LP + (4 * i) % P) = src[i];
     }
     // per-lane sums carried over the chunks
     float dD_acc = 0.0f;                  // channel 16 wave + r of Y tiles (waves < kTP)
@@ -378,31 +427,29 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
     for (int64_t cl = nck_seg - 1; cl >= 0; --cl) {
         const int64_t t0 = t_seg0 + cl * kQ;
         const int64_t ci = t0 / kQ;
-        // ---- stage: B, C, x, dY, the state entering the chunk, scalars
-        for (int i = tid; i < kQ * NT; i += kThreads) {
-            const int t = i / NT, n = i % NT;
-            const int64_t tg = t0 + t;
-            const bool v = tg < t_seg1;
-            const int64_t o = (static_cast<int64_t>(b) * L + (v ? tg : t0)) * NT + n;
-            sB[t * LN + n] = v ? ld<T>(p.B, o) : 0.0f;
-            sC[t * LN + n] = v ? ld<T>(p.C, o) : 0.0f;
-        }
-        for (int i = tid; i < kQ * P; i += kThreads) {
-            const int t = i / P, c = i % P;
-            const int64_t tg = t0 + t;
-            const bool v = tg < t_seg1;
-            const int64_t o = (static_cast<int64_t>(b) * L + (v ? tg : t0)) * p.dim + h * P + c;
-            const float x = v ? ld<T>(p.u, o) : 0.0f;
-            float dy = v ? ld<T>(p.dout, o) : 0.0f;
-            if (p.has_z) dy *= silu_f(ld<T>(p.z, o));
-            sX[t * LP + c] = x;
-            sDY[t * LP + c] = dy;
-        }
+        // ---- stage: the state entering the chunk (its loads first), B, C, x, dY, scalars
         {
-            const float* ckp = p.ck + (bh * p.nck + ci) * PN;
+            constexpr int kH4 = NT * P / 4;                          // float4 of the state
+            constexpr int kHv = (kH4 + kThreads - 1) / kThreads;    // per thread
+            const float4* ckp = reinterpret_cast<const float4*>(p.ck + (bh * p.nck + ci) * PN);
+            const float4* hsp = reinterpret_cast<const float4*>(hin_seg);
+            float4 c4[kHv], h4[kHv];
+#pragma unroll
+            for (int k = 0; k < kHv; ++k) {
+                const int j = tid + kThreads * k < kH4 ? tid + kThreads * k : 0;
+                c4[k] = ckp[j];
+                h4[k] = hsp[j];
+            }
+            stage_chunk<T, NT, P>(p, b, h, t0, t_seg1, sB, sC, sX, sDY, tid);
             const float gi = p.gin[bh * p.nck + ci];
-            for (int i = tid; i < NT * P; i += kThreads)
-                sH[(i / P) * LP + i % P] = __builtin_fmaf(gi, hin_seg[i], ckp[i]);
+#pragma unroll
+            for (int k = 0; k < kHv; ++k) {
+                if (tid + kThreads * k >= kH4) break;
+                const int i = 4 * (tid + kThreads * k);
+                *reinterpret_cast<float4*>(sH + (i / P) * LP + i % P) =
+                    make_float4(__builtin_fmaf(gi, h4[k].x, c4[k].x), __builtin_fmaf(gi, h4[k].y, c4[k].y),
+                                __builtin_fmaf(gi, h4[k].z, c4[k].z), __builtin_fmaf(gi, h4[k].w, c4[k].w));
+            }
         }
         if (wave == 0) {
             const ChunkScalars s = chunk_scalars<T>(p, b, h, t0, a_l2, dbias);
@@ -417,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
                 sPre[lane] = s.pre;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- products over the states and channels: C H on waves 0 .. 3, B dH on
         //      waves 4 .. 7 (channel tiles kTP <= 4), C B^T and dY x^T on the two
@@ -445,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
 #pragma unroll
             for (int e = 0; e < 4; ++e) sBdH[(4 * q + e) * LP + 16 * pt + r] = c[e];
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- the Q x Q terms (one element per thread), and the row sums of dY o (C H) and x o (B dH)
         if (tid < kQ * kQ) {
@@ -478,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
             }
             sRed[tid] = acc;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- outputs over the tokens: Y tiles (waves 0 .. kTP-1: dz, dD) and dx
         //      tiles (waves kTP .. 2 kTP-1: du) of channel tile `ptile`; dC and dB
@@ -570,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
             dA_acc += da;
             db_acc += ddelta;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- the gradient leaving the chunk start: dH <- g dH + C^T diag(scale) dY
         {
@@ -590,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // partial sums of this (row, head, segment)

@@ -106,12 +106,6 @@ __device__ __forceinline__ f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
-// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
-// outstanding global load of the wave, which would stall the next chunk's
-// prefetch at each barrier; here the wave waits for its own LDS operations
-// (lgkmcnt) and then meets the others.  The "memory" clobber keeps the compiler
-// from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Makes v a value defined here, so later uses do not wait on the load it came
 // from (a wait there would also drain every load issued after it).
