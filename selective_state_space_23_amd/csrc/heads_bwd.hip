@@ -252,12 +252,14 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_fwd_kernel(const HbParams 
     constexpr int LN = Lay::LN, LP = Lay::LP;
     constexpr int kTN = NT / 16, kTP = P / 16, kT = kTN * kTP;
     constexpr int kSt = (kT + kWaves - 1) / kWaves;
-    __shared__ float lds[Lay::kFloats];
+    // Only the staged chunk and the scalars (the main pass's layout up to its
+    // state tiles): 25 KB at N = 128, P = 64, so two workgroups fit a CU.
+    __shared__ float lds[Lay::oH + 3 * kQ];
     float* sB = lds + Lay::oB;
     float* sC = lds + Lay::oC;
     float* sX = lds + Lay::oX;
     float* sDY = lds + Lay::oDY;
-    float* sSc = lds + Lay::oSc;      // rows: 0 dt, 1 scale, 2 W
+    float* sSc = lds + Lay::oH;       // rows: 0 dt, 1 scale, 2 W
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = blockIdx.x;
     const int h = li % p.nheads, seg = (li / p.nheads) % p.nseg, b = li / (p.nheads * p.nseg);
