@@ -356,7 +356,7 @@ def main():
     ap.add_argument("--config", default="packed_32k",
                     help="workload name from workloads.CONFIGS (default: the 32K packed bf16 shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle, one core: tokens per row")
+    ap.add_argument("--cpu-tokens", type=int, default=32768, help="oracle, one core: tokens per row")
     ap.add_argument("--cpu-tokens-all", type=int, default=32768, help="oracle, all cores: tokens per row")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the device copy probe (0: skip)")
     ap.add_argument("--no-u", action="store_true",
@@ -389,8 +389,8 @@ def main():
     if not args.no_cpu_baseline and args.path in ("fused", "split"):
         cpu = cpu_baseline(inp, args.cpu_tokens, args.cpu_tokens_all)
     if not args.no_cpu_baseline and args.path == "bwd":
-        # about 15 s of one core: the heads workload (N = 128) costs 8x per token
-        cpu = cpu_baseline_bwd(inp, dout_seed=7, tokens_per_row=min(args.cpu_tokens, 1024 if inp.nheads else 4096))
+        # about 10 s of one core (the heads workload, N = 128, costs 4x per token)
+        cpu = cpu_baseline_bwd(inp, dout_seed=7, tokens_per_row=min(args.cpu_tokens, 4096 if inp.nheads else 16384))
 
     import torch
 

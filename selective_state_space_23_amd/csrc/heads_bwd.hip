@@ -426,22 +426,25 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
     const float Dp = (wave < 2 * kTP && p.D != nullptr) ? p.D[h * P + 16 * ptile + r] : 0.0f;
 
     const int64_t nck_seg = (t_seg1 - t_seg0 + kQ - 1) / kQ;
+    // The state entering each chunk is gin * (state entering the segment) + ck;
+    // the segment's part stays in registers for all its chunks.
+    constexpr int kH4 = NT * P / 4;                          // float4 of a state
+    constexpr int kHv = (kH4 + kThreads - 1) / kThreads;    // per thread
+    float4 h4[kHv];
+    {
+        const float4* hsp = reinterpret_cast<const float4*>(hin_seg);
+#pragma unroll
+        for (int k = 0; k < kHv; ++k) h4[k] = hsp[tid + kThreads * k < kH4 ? tid + kThreads * k : 0];
+    }
     for (int64_t cl = nck_seg - 1; cl >= 0; --cl) {
         const int64_t t0 = t_seg0 + cl * kQ;
         const int64_t ci = t0 / kQ;
         // ---- stage: the state entering the chunk (its loads first), B, C, x, dY, scalars
         {
-            constexpr int kH4 = NT * P / 4;                          // float4 of the state
-            constexpr int kHv = (kH4 + kThreads - 1) / kThreads;    // per thread
             const float4* ckp = reinterpret_cast<const float4*>(p.ck + (bh * p.nck + ci) * PN);
-            const float4* hsp = reinterpret_cast<const float4*>(hin_seg);
-            float4 c4[kHv], h4[kHv];
+            float4 c4[kHv];
 #pragma unroll
-            for (int k = 0; k < kHv; ++k) {
-                const int j = tid + kThreads * k < kH4 ? tid + kThreads * k : 0;
-                c4[k] = ckp[j];
-                h4[k] = hsp[j];
-            }
+            for (int k = 0; k < kHv; ++k) c4[k] = ckp[tid + kThreads * k < kH4 ? tid + kThreads * k : 0];
             stage_chunk<T, NT, P>(p, b, h, t0, t_seg1, sB, sC, sX, sDY, tid);
             const float gi = p.gin[bh * p.nck + ci];
 #pragma unroll
