@@ -48,9 +48,20 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kQ = 64;                  // tokens per chunk
-constexpr int kWaves = 8;
+#ifndef MAMBA_SSD_WAVES
+#define MAMBA_SSD_WAVES 8               // waves per workgroup: 8, or 4 (two workgroups per CU)
+#endif
+constexpr int kWaves = MAMBA_SSD_WAVES;
+static_assert(kWaves == 4 || kWaves == 8, "one or two waves per 16-token output row tile");
 constexpr int kRowW = kWaves / 4;       // waves sharing one 16-token output row tile
 constexpr int kThreads = 64 * kWaves;
+// B rows, x^T and the per-token scalars double-buffered by chunk parity (no
+// barrier between chunks), or single-buffered (a barrier at each chunk's end,
+// and an LDS footprint that lets two 4-wave workgroups share a CU).
+#ifndef MAMBA_SSD_DBUF
+#define MAMBA_SSD_DBUF (MAMBA_SSD_WAVES == 8)
+#endif
+constexpr int kBuf = MAMBA_SSD_DBUF ? 2 : 1;
 #ifndef MAMBA_SSD_TARGET_BLOCKS
 #define MAMBA_SSD_TARGET_BLOCKS 768
 #endif
@@ -149,17 +160,15 @@ struct SsdLds {
     static_assert(SN % 8 == 0 && SQ % 8 == 0 && SY % 4 == 0, "row strides of the fragment and vector accesses");
     static constexpr int kBBytes = kQ * SN * 2;
     static constexpr int kYBytes = OUTPUT ? kWaves * 16 * SY * 4 : 0;
-    // B rows, x^T and the per-token scalars are double-buffered by chunk parity:
-    // the next chunk is staged while slower waves still read the current one, so
-    // no barrier is needed between chunks.
+    // B rows, x^T and the per-token scalars: kBuf copies (chunk parity).
     static constexpr int kBRegion = kBBytes > kYBytes ? kBBytes : kYBytes;
-    static constexpr int oB = 0;                                    // 2 x B rows [s][n]; later the output tiles
-    static constexpr int oBw = oB + 2 * kBRegion;                   // dt-weighted B^T [n][s]
-    static constexpr int oXT = oBw + NP * SQ * 2;                   // 2 x x^T [p][s]
-    static constexpr int oM = oXT + 2 * P * SQ * 2;                 // M [t][s]
+    static constexpr int oB = 0;                                    // kBuf x B rows [s][n]; later the output tiles
+    static constexpr int oBw = oB + kBuf * kBRegion;                // dt-weighted B^T [n][s]
+    static constexpr int oXT = oBw + NP * SQ * 2;                   // kBuf x x^T [p][s]
+    static constexpr int oM = oXT + kBuf * P * SQ * 2;              // M [t][s]
     static constexpr int oHT = oM + (OUTPUT ? kQ * SQ * 2 : 0);     // chunk-entry state^T [p][n]
-    static constexpr int oTok = oHT + (OUTPUT ? P * SN * 2 : 0);    // 2 x per-token scalars
-    static constexpr int oCw = oTok + 2 * 5 * kQ * 4;               // fused conv: taps [P][4], bias [P]
+    static constexpr int oTok = oHT + (OUTPUT ? P * SN * 2 : 0);    // kBuf x per-token scalars
+    static constexpr int oCw = oTok + kBuf * 5 * kQ * 4;            // fused conv: taps [P][4], bias [P]
     static constexpr int kBytes = oCw + P * 5 * 4;
 };
 
@@ -237,11 +246,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
     float seg_decay = 1.0f;
 
     // This wave's part of the chunk: output row tile `wt` (tokens 16 wt ..), channels
-    // wp .. wp + kPW - 1.  x staging and the epilogue: lane -> token x_row, channels
-    // x_p0 .. x_p0 + 7 (lanes past 16 kLPR idle).
+    // wp .. wp + kPW - 1.  x staging and the epilogue: lane -> tokens x_row + kXStep r
+    // (r < kXR), channels x_p0 .. x_p0 + 7 (lanes past kXL idle).
+    constexpr int kXL = 16 * kLPR < 64 ? 16 * kLPR : 64;   // lanes that stage x rows
+    constexpr int kXR = 16 * kLPR / kXL;                    // x rows per lane
+    constexpr int kXStep = 64 / kLPR;                       // token step between a lane's rows
     const int wt = wave / kRowW;
     const int wp = (wave % kRowW) * kPW;
-    const bool x_lane = lane < 16 * kLPR;
+    const bool x_lane = lane < kXL;
     const int x_row = 16 * wt + (x_lane ? lane / kLPR : 0);
     const int x_p0 = wp + (lane % kLPR) * 8;
     float Dp[8];
@@ -261,13 +273,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
     // loads overlap the current chunk's work.  Every load is unconditional (token
     // and state indices clamped into range): rows past the segment end only ever
     // meet a zero step size, and padded states are zeroed when consumed.
-    u32x4_t pb_[kBV], pc_[kKB], px_, pz_;
+    u32x4_t pb_[kBV], pc_[kKB], px_[kXR], pz_[kXR];
     uint32_t pdelta = 0, pflag = 0;
-    // Fused conv: x of the three tokens before this lane's token (row offsets 1..3)
-    // and doc_start of the token and the two before it.
+    // Fused conv: x of the three tokens before each of this lane's tokens (row
+    // offsets 1..3) and doc_start of the token and the two before it.
     constexpr int kCH = CONV != kConvNone ? 3 : 1;
-    u32x4_t ph_[kCH];
-    uint32_t pf_[kCH];
+    u32x4_t ph_[kXR][kCH];
+    uint32_t pf_[kXR][kCH];
     // Buffer resources per row: wave-uniform base and size in SGPRs, 32-bit byte
     // offsets per lane (a row of any tensor is below 2 GiB, checked on the host).
     // A load past a resource's end returns zeros.
@@ -294,18 +306,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
 #pragma unroll
             for (int kb = 0; kb < kKB; ++kb) pc_[kb] = load16(rsC, cbase + 64 * kb);
         }
-        const int xoff = ((c0i + x_row) * p.dim + xcol) * 2;
-        px_ = load16(rsU, xoff);
-        if constexpr (CONV != kConvNone) {
-            // Rows before the row start give negative offsets: past the resource
-            // (as unsigned), so they load zeros, as do flags past the row.
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                ph_[k] = load16(rsU, xoff - (k + 1) * p.dim * 2);
-                pf_[k] = __builtin_amdgcn_raw_buffer_load_b8(rsDs, c0i + x_row - k, 0, 0);
+        for (int r = 0; r < kXR; ++r) {
+            const int xr = x_row + kXStep * r;
+            const int xoff = ((c0i + xr) * p.dim + xcol) * 2;
+            px_[r] = load16(rsU, xoff);
+            if constexpr (CONV != kConvNone) {
+                // Rows before the row start give negative offsets: past the resource
+                // (as unsigned), so they load zeros, as do flags past the row.
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    ph_[r][k] = load16(rsU, xoff - (k + 1) * p.dim * 2);
+                    pf_[r][k] = __builtin_amdgcn_raw_buffer_load_b8(rsDs, c0i + xr - k, 0, 0);
+                }
             }
+            if (OUTPUT && HAS_Z) pz_[r] = load16(rsZ, xoff);
         }
-        if (OUTPUT && HAS_Z) pz_ = load16(rsZ, xoff);
         if (wave == 0) {
             pdelta = __builtin_amdgcn_raw_buffer_load_b16(rsDl, ((c0i + lane) * p.nheads + h) * 2, 0, 0);
             pflag = __builtin_amdgcn_raw_buffer_load_b8(rsDs, c0i + lane, 0, 0);
@@ -318,7 +334,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
     if (t_seg0 < t_seg1) fetch(t_seg0);
     const u32x4_t kZero = {0u, 0u, 0u, 0u};
     for (int64_t t0 = t_seg0; t0 < t_seg1; t0 += kQ) {
-        const int par = static_cast<int>(((t0 - t_seg0) / kQ) & 1);
+        const int par = kBuf == 2 ? static_cast<int>(((t0 - t_seg0) / kQ) & 1) : 0;
         uint16_t* sB = sB0 + par * (Lay::kBRegion / 2);
         uint16_t* sXT = sXT0 + par * P * SQ;
         float* sDt = sTok0 + par * 5 * kQ;
@@ -330,59 +346,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
         // ---- 1. take the prefetched chunk: u (formed by the fused conv), B rows to
         //         LDS, u transposed to LDS, per-token scalars, this wave's C
         //         fragments, the gate
-        u32x4_t cx = px_, cz = kZero;
-        pin(cx);
-        if constexpr (CONV != kConvNone) {
-            u32x4_t hx[3];
-            uint32_t fl[3];
+        u32x4_t cx[kXR], cz[kXR];
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                hx[k] = ph_[k];
-                fl[k] = pf_[k];
-                pin(hx[k]);
-                pin(fl[k]);
-            }
-            if (p.conv_state != nullptr && t0 + x_row < 3) {
-                // the given history before token 0: (B, D, 3), oldest first
-                const uint16_t* cs = p.conv_state + (static_cast<int64_t>(b) * p.dim + h * P + x_p0) * 3;
+        for (int r = 0; r < kXR; ++r) {
+            cx[r] = px_[r];
+            cz[r] = kZero;
+            pin(cx[r]);
+        }
+        if constexpr (CONV != kConvNone) {
+#pragma unroll
+            for (int r = 0; r < kXR; ++r) {
+                const int xr = x_row + kXStep * r;
+                u32x4_t hx[3];
+                uint32_t fl[3];
 #pragma unroll
                 for (int k = 0; k < 3; ++k) {
-                    const int r = static_cast<int>(t0) + x_row - (k + 1);
-                    if (r < 0) {
+                    hx[k] = ph_[r][k];
+                    fl[k] = pf_[r][k];
+                    pin(hx[k]);
+                    pin(fl[k]);
+                }
+                if (p.conv_state != nullptr && t0 + xr < 3) {
+                    // the given history before token 0: (B, D, 3), oldest first
+                    const uint16_t* cs = p.conv_state + (static_cast<int64_t>(b) * p.dim + h * P + x_p0) * 3;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            hx[k][j] = static_cast<uint32_t>(cs[(2 * j) * 3 + 3 + r]) |
-                                       (static_cast<uint32_t>(cs[(2 * j + 1) * 3 + 3 + r]) << 16);
+                    for (int k = 0; k < 3; ++k) {
+                        const int rr = static_cast<int>(t0) + xr - (k + 1);
+                        if (rr < 0) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                hx[k][j] = static_cast<uint32_t>(cs[(2 * j) * 3 + 3 + rr]) |
+                                           (static_cast<uint32_t>(cs[(2 * j + 1) * 3 + 3 + rr]) << 16);
+                        }
                     }
                 }
-            }
-            // A document start at the token (or one or two before it) cuts the taps
-            // that reach past it: they read zero, as in the conv kernel.
-            const bool c1 = fl[0] == 0, c2 = c1 && fl[1] == 0, c3 = c2 && fl[2] == 0;
-            const float4 cb0 = *reinterpret_cast<const float4*>(sCb + x_p0);
-            const float4 cb1 = *reinterpret_cast<const float4*>(sCb + x_p0 + 4);
-            const float cbias[8] = {cb0.x, cb0.y, cb0.z, cb0.w, cb1.x, cb1.y, cb1.z, cb1.w};
-            uint32_t uo[4];
+                // A document start at the token (or one or two before it) cuts the
+                // taps that reach past it: they read zero, as in the conv kernel.
+                const bool c1 = fl[0] == 0, c2 = c1 && fl[1] == 0, c3 = c2 && fl[2] == 0;
+                const float4 cb0 = *reinterpret_cast<const float4*>(sCb + x_p0);
+                const float4 cb1 = *reinterpret_cast<const float4*>(sCb + x_p0 + 4);
+                const float cbias[8] = {cb0.x, cb0.y, cb0.z, cb0.w, cb1.x, cb1.y, cb1.z, cb1.w};
+                uint32_t uo[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float uv[2];
+                for (int j = 0; j < 4; ++j) {
+                    float uv[2];
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int e = 2 * j + q;
-                    const float4 w = *reinterpret_cast<const float4*>(sCw + (x_p0 + e) * 4);
-                    auto el = [&](uint32_t v) { return q == 0 ? lo_bf16(v) : hi_bf16(v); };
-                    const float h1 = c1 ? el(hx[0][j]) : 0.0f;
-                    const float h2 = c2 ? el(hx[1][j]) : 0.0f;
-                    const float h3 = c3 ? el(hx[2][j]) : 0.0f;
-                    float acc = __builtin_fmaf(w.w, el(cx[j]), cbias[e]);
-                    acc = __builtin_fmaf(w.z, h1, acc);
-                    acc = __builtin_fmaf(w.y, h2, acc);
-                    acc = __builtin_fmaf(w.x, h3, acc);
-                    uv[q] = silu_f(acc);
+                    for (int q = 0; q < 2; ++q) {
+                        const int e = 2 * j + q;
+                        const float4 w = *reinterpret_cast<const float4*>(sCw + (x_p0 + e) * 4);
+                        auto el = [&](uint32_t v) { return q == 0 ? lo_bf16(v) : hi_bf16(v); };
+                        const float h1 = c1 ? el(hx[0][j]) : 0.0f;
+                        const float h2 = c2 ? el(hx[1][j]) : 0.0f;
+                        const float h3 = c3 ? el(hx[2][j]) : 0.0f;
+                        float acc = __builtin_fmaf(w.w, el(cx[r][j]), cbias[e]);
+                        acc = __builtin_fmaf(w.z, h1, acc);
+                        acc = __builtin_fmaf(w.y, h2, acc);
+                        acc = __builtin_fmaf(w.x, h3, acc);
+                        uv[q] = silu_f(acc);
+                    }
+                    uo[j] = pack2(uv[0], uv[1]);
                 }
-                uo[j] = pack2(uv[0], uv[1]);
+                cx[r] = u32x4_t{uo[0], uo[1], uo[2], uo[3]};
             }
-            cx = u32x4_t{uo[0], uo[1], uo[2], uo[3]};
         }
 #pragma unroll
         for (int k = 0; k < kBV; ++k) {
@@ -401,14 +426,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
             }
         }
         if constexpr (OUTPUT && HAS_Z) {
-            cz = pz_;
-            pin(cz);
+#pragma unroll
+            for (int r = 0; r < kXR; ++r) {
+                cz[r] = pz_[r];
+                pin(cz[r]);
+            }
         }
         if (x_lane) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sXT[(x_p0 + 2 * j) * SQ + x_row] = static_cast<uint16_t>(cx[j] & 0xffffu);
-                sXT[(x_p0 + 2 * j + 1) * SQ + x_row] = static_cast<uint16_t>(cx[j] >> 16);
+            for (int r = 0; r < kXR; ++r) {
+                const int xr = x_row + kXStep * r;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sXT[(x_p0 + 2 * j) * SQ + xr] = static_cast<uint16_t>(cx[r][j] & 0xffffu);
+                    sXT[(x_p0 + 2 * j + 1) * SQ + xr] = static_cast<uint16_t>(cx[r][j] >> 16);
+                }
             }
         }
         if (wave == 0) {
@@ -548,24 +580,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAMBA_
             for (int tp = 0; tp < kTPW; ++tp)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sYw[(4 * lg + i) * SY + 16 * tp + l16] = y[tp][i];
-            const int64_t tx = t0 + x_row;
-            if (x_lane && tx < t_seg1) {
-                const float* yr = sYw + (x_row - 16 * wt) * SY + (x_p0 - wp);
-                uint32_t o[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float y0 = __builtin_fmaf(Dp[2 * j], lo_bf16(cx[j]), yr[2 * j]);
-                    float y1 = __builtin_fmaf(Dp[2 * j + 1], hi_bf16(cx[j]), yr[2 * j + 1]);
-                    if constexpr (HAS_Z) {
-                        y0 *= silu_f(lo_bf16(cz[j]));
-                        y1 *= silu_f(hi_bf16(cz[j]));
+            for (int r = 0; r < kXR; ++r) {
+                const int xr = x_row + kXStep * r;
+                const int64_t tx = t0 + xr;
+                if (x_lane && tx < t_seg1) {
+                    const float* yr = sYw + (xr - 16 * wt) * SY + (x_p0 - wp);
+                    uint32_t o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float y0 = __builtin_fmaf(Dp[2 * j], lo_bf16(cx[r][j]), yr[2 * j]);
+                        float y1 = __builtin_fmaf(Dp[2 * j + 1], hi_bf16(cx[r][j]), yr[2 * j + 1]);
+                        if constexpr (HAS_Z) {
+                            y0 *= silu_f(lo_bf16(cz[r][j]));
+                            y1 *= silu_f(hi_bf16(cz[r][j]));
+                        }
+                        o[j] = pack2(y0, y1);
                     }
-                    o[j] = pack2(y0, y1);
+                    const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
+                    *reinterpret_cast<u32x4_t*>(p.out + off) = u32x4_t{o[0], o[1], o[2], o[3]};
                 }
-                const int64_t off = (static_cast<int64_t>(b) * L + tx) * p.dim + h * P + x_p0;
-                *reinterpret_cast<u32x4_t*>(p.out + off) = u32x4_t{o[0], o[1], o[2], o[3]};
             }
         }
+        // Single-buffered: every wave is done with this chunk's B rows (and the
+        // output tiles over them), x^T and scalars before the next chunk is staged.
+        if constexpr (kBuf == 1) lds_barrier();
     }
 
 #pragma unroll
