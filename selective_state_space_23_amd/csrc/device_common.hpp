@@ -95,6 +95,24 @@ __device__ __forceinline__ float row16_suffix_sum(float x) {
     return x;
 }
 
+// Sum over aligned groups of G consecutive lanes (G = 2, 4 or 8), every lane of a
+// group getting the group's sum: DPP quad_perm swaps of neighbours and pairs,
+// then row_half_mirror (lane i of an 8-lane half-row reads lane 7 - i, in the
+// other quad).
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    static_assert(G == 2 || G == 4 || G == 8, "groups inside a DPP half-row");
+    auto moved = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    using I = int;
+    x += moved(x, std::integral_constant<I, 0xB1>{});               // quad_perm [1, 0, 3, 2]
+    if constexpr (G >= 4) x += moved(x, std::integral_constant<I, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+    if constexpr (G >= 8) x += moved(x, std::integral_constant<I, 0x141>{});  // row_half_mirror
+    return x;
+}
+
 // Lane `src`'s value of x in every lane (v_readlane: a scalar register).
 __device__ __forceinline__ float lane_value(float x, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));

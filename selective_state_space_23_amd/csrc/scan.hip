@@ -169,9 +169,16 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     __shared__ float4 smem4[kRows * kWinFloats / 4];
     float* smem = reinterpret_cast<float*>(smem4);
 
+    // Scalar-A heads: the N states of a channel share one decay per token, so
+    // LPC lanes split them (NL = 16 each) and add their parts of C . h with DPP;
+    // per-channel A keeps all N states of a channel in one lane.
+    constexpr int LPC = (HEADS && N > 16) ? N / 16 : 1;
+    constexpr int NL = N / LPC;
+    static_assert(LPC == 1 || LPC == 2 || LPC == 4 || LPC == 8, "lane groups inside a DPP row half");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int d = blockIdx.x * kScanBlock + tid;
+    const int d = (blockIdx.x * kScanBlock + tid) / LPC;      // channel
+    const int n0 = (tid % LPC) * NL;                          // this lane's first state
     const bool active = d < p.dim;
     const int dc = active ? d : p.dim - 1;          // clamped channel for loads
     const int64_t c = blockIdx.y;
@@ -217,15 +224,15 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
 
     // Chunk carry (pass 3) or zero.
     const int64_t slot_stride = static_cast<int64_t>(p.nbatch) * p.dim * N;
-    const int64_t my_slot = (b * p.dim + dc) * N;
-    float h[N];
+    const int64_t my_slot = (b * p.dim + dc) * N + n0;
+    float h[NL];
     if (OUTPUT && (c > 0 || p.initial_state != nullptr)) {
         const float* carry = c > 0 ? p.ws_P + (c - 1) * slot_stride + my_slot : p.initial_state + my_slot;
 #pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = carry[n];
+        for (int n = 0; n < NL; ++n) h[n] = carry[n];
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = 0.0f;
+        for (int n = 0; n < NL; ++n) h[n] = 0.0f;
     }
     float sum_dt = 0.0f;          // pass 1: sum of dt since the chunk start
     bool any_reset = false;       // pass 1: a document starts inside the chunk
@@ -414,10 +421,10 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             float y0 = 0.0f, y1 = 0.0f;          // two partial sums of C . h
             float a_head = 0.0f;
             if constexpr (HEADS) a_head = exp2_fast(__builtin_fmaf(dt, Al2[0], r));
-            const float4* Bq = reinterpret_cast<const float4*>(smem + (off + k) * N);
-            const float4* Cq = reinterpret_cast<const float4*>(smem + kWinFloats + (off + k) * N);
+            const float4* Bq = reinterpret_cast<const float4*>(smem + (off + k) * N + n0);
+            const float4* Cq = reinterpret_cast<const float4*>(smem + kWinFloats + (off + k) * N + n0);
 #pragma unroll
-            for (int q = 0; q < N / 4; ++q) {
+            for (int q = 0; q < NL / 4; ++q) {
                 const float4 bv = Bq[q];
                 float4 cv;
                 if constexpr (OUTPUT) cv = Cq[q];
@@ -437,7 +444,9 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
                 }
             }
             if constexpr (OUTPUT) {
-                float y = (y0 + y1) + Dd * cu[k];
+                float yp = y0 + y1;
+                if constexpr (LPC > 1) yp = lane_group_sum<LPC>(yp);   // C . h over the channel's lanes
+                float y = yp + Dd * cu[k];
                 if constexpr (HAS_Z) y *= silu_f(cz[k]);
                 if constexpr (FAST) buf_store_s<T>(uo_rs, dc * kEsz, static_cast<int>(t) * p.dim * kEsz, y);
                 else if (active && valid) buf_store<T>(uo_rs, (static_cast<int>(t) * p.dim + d) * kEsz, y);
@@ -495,14 +504,14 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
         if (p.final_state != nullptr && t_end == L) {
             float* fs = p.final_state + my_slot;
 #pragma unroll
-            for (int n = 0; n < N; ++n) fs[n] = h[n];
+            for (int n = 0; n < NL; ++n) fs[n] = h[n];
         }
     } else {
         if (c >= p.nslots) return;          // the last chunk's aggregate is never used
         float* P = p.ws_P + c * slot_stride + my_slot;
         float* H = p.ws_H + c * slot_stride + my_slot;
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
+        for (int n = 0; n < NL; ++n) {
             float al;
             if constexpr (HEADS) al = Al2[0];
             else al = Al2[n];
@@ -586,7 +595,8 @@ hipError_t launch_scan_typed(const ScanArgs& a, const ScanPlan& plan) {
     p.u_out = a.conv_x ? const_cast<void*>(a.u) : nullptr;
     p.nslots = nslots;
 
-    const unsigned gx = static_cast<unsigned>((a.dim + kScanBlock - 1) / kScanBlock);
+    constexpr int64_t LPC = (HEADS && N > 16) ? N / 16 : 1;     // lanes per channel (as in the kernel)
+    const unsigned gx = static_cast<unsigned>((a.dim * LPC + kScanBlock - 1) / kScanBlock);
     const dim3 gall(gx, static_cast<unsigned>(plan.nchunks), static_cast<unsigned>(a.batch));
     // Without a u output the conv is formed in both passes, else pass 3 reads u.
     const bool store_u = p.u_out != nullptr;
@@ -699,10 +709,14 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim) {
     return p;
 }
 
+// fp32 scalar-A heads give each channel dstate / 16 lanes (all of them for
+// fewer): the chunk plan counts those lanes as channels.
+static int64_t heads_f32_lanes(int64_t dstate) { return dstate > 16 ? dstate / 16 : 1; }
+
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int nheads, bool bf16,
                             bool dt_handoff) {
     if (nheads > 0 && bf16) return ssd_workspace_bytes(batch, seqlen, dim, dstate, nheads);
-    const ScanPlan plan = plan_scan(batch, seqlen, dim);
+    const ScanPlan plan = plan_scan(batch, seqlen, nheads > 0 ? dim * heads_f32_lanes(dstate) : dim);
     const size_t carries =
         plan.nchunks > 1
             ? static_cast<size_t>(2 * (plan.nchunks - 1)) * static_cast<size_t>(batch * dim * dstate) * sizeof(float)
@@ -714,7 +728,9 @@ size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
 }
 
 hipError_t launch_selective_scan(const ScanArgs& a) {
-    if (a.nheads > 0) return a.bf16 ? launch_ssd(a) : launch_heads_f32(a, plan_scan(a.batch, a.seqlen, a.dim));
+    if (a.nheads > 0)
+        return a.bf16 ? launch_ssd(a)
+                      : launch_heads_f32(a, plan_scan(a.batch, a.seqlen, a.dim * heads_f32_lanes(a.dstate)));
     const ScanPlan plan = plan_scan(a.batch, a.seqlen, a.dim);
     return a.bf16 ? launch_scan_dtype<bf16_t>(a, plan) : launch_scan_dtype<float>(a, plan);
 }
