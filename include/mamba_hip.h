@@ -276,9 +276,9 @@ int mamba_causal_conv1d_bwd(const void* x, const float* weight, const float* bia
  * the head's channels). */
 
 /* Bytes of device workspace mamba_selective_scan_bwd needs for `dims`.
- * Per channel: about B L D (N + 2) * 4 / 16 + B L D * 4 + B L ceil(D / 128) * 8 N
- * bytes plus the per-chunk carries and two (B, D, N) float32 arrays; 1.08 GB at
- * B = 2, L = 32768, D = 1536, N = 16.  Scalar-A heads: about B D N ceil(L / 16)
+ * Per channel: about B L D (N + 2) * 4 / 16 + B L ceil(D / 128) * 8 N bytes plus
+ * the per-chunk carries and two (B, D, N) float32 arrays; 0.68 GB at B = 2,
+ * L = 32768, D = 1536, N = 16.  Scalar-A heads: about B D N ceil(L / 16)
  * * 4 (the state entering every 16-token chunk) + 2 B H L N * 4 (per-head dB,
  * dC) bytes; 4.88 GB at B = 2, L = 32768, D = 1536, H = 24, N = 128.  States
  * padded to a compiled size (below) add their zero-padded copies. */

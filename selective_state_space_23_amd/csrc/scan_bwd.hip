@@ -17,9 +17,7 @@
 // trajectory).
 //
 // Parallel structure, on the forward's chunking of L:
-//   1. aggregate pass, one forward sweep per chunk from a zero state: stores dt
-//      (float32: the step sizes are not rounded to the I/O dtype here, since the
-//      token sums dA, dD and ddelta_bias cancel and would show that rounding),
+//   1. aggregate pass, one forward sweep per chunk from a zero state: stores
 //      a checkpoint before every 16-token block (the local state, the step-size
 //      sum since the chunk start and whether a document started since), and per
 //      chunk the local end state H_c, R_c = prod of a over the chunk (0 if a
@@ -47,9 +45,12 @@
 // wave adds its 2N per-lane values of a token across its lanes with permlane
 // swaps and DPP (no LDS), the 4 waves' sums meet in LDS, and each block writes
 // one partial per token.  The main pass reads a 16-token block's per-channel
-// inputs (dt, u, dout, z, delta) from LDS, where buffer loads that write LDS
+// inputs (u, dout, z, delta) from LDS, where buffer loads that write LDS
 // directly put them while the block after it (in time) is finishing, so the
-// memory latency is hidden without holding registers.
+// memory latency is hidden without holding registers; each block's step sizes
+// dt are formed there from delta once it has landed, in float32 (not rounded to
+// the I/O dtype: the token sums dA, dD and ddelta_bias cancel and would show
+// that rounding), with the arithmetic every pass uses.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -90,8 +91,6 @@ struct BwdKParams {
     const float* delta_bias;
     const uint8_t* doc_start;
     const void* dout;
-    const float* dt;         // (B, L, D) float32: step sizes from the aggregate pass
-    float* dt_out;           // the same array, written by the aggregate pass
     float* h_agg_P;          // [nslots][B][D][N]: R_s, then (forward carry) the state entering chunk s + 1
     float* h_agg_H;          // [nslots][B][D][N]: H_s
     float* ckpt_out;         // checkpoints, written by the aggregate pass
@@ -202,7 +201,6 @@ __device__ __forceinline__ float step_size(float delta, float bias) {
 // 1. One forward sweep of chunk blockIdx.y of row blockIdx.z from a zero state
 // (lanes are channels, N states in VGPRs, B and C of a 64-token window in LDS).
 // It yields, with one exponential per element:
-//   - dt (fp32) of every token, read by the later passes;
 //   - before every 16-token block a local checkpoint: the state reached from zero
 //     at the chunk start, the step-size sum since then (since the latest
 //     document start), and whether a document started;
@@ -238,7 +236,6 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
     const __amdgpu_buffer_rsrc_t dl_rs = make_rsrc(static_cast<const T*>(p.delta) + b * act_row, rb);
     const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, rb);
     const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, rb);
-    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(p.dt_out + b * act_row, act_row * 4);
     const T* B_row = static_cast<const T*>(p.B) + b * L * N;
     const T* C_row = static_cast<const T*>(p.C) + b * L * N;
     const uint8_t* ds_row = p.doc_start ? p.doc_start + b * L : nullptr;
@@ -296,7 +293,6 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(MAMBA_BWD_
             const bool reset = (starts >> o) & 1ull;
             const float r = reset ? -__builtin_inff() : 0.0f;
             float dt = step_size<SOFTPLUS>(dl[k], dbias);
-            buf_store_s<float>(dt_rs, dc * 4, static_cast<int>((valid ? t : t_end - 1) * p.dim * 4), dt);
             dt = valid ? dt : 0.0f;
             float dy = go[k];
             if constexpr (HAS_Z) dy *= silu_f(zz[k]);
@@ -555,10 +551,11 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
     __shared__ float sP[2][kWaves * kCk * NOUT];         // per-wave sums of a 16-token block (2 buffers)
     float* sBC = reinterpret_cast<float*>(sBC4);
     // Per-wave staging of one 16-token block's per-channel inputs, token-major:
-    // dt (fp32), then u, dout, [z], [delta] (T) of the wave's CPW channels.
+    // dt (fp32, formed in place from delta once the block has landed), then u,
+    // dout, [z], delta (T) of the wave's CPW channels.
     constexpr int CPW = 64 / G;                                          // channels per wave
     constexpr int kTsz = static_cast<int>(sizeof(T));
-    constexpr int kNArr = 2 + (HAS_Z ? 1 : 0) + (SOFTPLUS ? 1 : 0);
+    constexpr int kNArr = 3 + (HAS_Z ? 1 : 0);
     constexpr int kStgBytes = kCk * CPW * (4 + kNArr * kTsz);
     static_assert(kStgBytes % 16 == 0, "staging rows");
     __shared__ float4 sStg4[kWaves * kStgBytes / 16];
@@ -588,7 +585,6 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
     const int64_t act_row = L * p.dim;
     const int64_t rb = act_row * kEsz;
     const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(static_cast<const T*>(p.u) + b * act_row, rb);
-    const __amdgpu_buffer_rsrc_t dt_rs = make_rsrc(p.dt + b * act_row, act_row * 4);
     const __amdgpu_buffer_rsrc_t dl_rs = make_rsrc(static_cast<const T*>(p.delta) + b * act_row, rb);
     const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(static_cast<const T*>(p.dout) + b * act_row, rb);
     const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(static_cast<const T*>(HAS_Z ? p.z : p.dout) + b * act_row, rb);
@@ -657,7 +653,6 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
         const int ch = cw0 + ce < p.dim ? cw0 + ce : p.dim - 4 / esz;
         return ((lane / lpr) * p.dim + ch) * esz;
     };
-    const int voff_f = stage_voff(4);
     const int voff_t = stage_voff(kTsz);
     auto stage_arr = [&](__amdgpu_buffer_rsrc_t rs, int esz, int voff, char* dst, int64_t s0) {
         const int tpi = 64 / (CPW * esz / 4);   // token rows per load
@@ -673,9 +668,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
     };
     auto stage_block = [&](int64_t s0) {
         __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's reads of the buffer are done
-        char* q = stg;
-        stage_arr(dt_rs, 4, voff_f, q, s0);
-        q += kCk * CPW * 4;
+        char* q = stg + kCk * CPW * 4;          // the dt rows are formed from delta
         stage_arr(u_rs, kTsz, voff_t, q, s0);
         q += kCk * CPW * kTsz;
         stage_arr(do_rs, kTsz, voff_t, q, s0);
@@ -684,7 +677,7 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
             stage_arr(z_rs, kTsz, voff_t, q, s0);
             q += kCk * CPW * kTsz;
         }
-        if constexpr (SOFTPLUS) stage_arr(dl_rs, kTsz, voff_t, q, s0);
+        stage_arr(dl_rs, kTsz, voff_t, q, s0);
     };
     auto stg_val = [&](int arr, int k) -> float {          // arr 0: dt, 1: u, 2: dout, 3: z, 4: delta
         if (arr == 0) return reinterpret_cast<const float*>(stg)[k * CPW + chw];
@@ -895,6 +888,12 @@ __global__ __launch_bounds__(kBlk) __attribute__((amdgpu_waves_per_eu(kBwdWavesP
             // The block's staged inputs and checkpoint have landed.
             s_cur = s;
             __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
+            // dt of the block's tokens from the staged delta, with the aggregate
+            // pass's arithmetic (bitwise the same values); the G lanes of a
+            // channel take every G-th token.  Lanes of one wave read and write
+            // LDS in order, so the other lanes see these rows when they load them.
+            for (int k = lane % G; k < kCk; k += G)
+                reinterpret_cast<float*>(stg)[k * CPW + chw] = step_size<SOFTPLUS>(stg_val(4, k), dbias);
             // local checkpoint + exp(A * sum dt) * (state entering the chunk)
             {
                 const bool fresh = !carried_in || ck_flag != 0.0f;
@@ -1008,7 +1007,7 @@ constexpr int lanes_per_channel(int64_t n) { return n == 16 ? MAMBA_BWD_G16 : (n
 
 // Workspace layout (byte offsets, each region 256-byte aligned).
 struct BwdLayout {
-    size_t h_carry, h_agg, g_carry, p_rev, dt, ckpt, part_bc, part_w, x0, r0, total;
+    size_t h_carry, h_agg, g_carry, p_rev, ckpt, part_bc, part_w, x0, r0, total;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1025,8 +1024,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     l.h_agg = l.h_carry + carry;
     l.g_carry = l.h_agg + carry;
     l.p_rev = l.g_carry + carry;
-    l.dt = l.p_rev + carry;
-    l.ckpt = l.dt + align256(static_cast<size_t>(batch * seqlen * dim) * sizeof(float));
+    l.ckpt = l.p_rev + carry;
     l.part_bc = l.ckpt + align256(static_cast<size_t>(batch * nk * (dstate + 2) * dim) * sizeof(float));
     l.part_w = l.part_bc + align256(static_cast<size_t>(batch * seqlen * nblk * 2 * dstate) * sizeof(float));
     l.x0 = l.part_w + align256(static_cast<size_t>(batch * plan.nchunks * (dstate + 2) * dim) * sizeof(float));
@@ -1041,8 +1039,6 @@ hipError_t launch_bwd_typed(const ScanBwdArgs& a, const ScanPlan& plan, const Bw
     BwdKParams p{};
     p.u = a.u; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
     p.delta_bias = a.delta_bias; p.doc_start = a.doc_start; p.dout = a.dout;
-    p.dt = reinterpret_cast<const float*>(ws + l.dt);
-    p.dt_out = reinterpret_cast<float*>(ws + l.dt);
     p.h_agg_P = reinterpret_cast<float*>(ws + l.h_carry);
     p.h_agg_H = reinterpret_cast<float*>(ws + l.h_agg);
     p.ckpt_out = reinterpret_cast<float*>(ws + l.ckpt);
@@ -1127,7 +1123,7 @@ int64_t scan_bwd_kernel_dstate(int64_t dstate, int nheads) {
 bool scan_bwd_supported(int64_t dstate, int nheads) { return scan_bwd_kernel_dstate(dstate, nheads) != 0; }
 
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool bf16) {
-    (void)bf16;   // the step sizes are float32 for either I/O dtype
+    (void)bf16;   // the layout holds float32 carries, checkpoints and partials for either I/O dtype
     return bwd_layout(batch, seqlen, dim, dstate, plan_scan(batch, seqlen, dim)).total;
 }
 

@@ -252,8 +252,8 @@ def test_bwd_workspace_query(lib):
     n = ctypes.c_size_t(7)
     d = dims(batch=2, seqlen=32768, dim=1536, dstate=16)
     assert lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == _lib.MAMBA_OK
-    # at least the 16-token checkpoints and the step sizes
-    assert n.value >= 2 * 2048 * 1536 * 16 * 4 + 2 * 32768 * 1536 * 2
+    # at least the 16-token checkpoints (N states, the step-size sum, a flag)
+    assert n.value >= 2 * 2048 * 1536 * (16 + 2) * 4
     st = lib.mamba_selective_scan_bwd_workspace_bytes(ctypes.byref(dims(nheads=24, dstate=128, seqlen=32768)),
                                                       ctypes.byref(n))
     assert st == _lib.MAMBA_OK and n.value > 0            # scalar-A heads (heads_bwd.hip)
