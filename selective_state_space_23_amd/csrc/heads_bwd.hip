@@ -28,7 +28,7 @@
 // products (the sums dA, ddelta_bias over tens of thousands of tokens cancel
 // heavily, and bf16 operands would show there).
 //
-// Launches, on segments of the row (one workgroup of 4 waves per (row, head,
+// Launches, on segments of the row (one workgroup of 8 waves per (row, head,
 // segment)):
 //   1. forward pass: each segment from a zero state, chunk by chunk; stores the
 //      state entering every chunk (relative to the segment start) and the decay

@@ -11,23 +11,27 @@
 // Mapping ("lanes are channels").  One lane owns one channel d of one row b and
 // keeps its N states in fp32 VGPRs; the 64 lanes of a wave are 64 consecutive
 // channels, so every activation load and store of a wave is one contiguous 128 B
-// (bf16) span of a (B, L, D) row, and B_t, C_t, doc_start and the token index
-// are wave-uniform: B_t and C_t are read with scalar loads into SGPRs and used as
-// VALU operands directly, and a document start is a uniform branch.  Per element
-// the recurrence costs one v_exp_f32 and four fp32 ops (dt*A, dt*u*B, the state
-// FMA, the C*h FMA).
+// (bf16) span of a (B, L, D) row.  B_t and C_t, shared by all channels, are
+// staged per 64-token window in LDS as fp32 and read back with broadcast 16-byte
+// loads; doc_start becomes a wave-uniform bit mask per window, and a document
+// start rides in the decay's exponent (-inf).  Per element the recurrence costs
+// one v_exp_f32 and four fp32 ops (dt*A, dt*u*B, the state FMA, the C*h FMA).
+// With scalar-A heads the states of a channel share one decay per token, so
+// N / 16 consecutive lanes split them (16 each) and add their parts of C . h.
 //
 // Parallelism along L.  B * D / 64 waves are far too few to fill 256 CUs at the
 // target shapes, so L is cut into chunks and the chunks are joined with the
 // associative operator of the "Hardware-Aware Parallel Scan" section:
-//   pass 1 (aggregate): every chunk but the last runs its recurrence from a zero
-//          state and stores (P, H): P = prod of exp(dt A) over the chunk (0 if a
-//          document starts inside it), H = its end state.
+//   pass 1 (aggregate): each chunk runs its recurrence from a zero state and
+//          stores (P, H): P = prod of exp(dt A) over the chunk (0 if a document
+//          starts inside it), H = its end state (the last chunk's is never
+//          needed; the tokens before a chunk's last document start cannot reach
+//          it).  With per-channel A it also hands the step sizes dt to pass 3
+//          and, in the fused call, forms u from x (storing it when asked to).
 //   pass 2 (carry):     per (b, d, n), carry_{c+1} = P_c * carry_c + H_c.
 //   pass 3 (output):    every chunk reruns its recurrence from its carry and
 //          writes out and, for the last chunk, final_state.
-// The carries are the only intermediate data; the (B, L, D, N) state trajectory
-// is never stored.
+// The (B, L, D, N) state trajectory is never stored.
 #include <type_traits>
 
 #include "device_common.hpp"
