@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make_cotangent, make_custom, make_inputs
+from workloads import bf16_round, make_cotangent, make_custom, make_inputs
 
 from gpu_helpers import assert_close, to_dev, to_host, torch_mod, upload
 
@@ -129,3 +129,50 @@ def test_heads_bwd_workload(ssm):
     others = np.setdiff1d(np.arange(Dm), ch)
     assert float(got["du"][:, :, torch.from_numpy(others).cuda()].abs().max()) == 0.0
     assert float(got["ddelta"][:, :, [h for h in range(H) if h != hsel]].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("flags", [
+    dict(use_z=False), dict(use_D=False), dict(use_bias=False), dict(softplus=False, use_bias=False),
+    dict(use_docs=False), dict(use_z=False, use_D=False, use_bias=False),
+], ids=lambda f: ",".join(f"{k}={v}" for k, v in f.items()))
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_heads_bwd_optional_inputs(ssm, flags, dt):
+    """z, D, delta_bias, the softplus and doc_start each absent: the gradients the
+    absent inputs would have are not returned, the others match the oracle."""
+    torch = torch_mod()
+    use_z, use_D = flags.get("use_z", True), flags.get("use_D", True)
+    use_bias, softplus = flags.get("use_bias", True), flags.get("softplus", True)
+    use_docs = flags.get("use_docs", True)
+    inp = make_custom(2, 450, 128, 32, nheads=2, dtype=dt, docs=110.0, seed=1950)
+    if not softplus:
+        # delta is the step size itself: positive ones (negative steps make the
+        # decays exceed 1 and the gradient sums ill-conditioned)
+        pos = np.abs(inp.delta) * np.float32(0.5) + np.float32(0.001)
+        inp.delta[:] = bf16_round(pos) if dt == "bf16" else pos
+    dout = make_cotangent(2, 450, 128, dtype=dt, seed=1951)
+    print(f"[heads bwd] optional {flags} {dt}", flush=True)
+    dev = upload(inp)
+    got = ssm.selective_scan_bwd(to_dev(inp.x, dt), dev["delta"], dev["A"], dev["B"], dev["C"], to_dev(dout, dt),
+                                 D=dev["D"] if use_D else None, z=dev["z"] if use_z else None,
+                                 delta_bias=dev["delta_bias"] if use_bias else None,
+                                 doc_start=dev["doc_start"] if use_docs else None, delta_softplus=softplus)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(inp.x, inp.delta, inp.A, inp.B, inp.C, dout, D=inp.D if use_D else None,
+                                    z=inp.z if use_z else None, delta_bias=inp.delta_bias if use_bias else None,
+                                    delta_softplus=softplus, doc_start=inp.doc_start if use_docs else None)
+    compare(got, ref, dt, f"heads bwd {flags}")
+
+
+def test_heads_bwd_documents_at_chunk_edges(ssm):
+    """Documents starting on 16-token chunk boundaries, one token before and after
+    them, on segment boundaries, and one-token documents."""
+    inp = make_custom(2, 1100, 128, 64, nheads=2, dtype="f32", docs=None, seed=1960)
+    inp.doc_start[:] = 0
+    inp.doc_start[:, 0] = 1
+    for t in (15, 16, 17, 31, 32, 33, 47, 48, 256, 257, 511, 512, 513, 514, 1024, 1099):
+        inp.doc_start[0, t] = 1
+    for t in range(40, 1100, 53):
+        inp.doc_start[1, t] = 1
+    dout = make_cotangent(2, 1100, 128, dtype="f32", seed=1961)
+    print("[heads bwd] documents at chunk edges", flush=True)
+    compare(run(ssm, inp, dout), reference(inp, dout), "f32", "heads bwd doc edges")

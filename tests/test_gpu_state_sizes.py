@@ -153,3 +153,23 @@ def test_noalloc_padded(ssm, N):
                                    dev["delta_bias"], dev["doc_start"], final_state=fin)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin)
+
+
+@pytest.mark.parametrize("N", [128, 64])
+def test_heads_f32_lanes_per_channel(ssm, N):
+    """fp32 scalar-A heads split a channel's states over N / 16 lanes (8 at
+    N = 128) that add their parts of C . h: 8192 tokens in many chunks with packed
+    documents, sampled channels from every head against the oracle."""
+    torch = torch_mod()
+    inp = make_custom(1, 8192, 384, N, nheads=6, dtype="f32", docs=1500.0, seed=1260 + N)
+    ch = np.array([0, 63, 64, 130, 200, 257, 383])
+    print(f"[N] fp32 heads lanes N={N}", flush=True)
+    dev = upload(inp)
+    u, out, fin = ssm.conv_scan_fwd(dev["x"], dev["conv_w"], dev["conv_b"], dev["delta"], dev["A"], dev["B"],
+                                    dev["C"], dev["D"], dev["z"], dev["delta_bias"], dev["doc_start"])
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(ch).to(out.device)
+    got_out, got_fin = to_host(out.index_select(2, idx)), to_host(fin.index_select(1, idx))
+    _, out_ref, fin_ref = oracle_pipeline(inp, ch)
+    assert_close(got_out, out_ref, "f32", f"fp32 heads out N={N}")
+    assert_close(got_fin, fin_ref, "f32", f"fp32 heads final_state N={N}")
