@@ -155,10 +155,23 @@ __device__ ChunkScalars chunk_scalars(const HbParams& p, int b, int h, int64_t t
     return s;
 }
 
-// LDS layout of a workgroup (floats).  Row strides padded by 4.
+// Row padding of the LDS tiles, in floats (the [*][N] and [*][P] rows take
+// float4 stores, so their padding stays a multiple of 4).
+#ifndef MAMBA_HB_PAD_N
+#define MAMBA_HB_PAD_N 4
+#endif
+#ifndef MAMBA_HB_PAD_P
+#define MAMBA_HB_PAD_P 4
+#endif
+#ifndef MAMBA_HB_PAD_Q
+#define MAMBA_HB_PAD_Q 1
+#endif
+
+// LDS layout of a workgroup (floats).
 template <int NT, int P>
 struct HbLds {
-    static constexpr int LN = NT + 4, LP = P + 4, LQ = kQ + 1;
+    static_assert(MAMBA_HB_PAD_N % 4 == 0 && MAMBA_HB_PAD_P % 4 == 0, "float4 rows");
+    static constexpr int LN = NT + MAMBA_HB_PAD_N, LP = P + MAMBA_HB_PAD_P, LQ = kQ + MAMBA_HB_PAD_Q;
     static constexpr int oB = 0;                       // B   [Q][LN]
     static constexpr int oC = oB + kQ * LN;             // C   [Q][LN]
     static constexpr int oX = oC + kQ * LN;             // x   [Q][LP]
