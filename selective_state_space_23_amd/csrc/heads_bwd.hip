@@ -196,9 +196,13 @@ struct HbLds {
 // all of its 16-byte loads before its first LDS store, so their latencies
 // overlap (element loads interleaved with LDS stores go one latency at a time:
 // a flat load may alias LDS, so none can move above the previous store).
-template <typename T, int NT, int P>
+// `between()` runs after the loads are issued: global stores placed there do
+// not hold up the wait for these loads (a wave's loads and stores retire in
+// issue order), and have the rest of the chunk's work to drain before the next
+// chunk's loads.
+template <typename T, int NT, int P, typename Between>
 __device__ __forceinline__ void stage_chunk(const HbParams& p, int b, int h, int64_t t0, int64_t t_end, float* sB,
-                                            float* sC, float* sX, float* sDY, int tid) {
+                                            float* sC, float* sX, float* sDY, int tid, Between between) {
     using Lay = HbLds<NT, P>;
     constexpr int LN = Lay::LN, LP = Lay::LP;
     constexpr int VEC = 16 / Elem<T>::kBytes;            // elements per 16-byte load
@@ -226,6 +230,7 @@ __device__ __forceinline__ void stage_chunk(const HbParams& p, int b, int h, int
         VecIO<T, VEC>::load(p.dout, xo, dv);
         if (p.has_z) VecIO<T, VEC>::load(p.z, xo, zv);
     }
+    between();
 #pragma unroll
     for (int k = 0; k < kBCit; ++k) {
         const int i = tid + kThreads * k;
@@ -294,19 +299,22 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_fwd_kernel(const HbParams 
     const int r = lane & 15, q = lane >> 4;
     for (int64_t t0 = t_seg0; t0 < t_seg1; t0 += kQ) {
         const int64_t ci = t0 / kQ;
-        // the state entering this chunk (relative to the segment start) and its decay
-        float* ckp = p.ck + (bh * p.nck + ci) * PN;
+        // the state entering this chunk (relative to the segment start) and its
+        // decay, stored once the chunk's loads are on their way
+        auto store_entry = [&]() {
+            float* ckp = p.ck + (bh * p.nck + ci) * PN;
 #pragma unroll
-        for (int j = 0; j < kSt; ++j) {
-            const int k = wave + kWaves * j;
-            if (k < kT) {
-                const int nb = k / kTP, pb = k % kTP;
+            for (int j = 0; j < kSt; ++j) {
+                const int k = wave + kWaves * j;
+                if (k < kT) {
+                    const int nb = k / kTP, pb = k % kTP;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ckp[(16 * nb + 4 * q + e) * P + 16 * pb + r] = Hs[j][e];
+                    for (int e = 0; e < 4; ++e) ckp[(16 * nb + 4 * q + e) * P + 16 * pb + r] = Hs[j][e];
+                }
             }
-        }
-        if (tid == 0) p.gin[bh * p.nck + ci] = G;
-        stage_chunk<T, NT, P>(p, b, h, t0, t_seg1, sB, sC, sX, sDY, tid);
+            if (tid == 0) p.gin[bh * p.nck + ci] = G;
+        };
+        stage_chunk<T, NT, P>(p, b, h, t0, t_seg1, sB, sC, sX, sDY, tid, store_entry);
         if (wave == 0) {
             const ChunkScalars s = chunk_scalars<T>(p, b, h, t0, a_l2, dbias);
             if (lane < kQ) {
@@ -458,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void heads_bwd_main_kernel(const HbParams
             float4 c4[kHv];
 #pragma unroll
             for (int k = 0; k < kHv; ++k) c4[k] = ckp[tid + kThreads * k < kH4 ? tid + kThreads * k : 0];
-            stage_chunk<T, NT, P>(p, b, h, t0, t_seg1, sB, sC, sX, sDY, tid);
+            stage_chunk<T, NT, P>(p, b, h, t0, t_seg1, sB, sC, sX, sDY, tid, [] {});
             const float gi = p.gin[bh * p.nck + ci];
 #pragma unroll
             for (int k = 0; k < kHv; ++k) {
