@@ -167,8 +167,13 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
     static_assert(!(OUTPUT && CONV == kConvStoreU), "u is stored by pass 1");
     static_assert(!(HEADS && DTWS), "step sizes are handed over for per-channel A only");
     constexpr int G = kGroup;
-    constexpr int kWin = 64;                                   // tokens per staged window
     constexpr int kRows = OUTPUT ? 2 : 1;                      // B and C, or B only
+    // Tokens per staged window: 64, or 32 where 64 tokens of B and C in fp32
+    // would take over 32 KB of LDS (N = 128: 64 KB held the output pass of fp32
+    // scalar-A heads to two workgroups a CU).  A power of two up to 64: the
+    // window's document starts are one wave-wide bit mask.
+    constexpr int kWin = kRows * 64 * N * 4 > 32768 ? 32 : 64;
+    static_assert(kWin == 32 || kWin == 64, "window of at most one bit per lane");
     constexpr int kWinFloats = kWin * N;                       // one tensor's window
     __shared__ float4 smem4[kRows * kWinFloats / 4];
     float* smem = reinterpret_cast<float*>(smem4);
@@ -335,8 +340,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
         } else {
             for (int64_t w0 = t_begin; w0 < t_end; w0 += kWin) {
                 const int64_t tl = w0 + lane;
-                const bool st = tl < t_end && ((tl == 0 && p.initial_state == nullptr) ||
-                                               (ds_row != nullptr && ds_row[tl] != 0));
+                const bool st = lane < kWin && tl < t_end &&
+                                ((tl == 0 && p.initial_state == nullptr) || (ds_row != nullptr && ds_row[tl] != 0));
                 const uint64_t m = __ballot(st);
                 if (m != 0) rec_from = w0 + 63 - __builtin_clzll(m);
             }
@@ -472,7 +477,8 @@ __global__ __launch_bounds__(kScanBlock) __attribute__((amdgpu_waves_per_eu(MAMB
             const int64_t tl = w0 + lane;
             bool st = false;
             // Token 0 starts a document unless the row continues an initial state.
-            if (tl < t_end) st = (tl == 0 && p.initial_state == nullptr) || (ds_row != nullptr && ds_row[tl] != 0);
+            if (lane < kWin && tl < t_end)
+                st = (tl == 0 && p.initial_state == nullptr) || (ds_row != nullptr && ds_row[tl] != 0);
             starts = __ballot(st);
         }
         if (OUTPUT || w0 + kWin > rec_from) {    // B is read by some group of the window
