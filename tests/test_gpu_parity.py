@@ -168,6 +168,19 @@ def test_heads_documents_at_chunk_edges(ssm, dtype):
     scan_case(ssm, inp)
 
 
+def test_heads_f32_n128_window_edges(ssm):
+    """fp32 scalar-A heads at N = 128 stage B and C 32 tokens at a time in the
+    output pass: document starts on either side of those window edges and of the
+    chunk edges, a carried state, a row length that ends mid-window."""
+    inp = make_custom(2, 1331, 128, 128, nheads=2, dtype="f32", docs=None, seed=315)
+    inp.doc_start[:] = 0
+    for t in (31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 500, 1023, 1024, 1025, 1300):
+        inp.doc_start[0, t] = 1
+    inp.doc_start[1, 7::37] = 1
+    init = (0.5 * np.random.default_rng(316).standard_normal((2, 128, 128))).astype(np.float32)
+    scan_case(ssm, inp, initial_state=init, final_state=True)
+
+
 INIT_CASES = [
     # (dim, dstate, nheads, dtype): both A layouts, both dtypes, and the matrix-core form
     (96, 16, 0, "bf16"), (64, 8, 0, "f32"), (128, 32, 2, "bf16"), (128, 16, 2, "f32"), (128, 128, 2, "bf16"),
